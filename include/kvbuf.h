@@ -1,0 +1,224 @@
+/*
+ * kvbuf.h -- KVBuffer linear-attention decode for AMD Instinct MI355X (gfx950).
+ *
+ * The method (KVBuffer: IO-aware Serving for Linear Attention, Zou and Zhong,
+ * arXiv 2605.19049; pith.science page, abstract and Figures 1-3):
+ * a request's linear-attention state S (d_k x d_v per head) is not rewritten at
+ * every decoded token.  Instead the request keeps its most recent keys and
+ * values in a paged buffer; a token's output is computed from the state plus
+ * the buffered keys and values, and the buffered tokens are folded into the
+ * state in one batched update once the buffer holds m of them.  The same
+ * buffer verifies n draft tokens of speculative decoding in one call without
+ * temporary states, and serves short requests from the buffer alone, without
+ * ever creating a state.
+ *
+ * Update rules (the pages name none; these are the ones this library serves),
+ * for a token with key k, value v, log-gate g and step size beta:
+ *   KVBUF_RULE_LINEAR  S <- S + k v^T
+ *   KVBUF_RULE_GATED   S <- exp(g) S + k v^T
+ *   KVBUF_RULE_DELTA   S <- exp(g) (I - beta k k^T) S + beta k v^T
+ * and the token's output is o = S^T (scale q), read after the token's own update.
+ *
+ * Everything is asynchronous on the caller's HIP stream.  The library
+ * allocates no memory and holds no mutable global state: the caller owns every
+ * buffer below (for example as PyTorch tensors).  Argument validation happens
+ * on the host before anything is enqueued, so a call that returns an error
+ * has changed nothing.  Metadata that lives on the device (occupancy, block
+ * ids, state slots, accepted counts) is checked by the kernels: a request whose
+ * metadata is out of range is skipped entirely (no memory outside the pools is
+ * touched) and a bit is set in the optional device error word.
+ *
+ * Concurrency: calls on one stream are ordered; two calls that overlap in time
+ * (different streams) must not touch the same requests, blocks or state slots.
+ */
+#ifndef KVBUF_H
+#define KVBUF_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVBUF_ABI_VERSION 1
+
+typedef enum kvbuf_status {
+    KVBUF_OK = 0,
+    KVBUF_EINVAL = -1,       /* null pointer, negative size, inconsistent layout */
+    KVBUF_EUNSUPPORTED = -2, /* head dims / dtype / rule / mode not provided */
+    KVBUF_ECAPACITY = -3,    /* m not a multiple of block_size, buffer too small */
+    KVBUF_EHIP = -4          /* the HIP runtime refused the launch */
+} kvbuf_status;
+
+typedef enum kvbuf_rule {
+    KVBUF_RULE_LINEAR = 0,
+    KVBUF_RULE_GATED = 1,
+    KVBUF_RULE_DELTA = 2
+} kvbuf_rule;
+
+typedef enum kvbuf_dtype {
+    KVBUF_BF16 = 0,
+    KVBUF_F32 = 1
+} kvbuf_dtype;
+
+typedef enum kvbuf_flush_policy {
+    /* kvbuf_decode and kvbuf_commit fold a request's buffer into its state in
+     * the same kernel as soon as it holds m tokens. */
+    KVBUF_FLUSH_EAGER = 0,
+    /* they only append; the caller folds with kvbuf_flush. */
+    KVBUF_FLUSH_DEFERRED = 1
+} kvbuf_flush_policy;
+
+/* Bits of the device error word (kvbuf_batch.error). */
+#define KVBUF_DEVERR_BLOCK 1u    /* a block id outside [0, num_blocks) */
+#define KVBUF_DEVERR_SLOT 2u     /* a state slot >= num_state_slots, or none where one is required */
+#define KVBUF_DEVERR_OVERFLOW 4u /* occupancy < 0, or appending would exceed the buffer capacity */
+#define KVBUF_DEVERR_ACCEPT 8u   /* accepted[b] outside [0, n] */
+
+/* Shapes and policy.  Host struct, read during the call only. */
+typedef struct kvbuf_layout {
+    int32_t num_heads;       /* H */
+    int32_t d_k;             /* key/query head dim; d_k == d_v, one of 16, 64, 128 */
+    int32_t d_v;             /* value head dim */
+    int32_t m;               /* tokens folded per flush; 0 = recurrent mode (no buffer) */
+    int32_t block_size;      /* tokens per pool block; m must be a multiple of it */
+    int32_t blocks_per_req;  /* table row length; capacity = block_size * blocks_per_req >= m, <= 64 entries */
+    int32_t num_blocks;      /* blocks in the pool */
+    int32_t num_state_slots; /* slots in the state pool */
+    int32_t rule;            /* kvbuf_rule */
+    int32_t io_dtype;        /* kvbuf_dtype of q, k, v inputs and of the pool's key plane
+                                (and of its value plane for the linear and gated rules) */
+    int32_t flush;           /* kvbuf_flush_policy */
+    float scale;             /* queries are multiplied by it (1.0 = none) */
+} kvbuf_layout;
+
+/* Device memory pools (caller-owned, row-major):
+ *   state [num_state_slots][H][d_k][d_v]   fp32
+ *   key   [num_blocks][H][block_size][d_k] io_dtype
+ *   value [num_blocks][H][block_size][d_v] io_dtype for the linear and gated rules;
+ *         fp32 for the delta rule, where it holds each token's pseudo-value
+ *         u = beta (v - exp(g) S_prev^T k), so that S = exp(g) S_prev + k u^T
+ *   gate  [num_blocks][H][block_size]      fp32 log-gates (NULL for the linear rule)
+ * In recurrent mode (m = 0) only `state` is used. */
+typedef struct kvbuf_pools {
+    float* state;
+    void* key;
+    void* value;
+    float* gate;
+} kvbuf_pools;
+
+/* The batch: B requests.  All arrays are int32 in device memory, caller-owned,
+ * and updated by the library in stream order.
+ *   state_slot  [B]                  slot in the state pool; -1 = no state (the
+ *                                    request is served from its buffer alone and
+ *                                    never folds)
+ *   block_table [B][blocks_per_req]  pool block ids, in buffer order: buffer
+ *                                    position p is block_table[b][p / block_size],
+ *                                    offset p % block_size.  A fold moves the
+ *                                    m / block_size leading blocks to the back.
+ *   occupancy   [B]                  tokens buffered since the last fold
+ *   ticket      [B]                  workspace; must be all zero before the first
+ *                                    call and is left all zero by every call
+ *   error       [1] or NULL          KVBUF_DEVERR_* bits are OR-ed into it */
+typedef struct kvbuf_batch {
+    int32_t size;
+    int32_t* state_slot;
+    int32_t* block_table;
+    int32_t* occupancy;
+    int32_t* ticket;
+    int32_t* error;
+} kvbuf_batch;
+
+/*
+ * kvbuf_decode -- one decode step for every request of the batch.
+ * (pith.science page, Figure 1 caption: the state is loaded together with the
+ * buffered keys and values to compute the output; once the buffer is full the
+ * state is updated with all buffered tokens and written back to its slot.
+ * Figure 3 caption: the buffer size m = 0 case is the recurrent form.)
+ *
+ * Inputs  q, k [B][H][d_k] and v [B][H][d_v] in io_dtype; g [B][H] fp32
+ *         log-gates (rules GATED, DELTA; else NULL); beta [B][H] fp32 (DELTA;
+ *         else NULL).
+ * Output  out [B][H][d_v] fp32, o = S_t^T (scale q) with S_t the state after
+ *         this token.
+ * m > 0:  appends the token at buffer position occupancy[b] and advances the
+ *         occupancy.  A request with a state slot computes its output from the
+ *         state at its last fold plus the buffer; one without (slot -1) from
+ *         the buffer alone.  With KVBUF_FLUSH_EAGER a request with a state
+ *         whose buffer reaches m folds in the same kernel.
+ * m = 0:  recurrent: reads, updates and writes back every request's state.
+ */
+kvbuf_status kvbuf_decode(const kvbuf_layout* layout, const kvbuf_pools* pools,
+                          const kvbuf_batch* batch, const void* q, const void* k,
+                          const void* v, const float* g, const float* beta, float* out,
+                          hipStream_t stream);
+
+/*
+ * kvbuf_flush -- fold the first m buffered tokens of every request that has a
+ * state slot and at least m buffered tokens into its state, write the state
+ * back, rotate its block table and lower its occupancy by m.  Other requests
+ * are left untouched.  (Figure 1 caption, the deferred batched state update;
+ * abstract: state updates are deferred and applied in batch.)  No-op when m = 0.
+ */
+kvbuf_status kvbuf_flush(const kvbuf_layout* layout, const kvbuf_pools* pools,
+                         const kvbuf_batch* batch, hipStream_t stream);
+
+/*
+ * kvbuf_verify -- parallel verification of n draft tokens per request
+ * (Figure 2 caption: the drafts' keys and values are buffered and verified
+ * together, without a temporary state per draft).
+ * Inputs  q, k [B][n][H][d_k], v [B][n][H][d_v] (io_dtype); g, beta [B][n][H].
+ * Output  out [B][n][H][d_v] fp32: draft d attends to the state, the buffer and
+ *         drafts 0..d (causal within the drafts).
+ * The drafts are written at buffer positions occupancy .. occupancy+n-1; the
+ * occupancy does not change.  Requires m > 0 and 1 <= n <= 8.
+ */
+kvbuf_status kvbuf_verify(const kvbuf_layout* layout, const kvbuf_pools* pools,
+                          const kvbuf_batch* batch, int32_t n, const void* q,
+                          const void* k, const void* v, const float* g,
+                          const float* beta, float* out, hipStream_t stream);
+
+/*
+ * kvbuf_commit -- keep the first accepted[b] (0..n) drafts of the preceding
+ * kvbuf_verify: the occupancy advances over them; rejected drafts stay behind
+ * as dead data.  With KVBUF_FLUSH_EAGER a request with a state whose buffer
+ * reaches m folds its first m tokens in the same kernel.
+ * accepted: [B] int32, device memory.
+ */
+kvbuf_status kvbuf_commit(const kvbuf_layout* layout, const kvbuf_pools* pools,
+                          const kvbuf_batch* batch, int32_t n, const int32_t* accepted,
+                          hipStream_t stream);
+
+/*
+ * kvbuf_direct -- decode from the buffer alone for every request, whatever its
+ * state slot (abstract: for short contexts the output is computed directly
+ * from the buffered keys and values, without creating or updating a state).
+ * Same arguments as kvbuf_decode; the state pool is never read or written and
+ * no request folds.  Requires m > 0.
+ */
+kvbuf_status kvbuf_direct(const kvbuf_layout* layout, const kvbuf_pools* pools,
+                          const kvbuf_batch* batch, const void* q, const void* k,
+                          const void* v, const float* g, const float* beta, float* out,
+                          hipStream_t stream);
+
+/*
+ * kvbuf_materialize -- write every request's current effective state (its
+ * state at the last fold, or zero without a slot, with all buffered tokens
+ * applied) to states [B][H][d_k][d_v] fp32.  Reads only; pools, tables and
+ * occupancies are unchanged.  For checkpointing, migration and checks.
+ */
+kvbuf_status kvbuf_materialize(const kvbuf_layout* layout, const kvbuf_pools* pools,
+                               const kvbuf_batch* batch, float* states, hipStream_t stream);
+
+/* Static description of a status code. */
+const char* kvbuf_strerror(kvbuf_status status);
+
+/* KVBUF_ABI_VERSION of the built library. */
+int32_t kvbuf_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVBUF_H */

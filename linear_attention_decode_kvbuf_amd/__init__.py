@@ -1,0 +1,247 @@
+"""KVBuffer linear-attention decode on AMD Instinct MI355X (gfx950).
+
+Thin Python binding of ``libkvbuf.so`` (C ABI declared in ``include/kvbuf.h``).
+The functions ``kvbuf_decode``, ``kvbuf_flush``, ``kvbuf_verify``,
+``kvbuf_commit``, ``kvbuf_direct`` and ``kvbuf_materialize`` only marshal
+arguments: every step of the decode path runs in the library's HIP kernels.
+PyTorch supplies device memory and the current stream.  There is no CPU
+fallback: without the built library every call raises.
+
+``KVBuffer`` owns the pools and per-request metadata of one layer as torch
+tensors and calls the entry points with them.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvbuf.so")
+
+RULE_LINEAR, RULE_GATED, RULE_DELTA = 0, 1, 2
+BF16, F32 = 0, 1
+FLUSH_EAGER, FLUSH_DEFERRED = 0, 1
+
+OK, EINVAL, EUNSUPPORTED, ECAPACITY, EHIP = 0, -1, -2, -3, -4
+DEVERR_BLOCK, DEVERR_SLOT, DEVERR_OVERFLOW, DEVERR_ACCEPT = 1, 2, 4, 8
+
+EXPORTED = ("kvbuf_decode", "kvbuf_flush", "kvbuf_verify", "kvbuf_commit", "kvbuf_direct",
+            "kvbuf_materialize", "kvbuf_strerror", "kvbuf_abi_version")
+
+
+class Layout(ctypes.Structure):
+    _fields_ = [("num_heads", ctypes.c_int32), ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
+                ("m", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("blocks_per_req", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
+                ("num_state_slots", ctypes.c_int32), ("rule", ctypes.c_int32),
+                ("io_dtype", ctypes.c_int32), ("flush", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
+class Pools(ctypes.Structure):
+    _fields_ = [("state", ctypes.c_void_p), ("key", ctypes.c_void_p), ("value", ctypes.c_void_p),
+                ("gate", ctypes.c_void_p)]
+
+
+class Batch(ctypes.Structure):
+    _fields_ = [("size", ctypes.c_int32), ("state_slot", ctypes.c_void_p),
+                ("block_table", ctypes.c_void_p), ("occupancy", ctypes.c_void_p),
+                ("ticket", ctypes.c_void_p), ("error", ctypes.c_void_p)]
+
+
+class KVBufError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__("%s failed: %s (status %d)" % (what, strerror(status), status))
+
+
+_lib = None
+
+
+def load():
+    """The loaded library.  Raises if it has not been built (no fallback)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                "libkvbuf.so is not built (expected at %s); run "
+                "`python -m linear_attention_decode_kvbuf_amd._build` or __graft_entry__.build()" % LIB_PATH)
+        lib = ctypes.CDLL(LIB_PATH)
+        P = ctypes.c_void_p
+        L, PO, B = ctypes.POINTER(Layout), ctypes.POINTER(Pools), ctypes.POINTER(Batch)
+        i32 = ctypes.c_int32
+        lib.kvbuf_decode.argtypes = [L, PO, B, P, P, P, P, P, P, P]
+        lib.kvbuf_direct.argtypes = [L, PO, B, P, P, P, P, P, P, P]
+        lib.kvbuf_verify.argtypes = [L, PO, B, i32, P, P, P, P, P, P, P]
+        lib.kvbuf_flush.argtypes = [L, PO, B, P]
+        lib.kvbuf_commit.argtypes = [L, PO, B, i32, P, P]
+        lib.kvbuf_materialize.argtypes = [L, PO, B, P, P]
+        for name in ("kvbuf_decode", "kvbuf_direct", "kvbuf_verify", "kvbuf_flush",
+                     "kvbuf_commit", "kvbuf_materialize"):
+            getattr(lib, name).restype = ctypes.c_int
+        lib.kvbuf_strerror.argtypes = [ctypes.c_int]
+        lib.kvbuf_strerror.restype = ctypes.c_char_p
+        lib.kvbuf_abi_version.argtypes = []
+        lib.kvbuf_abi_version.restype = ctypes.c_int32
+        _lib = lib
+    return _lib
+
+
+def strerror(status: int) -> str:
+    return load().kvbuf_strerror(int(status)).decode()
+
+
+def _ptr(x):
+    """Device (or host) address of a tensor, an int address, or NULL."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status, what, raise_on_error):
+    if raise_on_error and status != OK:
+        raise KVBufError(status, what)
+    return status
+
+
+def _ref(s):
+    return None if s is None else ctypes.byref(s)
+
+
+def kvbuf_decode(layout, pools, batch, q, k, v, g, beta, out, stream=None, raise_on_error=True):
+    st = load().kvbuf_decode(_ref(layout), _ref(pools), _ref(batch), _ptr(q), _ptr(k), _ptr(v),
+                             _ptr(g), _ptr(beta), _ptr(out), _stream(stream))
+    return _check(st, "kvbuf_decode", raise_on_error)
+
+
+def kvbuf_direct(layout, pools, batch, q, k, v, g, beta, out, stream=None, raise_on_error=True):
+    st = load().kvbuf_direct(_ref(layout), _ref(pools), _ref(batch), _ptr(q), _ptr(k), _ptr(v),
+                             _ptr(g), _ptr(beta), _ptr(out), _stream(stream))
+    return _check(st, "kvbuf_direct", raise_on_error)
+
+
+def kvbuf_verify(layout, pools, batch, n, q, k, v, g, beta, out, stream=None, raise_on_error=True):
+    st = load().kvbuf_verify(_ref(layout), _ref(pools), _ref(batch), int(n), _ptr(q), _ptr(k),
+                             _ptr(v), _ptr(g), _ptr(beta), _ptr(out), _stream(stream))
+    return _check(st, "kvbuf_verify", raise_on_error)
+
+
+def kvbuf_flush(layout, pools, batch, stream=None, raise_on_error=True):
+    st = load().kvbuf_flush(_ref(layout), _ref(pools), _ref(batch), _stream(stream))
+    return _check(st, "kvbuf_flush", raise_on_error)
+
+
+def kvbuf_commit(layout, pools, batch, n, accepted, stream=None, raise_on_error=True):
+    st = load().kvbuf_commit(_ref(layout), _ref(pools), _ref(batch), int(n), _ptr(accepted),
+                             _stream(stream))
+    return _check(st, "kvbuf_commit", raise_on_error)
+
+
+def kvbuf_materialize(layout, pools, batch, states, stream=None, raise_on_error=True):
+    st = load().kvbuf_materialize(_ref(layout), _ref(pools), _ref(batch), _ptr(states),
+                                  _stream(stream))
+    return _check(st, "kvbuf_materialize", raise_on_error)
+
+
+def kvbuf_abi_version() -> int:
+    return int(load().kvbuf_abi_version())
+
+
+class KVBuffer:
+    """Pools and per-request metadata of one linear-attention layer, as torch
+    tensors on ``device``, with the library's entry points bound to them.
+
+    state      [num_state_slots, H, d_k, d_v] fp32
+    key        [num_blocks, H, block_size, d_k] io dtype
+    value      [num_blocks, H, block_size, d_v] io dtype (fp32 for the delta rule)
+    gate       [num_blocks, H, block_size] fp32 (None for the linear rule)
+    state_slot, occupancy, ticket [B] int32; block_table [B, blocks_per_req] int32
+    error      [1] int32
+    """
+
+    def __init__(self, *, batch, heads, d, m, block_size=None, blocks_per_req=2, num_blocks=None,
+                 num_state_slots=None, rule=RULE_GATED, io_dtype=BF16, flush=FLUSH_EAGER,
+                 scale=1.0, device="cuda"):
+        import torch
+
+        load()
+        self.torch = torch
+        block_size = block_size if block_size is not None else max(m, 1)
+        num_blocks = num_blocks if num_blocks is not None else batch * blocks_per_req
+        num_state_slots = num_state_slots if num_state_slots is not None else batch
+        self.layout = Layout(heads, d, d, m, block_size, blocks_per_req, num_blocks,
+                             num_state_slots, rule, io_dtype, flush, float(scale))
+        self.B, self.H, self.d, self.m = batch, heads, d, m
+        self.rule, self.io_dtype = rule, io_dtype
+        io = torch.bfloat16 if io_dtype == BF16 else torch.float32
+        self.io_torch = io
+        dev = torch.device(device)
+        self.state = torch.zeros((max(num_state_slots, 1), heads, d, d), dtype=torch.float32, device=dev)
+        if m > 0:
+            self.key = torch.zeros((num_blocks, heads, block_size, d), dtype=io, device=dev)
+            vdt = torch.float32 if rule == RULE_DELTA else io
+            self.value = torch.zeros((num_blocks, heads, block_size, d), dtype=vdt, device=dev)
+            self.gate = (torch.zeros((num_blocks, heads, block_size), dtype=torch.float32, device=dev)
+                         if rule != RULE_LINEAR else None)
+        else:
+            self.key = self.value = self.gate = None
+        i32 = torch.int32
+        self.state_slot = torch.arange(batch, dtype=i32, device=dev) % max(num_state_slots, 1)
+        self.block_table = torch.arange(batch * blocks_per_req, dtype=i32, device=dev).reshape(
+            batch, blocks_per_req) % max(num_blocks, 1)
+        self.occupancy = torch.zeros(batch, dtype=i32, device=dev)
+        self.ticket = torch.zeros(batch, dtype=i32, device=dev)
+        self.error = torch.zeros(1, dtype=i32, device=dev)
+        self._refresh()
+
+    def _refresh(self):
+        self.pools = Pools(_ptr(self.state), _ptr(self.key), _ptr(self.value), _ptr(self.gate))
+        self.batch = Batch(self.B, _ptr(self.state_slot), _ptr(self.block_table), _ptr(self.occupancy),
+                           _ptr(self.ticket), _ptr(self.error))
+
+    @property
+    def capacity(self):
+        return self.layout.block_size * self.layout.blocks_per_req
+
+    def decode(self, q, k, v, g=None, beta=None, out=None, stream=None):
+        if out is None:
+            out = self.torch.empty((self.B, self.H, self.d), dtype=self.torch.float32, device=q.device)
+        kvbuf_decode(self.layout, self.pools, self.batch, q, k, v, g, beta, out, stream)
+        return out
+
+    def direct(self, q, k, v, g=None, beta=None, out=None, stream=None):
+        if out is None:
+            out = self.torch.empty((self.B, self.H, self.d), dtype=self.torch.float32, device=q.device)
+        kvbuf_direct(self.layout, self.pools, self.batch, q, k, v, g, beta, out, stream)
+        return out
+
+    def verify(self, q, k, v, g=None, beta=None, out=None, stream=None):
+        n = q.shape[1]
+        if out is None:
+            out = self.torch.empty((self.B, n, self.H, self.d), dtype=self.torch.float32, device=q.device)
+        kvbuf_verify(self.layout, self.pools, self.batch, n, q, k, v, g, beta, out, stream)
+        return out
+
+    def commit(self, n, accepted, stream=None):
+        kvbuf_commit(self.layout, self.pools, self.batch, n, accepted, stream)
+
+    def flush(self, stream=None):
+        kvbuf_flush(self.layout, self.pools, self.batch, stream)
+
+    def materialize(self, out=None, stream=None):
+        if out is None:
+            out = self.torch.empty((self.B, self.H, self.d, self.d), dtype=self.torch.float32,
+                                   device=self.state.device)
+        kvbuf_materialize(self.layout, self.pools, self.batch, out, stream)
+        return out

@@ -1,0 +1,61 @@
+// Internal interface between the C-ABI layer (abi.cpp) and the kernel
+// launchers (*.hip).  Not installed; the public interface is include/kvbuf.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvbuf.h"
+
+namespace kvbuf {
+
+// What one launch does to each (request, head) tile.
+enum Mode : int32_t {
+    MODE_DECODE = 0,       // append one token, output, advance (maybe fold)
+    MODE_VERIFY = 1,       // append n drafts, n outputs, no advance
+    MODE_DIRECT = 2,       // decode from the buffer alone (no state, no fold)
+    MODE_FLUSH = 3,        // fold requests whose buffer holds >= m tokens
+    MODE_COMMIT = 4,       // advance by accepted[b], fold when eager and full
+    MODE_MATERIALIZE = 5,  // write the effective state elsewhere; change nothing
+    MODE_RECURRENT = 6     // m = 0: read, update and write the state every token
+};
+
+// Kernel arguments, passed by value.  Pointers are device pointers.
+struct TileParams {
+    int32_t H, block_size, blocks_per_req, m, num_blocks, num_slots;
+    int32_t n;      // tokens appended per request by this call (decode 1, verify n)
+    int32_t mode;   // Mode
+    int32_t fuse;   // eager policy: fold inside decode / commit
+    float scale;
+    float* state;
+    void* key;
+    void* value;
+    float* gate;
+    const int32_t* slot;
+    int32_t* table;
+    int32_t* occ;
+    int32_t* ticket;
+    int32_t* err;
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* g;
+    const float* beta;
+    float* out;
+    const int32_t* accepted;
+    float* states_out;
+};
+
+// Launchers: each picks the template instance for (rule, d, io dtype) and
+// enqueues one grid of B * H workgroups.  Return hipSuccess or the launch error.
+hipError_t launch_chunk(const TileParams& p, int rule, int d, int io, int batch, hipStream_t s);
+hipError_t launch_fold(const TileParams& p, int rule, int d, int io, int batch, hipStream_t s);
+hipError_t launch_recurrent(const TileParams& p, int rule, int d, int io, int batch, hipStream_t s);
+
+// Head dims with compiled kernels (d_k == d_v).
+inline bool supported_dim(int d) { return d == 16 || d == 64 || d == 128; }
+
+constexpr int kMaxDrafts = 8;
+constexpr int kMaxTableRow = 64;
+
+}  // namespace kvbuf

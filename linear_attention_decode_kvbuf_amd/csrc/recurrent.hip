@@ -1,0 +1,131 @@
+// Recurrent decode: the buffer size m = 0 case.
+//
+// KVBuffer: IO-aware Serving for Linear Attention (pith.science page,
+// abstract: existing serving systems recompute and update the whole state at
+// every decoding step; Figure 3 caption: this is the m = 0 baseline the
+// buffered kernels are normalised by).  Per token and (request, head):
+//   linear   S <- S + k v^T
+//   gated    S <- e^g S + k v^T
+//   delta    S <- e^g S + k u^T,  u = beta (v - e^g S^T k)
+//            (the same as e^g (I - beta k k^T) S + beta k v^T)
+//   output   o = S^T (scale q) with the updated S.
+// One workgroup per tile reads the 64 KiB state once and writes it once:
+// 2 |S| bytes of HBM traffic per token, which is what the buffered path avoids.
+#include "device_common.hpp"
+
+namespace kvbuf {
+namespace {
+
+template <int RULE, int DK, int DV, typename IO>
+__global__ __launch_bounds__((Geo<DK, DV>::NT)) void recurrent_kernel(TileParams P) {
+    using G = Geo<DK, DV>;
+    constexpr int NT = G::NT, TPR = G::TPR, RG = G::RG, RPT = G::RPT;
+    constexpr bool DELTA = RULE == KVBUF_RULE_DELTA;
+    constexpr bool GATED = RULE != KVBUF_RULE_LINEAR;
+
+    __shared__ float qs[DK];
+    __shared__ float kf[DK];
+    __shared__ float red[RG * DV];
+    __shared__ float sk[DELTA ? DV : 1];
+
+    const int tile = blockIdx.x;
+    const int b = tile / P.H;
+    const int h = tile - b * P.H;
+    const int tid = threadIdx.x;
+    const int rg = tid / TPR;
+    const int c0 = (tid % TPR) * 4;
+
+    const int slot = P.slot[b];
+    if (slot < 0 || slot >= P.num_slots) {
+        report(P, KVBUF_DEVERR_SLOT);
+        return;
+    }
+    float* stile = P.state + (static_cast<size_t>(slot) * P.H + h) * DK * DV;
+    f4 s[RPT];
+#pragma unroll
+    for (int j = 0; j < RPT; ++j)
+        s[j] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(stile + (rg + RG * j) * DV + c0));
+
+    const size_t in_row = static_cast<size_t>(b) * P.H + h;
+    const IO* q = static_cast<const IO*>(P.q) + in_row * DK;
+    const IO* k = static_cast<const IO*>(P.k) + in_row * DK;
+    for (int r = tid; r < DK; r += NT) {
+        qs[r] = P.scale * load1(q + r);
+        kf[r] = load1(k + r);
+    }
+    f4 x = load4(static_cast<const IO*>(P.v) + in_row * DV + c0);
+    const float gamma = GATED ? expf(P.g[in_row]) : 1.0f;
+    __syncthreads();
+
+    if constexpr (DELTA) {
+        f4 a = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < RPT; ++j) a += s[j] * kf[rg + RG * j];
+        *reinterpret_cast<f4*>(red + rg * DV + c0) = a;
+        __syncthreads();
+        for (int c = tid; c < DV; c += NT) {
+            float sum = 0.f;
+#pragma unroll
+            for (int g2 = 0; g2 < RG; ++g2) sum += red[g2 * DV + c];
+            sk[c] = sum;
+        }
+        __syncthreads();
+        const float beta = P.beta[in_row];
+        const f4 skv = *reinterpret_cast<const f4*>(sk + c0);
+        x = beta * (x - gamma * skv);
+    }
+
+    f4 o = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) {
+        const int r = rg + RG * j;
+        s[j] = gamma * s[j] + kf[r] * x;
+        o += s[j] * qs[r];
+    }
+#pragma unroll
+    for (int j = 0; j < RPT; ++j)
+        __builtin_nontemporal_store(s[j], reinterpret_cast<f4*>(stile + (rg + RG * j) * DV + c0));
+
+    *reinterpret_cast<f4*>(red + rg * DV + c0) = o;
+    __syncthreads();
+    for (int c = tid; c < DV; c += NT) {
+        float sum = 0.f;
+#pragma unroll
+        for (int g2 = 0; g2 < RG; ++g2) sum += red[g2 * DV + c];
+        P.out[in_row * DV + c] = sum;
+    }
+}
+
+template <int RULE, int D, typename IO>
+hipError_t launch_rec_t(const TileParams& p, int batch, hipStream_t s) {
+    using G = Geo<D, D>;
+    recurrent_kernel<RULE, D, D, IO><<<dim3(static_cast<unsigned>(batch) * p.H), dim3(G::NT), 0, s>>>(p);
+    return hipGetLastError();
+}
+
+template <int RULE, typename IO>
+hipError_t launch_rec_d(const TileParams& p, int d, int batch, hipStream_t s) {
+    switch (d) {
+        case 16: return launch_rec_t<RULE, 16, IO>(p, batch, s);
+        case 64: return launch_rec_t<RULE, 64, IO>(p, batch, s);
+        default: return launch_rec_t<RULE, 128, IO>(p, batch, s);
+    }
+}
+
+template <typename IO>
+hipError_t launch_rec_r(const TileParams& p, int rule, int d, int batch, hipStream_t s) {
+    switch (rule) {
+        case KVBUF_RULE_LINEAR: return launch_rec_d<KVBUF_RULE_LINEAR, IO>(p, d, batch, s);
+        case KVBUF_RULE_GATED: return launch_rec_d<KVBUF_RULE_GATED, IO>(p, d, batch, s);
+        default: return launch_rec_d<KVBUF_RULE_DELTA, IO>(p, d, batch, s);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_recurrent(const TileParams& p, int rule, int d, int io, int batch, hipStream_t s) {
+    return io == KVBUF_BF16 ? launch_rec_r<bf16_bits>(p, rule, d, batch, s)
+                            : launch_rec_r<float>(p, rule, d, batch, s);
+}
+
+}  // namespace kvbuf

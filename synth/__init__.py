@@ -24,7 +24,7 @@ from dataclasses import dataclass, replace
 import numpy as np
 
 # Stream ids of the seed tuple.
-Q, K, V, G, BETA, ACCEPT, LENGTHS, STATE, PERM = range(1, 10)
+Q, K, V, G, BETA, ACCEPT, LENGTHS, STATE, PERM, SLOTS = range(1, 11)
 
 
 def rng(workload: int, step: int, stream: int) -> np.random.Generator:
@@ -135,6 +135,11 @@ def block_permutation(w: Workload, num_blocks: int) -> np.ndarray:
     return rng(w.ident, 0, PERM).permutation(num_blocks).astype(np.int32)
 
 
+def slot_permutation(w: Workload, nslots: int) -> np.ndarray:
+    """A seeded shuffle of the state-slot ids 0 .. nslots-1."""
+    return rng(w.ident, 0, SLOTS).permutation(nslots).astype(np.int32)
+
+
 def accepted_lengths(w: Workload, call: int, B: int, n: int) -> np.ndarray:
     """Accepted-prefix lengths a ~ U{0..n}, one per request, for one verify call."""
     return rng(w.ident, call, ACCEPT).integers(0, n + 1, size=B).astype(np.int32)
@@ -143,3 +148,54 @@ def accepted_lengths(w: Workload, call: int, B: int, n: int) -> np.ndarray:
 def short_lengths(w: Workload, draw: int, count: int) -> np.ndarray:
     """Lifetimes L ~ U{1..m} of buffer-only (short-context) requests."""
     return rng(w.ident, draw, LENGTHS).integers(1, w.m + 1, size=count).astype(np.int32)
+
+
+# ---------------------------------------------------------------------------
+# Device-side generation for the full-size workloads.  Same recipe (normal
+# q, k, v; k L2-normalised in fp32 then rounded; uniform gates and step
+# sizes), drawn with torch's seeded generator on the GPU so that hundreds of
+# steps of a 256-request batch need no host round trip.  Consumers that need
+# the values on the host (the oracle) copy them back from these tensors.
+# ---------------------------------------------------------------------------
+
+def _torch_gen(device, workload: int, step: int, stream: int):
+    import torch
+
+    seed = int(np.random.SeedSequence([int(workload), int(step), int(stream)]).generate_state(1)[0])
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    return gen
+
+
+def device_token_inputs(w: Workload, step: int, device, B: int | None = None, n: int | None = None,
+                        stream_base: int = 0):
+    """As ``token_inputs`` but drawn on ``device``; q, k, v in the storage dtype
+    (bf16 or fp32), g and beta fp32 (or None)."""
+    import torch
+
+    B = w.B if B is None else B
+    lead = (B,) if n is None else (B, n)
+    s = stream_base
+    io = torch.bfloat16 if w.io == "bf16" else torch.float32
+    f = dict(device=device, dtype=torch.float32)
+    q = torch.randn(lead + (w.H, w.dk), generator=_torch_gen(device, w.ident, step, Q + s), **f)
+    k = torch.randn(lead + (w.H, w.dk), generator=_torch_gen(device, w.ident, step, K + s), **f)
+    k = k / torch.sqrt(torch.sum(k * k, dim=-1, keepdim=True))
+    v = torch.randn(lead + (w.H, w.dv), generator=_torch_gen(device, w.ident, step, V + s), **f)
+    g = beta = None
+    if w.rule >= 1:
+        g = -0.1 * torch.rand(lead + (w.H,), generator=_torch_gen(device, w.ident, step, G + s), **f)
+    if w.rule == 2:
+        beta = torch.rand(lead + (w.H,), generator=_torch_gen(device, w.ident, step, BETA + s), **f)
+    return dict(q=q.to(io), k=k.to(io), v=v.to(io), g=g, beta=beta)
+
+
+def device_initial_state(w: Workload, nslots: int, device):
+    """fp32 state pool [nslots, H, dk, dv] ~ N(0, state_std), drawn on ``device``."""
+    import torch
+
+    shape = (nslots, w.H, w.dk, w.dv)
+    if w.state_std == 0.0:
+        return torch.zeros(shape, dtype=torch.float32, device=device)
+    x = torch.randn(shape, generator=_torch_gen(device, w.ident, 0, STATE), dtype=torch.float32, device=device)
+    return x.mul_(w.state_std)

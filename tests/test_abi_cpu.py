@@ -1,0 +1,114 @@
+"""The C-ABI library on a machine without a GPU: it loads, exports every
+symbol include/kvbuf.h declares, mirrors the header's structs, and rejects
+bad arguments on the host before any HIP call (no kernel is launched here)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import linear_attention_decode_kvbuf_amd as kb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvbuf.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(kb.LIB_PATH):
+        from linear_attention_decode_kvbuf_amd import _build
+        _build.build()
+    return kb.load()
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(kvbuf_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    assert _declared() == sorted(kb.EXPORTED)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_struct_sizes_match_header(lib):
+    # kvbuf_layout: 11 int32 + 1 float; pools: 4 pointers; batch: int32 (+pad) + 5 pointers
+    assert ctypes.sizeof(kb.Layout) == 48
+    assert ctypes.sizeof(kb.Pools) == 32
+    assert ctypes.sizeof(kb.Batch) == 48
+
+
+def test_abi_version_and_strerror(lib):
+    assert kb.kvbuf_abi_version() == 1
+    for st in (kb.OK, kb.EINVAL, kb.EUNSUPPORTED, kb.ECAPACITY, kb.EHIP):
+        assert len(kb.strerror(st)) > 5
+    assert "unknown" in kb.strerror(-99)
+
+
+def _layout(**kw):
+    base = dict(num_heads=2, d_k=16, d_v=16, m=4, block_size=4, blocks_per_req=2, num_blocks=4,
+                num_state_slots=2, rule=kb.RULE_GATED, io_dtype=kb.F32, flush=kb.FLUSH_EAGER, scale=1.0)
+    base.update(kw)
+    return kb.Layout(*[base[f] for f, _ in kb.Layout._fields_])
+
+
+FAKE = 0x1000  # never dereferenced: every case below fails validation first
+POOLS = kb.Pools(FAKE, FAKE, FAKE, FAKE)
+BATCH = kb.Batch(2, FAKE, FAKE, FAKE, FAKE, None)
+
+
+def _decode(layout, pools=POOLS, batch=BATCH, q=FAKE, g=FAKE, beta=None):
+    return kb.kvbuf_decode(layout, pools, batch, q, FAKE, FAKE, g, beta, FAKE, stream=0,
+                           raise_on_error=False)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(num_heads=0), kb.EINVAL),
+    (dict(d_k=32, d_v=32), kb.EUNSUPPORTED),
+    (dict(d_k=128, d_v=64), kb.EUNSUPPORTED),
+    (dict(rule=3), kb.EUNSUPPORTED),
+    (dict(io_dtype=7), kb.EUNSUPPORTED),
+    (dict(flush=5), kb.EINVAL),
+    (dict(m=6), kb.ECAPACITY),             # not a multiple of block_size
+    (dict(m=12), kb.ECAPACITY),            # beyond capacity 8
+    (dict(blocks_per_req=65), kb.ECAPACITY),
+    (dict(m=-1), kb.EINVAL),
+    (dict(scale=float("nan")), kb.EINVAL),
+])
+def test_layout_validation(lib, kw, status):
+    assert _decode(_layout(**kw)) == status
+
+
+def test_null_arguments(lib):
+    L = _layout()
+    assert kb.kvbuf_decode(None, POOLS, BATCH, FAKE, FAKE, FAKE, FAKE, None, FAKE, 0, False) == kb.EINVAL
+    assert _decode(L, pools=kb.Pools(FAKE, None, FAKE, FAKE)) == kb.EINVAL
+    assert _decode(L, pools=kb.Pools(FAKE, FAKE, FAKE, None)) == kb.EINVAL  # gated rule needs gates
+    assert _decode(L, batch=kb.Batch(2, FAKE, None, FAKE, FAKE, None)) == kb.EINVAL
+    assert _decode(L, batch=kb.Batch(2, FAKE, FAKE, FAKE, None, None)) == kb.EINVAL  # ticket
+    assert _decode(L, batch=kb.Batch(-1, FAKE, FAKE, FAKE, FAKE, None)) == kb.EINVAL
+    assert _decode(L, q=None) == kb.EINVAL
+    assert _decode(L, g=None) == kb.EINVAL
+    assert _decode(_layout(rule=kb.RULE_DELTA), beta=None) == kb.EINVAL
+
+
+def test_mode_specific_validation(lib):
+    L = _layout()
+    v = lambda n: kb.kvbuf_verify(L, POOLS, BATCH, n, FAKE, FAKE, FAKE, FAKE, None, FAKE, 0, False)
+    assert v(0) == kb.EUNSUPPORTED
+    assert v(9) == kb.EUNSUPPORTED
+    L0 = _layout(m=0)
+    assert kb.kvbuf_verify(L0, POOLS, BATCH, 2, FAKE, FAKE, FAKE, FAKE, None, FAKE, 0, False) == kb.EUNSUPPORTED
+    assert kb.kvbuf_direct(L0, POOLS, BATCH, FAKE, FAKE, FAKE, FAKE, None, FAKE, 0, False) == kb.EUNSUPPORTED
+    assert kb.kvbuf_commit(L, POOLS, BATCH, 2, None, 0, False) == kb.EINVAL
+    assert kb.kvbuf_commit(L, POOLS, BATCH, 9, FAKE, 0, False) == kb.EUNSUPPORTED
+    assert kb.kvbuf_materialize(L, POOLS, BATCH, None, 0, False) == kb.EINVAL
+    # empty batches and m = 0 flushes enqueue nothing and succeed
+    empty = kb.Batch(0, None, None, None, None, None)
+    assert _decode(L, batch=empty) == kb.OK
+    assert kb.kvbuf_flush(L0, POOLS, BATCH, 0, False) == kb.OK

@@ -1,0 +1,308 @@
+"""GPU parity: the HIP library (called through its C ABI) against the oracle.
+
+Every test drives seeded synthetic inputs through kvbuf_* and through the
+fp64 per-token recurrence, and compares outputs at every step, stored states
+after every fold, effective states, and the bookkeeping (block tables,
+occupancies, buffered bits) exactly.  Small cases compare every tile; the
+full-size workloads compare a spread sample of (request, head) tiles.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+import linear_attention_decode_kvbuf_amd as kb
+from tests.harness import Run
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# Tiny workload: fp32, B=2 H=2 d=16 m=4, 32 steps, state from zero.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("flush", [kb.FLUSH_EAGER, kb.FLUSH_DEFERRED])
+def test_tiny_every_step(flush):
+    w = synth.workload(1)
+    _say("tiny workload", w, "flush", flush)
+    run = Run(w, flush=flush)
+    for t in range(w.steps):
+        run.decode(t)
+        if flush == kb.FLUSH_DEFERRED:
+            run.flush()
+        run.check_effective_states()
+        run.check_pool()
+    assert run.folds_checked == w.B * w.H * (w.steps // w.m)
+    _say("max out err %.2e, max state err %.2e" % (run.max_out, run.max_state))
+
+
+@pytest.mark.parametrize("rule", [0, 1, 2])
+@pytest.mark.parametrize("d,io", [(16, "f32"), (64, "bf16"), (128, "bf16"), (128, "f32")])
+@pytest.mark.parametrize("m,bs,bpr", [(4, 4, 2), (4, 2, 3), (1, 1, 3), (6, 3, 3)])
+def test_small_rules(rule, d, io, m, bs, bpr):
+    w = synth.workload(1, B=3, H=2, dk=d, dv=d, m=m, block_size=bs, blocks_per_req=bpr, steps=13,
+                       rule=rule, io=io, state_std=0.02)
+    _say("small", w)
+    run = Run(w)
+    for t in range(w.steps):
+        run.decode(t)
+    run.check_effective_states()
+    run.check_pool()
+    run.check_bookkeeping()
+
+
+@pytest.mark.parametrize("rule", [0, 1, 2])
+def test_deferred_flush_with_tail(rule):
+    """Decode past m before folding: the fold takes the first m tokens and
+    leaves the rest buffered in the rotated table."""
+    w = synth.workload(1, B=2, H=3, dk=64, dv=64, m=4, block_size=2, blocks_per_req=5, steps=14,
+                       rule=rule, io="bf16", state_std=0.02)
+    run = Run(w, flush=kb.FLUSH_DEFERRED)
+    t = 0
+    for burst in (6, 5, 3):
+        for _ in range(burst):
+            run.decode(t)
+            t += 1
+        run.check_effective_states()
+        run.flush()
+        run.check_effective_states()
+        run.check_pool()
+    run.check_bookkeeping()
+
+
+@pytest.mark.parametrize("rule", [0, 1, 2])
+def test_recurrent_m0(rule):
+    w = synth.workload(1, B=3, H=4, dk=128, dv=128, m=0, block_size=1, blocks_per_req=1, steps=9,
+                       rule=rule, io="bf16", state_std=0.02)
+    run = Run(w)
+    for t in range(w.steps):
+        run.decode(t)
+    st = run.kv.state.detach()
+    for j, (b, h) in enumerate(run.sample):
+        gpu = st[run.slots[b], h].double().cpu().numpy()
+        ref = run.S[j]
+        assert np.max(np.abs(gpu - ref)) / np.max(np.abs(ref)) <= 1e-5
+
+
+@pytest.mark.parametrize("rule", [0, 1, 2])
+@pytest.mark.parametrize("n", [1, 3, 8])
+def test_verify_commit_small(rule, n):
+    w = synth.workload(1, B=4, H=2, dk=64, dv=64, m=4, block_size=4, blocks_per_req=4, steps=6,
+                       rule=rule, io="bf16", state_std=0.02)
+    run = Run(w)
+    t = 0
+    for call in range(6):
+        run.decode(t)
+        t += 1
+        acc = synth.accepted_lengths(w, call, w.B, n)
+        run.verify_commit(call, n, acc)
+        run.check_effective_states()
+        run.check_pool()
+        run.check_bookkeeping()
+
+
+@pytest.mark.parametrize("rule", [0, 1, 2])
+def test_staggered_occupancies(rule):
+    """Commits of different lengths desynchronise the requests' occupancies,
+    so one decode launch serves requests at every buffer position and folds
+    some of them."""
+    w = synth.workload(1, B=8, H=2, dk=128, dv=128, m=8, block_size=4, blocks_per_req=4, steps=20,
+                       rule=rule, io="bf16", state_std=0.02)
+    run = Run(w)
+    run.verify_commit(0, 7, np.arange(w.B, dtype=np.int32) % 8)
+    for t in range(w.steps):
+        run.decode(t)
+    run.check_effective_states()
+    run.check_pool()
+
+
+@pytest.mark.parametrize("rule", [0, 1, 2])
+def test_direct_and_promotion(rule):
+    """Buffer-only decode equals the recurrence from a zero state; giving the
+    request a zeroed state slot afterwards and folding creates its state."""
+    w = synth.workload(1, B=3, H=2, dk=128, dv=128, m=8, block_size=8, blocks_per_req=2, steps=11,
+                       rule=rule, io="bf16", state_std=0.02)
+    run = Run(w, stateless=np.ones(3, bool), flush=kb.FLUSH_DEFERRED)
+    for t in range(w.steps):
+        run.decode(t, direct=True)
+    run.check_effective_states()
+    # promotion: a zeroed slot per request, then a fold of the first m tokens
+    slots = np.array([0, 1, 2], np.int32)
+    run.kv.state[:3].zero_()
+    run.kv.state_slot.copy_(torch.from_numpy(slots))
+    run.slots = slots
+    for b in range(w.B):
+        run.model.requests[b].has_state = True
+    run.flush()
+    run.check_effective_states()
+    for t in range(w.steps, w.steps + 5):
+        run.decode(t)
+    run.check_effective_states()
+
+
+def test_mixed_stateful_and_stateless_one_launch():
+    w = synth.workload(1, B=6, H=2, dk=128, dv=128, m=4, block_size=4, blocks_per_req=3, steps=10,
+                       rule=2, io="bf16", state_std=0.02)
+    run = Run(w, stateless=np.array([0, 1, 0, 1, 1, 0], bool))
+    for t in range(w.steps):
+        run.decode(t)
+    run.check_effective_states()
+    run.check_pool()
+
+
+# ---------------------------------------------------------------------------
+# Edge cases and device-side checks.
+# ---------------------------------------------------------------------------
+
+def test_empty_batch_is_a_no_op():
+    kv = kb.KVBuffer(batch=2, heads=2, d=16, m=4, rule=kb.RULE_GATED, io_dtype=kb.F32)
+    empty = kb.Batch(0, None, None, None, None, None)
+    z = torch.zeros(1, device="cuda")
+    assert kb.kvbuf_decode(kv.layout, kv.pools, empty, z, z, z, z, None, z) == kb.OK
+    assert kb.kvbuf_flush(kv.layout, kv.pools, empty) == kb.OK
+
+
+def _errors(kv):
+    torch.cuda.synchronize()
+    return int(kv.error.item())
+
+
+def test_device_errors_skip_the_request():
+    w = synth.workload(1, B=3, H=2, dk=16, dv=16, m=4, block_size=4, blocks_per_req=2, steps=1,
+                       rule=1, io="f32", state_std=0.02)
+    run = Run(w)
+    kv = run.kv
+    before_state = kv.state.clone()
+    # request 1: a block id outside the pool
+    kv.block_table[1, 0] = 10_000
+    inp = run.inputs(0)
+    out = kv.decode(inp["q"], inp["k"], inp["v"], inp["g"])
+    assert _errors(kv) & kb.DEVERR_BLOCK
+    assert kv.occupancy.cpu().tolist() == [1, 0, 1]  # request 1 was skipped
+    kv.error.zero_()
+    # request 0: occupancy at capacity -> overflow, nothing written
+    kv.occupancy[0] = run.kv.capacity
+    kv.block_table[1, 0] = run.model.requests[1].table[0]
+    kv.decode(inp["q"], inp["k"], inp["v"], inp["g"], out=out)
+    assert _errors(kv) & kb.DEVERR_OVERFLOW
+    assert kv.occupancy.cpu().tolist() == [run.kv.capacity, 1, 2]
+    kv.error.zero_()
+    # accepted count beyond n
+    kv.occupancy[0] = 0
+    acc = torch.tensor([0, 5, 0], dtype=torch.int32, device="cuda")
+    kv.commit(2, acc)
+    assert _errors(kv) & kb.DEVERR_ACCEPT
+    # state slot outside the pool (recurrent mode)
+    kv0 = kb.KVBuffer(batch=2, heads=2, d=16, m=0, rule=kb.RULE_LINEAR, io_dtype=kb.F32, num_state_slots=2)
+    kv0.state_slot[1] = 7
+    z = torch.zeros((2, 2, 16), device="cuda")
+    kv0.decode(z, z, z)
+    assert _errors(kv0) & kb.DEVERR_SLOT
+    assert int(kv.ticket.abs().sum().item()) == 0
+    assert torch.equal(kv.state, before_state)
+
+
+def test_validation_errors_touch_nothing():
+    kv = kb.KVBuffer(batch=2, heads=2, d=16, m=4, rule=kb.RULE_GATED, io_dtype=kb.F32)
+    z = torch.zeros((2, 2, 16), device="cuda")
+    g = torch.zeros((2, 2), device="cuda")
+    assert kb.kvbuf_decode(kv.layout, kv.pools, kv.batch, z, z, z, None, None, z,
+                           raise_on_error=False) == kb.EINVAL  # gated rule needs g
+    assert kb.kvbuf_verify(kv.layout, kv.pools, kv.batch, 9, z, z, z, g, None, z,
+                           raise_on_error=False) == kb.EUNSUPPORTED
+    torch.cuda.synchronize()
+    assert kv.occupancy.cpu().tolist() == [0, 0]
+    kb.kvbuf_decode(kv.layout, kv.pools, kv.batch, z, z, z, g, None, z)
+    torch.cuda.synchronize()
+    assert kv.occupancy.cpu().tolist() == [1, 1]
+
+
+# ---------------------------------------------------------------------------
+# Full-size workloads, sampled tiles, in the launch configuration the
+# benchmark times (eager fold inside the decode kernel).
+# ---------------------------------------------------------------------------
+
+def test_workload2_ungated_batched():
+    w = synth.workload(2)
+    _say("workload 2", w)
+    run = Run(w)
+    for t in range(w.steps):
+        run.decode(t)
+    run.check_effective_states()
+    run.check_pool()
+    _say("max out err %.2e, max state err %.2e, folds checked %d" % (run.max_out, run.max_state, run.folds_checked))
+    assert run.folds_checked == len(run.sample) * (w.steps // w.m)
+
+
+def test_workload3_gated_m8_full():
+    w = synth.workload(3)
+    _say("workload 3", w)
+    run = Run(w)
+    for t in range(w.steps):
+        run.decode(t)
+    run.check_effective_states()
+    run.check_pool()
+    _say("max out err %.2e, max state err %.2e, folds checked %d" % (run.max_out, run.max_state, run.folds_checked))
+
+
+@pytest.mark.parametrize("m", [0, 4, 16, 32])
+def test_workload3_gated_sweep(m):
+    steps = 2 * max(m, 8)
+    w = synth.workload(3, m=m, block_size=max(m, 1), blocks_per_req=2 if m else 1, steps=steps)
+    _say("workload 3 m=%d" % m, w)
+    run = Run(w)
+    for t in range(w.steps):
+        run.decode(t)
+    if m:
+        run.check_effective_states()
+        run.check_pool()
+    _say("max out err %.2e, max state err %.2e" % (run.max_out, run.max_state))
+
+
+@pytest.mark.parametrize("n", [1, 2, 4, 8])
+def test_workload4_verify_commit(n):
+    w = synth.workload(4)
+    _say("workload 4 n=%d" % n, w)
+    run = Run(w)
+    t = 0
+    for call in range(12):
+        run.decode(t)
+        t += 1
+        acc = synth.accepted_lengths(w, call + 1000 * n, w.B, n)
+        run.verify_commit(call, n, acc)
+    run.check_effective_states()
+    run.check_pool()
+    _say("max out err %.2e, max state err %.2e" % (run.max_out, run.max_state))
+
+
+def test_workload5_mixed_delta():
+    w = synth.workload(5)
+    _say("workload 5", w)
+    stateless = np.zeros(w.B, bool)
+    stateless[w.B - w.n_short:] = True
+    sample = [(b, h) for b, h in zip([0, 3, 100, 255, 256, 300, 401, 511], [0, 17, 31, 5, 0, 9, 22, 31])]
+    run = Run(w, stateless=stateless, sample=sample, spare_blocks=64)
+    short = np.arange(w.B - w.n_short, w.B)
+    life = synth.short_lengths(w, 0, len(short))
+    age = np.zeros(len(short), np.int64)
+    draws = 1
+    retired = 0
+    for t in range(w.steps):
+        run.decode(t)
+        age += 1
+        for i in np.nonzero(age >= life)[0]:
+            run.retire_and_admit(int(short[i]))
+            age[i] = 0
+            life[i] = synth.short_lengths(w, draws, 1)[0]
+            draws += 1
+            retired += 1
+    run.check_effective_states()
+    run.check_pool()
+    run.check_bookkeeping()
+    _say("retired %d; max out err %.2e, max state err %.2e" % (retired, run.max_out, run.max_state))
