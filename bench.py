@@ -1,0 +1,337 @@
+#!/usr/bin/env python3
+"""Benchmark of the KVBuffer decode path on one MI355X.
+
+Workload: one scalar-gated linear-attention layer, B=256 requests, H=32 heads,
+d_k=d_v=128, buffer m=8 (blocks of 8, two per request, shuffled pool), bf16
+q/k/v, fp32 state ~ N(0, 0.02), fold fused into the decode that fills the
+buffer.  One "step" is one full buffer cycle: m decode launches over the whole
+batch, the last of which folds the buffer into the state (KVBuffer: IO-aware
+Serving for Linear Attention, pith.science page, Figure 3 caption: kernel
+latency is averaged over a full buffer cycle -- occupancies 0 .. m-1 and the
+state update).  Inputs are a ring of 2m pre-generated steps resident in HBM.
+
+Also measured in the same run: the m = 0 recurrent kernel at the same shape
+(the figure's normaliser), the variant with a separate flush launch, a plain
+device copy (measured bandwidth ceiling) and the oracle on the host cores.
+
+Prints ONE JSON line.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, published
+
+
+# Algorithmic bytes per (request, head) tile, scalar-gated rule, 2-byte
+# q/k/v, 4-byte state, gates and outputs.
+def decode_bytes(j, dk, dv, io=2):
+    return (4 * dk * dv            # state tile read
+            + io * (2 * dk + dv)   # q, k, v of the new token
+            + io * (dk + dv)       # append of k, v to the pool
+            + io * j * (dk + dv)   # buffered keys and values
+            + 4 * dv               # output
+            + 4 * (j + 2))         # gates: buffered, new, appended
+
+
+def flush_bytes(m, dk, dv, io=2):
+    return 8 * dk * dv + m * (io * (dk + dv) + 4)
+
+
+def recurrent_bytes(dk, dv, io=2):
+    return 8 * dk * dv + io * (2 * dk + dv) + 4 * dv + 4
+
+
+def cycle_bytes_fused(m, dk, dv, io=2):
+    """Decodes at occupancy 0 .. m-1 plus one state write (the fold reads the
+    state and the buffered tokens the last decode already reads)."""
+    return sum(decode_bytes(j, dk, dv, io) for j in range(m)) + 4 * dk * dv
+
+
+def cycle_bytes_separate(m, dk, dv, io=2):
+    return sum(decode_bytes(j, dk, dv, io) for j in range(m)) + flush_bytes(m, dk, dv, io)
+
+
+def _traffic_file(m):
+    return os.path.join(ROOT, "profiles", "traffic_chunk_kernel_B256_H32_d128_m%d.txt" % m)
+
+
+def _kernel_source_digest():
+    import hashlib
+
+    h = hashlib.sha256()
+    for name in ("chunk.hip", "device_common.hpp", "kvbuf_internal.hpp"):
+        with open(os.path.join(ROOT, "linear_attention_decode_kvbuf_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(m, launches_per_cycle):
+    """HBM bytes per launch measured by rocprofv3 counters (FETCH_SIZE and
+    WRITE_SIZE, scaled by a copy kernel's reading), if measured for the
+    current kernel source; else None."""
+    path = _traffic_file(m)
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if "=" in line and not line.lstrip().startswith("#"):
+            key, val = line.split("=", 1)
+            vals[key.strip()] = val.strip()
+    if vals.get("kernel_source_digest") != _kernel_source_digest():
+        return None
+    try:
+        return float(vals["bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def build_kv(kb, synth, torch, w, flush, device):
+    kv = kb.KVBuffer(batch=w.B, heads=w.H, d=w.dk, m=w.m, block_size=max(w.block_size, 1),
+                     blocks_per_req=w.blocks_per_req, num_blocks=max(w.B * w.blocks_per_req, 1),
+                     num_state_slots=w.B, rule=w.rule, io_dtype=kb.BF16, flush=flush, device=device)
+    if w.m > 0:
+        perm = synth.block_permutation(w, w.B * w.blocks_per_req)
+        kv.block_table.copy_(torch.from_numpy(perm.reshape(w.B, w.blocks_per_req)))
+    kv.state_slot.copy_(torch.from_numpy(synth.slot_permutation(w, w.B)))
+    kv.state.copy_(synth.device_initial_state(w, w.B, device))
+    return kv
+
+
+def make_ring(synth, w, device, size):
+    return [synth.device_token_inputs(w, t, device) for t in range(size)]
+
+
+def time_loop(torch, fn, cycles, warmup):
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(cycles):
+        fn(warmup + i)
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0
+
+
+def per_launch_ms(torch, launches, reps):
+    """Average duration (ms) of each launch in ``launches`` (a list of
+    callables issued back to back), from HIP events recorded on the stream
+    the kernels run on, over ``reps`` repetitions."""
+    stream = torch.cuda.current_stream()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(launches) + 1)] for _ in range(reps)]
+    for r in range(reps):
+        evs[r][0].record(stream)
+        for i, fn in enumerate(launches):
+            fn()
+            evs[r][i + 1].record(stream)
+    torch.cuda.synchronize()
+    out = [0.0] * len(launches)
+    for r in range(reps):
+        for i in range(len(launches)):
+            out[i] += evs[r][i].elapsed_time(evs[r][i + 1]) / reps
+    return out
+
+
+def cpu_baseline(synth, oracle, np, torch, w, ring, max_tiles=None):
+    """The oracle (fp64 per-token recurrence) over m consecutive tokens of the
+    same workload on the host's cores; returns tokens/s in the metric's unit
+    (tokens of all B requests per second, scaled from the sampled tiles)."""
+    ncores = len(os.sched_getaffinity(0))
+    tiles = w.B * w.H if max_tiles is None else min(max_tiles, w.B * w.H)
+    steps = w.m
+    q = np.stack([r["q"].reshape(-1, w.dk)[:tiles].float().cpu().numpy() for r in ring[:steps]])
+    k = np.stack([r["k"].reshape(-1, w.dk)[:tiles].float().cpu().numpy() for r in ring[:steps]])
+    v = np.stack([r["v"].reshape(-1, w.dv)[:tiles].float().cpu().numpy() for r in ring[:steps]])
+    g = np.stack([r["g"].reshape(-1)[:tiles].cpu().numpy() for r in ring[:steps]])
+    S0 = synth.device_initial_state(w, w.B, torch.device("cuda")).reshape(
+        -1, w.dk, w.dv)[:tiles].double().cpu().numpy()
+    used = oracle.threads_used(ncores)
+    t0 = time.perf_counter()
+    oracle.recurrent(1, S0, q, k, v, g=g, nthreads=ncores)
+    dt = time.perf_counter() - t0
+    tile_tokens_per_s = tiles * steps / dt
+    return {
+        "value": tile_tokens_per_s / w.H,  # a token of one request = H tiles
+        "unit": "tokens/s",
+        "cores": used,
+        "kind": "oracle",
+        "sample": "fp64 recurrent oracle (C, OpenMP over tiles), %d consecutive tokens of %d of the %d "
+                  "(request, head) tiles of the same workload, %.1f s" % (steps, tiles, w.B * w.H, dt),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200, help="timed buffer cycles")
+    ap.add_argument("--warmup", type=int, default=20, help="untimed buffer cycles")
+    ap.add_argument("--m", type=int, default=8, help="buffer size")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing on the host")
+    ap.add_argument("--no-extras", action="store_true", help="skip the m=0 / separate-flush / copy legs")
+    ap.add_argument("--only", choices=["fused", "recurrent", "separate", "copy"], default=None,
+                    help="run one leg only (for profiling)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: the decode path has no cross-GPU step and this build "
+              "measures the per-GPU kernel (requested --gpus %d)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    import linear_attention_decode_kvbuf_amd as kb
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    m = args.m
+    w = synth.workload(3, m=m, block_size=m, blocks_per_req=2)
+    tiles = w.B * w.H
+    ring = make_ring(synth, w, dev, 2 * m)
+    out = torch.empty((w.B, w.H, w.dv), dtype=torch.float32, device=dev)
+    result = {}
+
+    def decode_fn(kv, t):
+        r = ring[t % len(ring)]
+        return lambda: kv.decode(r["q"], r["k"], r["v"], r["g"], out=out)
+
+    # ---- headline: fused fold, one step = one buffer cycle ----------------
+    if args.only in (None, "fused"):
+        kv = build_kv(kb, synth, torch, w, kb.FLUSH_EAGER, dev)
+
+        def cycle(i):
+            for j in range(m):
+                decode_fn(kv, i * m + j)()
+
+        wall = time_loop(torch, cycle, args.steps, args.warmup)
+        ms_per_step = wall / args.steps * 1e3
+        tok_s = w.B * m * args.steps / wall
+        # per-launch durations (events on the launch stream) over the cycle
+        reps = max(10, min(args.steps, 50))
+        per = per_launch_ms(torch, [decode_fn(kv, j) for j in range(m)], reps)
+        torch.cuda.synchronize()
+        assert int(kv.error.item()) == 0
+        cyc_bytes = cycle_bytes_fused(m, w.dk, w.dv) * tiles
+        avg_launch_ms = sum(per) / m
+        achieved = cyc_bytes / m / (avg_launch_ms * 1e-3) / 1e9
+        traffic = read_traffic(m, m)
+        result.update(
+            value=tok_s, ms_per_step=ms_per_step,
+            hbm_gbps=cyc_bytes / (wall / args.steps) / 1e9,
+            hbm_frac_of_peak=cyc_bytes / (wall / args.steps) / 1e9 / PEAK_HBM_GBPS,
+            bytes_per_token=cyc_bytes / m / w.B,
+            per_occupancy_ms=[round(x, 5) for x in per],
+            roofline={"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                      "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
+                      "kernel": "chunk_kernel (decode; the last launch of a cycle folds)",
+                      "avg_launch_ms": avg_launch_ms,
+                      "algorithmic_bytes_per_launch": cyc_bytes / m},
+        )
+        del kv
+
+    # ---- m = 0 recurrent kernel at the same shape -------------------------
+    if not args.no_extras and args.only in (None, "recurrent"):
+        w0 = synth.workload(3, m=0, block_size=1, blocks_per_req=1)
+        kv0 = build_kv(kb, synth, torch, w0, kb.FLUSH_EAGER, dev)
+        wall0 = time_loop(torch, lambda i: [decode_fn(kv0, i * m + j)() for j in range(m)],
+                          args.steps, args.warmup)
+        per0 = per_launch_ms(torch, [decode_fn(kv0, j) for j in range(m)], 20)
+        b0 = recurrent_bytes(w.dk, w.dv) * tiles
+        result["m0_recurrent"] = {
+            "tokens_per_s": w.B * m * args.steps / wall0,
+            "ms_per_token_step": wall0 / (args.steps * m) * 1e3,
+            "avg_launch_ms": sum(per0) / m,
+            "hbm_gbps": b0 / (sum(per0) / m * 1e-3) / 1e9,
+            "bytes_per_token": b0 / w.B,
+        }
+        del kv0
+
+    # ---- separate flush launch (deferred policy) --------------------------
+    if not args.no_extras and args.only in (None, "separate"):
+        kvd = build_kv(kb, synth, torch, w, kb.FLUSH_DEFERRED, dev)
+
+        def cycle_d(i):
+            for j in range(m):
+                decode_fn(kvd, i * m + j)()
+            kvd.flush()
+
+        walld = time_loop(torch, cycle_d, args.steps, args.warmup)
+        perd = per_launch_ms(torch, [decode_fn(kvd, j) for j in range(m)] + [kvd.flush], 20)
+        torch.cuda.synchronize()
+        assert int(kvd.error.item()) == 0
+        bd = cycle_bytes_separate(m, w.dk, w.dv) * tiles
+        result["separate_flush"] = {
+            "tokens_per_s": w.B * m * args.steps / walld,
+            "ms_per_cycle": walld / args.steps * 1e3,
+            "decode_avg_launch_ms": sum(perd[:m]) / m,
+            "flush_launch_ms": perd[m],
+            "flush_hbm_gbps": flush_bytes(m, w.dk, w.dv) * tiles / (perd[m] * 1e-3) / 1e9,
+            "hbm_gbps": bd / (walld / args.steps) / 1e9,
+            "bytes_per_token": bd / m / w.B,
+        }
+        del kvd
+
+    # ---- plain device copy: measured bandwidth ceiling --------------------
+    if not args.no_extras and args.only in (None, "copy"):
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).normal_()
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        pc = per_launch_ms(torch, [lambda: dst.copy_(src)], 20)[0]
+        result["copy_ceiling_gbps"] = 2 * src.numel() * 4 / (pc * 1e-3) / 1e9
+        del src, dst
+
+    if args.only not in (None, "fused"):
+        print(json.dumps(result))
+        return
+
+    cpu = None
+    if not args.no_cpu:
+        import oracle
+
+        cpu = cpu_baseline(synth, oracle, np, torch, w, ring)
+
+    line = {
+        "metric": "decode tokens/s + achieved HBM GB/s (%% peak), B=256 H=32 d=128 m=%d" % m,
+        "value": result["value"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": result["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "KVBuffer decode cycle: scalar-gated linear attention, B=256 H=32 d_k=d_v=128, "
+                        "m=%d (blocks of %d, 2 per request, shuffled pool), bf16 q/k/v, fp32 state and "
+                        "accumulation, fold fused into the filling decode; step = one buffer cycle "
+                        "(%d decode launches)" % (m, m, m),
+            "B": w.B, "H": w.H, "d_k": w.dk, "d_v": w.dv, "m": m, "io": "bf16",
+        },
+        "hbm_gbps": result["hbm_gbps"],
+        "hbm_frac_of_peak": result["hbm_frac_of_peak"],
+        "bytes_per_token": result["bytes_per_token"],
+        "roofline": result["roofline"],
+        "cpu_baseline": cpu,
+    }
+    for key in ("per_occupancy_ms", "m0_recurrent", "separate_flush", "copy_ceiling_gbps"):
+        if key in result:
+            line[key] = result[key]
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

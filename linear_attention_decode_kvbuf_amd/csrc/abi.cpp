@@ -87,6 +87,9 @@ TileParams make_params(const kvbuf_layout* L, const kvbuf_pools* P, const kvbuf_
     return t;
 }
 
+// Tokens staged in LDS per fold round for folds of up to `count` tokens.
+int32_t fold_chunk(int count) { return count < kvbuf::kFoldChunk ? (count > 0 ? count : 1) : kvbuf::kFoldChunk; }
+
 kvbuf_status from_hip(hipError_t e) { return e == hipSuccess ? KVBUF_OK : KVBUF_EHIP; }
 
 #define KVBUF_TRY(x)                       \
@@ -113,6 +116,11 @@ kvbuf_status chunk_call(const kvbuf_layout* layout, const kvbuf_pools* pools,
     TileParams t = make_params(layout, pools, batch);
     t.mode = mode;
     t.n = n;
+    // A decode under the eager policy folds inside the decode kernel when the
+    // m tokens fit one LDS staging round; otherwise a fold launch follows it.
+    const bool eager_decode = mode == kvbuf::MODE_DECODE && t.fuse && layout->m > 0;
+    const bool fused = eager_decode && layout->m <= kvbuf::kFoldChunk;
+    t.fold_chunk = fused ? layout->m : 0;
     t.q = q;
     t.k = k;
     t.v = v;
@@ -122,8 +130,13 @@ kvbuf_status chunk_call(const kvbuf_layout* layout, const kvbuf_pools* pools,
     if (layout->m == 0)
         return from_hip(kvbuf::launch_recurrent(t, layout->rule, layout->d_k, layout->io_dtype,
                                                 batch->size, stream));
-    return from_hip(kvbuf::launch_chunk(t, layout->rule, layout->d_k, layout->io_dtype,
-                                        batch->size, stream));
+    hipError_t e = kvbuf::launch_chunk(t, layout->rule, layout->d_k, layout->io_dtype, batch->size, stream);
+    if (e == hipSuccess && eager_decode && !fused) {
+        t.mode = kvbuf::MODE_FLUSH;
+        t.fold_chunk = fold_chunk(layout->m);
+        e = kvbuf::launch_fold(t, layout->rule, layout->d_k, layout->io_dtype, batch->size, stream);
+    }
+    return from_hip(e);
 }
 
 }  // namespace
@@ -160,6 +173,7 @@ kvbuf_status kvbuf_flush(const kvbuf_layout* layout, const kvbuf_pools* pools,
     KVBUF_TRY(check_grid(layout, batch));
     TileParams t = make_params(layout, pools, batch);
     t.mode = kvbuf::MODE_FLUSH;
+    t.fold_chunk = fold_chunk(layout->m);
     return from_hip(kvbuf::launch_fold(t, layout->rule, layout->d_k, layout->io_dtype,
                                        batch->size, stream));
 }
@@ -177,6 +191,7 @@ kvbuf_status kvbuf_commit(const kvbuf_layout* layout, const kvbuf_pools* pools,
     TileParams t = make_params(layout, pools, batch);
     t.mode = kvbuf::MODE_COMMIT;
     t.n = n;
+    t.fold_chunk = fold_chunk(layout->m);
     t.accepted = accepted;
     return from_hip(kvbuf::launch_fold(t, layout->rule, layout->d_k, layout->io_dtype,
                                        batch->size, stream));
@@ -192,6 +207,7 @@ kvbuf_status kvbuf_materialize(const kvbuf_layout* layout, const kvbuf_pools* po
     KVBUF_TRY(check_grid(layout, batch));
     TileParams t = make_params(layout, pools, batch);
     t.mode = kvbuf::MODE_MATERIALIZE;
+    t.fold_chunk = fold_chunk(layout->block_size * layout->blocks_per_req);
     t.states_out = states;
     return from_hip(kvbuf::launch_fold(t, layout->rule, layout->d_k, layout->io_dtype,
                                        batch->size, stream));

@@ -17,13 +17,13 @@
 //   x_t = u_t = beta_t (v_t - e^{b_t} S0^T k_t - sum_{i<t} e^{b_t - b_i} (k_i . k_t) u_i),
 // the pseudo-value the pool stores in place of v.
 //
-// One workgroup per (request, head).  The workgroup issues all loads of its
-// 64 KiB state tile first (128-bit, non-temporal: the tile is not reused
-// before it is evicted), computes the gates' prefix sums and the q . k scores
-// of the buffered tokens while they are in flight, then reduces S^T q and the
-// weighted buffer sum in one pass over its registers.  The state is the only
-// large operand, so the kernel is bound by HBM bandwidth; everything else is
-// sized to stay off that path.
+// One workgroup per (request, head).  The state waves issue all loads of the
+// 64 KiB state tile (128-bit, non-temporal: the tile is not reused before it
+// is evicted) and wait at a barrier; meanwhile the token wave forms the gate
+// prefix sums, the q . k scores and the decay-weighted sum of the buffered
+// values, and appends the new tokens to the pool.  After the barrier the state
+// waves reduce S^T q from registers.  The state is the only large operand, so
+// the kernel is bound by HBM bandwidth.
 #include "device_common.hpp"
 
 namespace kvbuf {
@@ -32,12 +32,12 @@ namespace {
 // LDS layout of the chunk kernel, in floats.  Shared by the launcher (size)
 // and the kernel (offsets).
 struct ChunkLds {
-    int qs, ks, bl, cq, ck, es, sq, sk, un, red, fk, fx, fw, total;
+    int qs, ks, bl, cq, ck, es, bq, bk, sq, sk, un, red, fk, fx, fw, total;
 };
 
 __host__ __device__ inline int round4(int x) { return (x + 3) & ~3; }
 
-__host__ __device__ inline ChunkLds chunk_lds(int rule, int DK, int DV, int NQ, int RG, int cap, bool fold) {
+__host__ __device__ inline ChunkLds chunk_lds(int rule, int DK, int DV, int NQ, int RG, int cap, int fold_chunk) {
     ChunkLds L;
     int o = 0;
     const bool delta = rule == KVBUF_RULE_DELTA;
@@ -46,38 +46,38 @@ __host__ __device__ inline ChunkLds chunk_lds(int rule, int DK, int DV, int NQ, 
     L.bl = o; o += round4(cap);                   // cumulative log-gates
     L.cq = o; o += NQ * round4(cap);              // e^{b_t - b_i} (q_t . k_i)
     L.ck = o; o += delta ? NQ * round4(cap) : 0;  // e^{b_t - b_i} (k_t . k_i)
-    L.es = o; o += round4(NQ);                    // e^{b_t}, the weight of S0
-    L.sq = o; o += delta ? NQ * DV : 0;           // reduced e^{b_t} S0^T q_t + buffer part
-    L.sk = o; o += delta ? NQ * DV : 0;           // reduced e^{b_t} S0^T k_t + buffer part
+    L.es = o; o += round4(NQ + 1);                // e^{b_t} per draft; [NQ]: e^{b_{m-1}}
+    L.bq = o; o += NQ * DV;                       // sum_i cq_i x_i (buffered values)
+    L.bk = o; o += delta ? NQ * DV : 0;           // sum_i ck_i x_i
+    L.sq = o; o += delta ? NQ * DV : 0;           // reduced e^{b_t} S0^T q_t + bq
+    L.sk = o; o += delta ? NQ * DV : 0;           // reduced e^{b_t} S0^T k_t + bk
     L.un = o; o += delta ? NQ * DV : 0;           // pseudo-values of the new tokens
-    // The row-group reduction area and the fold staging area are never live
-    // at the same time.
-    const int red = RG * DV * (delta ? 2 : 1);
-    const int stage = fold ? kFoldChunk * (DK + DV) + kFoldChunk : 0;
-    L.red = o;
-    L.fk = o;
-    L.fx = o + kFoldChunk * DK;
-    L.fw = L.fx + kFoldChunk * DV;
-    o += red > stage ? red : stage;
+    L.red = o; o += RG * DV * (delta ? 2 : 1);    // row-group partial sums
+    L.fk = o; o += fold_chunk * DK;               // fold staging: keys,
+    L.fx = o; o += fold_chunk * DV;               //   values,
+    L.fw = o; o += round4(fold_chunk);            //   weights
     L.total = o;
     return L;
 }
 
 template <int RULE, int DK, int DV, int NQ, typename IO>
-__global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) {
+__global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void chunk_kernel(TileParams P) {
     using G = Geo<DK, DV>;
-    constexpr int NT = G::NT, TPR = G::TPR, RG = G::RG, RPT = G::RPT;
+    constexpr int NT = G::NT, TPR = G::TPR, RG = G::RG, RPT = G::RPT, CPL = G::CPL;
     constexpr bool DELTA = RULE == KVBUF_RULE_DELTA;
     constexpr bool GATED = RULE != KVBUF_RULE_LINEAR;
     using XIO = typename std::conditional<DELTA, float, IO>::type;
 
     extern __shared__ float lds[];
     __shared__ int32_t s_row[kMaxTableRow];
+    __shared__ int s_last;
 
     const int tile = blockIdx.x;
     const int b = tile / P.H;
     const int h = tile - b * P.H;
     const int tid = threadIdx.x;
+    const bool token_wave = tid >= NT;
+    const int lane = tid - NT;  // token-wave lane
     const int rg = tid / TPR;
     const int c0 = (tid % TPR) * 4;
     const int n = P.n;
@@ -86,7 +86,7 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
 
     const int p = P.occ[b];
     const int slot = direct ? -1 : P.slot[b];
-    unsigned bad = (p < 0) ? KVBUF_DEVERR_OVERFLOW : load_row(P, b, p + n, s_row);
+    unsigned bad = (p < 0) ? KVBUF_DEVERR_OVERFLOW : load_row(P, b, p + n, s_row, NT);
     if (slot >= P.num_slots) bad |= KVBUF_DEVERR_SLOT;
     if (bad) {
         report(P, bad);
@@ -94,24 +94,19 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
     }
     const bool has_state = slot >= 0;
     const int T = p + n;  // positions touched by this call
-    const bool fold = P.mode == MODE_DECODE && P.fuse && has_state && T >= P.m;
+    const int fc = P.fold_chunk;  // > 0 only when this launch may fold (then fc >= m)
+    const bool fold = fc > 0 && has_state && T >= P.m;
 
-    // ---- 1. issue the state tile loads -----------------------------------
-    f4 s[RPT];
-    const float* stile = P.state + (static_cast<size_t>(has_state ? slot : 0) * P.H + h) * DK * DV;
-    if (has_state) {
-#pragma unroll
-        for (int j = 0; j < RPT; ++j)
-            s[j] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(stile + (rg + RG * j) * DV + c0));
-    }
-
-    const ChunkLds L = chunk_lds(RULE, DK, DV, NQ, RG, cap, P.fuse != 0);
+    const ChunkLds L = chunk_lds(RULE, DK, DV, NQ, RG, cap, fc);
     float* qs = lds + L.qs;
     float* ks = lds + L.ks;
     float* bl = lds + L.bl;
     float* cq = lds + L.cq;
     float* ck = lds + L.ck;
     float* es = lds + L.es;
+    float* fk = lds + L.fk;
+    float* fx = lds + L.fx;
+    float* fw = lds + L.fw;
     const int ldc = round4(cap);
 
     const size_t in_row = static_cast<size_t>(b) * n * P.H + h;  // (b, draft 0, h)
@@ -130,107 +125,195 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
     tok.in_stride_k = static_cast<size_t>(P.H) * DK;
     tok.in_stride_v = static_cast<size_t>(P.H) * DV;
 
-    // ---- 2. stage queries (and delta-rule keys) --------------------------
-    for (int e = tid; e < n * DK; e += NT) {
-        const int d = e / DK, r = e - d * DK;
-        qs[d * DK + r] = P.scale * load1(static_cast<const IO*>(P.q) + (in_row + d * P.H) * DK + r);
-        if constexpr (DELTA) ks[d * DK + r] = load1(tok.kin + d * tok.in_stride_k + r);
-    }
-    __syncthreads();  // s_row is complete
-
-    // ---- 3. cumulative log-gates ------------------------------------------
-    if constexpr (GATED) {
-        gate_prefix(bl, T, [&](int i) { return tok.gate(i); });
-    } else {
-        for (int i = tid; i < T; i += NT) bl[i] = 0.0f;
-    }
-    __syncthreads();
-    if (tid < n) es[tid] = GATED ? expf(bl[p + tid]) : 1.0f;
-
-    // ---- 4. scores: 16-lane groups, one (draft, position) pair per round --
-    {
-        const int lane = tid % G::DOT_LANES;
-        const int grp = tid / G::DOT_LANES;
-        const int npq = n * T;
-        const int npairs = DELTA ? 2 * npq : npq;
-        for (int pi = grp; pi < npairs; pi += G::GROUPS) {
-            const bool kk = DELTA && pi >= npq;
-            const int pp = kk ? pi - npq : pi;
-            const int d = pp / T;
-            const int i = pp - d * T;
-            const int t = p + d;  // position of draft d
-            const bool live = kk ? (i < t) : (i <= t);
-            float part = 0.0f;
-            if (live) {
-                float kv[G::E];
-                loadE<G::E>(tok.key(i) + lane * G::E, kv);
-                const float* a = (kk ? ks : qs) + d * DK + lane * G::E;
+    if (token_wave) {
+        // ---- token wave ------------------------------------------------------
+        // (s_row was written by lane 0 of this wave; the LDS operations of one
+        // wave complete in order.)  Sixteen lanes share a token row: lane
+        // group gl (0..3) takes one position per round, lane cl (0..15) one
+        // E-element chunk of it.  All loads of a batch of 8 positions are
+        // issued before any is used: one HBM round trip per batch.
+        constexpr int E = G::E, EV = DV / 16, NB = 2, NQR = (NQ + 3) / 4;
+        const int gl = lane >> 4, cl = lane & 15;
+        // queries (and, delta rule, keys) of this call's tokens
+        RawChunk<IO, E> qraw[NQR], kdraw[DELTA ? NQR : 1];
 #pragma unroll
-                for (int e = 0; e < G::E; ++e) part += a[e] * kv[e];
-            }
-            const float dot = group16_sum(part);
-            if (lane == 0) {
-                const float w = live ? (GATED ? expf(bl[t] - bl[i]) : 1.0f) * dot : 0.0f;
-                (kk ? ck : cq)[d * ldc + i] = w;
+        for (int r = 0; r < NQR; ++r) {
+            const int d = gl + 4 * r;
+            qraw[r].zero();
+            if constexpr (DELTA) kdraw[r].zero();
+            if (d < n) {
+                qraw[r].load(static_cast<const IO*>(P.q) + (in_row + d * P.H) * DK + cl * E);
+                if constexpr (DELTA) kdraw[r].load(tok.kin + d * tok.in_stride_k + cl * E);
             }
         }
-    }
-    __syncthreads();
-
-    // ---- 5. one pass over the state registers + the weighted buffer sum --
-    // Rows of this thread: r_j = rg + RG * j; columns c0 .. c0+3.
-    f4 acc[NQ];
-    f4 acck[DELTA ? NQ : 1];
+        float accq[NQ][EV], acck[DELTA ? NQ : 1][EV];
 #pragma unroll
-    for (int d = 0; d < NQ; ++d) {
-        acc[d] = f4{0.f, 0.f, 0.f, 0.f};
-        if constexpr (DELTA) acck[d] = f4{0.f, 0.f, 0.f, 0.f};
-    }
-    if (has_state) {
+        for (int d = 0; d < NQ; ++d)
+#pragma unroll
+            for (int e = 0; e < EV; ++e) {
+                accq[d][e] = 0.f;
+                if constexpr (DELTA) acck[d][e] = 0.f;
+            }
+        const int tacc = DELTA ? p : T;  // positions whose values enter the sums
+        const int nfold = fold ? P.m : 0;  // positions staged for the fold
+        IO* kpool = static_cast<IO*>(P.key);
+        XIO* xpool = static_cast<XIO*>(P.value);
+        for (int i0 = 0; i0 < T; i0 += 4 * NB) {
+            RawChunk<IO, E> kr[NB];
+            RawChunk<XIO, EV> xr[NB];
+#pragma unroll
+            for (int rr = 0; rr < NB; ++rr) {
+                const int i = i0 + 4 * rr + gl;
+                kr[rr].zero();
+                xr[rr].zero();
+                if (i < T) {
+                    kr[rr].load(tok.key(i) + cl * E);
+                    if (i < p) {
+                        xr[rr].load(tok.pooled_value(i) + cl * EV);
+                    } else if constexpr (!DELTA) {
+                        xr[rr].load(tok.new_value(i - p) + cl * EV);
+                    }
+                }
+            }
+            if (i0 == 0) {
+                // gate prefix sums (their loads join this round trip), then
+                // the queries to LDS
+                if constexpr (GATED) {
+                    gate_prefix(bl, T, lane, [&](int i) { return tok.gate(i); });
+                } else {
+                    for (int i = lane; i < T; i += 64) bl[i] = 0.0f;
+                }
+                if (lane < n) es[lane] = GATED ? expf(bl[p + lane]) : 1.0f;
+                if (fold && lane == 0) es[NQ] = GATED ? expf(bl[P.m - 1]) : 1.0f;
+#pragma unroll
+                for (int r = 0; r < NQR; ++r) {
+                    const int d = gl + 4 * r;
+                    if (d < n) {
+                        float f[E];
+                        qraw[r].to_float(f);
+#pragma unroll
+                        for (int e = 0; e < E; ++e) qs[d * DK + cl * E + e] = P.scale * f[e];
+                        if constexpr (DELTA) {
+                            kdraw[r].to_float(f);
+#pragma unroll
+                            for (int e = 0; e < E; ++e) ks[d * DK + cl * E + e] = f[e];
+                        }
+                    }
+                }
+            }
+#pragma unroll
+            for (int rr = 0; rr < NB; ++rr) {
+                const int i = i0 + 4 * rr + gl;
+                const int ic = min(i, T - 1);
+                float kf[E], xf[EV];
+                kr[rr].to_float(kf);
+                xr[rr].to_float(xf);
+#pragma unroll
+                for (int d = 0; d < NQ; ++d) {
+                    if (d < n) {
+                        const int t = p + d;
+                        float part = 0.f;
+#pragma unroll
+                        for (int e = 0; e < E; ++e) part += qs[d * DK + cl * E + e] * kf[e];
+                        const float dot = group16_sum(part);
+                        const float wq = (i <= t) ? (GATED ? expf(bl[t] - bl[ic]) : 1.0f) * dot : 0.f;
+                        if (cl == 0 && i < T) cq[d * ldc + i] = wq;
+                        if (i < tacc) {
+#pragma unroll
+                            for (int e = 0; e < EV; ++e) accq[d][e] += wq * xf[e];
+                        }
+                        if constexpr (DELTA) {
+                            float pk = 0.f;
+#pragma unroll
+                            for (int e = 0; e < E; ++e) pk += ks[d * DK + cl * E + e] * kf[e];
+                            const float dk = group16_sum(pk);
+                            const float wk = (i < t) ? (GATED ? expf(bl[t] - bl[ic]) : 1.0f) * dk : 0.f;
+                            if (cl == 0 && i < T) ck[d * ldc + i] = wk;
+                            if (i < tacc) {
+#pragma unroll
+                                for (int e = 0; e < EV; ++e) acck[d][e] += wk * xf[e];
+                            }
+                        }
+                    }
+                }
+                // the same registers feed the fold staging and the appends
+                if (i < nfold) {
+#pragma unroll
+                    for (int e = 0; e < E; ++e) fk[i * DK + cl * E + e] = kf[e];
+                    if (!DELTA || i < p) {
+#pragma unroll
+                        for (int e = 0; e < EV; ++e) fx[i * DV + cl * EV + e] = xf[e];
+                    }
+                }
+                if (i >= p && i < T) {
+                    kr[rr].store(kpool + tok.slot_index(i) * DK + cl * E);
+                    if constexpr (!DELTA) xr[rr].store(xpool + tok.slot_index(i) * DV + cl * EV);
+                }
+            }
+        }
+        // sum the four position groups; group 0 writes the totals
 #pragma unroll
         for (int d = 0; d < NQ; ++d) {
             if (d < n) {
-                f4 a = f4{0.f, 0.f, 0.f, 0.f};
-                f4 ak = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int j = 0; j < RPT; ++j) {
-                    a += s[j] * qs[d * DK + rg + RG * j];
-                    if constexpr (DELTA) ak += s[j] * ks[d * DK + rg + RG * j];
-                }
-                acc[d] = a * es[d];
-                if constexpr (DELTA) acck[d] = ak * es[d];
-            }
-        }
-    }
-    {
-        // Linear / gated: every position including the new tokens (their
-        // values are inputs).  Delta: buffered positions only; the new tokens'
-        // pseudo-values depend on this reduction and are added in step 7.
-        const int tacc = DELTA ? p : T;
-        for (int i = rg; i < tacc; i += RG) {
-            f4 x = (i < p) ? load4(tok.pooled_value(i) + c0) : load4(tok.new_value(i - p) + c0);
-#pragma unroll
-            for (int d = 0; d < NQ; ++d) {
-                if (d < n) {
-                    acc[d] += cq[d * ldc + i] * x;
-                    if constexpr (DELTA) acck[d] += ck[d * ldc + i] * x;
+                for (int e = 0; e < EV; ++e) {
+                    float v = accq[d][e];
+                    v += __shfl_xor(v, 16, 64);
+                    v += __shfl_xor(v, 32, 64);
+                    if (gl == 0) lds[L.bq + d * DV + cl * EV + e] = v;
+                    if constexpr (DELTA) {
+                        float vk = acck[d][e];
+                        vk += __shfl_xor(vk, 16, 64);
+                        vk += __shfl_xor(vk, 32, 64);
+                        if (gl == 0) lds[L.bk + d * DV + cl * EV + e] = vk;
+                    }
                 }
             }
         }
+        for (int ii = lane; ii < nfold; ii += 64) fw[ii] = GATED ? expf(bl[P.m - 1] - bl[ii]) : 1.0f;
+        if constexpr (GATED) {
+            if (lane < n) P.gate[tok.slot_index(p + lane)] = tok.gin[lane * P.H];
+        }
     }
+    // ---- state waves: put the whole tile in flight ------------------------------
+    // (After the token-wave block in program order, so that none of the token
+    // wave's registers are allocated on top of the tile's 64.)
+    f4 s[RPT];
+    if (!token_wave && has_state) {
+        const float* stile = P.state + (static_cast<size_t>(slot) * P.H + h) * DK * DV;
+#pragma unroll
+        for (int j = 0; j < RPT; ++j)
+            s[j] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(stile + (rg + RG * j) * DV + c0));
+    }
+    __syncthreads();
+    // Every wave is past its reads of the request's metadata.
+    const bool advance = P.mode != MODE_VERIFY;  // drafts do not advance the occupancy
+    if (advance && tid == NT) s_last = take_ticket(P, b);
 
-    // ---- 6. reduce over row groups ----------------------------------------
+    // ---- S^T q (and S^T k) from the state registers, reduced over row groups
     float* red = lds + L.red;
     float* outp = P.out + in_row * DV;
     const size_t out_stride = static_cast<size_t>(P.H) * DV;
 #pragma unroll
     for (int d = 0; d < NQ; ++d) {
         if (d < n) {
-            *reinterpret_cast<f4*>(red + rg * DV + c0) = acc[d];
-            if constexpr (DELTA) *reinterpret_cast<f4*>(red + (RG + rg) * DV + c0) = acck[d];
+            if (!token_wave) {
+                f4 a = f4{0.f, 0.f, 0.f, 0.f};
+                f4 ak = f4{0.f, 0.f, 0.f, 0.f};
+                if (has_state) {
+#pragma unroll
+                    for (int j = 0; j < RPT; ++j) {
+                        a += s[j] * qs[d * DK + rg + RG * j];
+                        if constexpr (DELTA) ak += s[j] * ks[d * DK + rg + RG * j];
+                    }
+                }
+                *reinterpret_cast<f4*>(red + rg * DV + c0) = a * es[d];
+                if constexpr (DELTA) *reinterpret_cast<f4*>(red + (RG + rg) * DV + c0) = ak * es[d];
+            }
             __syncthreads();
-            for (int c = tid; c < DV; c += NT) {
-                float sum = 0.f, sumk = 0.f;
+            for (int c = tid; c < DV; c += G::NTHREADS) {
+                float sum = lds[L.bq + d * DV + c];
+                float sumk = DELTA ? lds[L.bk + d * DV + c] : 0.f;
 #pragma unroll
                 for (int g2 = 0; g2 < RG; ++g2) {
                     sum += red[g2 * DV + c];
@@ -247,10 +330,10 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
         }
     }
 
-    // ---- 7. delta rule: pseudo-values and outputs of the new tokens -------
+    // ---- delta rule: pseudo-values and outputs of the new tokens -------------
     if constexpr (DELTA) {
         XIO* xpool = static_cast<XIO*>(P.value);
-        for (int c = tid; c < DV; c += NT) {
+        for (int c = tid; c < DV; c += G::NTHREADS) {
             float u[NQ];
 #pragma unroll
             for (int d = 0; d < NQ; ++d) {
@@ -268,74 +351,38 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
                     outp[d * out_stride + c] = o;
                     lds[L.un + d * DV + c] = x;
                     xpool[tok.slot_index(t) * DV + c] = x;
+                    if (fold && t < P.m) fx[t * DV + c] = x;  // the new token is folded too
                 }
             }
         }
         __syncthreads();
     }
 
-    // ---- 8. eager fold: the buffer reached m tokens ------------------------
+    // ---- eager fold: the buffer reached m tokens -----------------------------
+    // All m tokens were staged by the token wave (m <= fold_chunk: the
+    // launcher only lets this kernel fold when they fit one staging round).
     if (fold) {
-        const int last = P.m - 1;
-        const float e0 = GATED ? expf(bl[last]) : 1.0f;
+        if (!token_wave) {
+            const float e0 = es[NQ];
 #pragma unroll
-        for (int j = 0; j < RPT; ++j) s[j] *= e0;
-        float* fk = lds + L.fk;
-        float* fx = lds + L.fx;
-        float* fw = lds + L.fw;
-        for (int i0 = 0; i0 < P.m; i0 += kFoldChunk) {
-            const int cnt = min(kFoldChunk, P.m - i0);
-            for (int e = tid; e < cnt * DK; e += NT) {
-                const int ii = e / DK, r = e - ii * DK;
-                fk[ii * DK + r] = load1(tok.key(i0 + ii) + r);
-            }
-            for (int e = tid; e < cnt * DV; e += NT) {
-                const int ii = e / DV, c = e - ii * DV;
-                const int i = i0 + ii;
-                float x;
-                if (i < p) x = load1(tok.pooled_value(i) + c);
-                else if constexpr (DELTA) x = lds[L.un + (i - p) * DV + c];
-                else x = load1(tok.new_value(i - p) + c);
-                fx[ii * DV + c] = x;
-            }
-            for (int ii = tid; ii < cnt; ii += NT) fw[ii] = GATED ? expf(bl[last] - bl[i0 + ii]) : 1.0f;
-            __syncthreads();
-            for (int ii = 0; ii < cnt; ++ii) {
+            for (int j = 0; j < RPT; ++j) s[j] *= e0;
+            for (int ii = 0; ii < P.m; ++ii) {
                 const f4 x = *reinterpret_cast<const f4*>(fx + ii * DV + c0);
                 const float w = fw[ii];
 #pragma unroll
                 for (int j = 0; j < RPT; ++j) s[j] += (w * fk[ii * DK + rg + RG * j]) * x;
             }
-            __syncthreads();
-        }
-        float* wt = P.state + (static_cast<size_t>(slot) * P.H + h) * DK * DV;
+            float* wt = P.state + (static_cast<size_t>(slot) * P.H + h) * DK * DV;
 #pragma unroll
-        for (int j = 0; j < RPT; ++j)
-            __builtin_nontemporal_store(s[j], reinterpret_cast<f4*>(wt + (rg + RG * j) * DV + c0));
-    }
-
-    // ---- 9. append the new tokens to the pool ------------------------------
-    {
-        IO* kpool = static_cast<IO*>(P.key);
-        for (int e = tid; e < n * DK; e += NT) {
-            const int d = e / DK, r = e - d * DK;
-            kpool[tok.slot_index(p + d) * DK + r] = tok.kin[d * tok.in_stride_k + r];
-        }
-        if constexpr (!DELTA) {
-            IO* vpool = static_cast<IO*>(P.value);
-            for (int e = tid; e < n * DV; e += NT) {
-                const int d = e / DV, c = e - d * DV;
-                vpool[tok.slot_index(p + d) * DV + c] = tok.vin[d * tok.in_stride_v + c];
-            }
-        }
-        if constexpr (GATED) {
-            if (tid < n) P.gate[tok.slot_index(p + tid)] = tok.gin[tid * P.H];
+            for (int j = 0; j < RPT; ++j)
+                __builtin_nontemporal_store(s[j], reinterpret_cast<f4*>(wt + (rg + RG * j) * DV + c0));
         }
     }
 
-    // ---- 10. bookkeeping ----------------------------------------------------
-    if (P.mode == MODE_VERIFY) return;  // drafts do not advance the occupancy
-    finish_request(P, b, T - (fold ? P.m : 0), fold ? P.m / P.block_size : 0);
+    // ---- bookkeeping -----------------------------------------------------------
+    if (!advance) return;
+    __syncthreads();
+    apply_bookkeeping(P, b, s_last, T - (fold ? P.m : 0), fold ? P.m / P.block_size : 0);
 }
 
 template <int RULE, int D, typename IO>
@@ -343,8 +390,8 @@ hipError_t launch_chunk_t(const TileParams& p, int batch, hipStream_t s) {
     using G = Geo<D, D>;
     const int cap = p.block_size * p.blocks_per_req;
     const int nq = p.n <= 1 ? 1 : p.n <= 2 ? 2 : p.n <= 4 ? 4 : 8;
-    const size_t lds = sizeof(float) * chunk_lds(RULE, D, D, nq, G::RG, cap, p.fuse != 0).total;
-    const dim3 grid(static_cast<unsigned>(batch) * p.H), block(G::NT);
+    const size_t lds = sizeof(float) * chunk_lds(RULE, D, D, nq, G::RG, cap, p.fold_chunk).total;
+    const dim3 grid(static_cast<unsigned>(batch) * p.H), block(G::NTHREADS);
     switch (nq) {
         case 1: chunk_kernel<RULE, D, D, 1, IO><<<grid, block, lds, s>>>(p); break;
         case 2: chunk_kernel<RULE, D, D, 2, IO><<<grid, block, lds, s>>>(p); break;

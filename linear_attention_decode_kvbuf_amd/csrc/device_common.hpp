@@ -12,29 +12,39 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint16_t bf16_bits;  // bfloat16 kept as its raw bits
 
 // ---------------------------------------------------------------------------
-// Tile geometry.  One workgroup owns one (request, head) tile: a d_k x d_v
-// fp32 state read as rows of d_v floats.  A thread owns 4 consecutive columns
-// (one 128-bit load per row) of RPT rows; TPR threads cover a row, RG row
-// groups split the rows.  Row j of a thread is r = rg + RG * j, so the two row
-// groups of a wave read two adjacent rows: every load instruction of a wave
-// covers a contiguous 2 * d_v * 4 bytes.
+// Workgroup layout.  One workgroup owns one (request, head) tile: a d_k x d_v
+// fp32 state read as rows of d_v floats.
+//
+// The first NT threads ("state waves") hold the tile in registers: a thread
+// owns 4 consecutive columns (one 128-bit load per row) of RPT rows; TPR
+// threads cover a row and RG row groups split the rows.  Row j of a thread is
+// r = rg + RG * j, so the two row groups of a wave read two adjacent rows and
+// every load instruction of a wave covers a contiguous 2 * d_v * 4 bytes.
+//
+// One more wave ("token wave", 64 lanes) does everything that depends on the
+// individual tokens: staging queries, gate prefix sums, q . k scores, the
+// weighted sum of buffered values, fold staging and the appends.  The wave's
+// memory counter is private, so the state waves' 16 outstanding loads are
+// never waited on before they are needed: they stay in flight while the token
+// wave works, and the two sides meet at one barrier.
 // ---------------------------------------------------------------------------
 template <int DK, int DV>
 struct Geo {
-    static constexpr int NT = DV >= 128 ? 256 : (DV >= 64 ? 128 : 64);
+    static constexpr int NT = DV >= 128 ? 256 : (DV >= 64 ? 128 : 64);  // state threads
+    static constexpr int NTOK = 64;                                     // token wave
+    static constexpr int NTHREADS = NT + NTOK;
     static constexpr int TPR = DV / 4;
     static constexpr int RG = NT / TPR;
     static constexpr int RPT = DK / RG;
     static_assert(TPR * RG == NT && RG * RPT == DK, "tile geometry");
-    // Dot products (q . k over d_k) use groups of 16 lanes; each lane owns E
-    // consecutive elements.
+    // Dot products (q . k over d_k) use groups of 16 lanes of the token wave;
+    // each lane owns E consecutive elements.
     static constexpr int DOT_LANES = 16;
     static constexpr int E = DK / DOT_LANES;
-    static constexpr int GROUPS = NT / DOT_LANES;
+    static constexpr int GROUPS = NTOK / DOT_LANES;
+    // Value columns per token-wave lane in the buffer sums.
+    static constexpr int CPL = DV >= 64 ? DV / 64 : 1;
 };
-
-// Tokens folded per LDS staging round.
-constexpr int kFoldChunk = 32;
 
 __device__ __forceinline__ float bf2f(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
@@ -85,6 +95,64 @@ __device__ __forceinline__ void loadE(const bf16_bits* p, float (&o)[E]) {
     }
 }
 
+// A lane's share of one token row when 16 lanes split the row: E consecutive
+// elements of type T kept as raw bits, so that a batch of loads can be
+// issued before any of them is waited on.
+template <typename T, int E>
+struct RawChunk {
+    static constexpr int BYTES = E * static_cast<int>(sizeof(T));
+    static constexpr int WORDS = BYTES >= 4 ? BYTES / 4 : 1;
+    uint32_t w[WORDS];
+
+    __device__ __forceinline__ void zero() {
+#pragma unroll
+        for (int i = 0; i < WORDS; ++i) w[i] = 0u;
+    }
+    __device__ __forceinline__ void load(const T* p) {
+        if constexpr (BYTES >= 16) {
+#pragma unroll
+            for (int i = 0; i < WORDS; i += 4) {
+                const uint4 u = reinterpret_cast<const uint4*>(p)[i / 4];
+                w[i] = u.x; w[i + 1] = u.y; w[i + 2] = u.z; w[i + 3] = u.w;
+            }
+        } else if constexpr (BYTES == 8) {
+            const uint2 u = *reinterpret_cast<const uint2*>(p);
+            w[0] = u.x; w[1] = u.y;
+        } else if constexpr (BYTES == 4) {
+            w[0] = *reinterpret_cast<const uint32_t*>(p);
+        } else {
+            w[0] = *reinterpret_cast<const uint16_t*>(p);
+        }
+    }
+    __device__ __forceinline__ void store(T* p) const {
+        if constexpr (BYTES >= 16) {
+#pragma unroll
+            for (int i = 0; i < WORDS; i += 4)
+                reinterpret_cast<uint4*>(p)[i / 4] = make_uint4(w[i], w[i + 1], w[i + 2], w[i + 3]);
+        } else if constexpr (BYTES == 8) {
+            *reinterpret_cast<uint2*>(p) = make_uint2(w[0], w[1]);
+        } else if constexpr (BYTES == 4) {
+            *reinterpret_cast<uint32_t*>(p) = w[0];
+        } else {
+            *reinterpret_cast<uint16_t*>(p) = static_cast<uint16_t>(w[0]);
+        }
+    }
+    __device__ __forceinline__ void to_float(float (&o)[E]) const {
+        if constexpr (sizeof(T) == 4) {
+#pragma unroll
+            for (int i = 0; i < E; ++i) o[i] = __uint_as_float(w[i]);
+        } else if constexpr (E == 1) {
+            o[0] = __uint_as_float(w[0] << 16);
+        } else {
+#pragma unroll
+            for (int i = 0; i < E / 2; ++i) {
+                o[2 * i] = __uint_as_float(w[i] << 16);
+                o[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+            }
+        }
+    }
+};
+
 // Sum over the 16 lanes of a dot group (butterfly through lane shuffles).
 __device__ __forceinline__ float group16_sum(float x) {
     x += __shfl_xor(x, 8, 16);
@@ -95,12 +163,10 @@ __device__ __forceinline__ float group16_sum(float x) {
 }
 
 // Inclusive prefix sum of the log-gates of buffer positions 0 .. T-1 into
-// bl[0 .. T-1] (LDS), done by wave 0 in 64-wide segments.  gate_at(i) returns
-// the log-gate of position i.  Callers synchronise afterwards.
+// bl[0 .. T-1] (LDS), by one wave (lane = 0..63) in 64-wide segments.
+// gate_at(i) returns the log-gate of position i.
 template <typename GateAt>
-__device__ __forceinline__ void gate_prefix(float* bl, int T, GateAt gate_at) {
-    if (threadIdx.x >= 64) return;
-    const int lane = threadIdx.x;
+__device__ __forceinline__ void gate_prefix(float* bl, int T, int lane, GateAt gate_at) {
     float carry = 0.0f;
     for (int base = 0; base < T; base += 64) {
         const int i = base + lane;
@@ -146,27 +212,85 @@ struct TileTokens {
     }
 };
 
-// Orders this workgroup's reads of the request's metadata before the
-// request's bookkeeping update, which the last of its H workgroups applies:
-// the occupancy becomes new_occ and, when rotate > 0, the table row moves its
-// first `rotate` entries to the back.  Every thread of the workgroup calls it;
-// it must be the last thing the workgroup does with the metadata.
-__device__ __forceinline__ void finish_request(const TileParams& P, int b, int new_occ, int rotate) {
-    __shared__ int s_last;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        __threadfence();
-        const int t = atomicAdd(&P.ticket[b], 1);
-        s_last = (t == P.H - 1);
+// Token wave: copies the keys and values of positions i0 .. i0+cnt-1 of the
+// tile to LDS as fp32 rows (fk: d_k per row, fx: d_v per row).  Sixteen lanes
+// share a row (one 16-byte load each for bf16 rows of 128), four rows per
+// round, and the loads of two rounds are issued before any is used, so a
+// round trip to HBM is paid once per 8 rows.  Values of positions >= tok.p
+// come from `un` (delta-rule pseudo-values already in LDS) when given, else
+// from this call's inputs.
+template <int DK, int DV, typename IO, typename XIO>
+__device__ __forceinline__ void stage_rows(const TileTokens<DK, DV, IO, XIO>& tok, int i0, int cnt,
+                                           float* fk, float* fx, const float* un, int lane) {
+    constexpr int E = DK / 16, EV = DV / 16, NB = 2;
+    const int gl = lane >> 4, cl = lane & 15;
+    for (int b0 = 0; b0 < cnt; b0 += 4 * NB) {
+        RawChunk<IO, E> kr[NB];
+        RawChunk<XIO, EV> xr[NB];
+#pragma unroll
+        for (int rr = 0; rr < NB; ++rr) {
+            const int ii = b0 + 4 * rr + gl;
+            const int i = i0 + ii;
+            kr[rr].zero();
+            xr[rr].zero();
+            if (ii < cnt) {
+                kr[rr].load(tok.key(i) + cl * E);
+                if (i < tok.p) {
+                    xr[rr].load(tok.pooled_value(i) + cl * EV);
+                } else if constexpr (std::is_same<XIO, IO>::value) {
+                    if (!un) xr[rr].load(tok.new_value(i - tok.p) + cl * EV);
+                }
+            }
+        }
+#pragma unroll
+        for (int rr = 0; rr < NB; ++rr) {
+            const int ii = b0 + 4 * rr + gl;
+            const int i = i0 + ii;
+            if (ii < cnt) {
+                float kf[E], xf[EV];
+                kr[rr].to_float(kf);
+                xr[rr].to_float(xf);
+                if (i >= tok.p && un) {
+#pragma unroll
+                    for (int e = 0; e < EV; ++e) xf[e] = un[(i - tok.p) * DV + cl * EV + e];
+                }
+#pragma unroll
+                for (int e = 0; e < E; ++e) fk[ii * DK + cl * E + e] = kf[e];
+#pragma unroll
+                for (int e = 0; e < EV; ++e) fx[ii * DV + cl * EV + e] = xf[e];
+            }
+        }
     }
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
+}
+
+// Per-request bookkeeping.  All H workgroups of a request read its occupancy,
+// state slot and table row; the last of them to finish with those values
+// (found with a per-request ticket counter) applies the update: the occupancy
+// becomes new_occ and, when rotate > 0, the first `rotate` table entries move
+// to the back; then it clears the ticket.
+//
+// take_ticket is called by one thread after a barrier that follows every
+// read of the metadata by every wave of the workgroup, so those reads have
+// completed; nothing in the kernel reads the metadata afterwards (the table
+// row used later is an LDS copy).  No memory fence is needed -- an agent-scope
+// fence would write back the XCD's whole L2 for every workgroup -- because
+// the bookkeeping stores only have to be visible to the next kernel, which the
+// kernel boundary guarantees.  The ticket's round trip overlaps the rest of
+// the workgroup's work; its result is read after a later barrier.
+__device__ __forceinline__ int take_ticket(const TileParams& P, int b) {
+    return atomicAdd(&P.ticket[b], 1) == P.H - 1;
+}
+
+// Every thread of the workgroup calls this last; `last` is take_ticket's
+// result (as seen after a barrier).
+__device__ __forceinline__ void apply_bookkeeping(const TileParams& P, int b, bool last, int new_occ,
+                                                  int rotate) {
+    if (!last) return;
     const int bpr = P.blocks_per_req;
     int32_t* row = P.table + static_cast<size_t>(b) * bpr;
     int val = 0;
     const bool mine = rotate > 0 && static_cast<int>(threadIdx.x) < bpr;
-    if (mine) val = __atomic_load_n(&row[(threadIdx.x + rotate) % bpr], __ATOMIC_RELAXED);
+    if (mine) val = row[(threadIdx.x + rotate) % bpr];
     __syncthreads();
     if (mine) row[threadIdx.x] = val;
     if (threadIdx.x == 0) {
@@ -179,9 +303,11 @@ __device__ __forceinline__ void report(const TileParams& P, unsigned bits) {
     if (bits && P.err && threadIdx.x == 0) atomicOr(reinterpret_cast<unsigned*>(P.err), bits);
 }
 
-// Checks the request's buffer positions [0, end) against the pool and copies
-// the table row to LDS.  Returns KVBUF_DEVERR_* bits (0 = usable).
-__device__ __forceinline__ unsigned load_row(const TileParams& P, int b, int end, int32_t* s_row) {
+// Checks the request's buffer positions [0, end) against the pool; thread
+// `writer` copies the table entries that cover them to LDS.  Returns
+// KVBUF_DEVERR_* bits (0 = usable).
+__device__ __forceinline__ unsigned load_row(const TileParams& P, int b, int end, int32_t* s_row,
+                                             int writer) {
     const int bpr = P.blocks_per_req;
     const int cap = P.block_size * bpr;
     if (end < 0 || end > cap) return KVBUF_DEVERR_OVERFLOW;
@@ -190,7 +316,7 @@ __device__ __forceinline__ unsigned load_row(const TileParams& P, int b, int end
     for (int j = 0; j < nblk; ++j) {
         const int blk = P.table[static_cast<size_t>(b) * bpr + j];
         if (blk < 0 || blk >= P.num_blocks) bad |= KVBUF_DEVERR_BLOCK;
-        if (threadIdx.x == 0) s_row[j] = blk;
+        if (static_cast<int>(threadIdx.x) == writer) s_row[j] = blk;
     }
     return bad;
 }

@@ -12,22 +12,33 @@
 // into the state S0 at the last fold:
 //   S <- e^{b_{T-1}} S0 + sum_{i<T} e^{b_{T-1} - b_i} k_i x_i^T
 // a rank-T update of the d_k x d_v tile (x_i = v_i, or the delta rule's
-// pseudo-value u_i).  One workgroup per (request, head): read the 64 KiB tile,
-// apply the update from keys and values staged in LDS, write it back.  For
-// the buffer sizes served here the update costs 2 T flops per 8 bytes of
-// state traffic -- below the fp32 vector ridge of the chip -- so it runs on
-// the vector ALUs and the kernel is bound by HBM bandwidth.
+// pseudo-value u_i).  One workgroup per (request, head): the state waves put
+// the 64 KiB tile in flight while the token wave forms the decay weights and
+// stages the keys and values in LDS (double-buffered rounds of up to 32
+// tokens); the state waves apply the update from registers and write the tile
+// back.  For the buffer sizes served here the update costs 2 T flops per 8
+// bytes of state traffic -- below the fp32 vector ridge of the chip -- so it
+// runs on the vector ALUs and the kernel is bound by HBM bandwidth.
 #include "device_common.hpp"
 
 namespace kvbuf {
 namespace {
 
-__host__ __device__ inline int fold_lds_floats(int DK, int DV, int cap) {
-    return ((cap + 3) & ~3) + kFoldChunk * (DK + DV) + kFoldChunk;
+// LDS: cumulative log-gates, then two staging buffers of fc tokens
+// (keys, values, weights), then the state weight e^{b_{T-1}}.
+__host__ __device__ inline int fold_stage_floats(int DK, int DV, int fc) {
+    return fc * (DK + DV) + ((fc + 3) & ~3);
+}
+__host__ __device__ inline int fold_lds_floats(int DK, int DV, int cap, int fc) {
+    return ((cap + 3) & ~3) + 2 * fold_stage_floats(DK, DV, fc) + 4;
 }
 
-template <int RULE, int DK, int DV, typename IO>
-__global__ __launch_bounds__((Geo<DK, DV>::NT)) void fold_kernel(TileParams P) {
+// MULTI: the fold may take more than one staging round (then the token wave
+// stages round r+1 while the state waves apply round r).  Without it every
+// position is staged before the state loads are issued, which keeps the
+// token wave's registers out of the tile's live range.
+template <int RULE, int DK, int DV, typename IO, bool MULTI>
+__global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void fold_kernel(TileParams P) {
     using G = Geo<DK, DV>;
     constexpr int NT = G::NT, TPR = G::TPR, RG = G::RG, RPT = G::RPT;
     constexpr bool DELTA = RULE == KVBUF_RULE_DELTA;
@@ -36,11 +47,14 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void fold_kernel(TileParams P) {
 
     extern __shared__ float lds[];
     __shared__ int32_t s_row[kMaxTableRow];
+    __shared__ int s_last;
 
     const int tile = blockIdx.x;
     const int b = tile / P.H;
     const int h = tile - b * P.H;
     const int tid = threadIdx.x;
+    const bool token_wave = tid >= NT;
+    const int lane = tid - NT;
     const int rg = tid / TPR;
     const int c0 = (tid % TPR) * 4;
     const int cap = P.block_size * P.blocks_per_req;
@@ -61,25 +75,25 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void fold_kernel(TileParams P) {
     const bool fold = !materialize && has_state && P.m > 0 && pn >= P.m &&
                       (P.mode == MODE_FLUSH || P.fuse);
     const int T = materialize ? p : (fold ? P.m : 0);  // positions applied
-    if (!bad) bad |= load_row(P, b, T, s_row);
+    if (!bad) bad |= load_row(P, b, T, s_row, NT);
     if (bad) {
         report(P, bad);
         return;
     }
     if (!materialize && !fold && a == 0) return;  // nothing changes for this request
+    if (!materialize) {
+        // This workgroup is done with the request's metadata once every wave
+        // is past this barrier (the table row is copied to LDS).
+        __syncthreads();
+        if (tid == NT) s_last = take_ticket(P, b);
+    }
 
     if (materialize || fold) {
-        f4 s[RPT];
-        const float* stile = P.state + (static_cast<size_t>(has_state ? slot : 0) * P.H + h) * DK * DV;
-#pragma unroll
-        for (int j = 0; j < RPT; ++j)
-            s[j] = has_state ? __builtin_nontemporal_load(reinterpret_cast<const f4*>(stile + (rg + RG * j) * DV + c0))
-                             : f4{0.f, 0.f, 0.f, 0.f};
-
+        const int fc = P.fold_chunk;
         float* bl = lds;
-        float* fk = lds + ((cap + 3) & ~3);
-        float* fx = fk + kFoldChunk * DK;
-        float* fw = fx + kFoldChunk * DV;
+        float* stage0 = lds + ((cap + 3) & ~3);
+        const int stage_floats = fold_stage_floats(DK, DV, fc);
+        float* e0p = stage0 + 2 * stage_floats;
 
         TileTokens<DK, DV, IO, XIO> tok;
         tok.kpool = static_cast<const IO*>(P.key);
@@ -91,51 +105,88 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void fold_kernel(TileParams P) {
         tok.h = h;
         tok.p = cap;  // every position read here is in the pool
 
-        __syncthreads();  // s_row is complete
-        if constexpr (GATED) gate_prefix(bl, T, [&](int i) { return tok.gate(i); });
+        // Token wave: stage round r (tokens r*fc ..) into buffer r % 2.
+        auto stage = [&](int r) {
+            float* fk = stage0 + (r & 1) * stage_floats;
+            float* fx = fk + fc * DK;
+            float* fw = fx + fc * DV;
+            const int i0 = r * fc;
+            const int cnt = min(fc, T - i0);
+            stage_rows(tok, i0, cnt, fk, fx, nullptr, lane);
+            for (int ii = lane; ii < cnt; ii += 64)
+                fw[ii] = GATED ? expf(bl[T - 1] - bl[i0 + ii]) : 1.0f;
+        };
+
+        if (token_wave) {
+            if constexpr (GATED) gate_prefix(bl, T, lane, [&](int i) { return tok.gate(i); });
+            if (lane == 0) *e0p = (GATED && T > 0) ? expf(bl[T - 1]) : 1.0f;
+            if (T > 0) stage(0);
+        }
+        f4 s[RPT];
+        if (!token_wave) {
+            const float* stile = P.state + (static_cast<size_t>(has_state ? slot : 0) * P.H + h) * DK * DV;
+#pragma unroll
+            for (int j = 0; j < RPT; ++j)
+                s[j] = has_state
+                           ? __builtin_nontemporal_load(reinterpret_cast<const f4*>(stile + (rg + RG * j) * DV + c0))
+                           : f4{0.f, 0.f, 0.f, 0.f};
+        }
         __syncthreads();
-        if (T > 0) {
-            const int last = T - 1;
-            const float e0 = GATED ? expf(bl[last]) : 1.0f;
+        if (!token_wave) {
+            const float e0 = *e0p;
 #pragma unroll
             for (int j = 0; j < RPT; ++j) s[j] *= e0;
-            for (int i0 = 0; i0 < T; i0 += kFoldChunk) {
-                const int cnt = min(kFoldChunk, T - i0);
-                for (int e = tid; e < cnt * DK; e += NT) {
-                    const int ii = e / DK, r = e - ii * DK;
-                    fk[ii * DK + r] = load1(tok.key(i0 + ii) + r);
-                }
-                for (int e = tid; e < cnt * DV; e += NT) {
-                    const int ii = e / DV, c = e - ii * DV;
-                    fx[ii * DV + c] = load1(tok.pooled_value(i0 + ii) + c);
-                }
-                for (int ii = tid; ii < cnt; ii += NT) fw[ii] = GATED ? expf(bl[last] - bl[i0 + ii]) : 1.0f;
-                __syncthreads();
-                for (int ii = 0; ii < cnt; ++ii) {
-                    const f4 x = *reinterpret_cast<const f4*>(fx + ii * DV + c0);
-                    const float w = fw[ii];
+        }
+        auto apply = [&](int r) {
+            const float* fk = stage0 + (r & 1) * stage_floats;
+            const float* fx = fk + fc * DK;
+            const float* fw = fx + fc * DV;
+            const int cnt = min(fc, T - r * fc);
+            for (int ii = 0; ii < cnt; ++ii) {
+                const f4 x = *reinterpret_cast<const f4*>(fx + ii * DV + c0);
+                const float w = fw[ii];
 #pragma unroll
-                    for (int j = 0; j < RPT; ++j) s[j] += (w * fk[ii * DK + rg + RG * j]) * x;
+                for (int j = 0; j < RPT; ++j) s[j] += (w * fk[ii * DK + rg + RG * j]) * x;
+            }
+        };
+        if constexpr (!MULTI) {
+            if (!token_wave && T > 0) apply(0);
+        } else {
+            const int rounds = (T + fc - 1) / fc;
+            for (int r = 0; r < rounds; ++r) {
+                if (token_wave) {
+                    if (r + 1 < rounds) stage(r + 1);
+                } else {
+                    apply(r);
                 }
                 __syncthreads();
             }
         }
-        float* dst = materialize ? P.states_out + (static_cast<size_t>(b) * P.H + h) * DK * DV
-                                 : P.state + (static_cast<size_t>(slot) * P.H + h) * DK * DV;
+        if (!token_wave) {
+            float* dst = materialize ? P.states_out + (static_cast<size_t>(b) * P.H + h) * DK * DV
+                                     : P.state + (static_cast<size_t>(slot) * P.H + h) * DK * DV;
 #pragma unroll
-        for (int j = 0; j < RPT; ++j)
-            __builtin_nontemporal_store(s[j], reinterpret_cast<f4*>(dst + (rg + RG * j) * DV + c0));
+            for (int j = 0; j < RPT; ++j)
+                __builtin_nontemporal_store(s[j], reinterpret_cast<f4*>(dst + (rg + RG * j) * DV + c0));
+        }
     }
 
     if (materialize) return;
-    finish_request(P, b, pn - (fold ? P.m : 0), fold ? P.m / P.block_size : 0);
+    __syncthreads();
+    apply_bookkeeping(P, b, s_last, pn - (fold ? P.m : 0), fold ? P.m / P.block_size : 0);
 }
 
 template <int RULE, int D, typename IO>
 hipError_t launch_fold_t(const TileParams& p, int batch, hipStream_t s) {
     using G = Geo<D, D>;
-    const size_t lds = sizeof(float) * fold_lds_floats(D, D, p.block_size * p.blocks_per_req);
-    fold_kernel<RULE, D, D, IO><<<dim3(static_cast<unsigned>(batch) * p.H), dim3(G::NT), lds, s>>>(p);
+    const int cap = p.block_size * p.blocks_per_req;
+    const size_t lds = sizeof(float) * fold_lds_floats(D, D, cap, p.fold_chunk);
+    const int most = p.mode == MODE_MATERIALIZE ? cap : p.m;  // most positions one tile applies
+    const dim3 grid(static_cast<unsigned>(batch) * p.H), block(G::NTHREADS);
+    if (most <= p.fold_chunk)
+        fold_kernel<RULE, D, D, IO, false><<<grid, block, lds, s>>>(p);
+    else
+        fold_kernel<RULE, D, D, IO, true><<<grid, block, lds, s>>>(p);
     return hipGetLastError();
 }
 

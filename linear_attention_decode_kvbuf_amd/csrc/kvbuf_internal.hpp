@@ -26,6 +26,7 @@ struct TileParams {
     int32_t n;      // tokens appended per request by this call (decode 1, verify n)
     int32_t mode;   // Mode
     int32_t fuse;   // eager policy: fold inside decode / commit
+    int32_t fold_chunk;  // tokens staged in LDS per fold round (0: this launch never folds)
     float scale;
     float* state;
     void* key;
@@ -56,6 +57,7 @@ hipError_t launch_recurrent(const TileParams& p, int rule, int d, int io, int ba
 inline bool supported_dim(int d) { return d == 16 || d == 64 || d == 128; }
 
 constexpr int kMaxDrafts = 8;
+constexpr int kFoldChunk = 32;  // most tokens staged in LDS per fold round
 constexpr int kMaxTableRow = 64;
 
 }  // namespace kvbuf

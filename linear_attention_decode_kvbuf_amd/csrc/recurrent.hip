@@ -11,13 +11,15 @@
 //   output   o = S^T (scale q) with the updated S.
 // One workgroup per tile reads the 64 KiB state once and writes it once:
 // 2 |S| bytes of HBM traffic per token, which is what the buffered path avoids.
+// As in the buffered kernels, the state waves put the tile in flight while
+// the token wave stages q, k, v and the gate.
 #include "device_common.hpp"
 
 namespace kvbuf {
 namespace {
 
 template <int RULE, int DK, int DV, typename IO>
-__global__ __launch_bounds__((Geo<DK, DV>::NT)) void recurrent_kernel(TileParams P) {
+__global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void recurrent_kernel(TileParams P) {
     using G = Geo<DK, DV>;
     constexpr int NT = G::NT, TPR = G::TPR, RG = G::RG, RPT = G::RPT;
     constexpr bool DELTA = RULE == KVBUF_RULE_DELTA;
@@ -25,13 +27,17 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void recurrent_kernel(TileParams
 
     __shared__ float qs[DK];
     __shared__ float kf[DK];
+    __shared__ float vf[DV];
     __shared__ float red[RG * DV];
     __shared__ float sk[DELTA ? DV : 1];
+    __shared__ float gb[2];  // gamma, beta
 
     const int tile = blockIdx.x;
     const int b = tile / P.H;
     const int h = tile - b * P.H;
     const int tid = threadIdx.x;
+    const bool token_wave = tid >= NT;
+    const int lane = tid - NT;
     const int rg = tid / TPR;
     const int c0 = (tid % TPR) * 4;
 
@@ -41,54 +47,67 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void recurrent_kernel(TileParams
         return;
     }
     float* stile = P.state + (static_cast<size_t>(slot) * P.H + h) * DK * DV;
-    f4 s[RPT];
-#pragma unroll
-    for (int j = 0; j < RPT; ++j)
-        s[j] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(stile + (rg + RG * j) * DV + c0));
-
     const size_t in_row = static_cast<size_t>(b) * P.H + h;
-    const IO* q = static_cast<const IO*>(P.q) + in_row * DK;
-    const IO* k = static_cast<const IO*>(P.k) + in_row * DK;
-    for (int r = tid; r < DK; r += NT) {
-        qs[r] = P.scale * load1(q + r);
-        kf[r] = load1(k + r);
+    if (token_wave) {
+        const IO* q = static_cast<const IO*>(P.q) + in_row * DK;
+        const IO* k = static_cast<const IO*>(P.k) + in_row * DK;
+        const IO* v = static_cast<const IO*>(P.v) + in_row * DV;
+        for (int r = lane; r < DK; r += 64) {
+            qs[r] = P.scale * load1(q + r);
+            kf[r] = load1(k + r);
+        }
+        for (int c = lane; c < DV; c += 64) vf[c] = load1(v + c);
+        if (lane == 0) {
+            gb[0] = GATED ? expf(P.g[in_row]) : 1.0f;
+            gb[1] = DELTA ? P.beta[in_row] : 0.0f;
+        }
     }
-    f4 x = load4(static_cast<const IO*>(P.v) + in_row * DV + c0);
-    const float gamma = GATED ? expf(P.g[in_row]) : 1.0f;
+    // (after the token-wave block, so its registers are not allocated on top
+    // of the tile's)
+    f4 s[RPT];
+    if (!token_wave) {
+#pragma unroll
+        for (int j = 0; j < RPT; ++j)
+            s[j] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(stile + (rg + RG * j) * DV + c0));
+    }
     __syncthreads();
+    const float gamma = gb[0];
+    f4 x = *reinterpret_cast<const f4*>(vf + c0);
 
     if constexpr (DELTA) {
-        f4 a = f4{0.f, 0.f, 0.f, 0.f};
+        if (!token_wave) {
+            f4 a = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int j = 0; j < RPT; ++j) a += s[j] * kf[rg + RG * j];
-        *reinterpret_cast<f4*>(red + rg * DV + c0) = a;
+            for (int j = 0; j < RPT; ++j) a += s[j] * kf[rg + RG * j];
+            *reinterpret_cast<f4*>(red + rg * DV + c0) = a;
+        }
         __syncthreads();
-        for (int c = tid; c < DV; c += NT) {
+        for (int c = tid; c < DV; c += G::NTHREADS) {
             float sum = 0.f;
 #pragma unroll
             for (int g2 = 0; g2 < RG; ++g2) sum += red[g2 * DV + c];
             sk[c] = sum;
         }
         __syncthreads();
-        const float beta = P.beta[in_row];
         const f4 skv = *reinterpret_cast<const f4*>(sk + c0);
-        x = beta * (x - gamma * skv);
+        x = gb[1] * (x - gamma * skv);
     }
 
-    f4 o = f4{0.f, 0.f, 0.f, 0.f};
+    if (!token_wave) {
+        f4 o = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < RPT; ++j) {
-        const int r = rg + RG * j;
-        s[j] = gamma * s[j] + kf[r] * x;
-        o += s[j] * qs[r];
+        for (int j = 0; j < RPT; ++j) {
+            const int r = rg + RG * j;
+            s[j] = gamma * s[j] + kf[r] * x;
+            o += s[j] * qs[r];
+        }
+#pragma unroll
+        for (int j = 0; j < RPT; ++j)
+            __builtin_nontemporal_store(s[j], reinterpret_cast<f4*>(stile + (rg + RG * j) * DV + c0));
+        *reinterpret_cast<f4*>(red + rg * DV + c0) = o;
     }
-#pragma unroll
-    for (int j = 0; j < RPT; ++j)
-        __builtin_nontemporal_store(s[j], reinterpret_cast<f4*>(stile + (rg + RG * j) * DV + c0));
-
-    *reinterpret_cast<f4*>(red + rg * DV + c0) = o;
     __syncthreads();
-    for (int c = tid; c < DV; c += NT) {
+    for (int c = tid; c < DV; c += G::NTHREADS) {
         float sum = 0.f;
 #pragma unroll
         for (int g2 = 0; g2 < RG; ++g2) sum += red[g2 * DV + c];
@@ -99,7 +118,7 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void recurrent_kernel(TileParams
 template <int RULE, int D, typename IO>
 hipError_t launch_rec_t(const TileParams& p, int batch, hipStream_t s) {
     using G = Geo<D, D>;
-    recurrent_kernel<RULE, D, D, IO><<<dim3(static_cast<unsigned>(batch) * p.H), dim3(G::NT), 0, s>>>(p);
+    recurrent_kernel<RULE, D, D, IO><<<dim3(static_cast<unsigned>(batch) * p.H), dim3(G::NTHREADS), 0, s>>>(p);
     return hipGetLastError();
 }
 
