@@ -16,10 +16,11 @@ typedef uint16_t bf16_bits;  // bfloat16 kept as its raw bits
 // fp32 state read as rows of d_v floats.
 //
 // The first NT threads ("state waves") hold the tile in registers: a thread
-// owns 4 consecutive columns (one 128-bit load per row) of RPT rows; TPR
-// threads cover a row and RG row groups split the rows.  Row j of a thread is
-// r = rg + RG * j, so the two row groups of a wave read two adjacent rows and
-// every load instruction of a wave covers a contiguous 2 * d_v * 4 bytes.
+// owns 4 consecutive columns (one 128-bit load per row) of RPT consecutive
+// rows r = rg * RPT + j; TPR threads cover a row and RG row groups split the
+// rows.  Every load instruction of a wave covers whole 512-byte rows, and a
+// thread's rows are 512 bytes apart, so its RPT loads need only two base
+// addresses (the immediate offset reaches 4 KiB).
 //
 // One more wave ("token wave", 64 lanes) does everything that depends on the
 // individual tokens: staging queries, gate prefix sums, q . k scores, the

@@ -128,7 +128,7 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void fold_kernel(TileParam
 #pragma unroll
             for (int j = 0; j < RPT; ++j)
                 s[j] = has_state
-                           ? __builtin_nontemporal_load(reinterpret_cast<const f4*>(stile + (rg + RG * j) * DV + c0))
+                           ? __builtin_nontemporal_load(reinterpret_cast<const f4*>(stile + (rg * RPT + j) * DV + c0))
                            : f4{0.f, 0.f, 0.f, 0.f};
         }
         __syncthreads();
@@ -146,7 +146,7 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void fold_kernel(TileParam
                 const f4 x = *reinterpret_cast<const f4*>(fx + ii * DV + c0);
                 const float w = fw[ii];
 #pragma unroll
-                for (int j = 0; j < RPT; ++j) s[j] += (w * fk[ii * DK + rg + RG * j]) * x;
+                for (int j = 0; j < RPT; ++j) s[j] += (w * fk[ii * DK + rg * RPT + j]) * x;
             }
         };
         if constexpr (!MULTI) {
@@ -167,7 +167,7 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void fold_kernel(TileParam
                                      : P.state + (static_cast<size_t>(slot) * P.H + h) * DK * DV;
 #pragma unroll
             for (int j = 0; j < RPT; ++j)
-                __builtin_nontemporal_store(s[j], reinterpret_cast<f4*>(dst + (rg + RG * j) * DV + c0));
+                __builtin_nontemporal_store(s[j], reinterpret_cast<f4*>(dst + (rg * RPT + j) * DV + c0));
         }
     }
 

@@ -51,6 +51,7 @@ struct TileParams {
 // enqueues one grid of B * H workgroups.  Return hipSuccess or the launch error.
 hipError_t launch_chunk(const TileParams& p, int rule, int d, int io, int batch, hipStream_t s);
 hipError_t launch_fold(const TileParams& p, int rule, int d, int io, int batch, hipStream_t s);
+int chunk_fold_limit(int d);
 hipError_t launch_recurrent(const TileParams& p, int rule, int d, int io, int batch, hipStream_t s);
 
 // Head dims with compiled kernels (d_k == d_v).

@@ -68,7 +68,7 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void recurrent_kernel(Tile
     if (!token_wave) {
 #pragma unroll
         for (int j = 0; j < RPT; ++j)
-            s[j] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(stile + (rg + RG * j) * DV + c0));
+            s[j] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(stile + (rg * RPT + j) * DV + c0));
     }
     __syncthreads();
     const float gamma = gb[0];
@@ -78,7 +78,7 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void recurrent_kernel(Tile
         if (!token_wave) {
             f4 a = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int j = 0; j < RPT; ++j) a += s[j] * kf[rg + RG * j];
+            for (int j = 0; j < RPT; ++j) a += s[j] * kf[rg * RPT + j];
             *reinterpret_cast<f4*>(red + rg * DV + c0) = a;
         }
         __syncthreads();
@@ -97,13 +97,13 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void recurrent_kernel(Tile
         f4 o = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < RPT; ++j) {
-            const int r = rg + RG * j;
+            const int r = rg * RPT + j;
             s[j] = gamma * s[j] + kf[r] * x;
             o += s[j] * qs[r];
         }
 #pragma unroll
         for (int j = 0; j < RPT; ++j)
-            __builtin_nontemporal_store(s[j], reinterpret_cast<f4*>(stile + (rg + RG * j) * DV + c0));
+            __builtin_nontemporal_store(s[j], reinterpret_cast<f4*>(stile + (rg * RPT + j) * DV + c0));
         *reinterpret_cast<f4*>(red + rg * DV + c0) = o;
     }
     __syncthreads();
