@@ -169,6 +169,81 @@ def cpu_baseline(synth, oracle, np, torch, w, ring, max_tiles=None):
     }
 
 
+def verify_leg(kb, synth, torch, dev, args):
+    """B=128 H=32 d=128 m=8 gated: per n, one kvbuf_verify of n drafts then
+    one kvbuf_commit of the accepted prefixes (the fold, when a commit fills
+    the buffer, runs inside the commit)."""
+    w = synth.workload(4)
+    tiles = w.B * w.H
+    out = {}
+    for n in (1, 2, 4, 8):
+        kv = build_kv(kb, synth, torch, w, kb.FLUSH_EAGER, dev)
+        drafts = [synth.device_token_inputs(w, c, dev, n=n, stream_base=100) for c in range(4)]
+        accs = [torch.from_numpy(synth.accepted_lengths(w, c, w.B, n)).to(dev) for c in range(4)]
+        obuf = torch.empty((w.B, n, w.H, w.dv), dtype=torch.float32, device=dev)
+
+        def call(c):
+            d = drafts[c % 4]
+            return [lambda: kv.verify(d["q"], d["k"], d["v"], d["g"], out=obuf),
+                    lambda: kv.commit(n, accs[c % 4])]
+
+        for c in range(10):
+            for f in call(c):
+                f()
+        launches = []
+        for c in range(8):
+            launches += call(c)
+        per = per_launch_ms(torch, launches, 20)
+        torch.cuda.synchronize()
+        assert int(kv.error.item()) == 0
+        ver = sum(per[0::2]) / 8
+        com = sum(per[1::2]) / 8
+        accepted = float(sum(int(a.sum()) for a in accs[:4]) / 4)
+        # one state read serves all n drafts
+        vbytes = tiles * (4 * w.dk * w.dv + 2 * n * (2 * w.dk + w.dv) + 4 * n * w.dv)
+        out["n%d" % n] = {"verify_ms": ver, "commit_ms": com,
+                          "verify_hbm_gbps": vbytes / (ver * 1e-3) / 1e9,
+                          "accepted_tokens_per_s": accepted / ((ver + com) * 1e-3)}
+        del kv
+    return out
+
+
+def delta_leg(kb, synth, torch, dev, args):
+    """Gated delta rule, B=512 (256 requests with a state, 256 served from the
+    buffer alone), H=32 d=128 m=64: one decode launch per step (plus the fold
+    launch that follows it, since 64 positions exceed one staging pass), over
+    a full 64-step cycle."""
+    w = synth.workload(5)
+    kv = kb.KVBuffer(batch=w.B, heads=w.H, d=w.dk, m=w.m, block_size=w.block_size,
+                     blocks_per_req=w.blocks_per_req, num_blocks=w.B * w.blocks_per_req,
+                     num_state_slots=w.B - w.n_short, rule=kb.RULE_DELTA, io_dtype=kb.BF16,
+                     flush=kb.FLUSH_EAGER, device=dev)
+    perm = synth.block_permutation(w, w.B * w.blocks_per_req)
+    kv.block_table.copy_(torch.from_numpy(perm.reshape(w.B, w.blocks_per_req)))
+    slots = torch.full((w.B,), -1, dtype=torch.int32)
+    slots[: w.B - w.n_short] = torch.arange(w.B - w.n_short, dtype=torch.int32)
+    kv.state_slot.copy_(slots)
+    kv.state.copy_(synth.device_initial_state(w, w.B - w.n_short, dev))
+    ring = [synth.device_token_inputs(w, t, dev) for t in range(8)]
+    out = torch.empty((w.B, w.H, w.dv), dtype=torch.float32, device=dev)
+    fns = [(lambda r: (lambda: kv.decode(r["q"], r["k"], r["v"], r["g"], r["beta"], out=out)))(ring[t % 8])
+           for t in range(w.m)]
+    for f in fns:  # one warm cycle
+        f()
+    per = [0.0] * w.m
+    reps = 3
+    for _ in range(reps):
+        # every request starts the cycle empty: the stateful ones folded at
+        # its last step, the buffer-only ones are restarted (capacity 128)
+        kv.occupancy.zero_()
+        per = [a + b / reps for a, b in zip(per, per_launch_ms(torch, fns, 1))]
+    torch.cuda.synchronize()
+    assert int(kv.error.item()) == 0
+    cyc = sum(per)
+    return {"cycle_ms": cyc, "tokens_per_s": w.B * w.m / (cyc * 1e-3),
+            "decode_step_ms_mean": cyc / w.m, "fold_step_ms": per[-1]}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -177,7 +252,7 @@ def main():
     ap.add_argument("--m", type=int, default=8, help="buffer size")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing on the host")
     ap.add_argument("--no-extras", action="store_true", help="skip the m=0 / separate-flush / copy legs")
-    ap.add_argument("--only", choices=["fused", "recurrent", "separate", "copy"], default=None,
+    ap.add_argument("--only", choices=["fused", "recurrent", "separate", "copy", "verify", "delta"], default=None,
                     help="run one leg only (for profiling)")
     args = ap.parse_args()
 
@@ -291,6 +366,14 @@ def main():
         result["copy_ceiling_gbps"] = 2 * src.numel() * 4 / (pc * 1e-3) / 1e9
         del src, dst
 
+    # ---- speculative verification: n drafts, then commit a ~ U{0..n} -------
+    if not args.no_extras and args.only in (None, "verify"):
+        result["verify"] = verify_leg(kb, synth, torch, dev, args)
+
+    # ---- gated delta rule, half stateful / half buffer-only, m = 64 --------
+    if not args.no_extras and args.only in (None, "delta"):
+        result["delta_mixed"] = delta_leg(kb, synth, torch, dev, args)
+
     if args.only not in (None, "fused"):
         print(json.dumps(result))
         return
@@ -327,7 +410,8 @@ def main():
         "roofline": result["roofline"],
         "cpu_baseline": cpu,
     }
-    for key in ("per_occupancy_ms", "m0_recurrent", "separate_flush", "copy_ceiling_gbps"):
+    for key in ("per_occupancy_ms", "m0_recurrent", "separate_flush", "copy_ceiling_gbps", "verify",
+                "delta_mixed"):
         if key in result:
             line[key] = result[key]
     print(json.dumps(line))
