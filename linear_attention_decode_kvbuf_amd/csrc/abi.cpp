@@ -67,6 +67,7 @@ kvbuf_status check_tokens(const kvbuf_layout* L, const void* q, const void* k, c
 
 TileParams make_params(const kvbuf_layout* L, const kvbuf_pools* P, const kvbuf_batch* B) {
     TileParams t{};
+    t.batch = B->size;
     t.H = L->num_heads;
     t.block_size = L->block_size;
     t.blocks_per_req = L->blocks_per_req;

@@ -76,10 +76,11 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
     extern __shared__ float lds[];
     __shared__ int32_t s_row[kMaxTableRow];
     __shared__ int s_last;
+    __shared__ unsigned s_bad;
 
-    const int tile = blockIdx.x;
-    const int b = tile / P.H;
-    const int h = tile - b * P.H;
+    const TileIndex ti = tile_index(P);
+    const int b = ti.b;
+    const int h = ti.h;
     const int tid = threadIdx.x;
     const int rg = tid / TPR;
     const int c0 = (tid % TPR) * 4;
@@ -92,17 +93,20 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
     // ---- request metadata -----------------------------------------------------
     const int p = P.occ[b];
     const int slot = direct ? -1 : P.slot[b];
-    unsigned bad = (p < 0) ? KVBUF_DEVERR_OVERFLOW : load_row(P, b, p + n, s_row, 0);
-    if (slot >= P.num_slots) bad |= KVBUF_DEVERR_SLOT;
-    if (bad) {
-        report(P, bad);
+    if (tid < 64) {
+        unsigned bad = stage_row(P, b, p + n, s_row, tid);
+        if (slot >= P.num_slots) bad |= KVBUF_DEVERR_SLOT;
+        if (tid == 0) s_bad = bad;
+    }
+    __syncthreads();  // every wave has read the metadata; s_row and s_bad are complete
+    if (s_bad) {
+        report(P, s_bad);
         return;  // the whole request is skipped by all of its workgroups
     }
     const bool has_state = slot >= 0;
     const int T = p + n;                       // positions touched by this call
     const bool fold = P.fold_chunk > 0 && has_state && T >= P.m;  // launcher: fold_chunk >= m
     const bool advance = P.mode != MODE_VERIFY;  // drafts do not advance the occupancy
-    __syncthreads();  // every wave has read the metadata; s_row is complete
     // The ticket's round trip overlaps everything below; its result is read
     // at the very end.
     int last = 0;

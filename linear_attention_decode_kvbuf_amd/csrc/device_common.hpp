@@ -264,6 +264,19 @@ __device__ __forceinline__ void stage_rows(const TileTokens<DK, DV, IO, XIO>& to
     }
 }
 
+// Workgroups are numbered head-major: workgroup w serves request w % B and
+// head w / B.  The H workgroups of one request are therefore dispatched B
+// apart instead of back to back, so their per-request ticket atomics (one
+// counter per request) do not queue up on one address at the same moment.
+struct TileIndex {
+    int b, h;
+};
+__device__ __forceinline__ TileIndex tile_index(const TileParams& P) {
+    const int w = blockIdx.x;
+    const int h = w / P.batch;
+    return TileIndex{w - h * P.batch, h};
+}
+
 // Per-request bookkeeping.  All H workgroups of a request read its occupancy,
 // state slot and table row; the last of them to finish with those values
 // (found with a per-request ticket counter) applies the update: the occupancy
@@ -304,22 +317,23 @@ __device__ __forceinline__ void report(const TileParams& P, unsigned bits) {
     if (bits && P.err && threadIdx.x == 0) atomicOr(reinterpret_cast<unsigned*>(P.err), bits);
 }
 
-// Checks the request's buffer positions [0, end) against the pool; thread
-// `writer` copies the table entries that cover them to LDS.  Returns
-// KVBUF_DEVERR_* bits (0 = usable).
-__device__ __forceinline__ unsigned load_row(const TileParams& P, int b, int end, int32_t* s_row,
-                                             int writer) {
-    const int bpr = P.blocks_per_req;
+// One wave (lane = 0..63) copies the request's whole table row to LDS with a
+// single vector load -- it does not wait for the occupancy, so the row and
+// the occupancy arrive in the same round trip -- and checks the block ids
+// that cover buffer positions [0, end).  Returns KVBUF_DEVERR_* bits, the
+// same in every lane (0 = usable).
+__device__ __forceinline__ unsigned stage_row(const TileParams& P, int b, int end, int32_t* s_row, int lane) {
+    const int bpr = P.blocks_per_req;  // <= 64 (host-checked)
+    int blk = 0;
+    if (lane < bpr) {
+        blk = P.table[static_cast<size_t>(b) * bpr + lane];
+        s_row[lane] = blk;
+    }
     const int cap = P.block_size * bpr;
     if (end < 0 || end > cap) return KVBUF_DEVERR_OVERFLOW;
     const int nblk = (end + P.block_size - 1) / P.block_size;
-    unsigned bad = 0;
-    for (int j = 0; j < nblk; ++j) {
-        const int blk = P.table[static_cast<size_t>(b) * bpr + j];
-        if (blk < 0 || blk >= P.num_blocks) bad |= KVBUF_DEVERR_BLOCK;
-        if (static_cast<int>(threadIdx.x) == writer) s_row[j] = blk;
-    }
-    return bad;
+    const bool badblk = lane < nblk && (blk < 0 || blk >= P.num_blocks);
+    return __ballot(badblk) ? KVBUF_DEVERR_BLOCK : 0u;
 }
 
 }  // namespace kvbuf

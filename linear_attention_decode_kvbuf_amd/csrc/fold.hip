@@ -48,10 +48,11 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void fold_kernel(TileParam
     extern __shared__ float lds[];
     __shared__ int32_t s_row[kMaxTableRow];
     __shared__ int s_last;
+    __shared__ unsigned s_bad;
 
-    const int tile = blockIdx.x;
-    const int b = tile / P.H;
-    const int h = tile - b * P.H;
+    const TileIndex ti = tile_index(P);
+    const int b = ti.b;
+    const int h = ti.h;
     const int tid = threadIdx.x;
     const bool token_wave = tid >= NT;
     const int lane = tid - NT;
@@ -75,18 +76,17 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void fold_kernel(TileParam
     const bool fold = !materialize && has_state && P.m > 0 && pn >= P.m &&
                       (P.mode == MODE_FLUSH || P.fuse);
     const int T = materialize ? p : (fold ? P.m : 0);  // positions applied
-    if (!bad) bad |= load_row(P, b, T, s_row, NT);
-    if (bad) {
-        report(P, bad);
+    if (token_wave) {
+        const unsigned bb = bad | stage_row(P, b, T, s_row, lane);
+        if (lane == 0) s_bad = bb;
+    }
+    __syncthreads();  // every wave has read the metadata; s_row and s_bad are complete
+    if (s_bad) {
+        report(P, s_bad);
         return;
     }
     if (!materialize && !fold && a == 0) return;  // nothing changes for this request
-    if (!materialize) {
-        // This workgroup is done with the request's metadata once every wave
-        // is past this barrier (the table row is copied to LDS).
-        __syncthreads();
-        if (tid == NT) s_last = take_ticket(P, b);
-    }
+    if (!materialize && tid == NT) s_last = take_ticket(P, b);
 
     if (materialize || fold) {
         const int fc = P.fold_chunk;

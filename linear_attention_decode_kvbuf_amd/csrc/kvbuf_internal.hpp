@@ -22,6 +22,7 @@ enum Mode : int32_t {
 
 // Kernel arguments, passed by value.  Pointers are device pointers.
 struct TileParams {
+    int32_t batch;  // B; workgroup w serves request w % B, head w / B
     int32_t H, block_size, blocks_per_req, m, num_blocks, num_slots;
     int32_t n;      // tokens appended per request by this call (decode 1, verify n)
     int32_t mode;   // Mode

@@ -32,9 +32,9 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void recurrent_kernel(Tile
     __shared__ float sk[DELTA ? DV : 1];
     __shared__ float gb[2];  // gamma, beta
 
-    const int tile = blockIdx.x;
-    const int b = tile / P.H;
-    const int h = tile - b * P.H;
+    const TileIndex ti = tile_index(P);
+    const int b = ti.b;
+    const int h = ti.h;
     const int tid = threadIdx.x;
     const bool token_wave = tid >= NT;
     const int lane = tid - NT;
