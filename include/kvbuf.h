@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define KVBUF_ABI_VERSION 1
+#define KVBUF_ABI_VERSION 2
 
 typedef enum kvbuf_status {
     KVBUF_OK = 0,
@@ -118,15 +118,12 @@ typedef struct kvbuf_pools {
  *                                    offset p % block_size.  A fold moves the
  *                                    m / block_size leading blocks to the back.
  *   occupancy   [B]                  tokens buffered since the last fold
- *   ticket      [B]                  workspace; must be all zero before the first
- *                                    call and is left all zero by every call
  *   error       [1] or NULL          KVBUF_DEVERR_* bits are OR-ed into it */
 typedef struct kvbuf_batch {
     int32_t size;
     int32_t* state_slot;
     int32_t* block_table;
     int32_t* occupancy;
-    int32_t* ticket;
     int32_t* error;
 } kvbuf_batch;
 

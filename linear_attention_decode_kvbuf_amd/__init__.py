@@ -46,7 +46,7 @@ class Pools(ctypes.Structure):
 class Batch(ctypes.Structure):
     _fields_ = [("size", ctypes.c_int32), ("state_slot", ctypes.c_void_p),
                 ("block_table", ctypes.c_void_p), ("occupancy", ctypes.c_void_p),
-                ("ticket", ctypes.c_void_p), ("error", ctypes.c_void_p)]
+                ("error", ctypes.c_void_p)]
 
 
 class KVBufError(RuntimeError):
@@ -166,7 +166,7 @@ class KVBuffer:
     key        [num_blocks, H, block_size, d_k] io dtype
     value      [num_blocks, H, block_size, d_v] io dtype (fp32 for the delta rule)
     gate       [num_blocks, H, block_size] fp32 (None for the linear rule)
-    state_slot, occupancy, ticket [B] int32; block_table [B, blocks_per_req] int32
+    state_slot, occupancy [B] int32; block_table [B, blocks_per_req] int32
     error      [1] int32
     """
 
@@ -201,14 +201,13 @@ class KVBuffer:
         self.block_table = torch.arange(batch * blocks_per_req, dtype=i32, device=dev).reshape(
             batch, blocks_per_req) % max(num_blocks, 1)
         self.occupancy = torch.zeros(batch, dtype=i32, device=dev)
-        self.ticket = torch.zeros(batch, dtype=i32, device=dev)
         self.error = torch.zeros(1, dtype=i32, device=dev)
         self._refresh()
 
     def _refresh(self):
         self.pools = Pools(_ptr(self.state), _ptr(self.key), _ptr(self.value), _ptr(self.gate))
         self.batch = Batch(self.B, _ptr(self.state_slot), _ptr(self.block_table), _ptr(self.occupancy),
-                           _ptr(self.ticket), _ptr(self.error))
+                           _ptr(self.error))
 
     @property
     def capacity(self):

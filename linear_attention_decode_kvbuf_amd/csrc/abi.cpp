@@ -1,6 +1,7 @@
-// The C ABI of libkvbuf: argument validation on the host, then one kernel
-// launch on the caller's stream.  No allocation, no synchronisation, no
-// global mutable state.
+// The C ABI of libkvbuf: argument validation on the host, then the compute
+// launch and (for calls that move the buffer) a small bookkeeping launch on
+// the caller's stream.  No allocation, no synchronisation, no global mutable
+// state.
 #include <hip/hip_runtime.h>
 
 #include "kvbuf.h"
@@ -26,18 +27,20 @@ kvbuf_status check_layout(const kvbuf_layout* L, bool need_buffer) {
         if (L->m % L->block_size != 0) return KVBUF_ECAPACITY;
         if (static_cast<long long>(L->block_size) * L->blocks_per_req < L->m) return KVBUF_ECAPACITY;
         if (static_cast<long long>(L->block_size) * L->blocks_per_req > 4096) return KVBUF_ECAPACITY;
+        // pool rows (block, head, slot) are indexed with 32-bit integers
+        if (static_cast<long long>(L->num_blocks) * L->num_heads * L->block_size > 0x7fffffffLL)
+            return KVBUF_ECAPACITY;
     }
     return KVBUF_OK;
 }
 
-kvbuf_status check_batch(const kvbuf_layout* L, const kvbuf_batch* B, bool need_ticket) {
+kvbuf_status check_batch(const kvbuf_layout* L, const kvbuf_batch* B) {
     if (!B) return KVBUF_EINVAL;
     if (B->size < 0) return KVBUF_EINVAL;
     if (B->size == 0) return KVBUF_OK;
     if (!B->state_slot) return KVBUF_EINVAL;
     if (L->m == 0) return KVBUF_OK;  // recurrent mode: no buffer metadata
     if (!B->block_table || !B->occupancy) return KVBUF_EINVAL;
-    if (need_ticket && !B->ticket) return KVBUF_EINVAL;
     return KVBUF_OK;
 }
 
@@ -83,7 +86,6 @@ TileParams make_params(const kvbuf_layout* L, const kvbuf_pools* P, const kvbuf_
     t.slot = B->state_slot;
     t.table = B->block_table;
     t.occ = B->occupancy;
-    t.ticket = B->ticket;
     t.err = B->error;
     return t;
 }
@@ -99,13 +101,21 @@ kvbuf_status from_hip(hipError_t e) { return e == hipSuccess ? KVBUF_OK : KVBUF_
         if (st_ != KVBUF_OK) return st_;   \
     } while (0)
 
+// Flush and commit: the fold launch, then the bookkeeping launch that
+// advances occupancies and rotates table rows.
+kvbuf_status fold_then_advance(const TileParams& t, const kvbuf_layout* L, hipStream_t stream) {
+    hipError_t e = kvbuf::launch_fold(t, L->rule, L->d_k, L->io_dtype, t.batch, stream);
+    if (e == hipSuccess) e = kvbuf::launch_advance(t, stream);
+    return from_hip(e);
+}
+
 kvbuf_status chunk_call(const kvbuf_layout* layout, const kvbuf_pools* pools,
                         const kvbuf_batch* batch, int mode, int n, const void* q,
                         const void* k, const void* v, const float* g, const float* beta,
                         float* out, hipStream_t stream) {
     const bool direct = mode == kvbuf::MODE_DIRECT;
     KVBUF_TRY(check_layout(layout, mode != kvbuf::MODE_DECODE));
-    KVBUF_TRY(check_batch(layout, batch, mode != kvbuf::MODE_VERIFY));
+    KVBUF_TRY(check_batch(layout, batch));
     KVBUF_TRY(check_pools(layout, pools, !direct));
     if (batch->size == 0) return KVBUF_OK;
     KVBUF_TRY(check_tokens(layout, q, k, v, g, beta, out));
@@ -132,10 +142,12 @@ kvbuf_status chunk_call(const kvbuf_layout* layout, const kvbuf_pools* pools,
         return from_hip(kvbuf::launch_recurrent(t, layout->rule, layout->d_k, layout->io_dtype,
                                                 batch->size, stream));
     hipError_t e = kvbuf::launch_chunk(t, layout->rule, layout->d_k, layout->io_dtype, batch->size, stream);
+    if (e == hipSuccess && mode != kvbuf::MODE_VERIFY) e = kvbuf::launch_advance(t, stream);
     if (e == hipSuccess && eager_decode && !fused) {
         t.mode = kvbuf::MODE_FLUSH;
         t.fold_chunk = fold_chunk(layout->m);
         e = kvbuf::launch_fold(t, layout->rule, layout->d_k, layout->io_dtype, batch->size, stream);
+        if (e == hipSuccess) e = kvbuf::launch_advance(t, stream);
     }
     return from_hip(e);
 }
@@ -168,22 +180,21 @@ kvbuf_status kvbuf_verify(const kvbuf_layout* layout, const kvbuf_pools* pools,
 kvbuf_status kvbuf_flush(const kvbuf_layout* layout, const kvbuf_pools* pools,
                          const kvbuf_batch* batch, hipStream_t stream) {
     KVBUF_TRY(check_layout(layout, false));
-    KVBUF_TRY(check_batch(layout, batch, true));
+    KVBUF_TRY(check_batch(layout, batch));
     KVBUF_TRY(check_pools(layout, pools, true));
     if (batch->size == 0 || layout->m == 0) return KVBUF_OK;
     KVBUF_TRY(check_grid(layout, batch));
     TileParams t = make_params(layout, pools, batch);
     t.mode = kvbuf::MODE_FLUSH;
     t.fold_chunk = fold_chunk(layout->m);
-    return from_hip(kvbuf::launch_fold(t, layout->rule, layout->d_k, layout->io_dtype,
-                                       batch->size, stream));
+    return fold_then_advance(t, layout, stream);
 }
 
 kvbuf_status kvbuf_commit(const kvbuf_layout* layout, const kvbuf_pools* pools,
                           const kvbuf_batch* batch, int32_t n, const int32_t* accepted,
                           hipStream_t stream) {
     KVBUF_TRY(check_layout(layout, true));
-    KVBUF_TRY(check_batch(layout, batch, true));
+    KVBUF_TRY(check_batch(layout, batch));
     KVBUF_TRY(check_pools(layout, pools, true));
     if (batch->size == 0) return KVBUF_OK;
     if (!accepted) return KVBUF_EINVAL;
@@ -194,14 +205,13 @@ kvbuf_status kvbuf_commit(const kvbuf_layout* layout, const kvbuf_pools* pools,
     t.n = n;
     t.fold_chunk = fold_chunk(layout->m);
     t.accepted = accepted;
-    return from_hip(kvbuf::launch_fold(t, layout->rule, layout->d_k, layout->io_dtype,
-                                       batch->size, stream));
+    return fold_then_advance(t, layout, stream);
 }
 
 kvbuf_status kvbuf_materialize(const kvbuf_layout* layout, const kvbuf_pools* pools,
                                const kvbuf_batch* batch, float* states, hipStream_t stream) {
     KVBUF_TRY(check_layout(layout, true));
-    KVBUF_TRY(check_batch(layout, batch, false));
+    KVBUF_TRY(check_batch(layout, batch));
     KVBUF_TRY(check_pools(layout, pools, false));
     if (batch->size == 0) return KVBUF_OK;
     if (!states) return KVBUF_EINVAL;

@@ -31,39 +31,74 @@
 namespace kvbuf {
 namespace {
 
-// LDS layout in floats (shared by the launcher, for the size, and the kernel).
+// LDS layout in 4-byte words (shared by the launcher, for the size, and the
+// kernel).  Token rows are kept as the raw bits they were loaded with (bf16
+// or fp32) and converted where they are used, so that no converted copy
+// occupies registers while the state tile is in flight.
 struct ChunkLds {
-    int qs, ks, bl, cq, ck, es, vs, fk, fx, fw, red, sq, sk, total;
+    int pos, qr, kdr, bl, cq, ck, es, kr, vr, fw, red, sq, sk, total;
 };
 
 __host__ __device__ inline int round4(int x) { return (x + 3) & ~3; }
 
+// io / xo: bytes per element of the key plane and of the value plane.
 // NG positions are staged per pass; `fold` = the eager fold may happen in
-// this launch (then m <= NG and its m keys and values are staged too).
+// this launch (then m <= NG and its keys and values are the first pass's).
 __host__ __device__ inline ChunkLds chunk_lds(int rule, int DK, int DV, int NQ, int RG, int NG, int cap,
-                                              int m, bool fold) {
+                                              int m, bool fold, int io, int xo) {
     ChunkLds L;
     int o = 0;
     const bool delta = rule == KVBUF_RULE_DELTA;
-    L.qs = o; o += NQ * DK;                       // scaled queries of the new tokens
-    L.ks = o; o += delta ? NQ * DK : 0;           // keys of the new tokens (delta rule)
-    L.bl = o; o += round4(cap);                   // log-gates, then their prefix sums
-    L.cq = o; o += NQ * round4(cap);              // e^{b_t - b_i} (q_t . k_i)
-    L.ck = o; o += delta ? NQ * round4(cap) : 0;  // e^{b_t - b_i} (k_t . k_i)
-    L.es = o; o += round4(NQ + 1);                // e^{b_t} per new token; [NQ]: e^{b_{m-1}}
-    L.vs = o; o += NG * DV;                       // values of one pass of positions
-    L.fk = o; o += fold ? m * DK : 0;             // fold: keys,
-    L.fx = o; o += fold ? m * DV : 0;             //   values,
-    L.fw = o; o += fold ? round4(m) : 0;          //   weights
-    L.red = o; o += RG * DV * (delta ? 2 : 1);    // row-group partial sums
-    L.sq = o; o += delta ? NQ * DV : 0;           // reduced outputs before the new tokens
-    L.sk = o; o += delta ? NQ * DV : 0;           // reduced e^{b_t} S0^T k_t + buffer part
+    L.pos = o; o += round4(cap);                        // pool row of each buffer position
+    L.qr = o; o += round4(NQ * DK * io / 4);            // queries of the new tokens (raw)
+    L.kdr = o; o += delta ? round4(NQ * DK * io / 4) : 0;  // keys of the new tokens (delta rule)
+    L.bl = o; o += round4(cap);                         // log-gates, then their prefix sums
+    L.cq = o; o += NQ * round4(cap);                    // e^{b_t - b_i} scale (q_t . k_i)
+    L.ck = o; o += delta ? NQ * round4(cap) : 0;        // e^{b_t - b_i} (k_t . k_i)
+    L.es = o; o += round4(NQ + 1);                      // e^{b_t} per new token; [NQ]: e^{b_{m-1}}
+    L.kr = o; o += round4(NG * DK * io / 4);            // keys of one pass of positions (raw)
+    L.vr = o; o += round4(NG * DV * xo / 4);            // their values (raw)
+    L.fw = o; o += fold ? round4(m) : 0;                // fold weights
+    L.red = o; o += RG * DV * (delta ? 2 : 1);          // row-group partial sums
+    L.sq = o; o += delta ? NQ * DV : 0;                 // reduced outputs before the new tokens
+    L.sk = o; o += delta ? NQ * DV : 0;                 // reduced e^{b_t} S0^T k_t + buffer part
     L.total = o;
     return L;
 }
 
+// q . k over one 16-lane share of a row, from raw chunks (bf16 pairs through
+// the packed bf16 dot instruction: the products are exact in fp32).
+template <typename T, int E>
+__device__ __forceinline__ float chunk_dot(const RawChunk<T, E>& a, const RawChunk<T, E>& b) {
+    float acc = 0.f;
+    if constexpr (sizeof(T) == 2 && E >= 2) {
+        typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+        for (int w = 0; w < RawChunk<T, E>::WORDS; ++w)
+            acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, a.w[w]), __builtin_bit_cast(bf2, b.w[w]),
+                                                  acc, false);
+    } else {
+        float x[E], y[E];
+        a.to_float(x);
+        b.to_float(y);
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc += x[e] * y[e];
+    }
+    return acc;
+}
+
+// Waves per SIMD the register allocation must allow.  The one-token bf16
+// decode of the linear and gated rules fits 96 VGPRs without spilling, which
+// lets five 4-wave workgroups share a CU instead of four; the other variants
+// keep the compiler's choice (forcing them spills).
+template <int RULE, int NQ, typename IO>
+constexpr int chunk_waves_per_eu() {
+    return (RULE != KVBUF_RULE_DELTA && NQ == 1 && sizeof(IO) == 2) ? 5 : 1;
+}
+
 template <int RULE, int DK, int DV, int NQ, typename IO>
-__global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) {
+__global__ __launch_bounds__((Geo<DK, DV>::NT)) __attribute__((amdgpu_waves_per_eu(chunk_waves_per_eu<RULE, NQ, IO>())))
+void chunk_kernel(TileParams P) {
     using G = Geo<DK, DV>;
     constexpr int NT = G::NT, TPR = G::TPR, RG = G::RG, RPT = G::RPT;
     constexpr int E = DK / 16, EV = DV / 16;
@@ -74,8 +109,6 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
     using XIO = typename std::conditional<DELTA, float, IO>::type;
 
     extern __shared__ float lds[];
-    __shared__ int32_t s_row[kMaxTableRow];
-    __shared__ int s_last;
     __shared__ unsigned s_bad;
 
     const TileIndex ti = tile_index(P);
@@ -93,12 +126,25 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
     // ---- request metadata -----------------------------------------------------
     const int p = P.occ[b];
     const int slot = direct ? -1 : P.slot[b];
+    const ChunkLds L = chunk_lds(RULE, DK, DV, NQ, RG, NG, cap, P.m, P.fold_chunk > 0,
+                                 static_cast<int>(sizeof(IO)), static_cast<int>(sizeof(XIO)));
+    uint32_t* spos = reinterpret_cast<uint32_t*>(lds + L.pos);
+    IO* qr = reinterpret_cast<IO*>(lds + L.qr);
+    IO* kdr = reinterpret_cast<IO*>(lds + L.kdr);
+    float* bl = lds + L.bl;
+    float* cq = lds + L.cq;
+    float* ck = lds + L.ck;
+    float* es = lds + L.es;
+    IO* krs = reinterpret_cast<IO*>(lds + L.kr);
+    XIO* vrs = reinterpret_cast<XIO*>(lds + L.vr);
+    float* fw = lds + L.fw;
     if (tid < 64) {
-        unsigned bad = stage_row(P, b, p + n, s_row, tid);
+        unsigned bad = stage_row(P, b, h, p + n, spos, tid);
+        if (p < 0) bad |= KVBUF_DEVERR_OVERFLOW;
         if (slot >= P.num_slots) bad |= KVBUF_DEVERR_SLOT;
         if (tid == 0) s_bad = bad;
     }
-    __syncthreads();  // every wave has read the metadata; s_row and s_bad are complete
+    __syncthreads();  // every wave has read the metadata; spos and s_bad are complete
     if (s_bad) {
         report(P, s_bad);
         return;  // the whole request is skipped by all of its workgroups
@@ -106,23 +152,7 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
     const bool has_state = slot >= 0;
     const int T = p + n;                       // positions touched by this call
     const bool fold = P.fold_chunk > 0 && has_state && T >= P.m;  // launcher: fold_chunk >= m
-    const bool advance = P.mode != MODE_VERIFY;  // drafts do not advance the occupancy
-    // The ticket's round trip overlaps everything below; its result is read
-    // at the very end.
-    int last = 0;
-    if (advance && tid == 0) last = take_ticket(P, b);
 
-    const ChunkLds L = chunk_lds(RULE, DK, DV, NQ, RG, NG, cap, P.m, P.fold_chunk > 0);
-    float* qs = lds + L.qs;
-    float* ks = lds + L.ks;
-    float* bl = lds + L.bl;
-    float* cq = lds + L.cq;
-    float* ck = lds + L.ck;
-    float* es = lds + L.es;
-    float* vs = lds + L.vs;
-    float* fk = lds + L.fk;
-    float* fx = lds + L.fx;
-    float* fw = lds + L.fw;
     const int ldc = round4(cap);
 
     const size_t in_row = static_cast<size_t>(b) * n * P.H + h;  // (b, new token 0, h)
@@ -130,10 +160,8 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
     tok.kpool = static_cast<const IO*>(P.key);
     tok.xpool = static_cast<const XIO*>(P.value);
     tok.gpool = P.gate;
-    tok.row = s_row;
-    tok.bs = P.block_size;
+    tok.pos = spos;
     tok.H = P.H;
-    tok.h = h;
     tok.p = p;
     tok.kin = static_cast<const IO*>(P.k) + in_row * DK;
     tok.vin = static_cast<const IO*>(P.v) + in_row * DV;
@@ -176,48 +204,28 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
     __builtin_amdgcn_sched_barrier(0);  // keep every token load ahead of the state loads
 
     f4 s[RPT];
-    if (has_state) {
-        const float* stile = P.state + (static_cast<size_t>(slot) * P.H + h) * DK * DV;
-#pragma unroll
-        for (int j = 0; j < RPT; ++j)
-            s[j] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(stile + (rg * RPT + j) * DV + c0));
-    }
+    load_tile<RPT, DK, DV>(s, has_state ? P.state + (static_cast<size_t>(slot) * P.H + h) * DK * DV : P.state,
+                           has_state, rg, c0);
 
-    // ---- 2. queries, gates, first-pass values to LDS --------------------------
+    // ---- 2. token data to LDS as raw bits; appends from the same registers -----
 #pragma unroll
     for (int r = 0; r < NQR; ++r) {
         const int d = gp + NG * r;
         if (d < n) {
-            float f[E];
-            qraw[r].to_float(f);
-#pragma unroll
-            for (int e = 0; e < E; ++e) qs[d * DK + cl * E + e] = P.scale * f[e];
-            if constexpr (DELTA) {
-                kdraw[r].to_float(f);
-#pragma unroll
-                for (int e = 0; e < E; ++e) ks[d * DK + cl * E + e] = f[e];
-            }
+            qraw[r].store(qr + d * DK + cl * E);
+            if constexpr (DELTA) kdraw[r].store(kdr + d * DK + cl * E);
         }
     }
     if (GATED && tid < T) bl[tid] = graw;
     for (int i = NT + tid; GATED && i < T; i += NT) bl[i] = tok.gate(i);  // long buffers only
-    // The pass's key and value chunks stay in registers as raw bits (for the
-    // scores and the appends) and are converted where they are used.
     auto stage_pass = [&](int i0) {
         const int i = i0 + gp;
         if (i < T) {
-            float kf[E], xf[EV];
-            kr.to_float(kf);
-            xr.to_float(xf);
-#pragma unroll
-            for (int e = 0; e < EV; ++e) vs[gp * DV + cl * EV + e] = xf[e];
-            if (fold && i < P.m) {
-#pragma unroll
-                for (int e = 0; e < E; ++e) fk[i * DK + cl * E + e] = kf[e];
-                if (!DELTA || i < p) {
-#pragma unroll
-                    for (int e = 0; e < EV; ++e) fx[i * DV + cl * EV + e] = xf[e];
-                }
+            kr.store(krs + gp * DK + cl * E);
+            xr.store(vrs + gp * DV + cl * EV);
+            if (i >= p) {  // append this call's tokens
+                kr.store(kpool + tok.slot_index(i) * DK + cl * E);
+                if constexpr (!DELTA) xr.store(xpool + tok.slot_index(i) * DV + cl * EV);
             }
         }
     };
@@ -231,12 +239,12 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
         } else {
             for (int i = tid; i < T; i += 64) bl[i] = 0.0f;
         }
-        if (tid < n) es[tid] = GATED ? expf(bl[p + tid]) : 1.0f;
-        if (fold && tid == 0) es[NQ] = GATED ? expf(bl[P.m - 1]) : 1.0f;
+        if (tid < n) es[tid] = GATED ? exp_gate(bl[p + tid]) : 1.0f;
+        if (fold && tid == 0) es[NQ] = GATED ? exp_gate(bl[P.m - 1]) : 1.0f;
     }
     __syncthreads();
 
-    // ---- 4. per pass: scores of its positions, appends, weighted value sums ---
+    // ---- 4. per pass: scores of its positions, weighted value sums -------------
     f4 acc[NQ];
     f4 acck[DELTA ? NQ : 1];
 #pragma unroll
@@ -249,43 +257,37 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
         if (i0 > 0) {
             // Later passes (buffers longer than NG positions): these loads
             // follow the state loads, so they wait for them.
-            __syncthreads();  // the previous pass's vs is consumed
+            __syncthreads();  // the previous pass's rows are consumed
             load_pass(i0);
             stage_pass(i0);
+            __syncthreads();
         }
         const int i = i0 + gp;
         const int ic = min(i, T - 1);
-        float kf[E];
-        kr.to_float(kf);
+        RawChunk<IO, E> kc;
+        kc.load(krs + gp * DK + cl * E);
 #pragma unroll
         for (int d = 0; d < NQ; ++d) {
             if (d < n) {
                 const int t = p + d;
-                float part = 0.f;
-#pragma unroll
-                for (int e = 0; e < E; ++e) part += qs[d * DK + cl * E + e] * kf[e];
-                const float dot = group16_sum(part);
-                const float wq = (i <= t) ? (GATED ? expf(bl[t] - bl[ic]) : 1.0f) * dot : 0.f;
+                RawChunk<IO, E> qc;
+                qc.load(qr + d * DK + cl * E);
+                const float dot = group16_sum(chunk_dot(qc, kc));
+                const float wq = (i <= t) ? (GATED ? exp_gate(bl[t] - bl[ic]) : 1.0f) * P.scale * dot : 0.f;
                 if (cl == 0 && i < T) cq[d * ldc + i] = wq;
                 if constexpr (DELTA) {
-                    float pk = 0.f;
-#pragma unroll
-                    for (int e = 0; e < E; ++e) pk += ks[d * DK + cl * E + e] * kf[e];
-                    const float dk = group16_sum(pk);
-                    const float wk = (i < t) ? (GATED ? expf(bl[t] - bl[ic]) : 1.0f) * dk : 0.f;
+                    qc.load(kdr + d * DK + cl * E);
+                    const float dk = group16_sum(chunk_dot(qc, kc));
+                    const float wk = (i < t) ? (GATED ? exp_gate(bl[t] - bl[ic]) : 1.0f) * dk : 0.f;
                     if (cl == 0 && i < T) ck[d * ldc + i] = wk;
                 }
             }
-        }
-        if (i >= p && i < T) {  // append this call's tokens
-            kr.store(kpool + tok.slot_index(i) * DK + cl * E);
-            if constexpr (!DELTA) xr.store(xpool + tok.slot_index(i) * DV + cl * EV);
         }
         __syncthreads();
         // weighted sums: row group rg takes the pass positions ii = rg, rg+RG, ...
         const int cnt = min(NG, tacc - i0);
         for (int ii = rg; ii < cnt; ii += RG) {
-            const f4 x = *reinterpret_cast<const f4*>(vs + ii * DV + c0);
+            const f4 x = load4(vrs + ii * DV + c0);
 #pragma unroll
             for (int d = 0; d < NQ; ++d) {
                 if (d < n) {
@@ -295,8 +297,22 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
             }
         }
     }
+    if (fold && T > NG) {
+        // Rare: the buffer outgrew one pass before an eager fold (only after
+        // deferred-policy calls).  The m positions to fold are all in the
+        // pool (p >= m); stage them again.
+        __syncthreads();
+        kr.zero();
+        xr.zero();
+        if (gp < P.m) {
+            kr.load(tok.key(gp) + cl * E);
+            xr.load(tok.pooled_value(gp) + cl * EV);
+            kr.store(krs + gp * DK + cl * E);
+            xr.store(vrs + gp * DV + cl * EV);
+        }
+    }
     if (GATED && tid < n) P.gate[tok.slot_index(p + tid)] = tok.gin[tid * P.H];
-    if (fold && tid < P.m) fw[tid] = GATED ? expf(bl[P.m - 1] - bl[tid]) : 1.0f;
+    if (fold && tid < P.m) fw[tid] = GATED ? exp_gate(bl[P.m - 1] - bl[tid]) : 1.0f;
 
     // ---- 5. the state tile: S^T q (and S^T k), reduced over row groups --------
     float* red = lds + L.red;
@@ -310,12 +326,23 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
             if (has_state) {
                 f4 sa = f4{0.f, 0.f, 0.f, 0.f};
                 f4 sk = f4{0.f, 0.f, 0.f, 0.f};
+                {
+                    RawChunk<IO, RPT> qrow;
+                    float qf[RPT];
+                    qrow.load(qr + d * DK + rg * RPT);
+                    qrow.to_float(qf);
 #pragma unroll
-                for (int j = 0; j < RPT; ++j) {
-                    sa += s[j] * qs[d * DK + rg * RPT + j];
-                    if constexpr (DELTA) sk += s[j] * ks[d * DK + rg * RPT + j];
+                    for (int j = 0; j < RPT; ++j) sa += s[j] * qf[j];
                 }
-                a += sa * es[d];
+                if constexpr (DELTA) {
+                    RawChunk<IO, RPT> krow;
+                    float kf[RPT];
+                    krow.load(kdr + d * DK + rg * RPT);
+                    krow.to_float(kf);
+#pragma unroll
+                    for (int j = 0; j < RPT; ++j) sk += s[j] * kf[j];
+                }
+                a += sa * (P.scale * es[d]);
                 if constexpr (DELTA) ak += sk * es[d];
             }
             *reinterpret_cast<f4*>(red + rg * DV + c0) = a;
@@ -358,7 +385,7 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
                     for (int e = 0; e <= d; ++e) o += cq[d * ldc + p + e] * u[e];
                     outp[d * out_stride + c] = o;
                     xpool[tok.slot_index(t) * DV + c] = x;
-                    if (fold && t < P.m) fx[t * DV + c] = x;  // the new token is folded too
+                    if (fold && t < P.m) vrs[t * DV + c] = x;  // the new token is folded too
                 }
             }
         }
@@ -371,10 +398,14 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
 #pragma unroll
         for (int j = 0; j < RPT; ++j) s[j] *= e0;
         for (int ii = 0; ii < P.m; ++ii) {
-            const f4 x = *reinterpret_cast<const f4*>(fx + ii * DV + c0);
+            const f4 x = load4(vrs + ii * DV + c0);
+            RawChunk<IO, RPT> krow;
+            float kf[RPT];
+            krow.load(krs + ii * DK + rg * RPT);
+            krow.to_float(kf);
             const float w = fw[ii];
 #pragma unroll
-            for (int j = 0; j < RPT; ++j) s[j] += (w * fk[ii * DK + rg * RPT + j]) * x;
+            for (int j = 0; j < RPT; ++j) s[j] += (w * kf[j]) * x;
         }
         float* wt = P.state + (static_cast<size_t>(slot) * P.H + h) * DK * DV;
 #pragma unroll
@@ -382,11 +413,8 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
             __builtin_nontemporal_store(s[j], reinterpret_cast<f4*>(wt + (rg * RPT + j) * DV + c0));
     }
 
-    // ---- 8. bookkeeping ----------------------------------------------------------
-    if (!advance) return;
-    if (tid == 0) s_last = last;
-    __syncthreads();
-    apply_bookkeeping(P, b, s_last, T - (fold ? P.m : 0), fold ? P.m / P.block_size : 0);
+    // The occupancy and table row are updated by the bookkeeping launch that
+    // follows this one (decode, direct), once every workgroup is done with them.
 }
 
 template <int RULE, int D, typename IO>
@@ -394,8 +422,9 @@ hipError_t launch_chunk_t(const TileParams& p, int batch, hipStream_t s) {
     using G = Geo<D, D>;
     const int cap = p.block_size * p.blocks_per_req;
     const int nq = p.n <= 1 ? 1 : p.n <= 2 ? 2 : p.n <= 4 ? 4 : 8;
-    const size_t lds = sizeof(float) *
-                       chunk_lds(RULE, D, D, nq, G::RG, G::NT / 16, cap, p.m, p.fold_chunk > 0).total;
+    using XIO = typename std::conditional<RULE == KVBUF_RULE_DELTA, float, IO>::type;
+    const size_t lds = sizeof(float) * chunk_lds(RULE, D, D, nq, G::RG, G::NT / 16, cap, p.m, p.fold_chunk > 0,
+                                                 static_cast<int>(sizeof(IO)), static_cast<int>(sizeof(XIO))).total;
     const dim3 grid(static_cast<unsigned>(batch) * p.H), block(G::NT);
     switch (nq) {
         case 1: chunk_kernel<RULE, D, D, 1, IO><<<grid, block, lds, s>>>(p); break;

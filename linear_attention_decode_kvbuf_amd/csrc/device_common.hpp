@@ -11,6 +11,11 @@ namespace kvbuf {
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint16_t bf16_bits;  // bfloat16 kept as its raw bits
 
+// Word 3 of a raw (untyped) buffer resource on gfx9-family GPUs, and the
+// cache-policy bits of a non-temporal access.
+constexpr int kBufferFlags = 0x00020000;
+constexpr int kCachePolicyNT = 2;
+
 // ---------------------------------------------------------------------------
 // Workgroup layout.  One workgroup owns one (request, head) tile: a d_k x d_v
 // fp32 state read as rows of d_v floats.
@@ -154,14 +159,45 @@ struct RawChunk {
     }
 };
 
-// Sum over the 16 lanes of a dot group (butterfly through lane shuffles).
+// Issues the RPT 128-bit loads of a thread's share of a d_k x d_v fp32
+// state tile (rows rg*RPT .. rg*RPT+RPT-1, columns c0 .. c0+3) as buffer
+// loads through a range-checked resource.  A request without a state passes
+// present = false: the range is empty and every load returns zeros without
+// touching memory.  The loads are unconditional instructions either way, so
+// the compiler's memory-counter bookkeeping stays exact for loads issued
+// before them (a branch around them would make it wait for everything).
+// Non-temporal: a tile is not read again before it is evicted.
+template <int RPT, int DK, int DV>
+__device__ __forceinline__ void load_tile(f4 (&s)[RPT], const float* tile, bool present, int rg, int c0) {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(tile), 0, present ? DK * DV * static_cast<int>(sizeof(float)) : 0, kBufferFlags);
+    const int v = (rg * RPT * DV + c0) * static_cast<int>(sizeof(float));
+#pragma unroll
+    for (int j = 0; j < RPT; ++j)
+        s[j] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(r, v, j * DV * 4, kCachePolicyNT));
+}
+
+// DPP lane permutation of a float within each row of 16 lanes.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+
+// Sum over the 16 lanes of a dot group (one DPP row): swap neighbours, swap
+// pairs, mirror within 8, mirror within 16 -- every lane ends with the sum.
+// DPP needs no lane-index registers, unlike a shuffle through LDS permute.
 __device__ __forceinline__ float group16_sum(float x) {
-    x += __shfl_xor(x, 8, 16);
-    x += __shfl_xor(x, 4, 16);
-    x += __shfl_xor(x, 2, 16);
-    x += __shfl_xor(x, 1, 16);
+    x += dpp_f<0xB1>(x);   // quad_perm [1,0,3,2]
+    x += dpp_f<0x4E>(x);   // quad_perm [2,3,0,1]
+    x += dpp_f<0x141>(x);  // row_half_mirror
+    x += dpp_f<0x140>(x);  // row_mirror
     return x;
 }
+
+// e^x through the hardware base-2 exponential.  The arguments here are sums
+// of log-gates (|x| below about 10), where the relative error stays under
+// 1e-6.
+__device__ __forceinline__ float exp_gate(float x) { return __expf(x); }
 
 // Inclusive prefix sum of the log-gates of buffer positions 0 .. T-1 into
 // bl[0 .. T-1] (LDS), by one wave (lane = 0..63) in 64-wide segments.
@@ -184,24 +220,23 @@ __device__ __forceinline__ void gate_prefix(float* bl, int T, int lane, GateAt g
 }
 
 // Positions of the buffer and of this call's new tokens for one tile.
-// Position i < p lives in the pool; position p + d is new token d of this call
-// (inputs laid out [B][n][H][d]).  XIO is the value plane's element type.
+// Position i < p lives in the pool at row pos[i] (a row = one token of one
+// head; pos is the LDS table stage_row builds); position p + d is new token d
+// of this call (inputs laid out [B][n][H][d]).  XIO is the value plane's
+// element type.
 template <int DK, int DV, typename IO, typename XIO>
 struct TileTokens {
     const IO* kpool;
     const XIO* xpool;
     const float* gpool;
-    const int32_t* row;  // LDS copy of the request's table row
-    int bs, H, h, p;
+    const uint32_t* pos;  // pool row of each buffer position (LDS)
+    int H, p;
     const IO* kin;        // key of new token 0; new token d at kin + d * in_stride_k
     const IO* vin;
     const float* gin;     // gate of new token 0; new token d at gin + d * H
     size_t in_stride_k, in_stride_v;
 
-    __device__ __forceinline__ size_t slot_index(int i) const {
-        const int blk = row[i / bs];
-        return (static_cast<size_t>(blk) * H + h) * bs + (i % bs);
-    }
+    __device__ __forceinline__ size_t slot_index(int i) const { return pos[i]; }
     __device__ __forceinline__ const IO* key(int i) const {
         return i < p ? kpool + slot_index(i) * DK : kin + (i - p) * in_stride_k;
     }
@@ -265,9 +300,8 @@ __device__ __forceinline__ void stage_rows(const TileTokens<DK, DV, IO, XIO>& to
 }
 
 // Workgroups are numbered head-major: workgroup w serves request w % B and
-// head w / B.  The H workgroups of one request are therefore dispatched B
-// apart instead of back to back, so their per-request ticket atomics (one
-// counter per request) do not queue up on one address at the same moment.
+// head w / B, so consecutive workgroups stream different requests' state
+// slots and buffer blocks.
 struct TileIndex {
     int b, h;
 };
@@ -277,61 +311,33 @@ __device__ __forceinline__ TileIndex tile_index(const TileParams& P) {
     return TileIndex{w - h * P.batch, h};
 }
 
-// Per-request bookkeeping.  All H workgroups of a request read its occupancy,
-// state slot and table row; the last of them to finish with those values
-// (found with a per-request ticket counter) applies the update: the occupancy
-// becomes new_occ and, when rotate > 0, the first `rotate` table entries move
-// to the back; then it clears the ticket.
-//
-// take_ticket is called by one thread after a barrier that follows every
-// read of the metadata by every wave of the workgroup, so those reads have
-// completed; nothing in the kernel reads the metadata afterwards (the table
-// row used later is an LDS copy).  No memory fence is needed -- an agent-scope
-// fence would write back the XCD's whole L2 for every workgroup -- because
-// the bookkeeping stores only have to be visible to the next kernel, which the
-// kernel boundary guarantees.  The ticket's round trip overlaps the rest of
-// the workgroup's work; its result is read after a later barrier.
-__device__ __forceinline__ int take_ticket(const TileParams& P, int b) {
-    return atomicAdd(&P.ticket[b], 1) == P.H - 1;
-}
-
-// Every thread of the workgroup calls this last; `last` is take_ticket's
-// result (as seen after a barrier).
-__device__ __forceinline__ void apply_bookkeeping(const TileParams& P, int b, bool last, int new_occ,
-                                                  int rotate) {
-    if (!last) return;
-    const int bpr = P.blocks_per_req;
-    int32_t* row = P.table + static_cast<size_t>(b) * bpr;
-    int val = 0;
-    const bool mine = rotate > 0 && static_cast<int>(threadIdx.x) < bpr;
-    if (mine) val = row[(threadIdx.x + rotate) % bpr];
-    __syncthreads();
-    if (mine) row[threadIdx.x] = val;
-    if (threadIdx.x == 0) {
-        P.occ[b] = new_occ;
-        P.ticket[b] = 0;
-    }
-}
-
 __device__ __forceinline__ void report(const TileParams& P, unsigned bits) {
     if (bits && P.err && threadIdx.x == 0) atomicOr(reinterpret_cast<unsigned*>(P.err), bits);
 }
 
-// One wave (lane = 0..63) copies the request's whole table row to LDS with a
-// single vector load -- it does not wait for the occupancy, so the row and
-// the occupancy arrive in the same round trip -- and checks the block ids
-// that cover buffer positions [0, end).  Returns KVBUF_DEVERR_* bits, the
-// same in every lane (0 = usable).
-__device__ __forceinline__ unsigned stage_row(const TileParams& P, int b, int end, int32_t* s_row, int lane) {
+// One wave (lane = 0..63) reads the request's whole table row with a single
+// vector load -- it does not wait for the occupancy, so the row and the
+// occupancy arrive in the same round trip -- and writes, for every buffer
+// position i < capacity, its pool row (block * H + h) * block_size + i mod
+// block_size to pos[i] in LDS, so that later address arithmetic is one
+// lookup.  (The host bounds num_blocks * H * block_size below 2^31.)  Checks
+// the block ids covering positions [0, end).  Returns KVBUF_DEVERR_* bits,
+// the same in every lane (0 = usable).
+__device__ __forceinline__ unsigned stage_row(const TileParams& P, int b, int h, int end, uint32_t* pos,
+                                              int lane) {
     const int bpr = P.blocks_per_req;  // <= 64 (host-checked)
+    const int bs = P.block_size;
     int blk = 0;
-    if (lane < bpr) {
-        blk = P.table[static_cast<size_t>(b) * bpr + lane];
-        s_row[lane] = blk;
+    if (lane < bpr) blk = P.table[static_cast<size_t>(b) * bpr + lane];
+    const int cap = bs * bpr;
+    for (int i = lane; i < cap; i += 64) {
+        const int q = i / bs;
+        const uint32_t bi = static_cast<uint32_t>(__shfl(blk, q, 64));
+        pos[i] = (bi * static_cast<uint32_t>(P.H) + static_cast<uint32_t>(h)) * static_cast<uint32_t>(bs) +
+                 static_cast<uint32_t>(i - q * bs);
     }
-    const int cap = P.block_size * bpr;
     if (end < 0 || end > cap) return KVBUF_DEVERR_OVERFLOW;
-    const int nblk = (end + P.block_size - 1) / P.block_size;
+    const int nblk = (end + bs - 1) / bs;
     const bool badblk = lane < nblk && (blk < 0 || blk >= P.num_blocks);
     return __ballot(badblk) ? KVBUF_DEVERR_BLOCK : 0u;
 }

@@ -24,13 +24,13 @@
 namespace kvbuf {
 namespace {
 
-// LDS: cumulative log-gates, then two staging buffers of fc tokens
-// (keys, values, weights), then the state weight e^{b_{T-1}}.
+// LDS: pool row of each buffer position, cumulative log-gates, two staging
+// buffers of fc tokens (keys, values, weights), the state weight e^{b_{T-1}}.
 __host__ __device__ inline int fold_stage_floats(int DK, int DV, int fc) {
     return fc * (DK + DV) + ((fc + 3) & ~3);
 }
 __host__ __device__ inline int fold_lds_floats(int DK, int DV, int cap, int fc) {
-    return ((cap + 3) & ~3) + 2 * fold_stage_floats(DK, DV, fc) + 4;
+    return 2 * ((cap + 3) & ~3) + 2 * fold_stage_floats(DK, DV, fc) + 4;
 }
 
 // MULTI: the fold may take more than one staging round (then the token wave
@@ -40,14 +40,12 @@ __host__ __device__ inline int fold_lds_floats(int DK, int DV, int cap, int fc) 
 template <int RULE, int DK, int DV, typename IO, bool MULTI>
 __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void fold_kernel(TileParams P) {
     using G = Geo<DK, DV>;
-    constexpr int NT = G::NT, TPR = G::TPR, RG = G::RG, RPT = G::RPT;
+    constexpr int NT = G::NT, TPR = G::TPR, RPT = G::RPT;
     constexpr bool DELTA = RULE == KVBUF_RULE_DELTA;
     constexpr bool GATED = RULE != KVBUF_RULE_LINEAR;
     using XIO = typename std::conditional<DELTA, float, IO>::type;
 
     extern __shared__ float lds[];
-    __shared__ int32_t s_row[kMaxTableRow];
-    __shared__ int s_last;
     __shared__ unsigned s_bad;
 
     const TileIndex ti = tile_index(P);
@@ -77,103 +75,91 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void fold_kernel(TileParam
                       (P.mode == MODE_FLUSH || P.fuse);
     const int T = materialize ? p : (fold ? P.m : 0);  // positions applied
     if (token_wave) {
-        const unsigned bb = bad | stage_row(P, b, T, s_row, lane);
+        const unsigned bb = bad | stage_row(P, b, h, T, reinterpret_cast<uint32_t*>(lds), lane);
         if (lane == 0) s_bad = bb;
     }
-    __syncthreads();  // every wave has read the metadata; s_row and s_bad are complete
+    __syncthreads();  // every wave has read the metadata; the position table and s_bad are complete
     if (s_bad) {
         report(P, s_bad);
         return;
     }
-    if (!materialize && !fold && a == 0) return;  // nothing changes for this request
-    if (!materialize && tid == NT) s_last = take_ticket(P, b);
+    if (!materialize && !fold) return;  // no state change for this request
 
-    if (materialize || fold) {
-        const int fc = P.fold_chunk;
-        float* bl = lds;
-        float* stage0 = lds + ((cap + 3) & ~3);
-        const int stage_floats = fold_stage_floats(DK, DV, fc);
-        float* e0p = stage0 + 2 * stage_floats;
+    const int fc = P.fold_chunk;
+    float* bl = lds + ((cap + 3) & ~3);
+    float* stage0 = bl + ((cap + 3) & ~3);
+    const int stage_floats = fold_stage_floats(DK, DV, fc);
+    float* e0p = stage0 + 2 * stage_floats;
 
-        TileTokens<DK, DV, IO, XIO> tok;
-        tok.kpool = static_cast<const IO*>(P.key);
-        tok.xpool = static_cast<const XIO*>(P.value);
-        tok.gpool = P.gate;
-        tok.row = s_row;
-        tok.bs = P.block_size;
-        tok.H = P.H;
-        tok.h = h;
-        tok.p = cap;  // every position read here is in the pool
+    TileTokens<DK, DV, IO, XIO> tok;
+    tok.kpool = static_cast<const IO*>(P.key);
+    tok.xpool = static_cast<const XIO*>(P.value);
+    tok.gpool = P.gate;
+    tok.pos = reinterpret_cast<const uint32_t*>(lds);
+    tok.H = P.H;
+    tok.p = cap;  // every position read here is in the pool
 
-        // Token wave: stage round r (tokens r*fc ..) into buffer r % 2.
-        auto stage = [&](int r) {
-            float* fk = stage0 + (r & 1) * stage_floats;
-            float* fx = fk + fc * DK;
-            float* fw = fx + fc * DV;
-            const int i0 = r * fc;
-            const int cnt = min(fc, T - i0);
-            stage_rows(tok, i0, cnt, fk, fx, nullptr, lane);
-            for (int ii = lane; ii < cnt; ii += 64)
-                fw[ii] = GATED ? expf(bl[T - 1] - bl[i0 + ii]) : 1.0f;
-        };
+    // Token wave: stage round r (tokens r*fc ..) into buffer r % 2.
+    auto stage = [&](int r) {
+        float* fk = stage0 + (r & 1) * stage_floats;
+        float* fx = fk + fc * DK;
+        float* fw = fx + fc * DV;
+        const int i0 = r * fc;
+        const int cnt = min(fc, T - i0);
+        stage_rows(tok, i0, cnt, fk, fx, nullptr, lane);
+        for (int ii = lane; ii < cnt; ii += 64)
+            fw[ii] = GATED ? exp_gate(bl[T - 1] - bl[i0 + ii]) : 1.0f;
+    };
 
-        if (token_wave) {
-            if constexpr (GATED) gate_prefix(bl, T, lane, [&](int i) { return tok.gate(i); });
-            if (lane == 0) *e0p = (GATED && T > 0) ? expf(bl[T - 1]) : 1.0f;
-            if (T > 0) stage(0);
-        }
-        f4 s[RPT];
-        if (!token_wave) {
-            const float* stile = P.state + (static_cast<size_t>(has_state ? slot : 0) * P.H + h) * DK * DV;
+    if (token_wave) {
+        if constexpr (GATED) gate_prefix(bl, T, lane, [&](int i) { return tok.gate(i); });
+        if (lane == 0) *e0p = (GATED && T > 0) ? exp_gate(bl[T - 1]) : 1.0f;
+        if (T > 0) stage(0);
+    }
+    f4 s[RPT];
+    if (!token_wave)
+        load_tile<RPT, DK, DV>(s, has_state ? P.state + (static_cast<size_t>(slot) * P.H + h) * DK * DV : P.state,
+                               has_state, rg, c0);
+    __syncthreads();
+    if (!token_wave) {
+        const float e0 = *e0p;
 #pragma unroll
-            for (int j = 0; j < RPT; ++j)
-                s[j] = has_state
-                           ? __builtin_nontemporal_load(reinterpret_cast<const f4*>(stile + (rg * RPT + j) * DV + c0))
-                           : f4{0.f, 0.f, 0.f, 0.f};
-        }
-        __syncthreads();
-        if (!token_wave) {
-            const float e0 = *e0p;
+        for (int j = 0; j < RPT; ++j) s[j] *= e0;
+    }
+    auto apply = [&](int r) {
+        const float* fk = stage0 + (r & 1) * stage_floats;
+        const float* fx = fk + fc * DK;
+        const float* fw = fx + fc * DV;
+        const int cnt = min(fc, T - r * fc);
+        for (int ii = 0; ii < cnt; ++ii) {
+            const f4 x = *reinterpret_cast<const f4*>(fx + ii * DV + c0);
+            const float w = fw[ii];
 #pragma unroll
-            for (int j = 0; j < RPT; ++j) s[j] *= e0;
+            for (int j = 0; j < RPT; ++j) s[j] += (w * fk[ii * DK + rg * RPT + j]) * x;
         }
-        auto apply = [&](int r) {
-            const float* fk = stage0 + (r & 1) * stage_floats;
-            const float* fx = fk + fc * DK;
-            const float* fw = fx + fc * DV;
-            const int cnt = min(fc, T - r * fc);
-            for (int ii = 0; ii < cnt; ++ii) {
-                const f4 x = *reinterpret_cast<const f4*>(fx + ii * DV + c0);
-                const float w = fw[ii];
-#pragma unroll
-                for (int j = 0; j < RPT; ++j) s[j] += (w * fk[ii * DK + rg * RPT + j]) * x;
+    };
+    if constexpr (!MULTI) {
+        if (!token_wave && T > 0) apply(0);
+    } else {
+        const int rounds = (T + fc - 1) / fc;
+        for (int r = 0; r < rounds; ++r) {
+            if (token_wave) {
+                if (r + 1 < rounds) stage(r + 1);
+            } else {
+                apply(r);
             }
-        };
-        if constexpr (!MULTI) {
-            if (!token_wave && T > 0) apply(0);
-        } else {
-            const int rounds = (T + fc - 1) / fc;
-            for (int r = 0; r < rounds; ++r) {
-                if (token_wave) {
-                    if (r + 1 < rounds) stage(r + 1);
-                } else {
-                    apply(r);
-                }
-                __syncthreads();
-            }
-        }
-        if (!token_wave) {
-            float* dst = materialize ? P.states_out + (static_cast<size_t>(b) * P.H + h) * DK * DV
-                                     : P.state + (static_cast<size_t>(slot) * P.H + h) * DK * DV;
-#pragma unroll
-            for (int j = 0; j < RPT; ++j)
-                __builtin_nontemporal_store(s[j], reinterpret_cast<f4*>(dst + (rg * RPT + j) * DV + c0));
+            __syncthreads();
         }
     }
-
-    if (materialize) return;
-    __syncthreads();
-    apply_bookkeeping(P, b, s_last, pn - (fold ? P.m : 0), fold ? P.m / P.block_size : 0);
+    if (!token_wave) {
+        float* dst = materialize ? P.states_out + (static_cast<size_t>(b) * P.H + h) * DK * DV
+                                 : P.state + (static_cast<size_t>(slot) * P.H + h) * DK * DV;
+#pragma unroll
+        for (int j = 0; j < RPT; ++j)
+            __builtin_nontemporal_store(s[j], reinterpret_cast<f4*>(dst + (rg * RPT + j) * DV + c0));
+    }
+    // The occupancy and table row are updated by the bookkeeping launch that
+    // follows this one (flush, commit).
 }
 
 template <int RULE, int D, typename IO>

@@ -36,7 +36,6 @@ struct TileParams {
     const int32_t* slot;
     int32_t* table;
     int32_t* occ;
-    int32_t* ticket;
     int32_t* err;
     const void* q;
     const void* k;
@@ -53,6 +52,9 @@ struct TileParams {
 hipError_t launch_chunk(const TileParams& p, int rule, int d, int io, int batch, hipStream_t s);
 hipError_t launch_fold(const TileParams& p, int rule, int d, int io, int batch, hipStream_t s);
 int chunk_fold_limit(int d);
+// Bookkeeping of a decode / direct / flush / commit launch (p.mode, p.n,
+// p.fold_chunk as that launch had them); one thread per request.
+hipError_t launch_advance(const TileParams& p, hipStream_t s);
 hipError_t launch_recurrent(const TileParams& p, int rule, int d, int io, int batch, hipStream_t s);
 
 // Head dims with compiled kernels (d_k == d_v).

@@ -58,7 +58,7 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void recurrent_kernel(Tile
         }
         for (int c = lane; c < DV; c += 64) vf[c] = load1(v + c);
         if (lane == 0) {
-            gb[0] = GATED ? expf(P.g[in_row]) : 1.0f;
+            gb[0] = GATED ? exp_gate(P.g[in_row]) : 1.0f;
             gb[1] = DELTA ? P.beta[in_row] : 0.0f;
         }
     }

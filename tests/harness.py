@@ -239,7 +239,6 @@ class Run:
         assert int(self.kv.error.item()) == 0, "device error flags %d" % int(self.kv.error.item())
         np.testing.assert_array_equal(self.kv.block_table.cpu().numpy(), self.model.tables())
         np.testing.assert_array_equal(self.kv.occupancy.cpu().numpy(), self.model.occupancies())
-        assert int(self.kv.ticket.abs().sum().item()) == 0
 
     def check_pool(self):
         """Buffered keys, gates and (linear / gated rules) values of the sampled

@@ -40,11 +40,11 @@ def test_struct_sizes_match_header(lib):
     # kvbuf_layout: 11 int32 + 1 float; pools: 4 pointers; batch: int32 (+pad) + 5 pointers
     assert ctypes.sizeof(kb.Layout) == 48
     assert ctypes.sizeof(kb.Pools) == 32
-    assert ctypes.sizeof(kb.Batch) == 48
+    assert ctypes.sizeof(kb.Batch) == 40
 
 
 def test_abi_version_and_strerror(lib):
-    assert kb.kvbuf_abi_version() == 1
+    assert kb.kvbuf_abi_version() == 2
     for st in (kb.OK, kb.EINVAL, kb.EUNSUPPORTED, kb.ECAPACITY, kb.EHIP):
         assert len(kb.strerror(st)) > 5
     assert "unknown" in kb.strerror(-99)
@@ -59,7 +59,7 @@ def _layout(**kw):
 
 FAKE = 0x1000  # never dereferenced: every case below fails validation first
 POOLS = kb.Pools(FAKE, FAKE, FAKE, FAKE)
-BATCH = kb.Batch(2, FAKE, FAKE, FAKE, FAKE, None)
+BATCH = kb.Batch(2, FAKE, FAKE, FAKE, None)
 
 
 def _decode(layout, pools=POOLS, batch=BATCH, q=FAKE, g=FAKE, beta=None):
@@ -89,9 +89,9 @@ def test_null_arguments(lib):
     assert kb.kvbuf_decode(None, POOLS, BATCH, FAKE, FAKE, FAKE, FAKE, None, FAKE, 0, False) == kb.EINVAL
     assert _decode(L, pools=kb.Pools(FAKE, None, FAKE, FAKE)) == kb.EINVAL
     assert _decode(L, pools=kb.Pools(FAKE, FAKE, FAKE, None)) == kb.EINVAL  # gated rule needs gates
-    assert _decode(L, batch=kb.Batch(2, FAKE, None, FAKE, FAKE, None)) == kb.EINVAL
-    assert _decode(L, batch=kb.Batch(2, FAKE, FAKE, FAKE, None, None)) == kb.EINVAL  # ticket
-    assert _decode(L, batch=kb.Batch(-1, FAKE, FAKE, FAKE, FAKE, None)) == kb.EINVAL
+    assert _decode(L, batch=kb.Batch(2, FAKE, None, FAKE, None)) == kb.EINVAL
+    assert _decode(L, batch=kb.Batch(2, FAKE, FAKE, None, None)) == kb.EINVAL  # occupancy
+    assert _decode(L, batch=kb.Batch(-1, FAKE, FAKE, FAKE, None)) == kb.EINVAL
     assert _decode(L, q=None) == kb.EINVAL
     assert _decode(L, g=None) == kb.EINVAL
     assert _decode(_layout(rule=kb.RULE_DELTA), beta=None) == kb.EINVAL
@@ -109,6 +109,6 @@ def test_mode_specific_validation(lib):
     assert kb.kvbuf_commit(L, POOLS, BATCH, 9, FAKE, 0, False) == kb.EUNSUPPORTED
     assert kb.kvbuf_materialize(L, POOLS, BATCH, None, 0, False) == kb.EINVAL
     # empty batches and m = 0 flushes enqueue nothing and succeed
-    empty = kb.Batch(0, None, None, None, None, None)
+    empty = kb.Batch(0, None, None, None, None)
     assert _decode(L, batch=empty) == kb.OK
     assert kb.kvbuf_flush(L0, POOLS, BATCH, 0, False) == kb.OK

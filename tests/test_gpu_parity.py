@@ -57,6 +57,25 @@ def test_small_rules(rule, d, io, m, bs, bpr):
     run.check_bookkeeping()
 
 
+@pytest.mark.parametrize("m,bs,bpr,flush", [(8, 1, 64, kb.FLUSH_EAGER), (6, 2, 33, kb.FLUSH_DEFERRED),
+                                             (64, 8, 8, kb.FLUSH_EAGER)])
+def test_long_table_rows(m, bs, bpr, flush):
+    """Table rows up to the 64-entry limit: the fold's rotation moves m / bs
+    entries of a long row (five requests, so the bookkeeping spans more than
+    one workgroup)."""
+    w = synth.workload(1, B=5, H=2, dk=16, dv=16, m=m, block_size=bs, blocks_per_req=bpr,
+                       steps=2 * m + 3, rule=1, io="f32", state_std=0.02)
+    _say("long rows", w, "flush", flush)
+    run = Run(w, flush=flush)
+    for t in range(w.steps):
+        run.decode(t)
+        if flush == kb.FLUSH_DEFERRED and t % 5 == 4:
+            run.flush()
+    run.check_effective_states()
+    run.check_pool()
+    run.check_bookkeeping()
+
+
 @pytest.mark.parametrize("rule", [0, 1, 2])
 def test_deferred_flush_with_tail(rule):
     """Decode past m before folding: the fold takes the first m tokens and
@@ -162,7 +181,7 @@ def test_mixed_stateful_and_stateless_one_launch():
 
 def test_empty_batch_is_a_no_op():
     kv = kb.KVBuffer(batch=2, heads=2, d=16, m=4, rule=kb.RULE_GATED, io_dtype=kb.F32)
-    empty = kb.Batch(0, None, None, None, None, None)
+    empty = kb.Batch(0, None, None, None, None)
     z = torch.zeros(1, device="cuda")
     assert kb.kvbuf_decode(kv.layout, kv.pools, empty, z, z, z, z, None, z) == kb.OK
     assert kb.kvbuf_flush(kv.layout, kv.pools, empty) == kb.OK
@@ -204,7 +223,6 @@ def test_device_errors_skip_the_request():
     z = torch.zeros((2, 2, 16), device="cuda")
     kv0.decode(z, z, z)
     assert _errors(kv0) & kb.DEVERR_SLOT
-    assert int(kv.ticket.abs().sum().item()) == 0
     assert torch.equal(kv.state, before_state)
 
 
