@@ -130,7 +130,9 @@ kvbuf_status chunk_call(const kvbuf_layout* layout, const kvbuf_pools* pools,
     // A decode under the eager policy folds inside the decode kernel when the
     // m tokens fit its first staging pass; otherwise a fold launch follows it.
     const bool eager_decode = mode == kvbuf::MODE_DECODE && t.fuse && layout->m > 0;
-    const bool fused = eager_decode && layout->m <= kvbuf::chunk_fold_limit(layout->d_k);
+    const bool fused = eager_decode &&
+                       layout->m <= kvbuf::chunk_fold_limit(layout->rule, layout->d_k, layout->io_dtype, n,
+                                                            layout->block_size * layout->blocks_per_req);
     t.fold_chunk = fused ? layout->m : 0;
     t.q = q;
     t.k = k;

@@ -39,7 +39,7 @@ __global__ __launch_bounds__(64 * kAdvanceWaves) void advance_kernel(TileParams 
     int pn = p;           // occupancy after this launch's appends / kept drafts
     bool fold = false;
     int checked = 0;      // buffer positions whose blocks the compute kernel checked
-    bool bad = p < 0 || slot >= P.num_slots;
+    bool bad = p < 0 || p > cap || slot >= P.num_slots;  // (then p + n cannot overflow)
     if (P.mode == MODE_DECODE || P.mode == MODE_DIRECT) {
         pn = p + P.n;
         checked = pn;

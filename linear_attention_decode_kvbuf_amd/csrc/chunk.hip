@@ -66,27 +66,6 @@ __host__ __device__ inline ChunkLds chunk_lds(int rule, int DK, int DV, int NQ, 
     return L;
 }
 
-// q . k over one 16-lane share of a row, from raw chunks (bf16 pairs through
-// the packed bf16 dot instruction: the products are exact in fp32).
-template <typename T, int E>
-__device__ __forceinline__ float chunk_dot(const RawChunk<T, E>& a, const RawChunk<T, E>& b) {
-    float acc = 0.f;
-    if constexpr (sizeof(T) == 2 && E >= 2) {
-        typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
-#pragma unroll
-        for (int w = 0; w < RawChunk<T, E>::WORDS; ++w)
-            acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, a.w[w]), __builtin_bit_cast(bf2, b.w[w]),
-                                                  acc, false);
-    } else {
-        float x[E], y[E];
-        a.to_float(x);
-        b.to_float(y);
-#pragma unroll
-        for (int e = 0; e < E; ++e) acc += x[e] * y[e];
-    }
-    return acc;
-}
-
 // Waves per SIMD the register allocation must allow.  The one-token bf16
 // decode of the linear and gated rules fits 96 VGPRs without spilling, which
 // lets five 4-wave workgroups share a CU instead of four; the other variants
@@ -139,8 +118,7 @@ void chunk_kernel(TileParams P) {
     XIO* vrs = reinterpret_cast<XIO*>(lds + L.vr);
     float* fw = lds + L.fw;
     if (tid < 64) {
-        unsigned bad = stage_row(P, b, h, p + n, spos, tid);
-        if (p < 0) bad |= KVBUF_DEVERR_OVERFLOW;
+        unsigned bad = stage_row(P, b, h, (p < 0 || p > cap) ? -1 : p + n, spos, tid);
         if (slot >= P.num_slots) bad |= KVBUF_DEVERR_SLOT;
         if (tid == 0) s_bad = bad;
     }
@@ -362,7 +340,8 @@ void chunk_kernel(TileParams P) {
                     outp[d * out_stride + c] = sum;
                 }
             }
-            __syncthreads();
+            // `red` is reused by the next query; the delta rule reads sq / sk
+            if (DELTA || d + 1 < NQ) __syncthreads();
         }
     }
 
@@ -455,9 +434,11 @@ hipError_t launch_chunk_r(const TileParams& p, int rule, int d, int batch, hipSt
 
 }  // namespace
 
-// The eager fold happens inside the decode kernel when its m tokens fit the
-// first staging pass (NT / 16 positions); otherwise a fold launch follows.
-int chunk_fold_limit(int d) {
+// The eager fold happens inside the decode launch when its m tokens fit what
+// that kernel stages (the one-token kernel: an LDS budget; this kernel: the
+// first staging pass of NT / 16 positions); otherwise a fold launch follows.
+int chunk_fold_limit(int rule, int d, int io, int n, int cap) {
+    if (decode_eligible(rule, n, cap)) return decode_fold_limit(d, io);
     switch (d) {
         case 16: return Geo<16, 16>::NT / 16;
         case 64: return Geo<64, 64>::NT / 16;
@@ -466,6 +447,7 @@ int chunk_fold_limit(int d) {
 }
 
 hipError_t launch_chunk(const TileParams& p, int rule, int d, int io, int batch, hipStream_t s) {
+    if (decode_eligible(rule, p.n, p.block_size * p.blocks_per_req)) return launch_decode(p, rule, d, io, batch, s);
     return io == KVBUF_BF16 ? launch_chunk_r<bf16_bits>(p, rule, d, batch, s)
                             : launch_chunk_r<float>(p, rule, d, batch, s);
 }

@@ -1,0 +1,299 @@
+// One-token decode for the linear and gated rules, with the work of a tile
+// split between two roles that run at the same time.
+//
+// KVBuffer: IO-aware Serving for Linear Attention (pith.science page,
+// Figure 1 caption: the output of a token is computed from the state loaded
+// together with the buffered keys and values; once the buffer holds m tokens
+// the state absorbs them and is written back).  With b_i the cumulative
+// log-gate since the last fold and t = p the new token's position:
+//   o_t = e^{b_t} S0^T (scale q_t) + sum_{i<=t} e^{b_t - b_i} scale (q_t . k_i) v_i
+//   fold (t = m - 1):  S <- e^{b_{m-1}} S0 + sum_{i<m} e^{b_{m-1} - b_i} k_i v_i^T
+//
+// Serves kvbuf_decode, kvbuf_direct and a one-draft kvbuf_verify when the
+// table row covers at most 64 positions (one lane of the token wave per
+// position).
+//
+// * State waves (NT threads): read the slot, issue the tile's 128-bit loads
+//   at once (after only the query rows they multiply), and form their share
+//   of S0^T q as soon as the tile arrives.  Nothing they issue depends on the
+//   buffer metadata.
+// * Token wave (64 lanes): occupancy and table row (one round trip), then the
+//   keys, values and gates of every buffered position plus the new token (one
+//   more), then scores, gate prefix sums, the weighted value sum, fold
+//   staging and the appends -- all in registers and wave shuffles.
+// The roles meet at one barrier; then the row-group partials are reduced into
+// the output and, when the buffer fills, the state waves fold the staged
+// tokens into the tile still held in registers and write it back.  The
+// occupancy and table row are updated by the bookkeeping launch that follows
+// (decode, direct).
+#include "device_common.hpp"
+
+namespace kvbuf {
+namespace {
+
+__host__ __device__ inline int round4d(int x) { return (x + 3) & ~3; }
+
+// LDS layout in 4-byte words.  mf = positions staged for a fold in this
+// launch (0: it never folds); io = bytes per key / value element.
+struct DecodeLds {
+    int obuf, red, fw, kr, vr, total;
+};
+__host__ __device__ inline DecodeLds decode_lds(int DK, int DV, int RG, int mf, int io) {
+    DecodeLds L;
+    int o = 0;
+    L.obuf = o; o += DV;                        // weighted sum of buffered values (token wave)
+    L.red = o; o += RG * DV;                    // S0^T q partials, one row per row group
+    L.fw = o; o += round4d(mf);                 // fold weights e^{b_{m-1} - b_i}
+    L.kr = o; o += round4d(mf * DK * io / 4);   // keys to fold (raw bits)
+    L.vr = o; o += round4d(mf * DV * io / 4);   // values to fold (raw bits)
+    L.total = o;
+    return L;
+}
+
+template <int RULE, int DK, int DV, typename IO>
+__global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void decode_kernel(TileParams P) {
+    using G = Geo<DK, DV>;
+    constexpr int NT = G::NT, TPR = G::TPR, RG = G::RG, RPT = G::RPT;
+    constexpr int E = DK / 16, EV = DV / 16;
+    constexpr int NB = 4;  // rounds of 4 positions whose loads are in flight together
+    constexpr bool GATED = RULE != KVBUF_RULE_LINEAR;
+
+    extern __shared__ float lds[];
+    __shared__ unsigned s_bad;
+    __shared__ int s_fold;
+    __shared__ float s_es, s_e0;
+
+    const TileIndex ti = tile_index(P);
+    const int b = ti.b;
+    const int h = ti.h;
+    const int tid = threadIdx.x;
+    const bool token_wave = tid >= NT;
+    const int rg = tid / TPR;
+    const int c0 = (tid % TPR) * 4;
+    const bool direct = P.mode == MODE_DIRECT;
+    const int mf = P.fold_chunk;  // = m when this launch may fold
+    const DecodeLds L = decode_lds(DK, DV, RG, mf, static_cast<int>(sizeof(IO)));
+    float* obuf = lds + L.obuf;
+    float* red = lds + L.red;
+    float* fw = lds + L.fw;
+    IO* krs = reinterpret_cast<IO*>(lds + L.kr);
+    IO* vrs = reinterpret_cast<IO*>(lds + L.vr);
+    const size_t in_row = static_cast<size_t>(b) * P.H + h;  // one new token per request
+    const int slot = direct ? -1 : P.slot[b];
+    const IO* qin = static_cast<const IO*>(P.q) + in_row * DK;
+
+    // ---- token wave ------------------------------------------------------------
+    if (token_wave) {
+        const int lane = tid - NT;
+        const int bs = P.block_size;
+        const int bpr = P.blocks_per_req;  // bs * bpr <= 64 (launcher)
+        const int cap = bs * bpr;
+        const int p = P.occ[b];
+        int blk = 0;
+        if (lane < bpr) blk = P.table[static_cast<size_t>(b) * bpr + lane];
+        const int T = p + 1;  // positions after the append
+        unsigned bad = 0;
+        if (p < 0 || p >= cap) bad |= KVBUF_DEVERR_OVERFLOW;
+        if (slot >= P.num_slots) bad |= KVBUF_DEVERR_SLOT;
+        const int nblk = bad ? 0 : (T + bs - 1) / bs;
+        if (__ballot(lane < nblk && (blk < 0 || blk >= P.num_blocks))) bad |= KVBUF_DEVERR_BLOCK;
+        const int pc = bad ? 0 : p;  // p, clamped for the lane arithmetic below
+        const bool fold = !bad && mf > 0 && slot >= 0 && T >= P.m;
+
+        // pool row of position `lane` (host: num_blocks * H * block_size < 2^31)
+        const int qb = min(lane / bs, 63);
+        const uint32_t bi = static_cast<uint32_t>(__shfl(blk, qb, 64));
+        const uint32_t prow = (bi * static_cast<uint32_t>(P.H) + static_cast<uint32_t>(h)) *
+                                  static_cast<uint32_t>(bs) + static_cast<uint32_t>(lane - qb * bs);
+
+        const int gl = lane >> 4;  // position slot of the lane in a round
+        const int cl = lane & 15;  // its 1/16 of a row
+        const IO* kpool = static_cast<const IO*>(P.key);
+        const IO* vpool = static_cast<const IO*>(P.value);
+        const IO* kin = static_cast<const IO*>(P.k) + in_row * DK;
+        const IO* vin = static_cast<const IO*>(P.v) + in_row * DV;
+        const int Tl = bad ? 0 : T;
+
+        // Issue every load of the first 4 * NB positions -- the gate of
+        // position `lane`, the query chunk, keys and values -- before any is
+        // used: one round trip after the table row.
+        float g = 0.0f;
+        if constexpr (GATED) {
+            if (!bad && lane < pc) g = P.gate[prow];
+            else if (!bad && lane == pc) g = P.g[in_row];
+        }
+        RawChunk<IO, E> qc;
+        qc.load(qin + cl * E);
+        RawChunk<IO, E> kc[NB];
+        RawChunk<IO, EV> vc[NB];
+        uint32_t pr[NB];
+        auto issue = [&](int i0) {
+#pragma unroll
+            for (int r = 0; r < NB; ++r) {
+                const int i = i0 + 4 * r + gl;
+                pr[r] = static_cast<uint32_t>(__shfl(static_cast<int>(prow), i & 63, 64));
+                kc[r].zero();
+                vc[r].zero();
+                if (i < pc) {
+                    kc[r].load(kpool + static_cast<size_t>(pr[r]) * DK + cl * E);
+                    vc[r].load(vpool + static_cast<size_t>(pr[r]) * DV + cl * EV);
+                } else if (i == pc) {
+                    kc[r].load(kin + cl * E);
+                    vc[r].load(vin + cl * EV);
+                }
+            }
+        };
+        issue(0);
+
+        // cumulative log-gates b_i of positions 0 .. T-1, lane i holds b_i
+        float bcum = 0.0f;
+        if constexpr (GATED) {
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const float y = __shfl_up(g, off, 64);
+                if (lane >= off) g += y;
+            }
+            bcum = g;
+        }
+        const float bt = __shfl(bcum, pc, 64);
+
+        float ob[EV];
+#pragma unroll
+        for (int e = 0; e < EV; ++e) ob[e] = 0.0f;
+        for (int i0 = 0; i0 < Tl; i0 += 4 * NB) {
+            if (i0 > 0) issue(i0);  // buffers longer than 4 * NB positions
+#pragma unroll
+            for (int r = 0; r < NB; ++r) {
+                const int i = i0 + 4 * r + gl;
+                const float dot = group16_sum(chunk_dot(qc, kc[r]));
+                const float bi_ = __shfl(bcum, i & 63, 64);
+                const float w = i < Tl ? (GATED ? exp_gate(bt - bi_) : 1.0f) * P.scale * dot : 0.0f;
+                float vf[EV];
+                vc[r].to_float(vf);
+#pragma unroll
+                for (int e = 0; e < EV; ++e) ob[e] += w * vf[e];
+                if (fold && i < P.m) {
+                    kc[r].store(krs + i * DK + cl * E);
+                    vc[r].store(vrs + i * DV + cl * EV);
+                }
+                if (i == pc && i < Tl) {  // append the new token to the pool
+                    kc[r].store(const_cast<IO*>(kpool) + static_cast<size_t>(pr[r]) * DK + cl * E);
+                    vc[r].store(const_cast<IO*>(vpool) + static_cast<size_t>(pr[r]) * DV + cl * EV);
+                }
+            }
+        }
+        // sum the four position slots: lanes cl, cl+16, cl+32, cl+48
+#pragma unroll
+        for (int e = 0; e < EV; ++e) {
+            ob[e] += __shfl_xor(ob[e], 16, 64);
+            ob[e] += __shfl_xor(ob[e], 32, 64);
+        }
+        if (gl == 0) {
+#pragma unroll
+            for (int e = 0; e < EV; ++e) obuf[cl * EV + e] = ob[e];
+        }
+        if constexpr (GATED) {
+            if (!bad && lane == pc) P.gate[prow] = P.g[in_row];
+        }
+        if (fold) {
+            const float bm = __shfl(bcum, P.m - 1, 64);
+            if (lane < P.m) fw[lane] = GATED ? exp_gate(bm - bcum) : 1.0f;
+            if (lane == 0) s_e0 = GATED ? exp_gate(bm) : 1.0f;
+        }
+        if (lane == 0) {
+            s_bad = bad;
+            s_fold = fold ? 1 : 0;
+            s_es = GATED ? exp_gate(bt) : 1.0f;
+        }
+    }
+
+    // ---- state waves: query rows, then the tile; S0^T q per row group ----------
+    f4 s[RPT];
+    if (!token_wave) {
+        RawChunk<IO, RPT> qrow;
+        qrow.load(qin + rg * RPT);
+        const bool present = slot >= 0 && slot < P.num_slots;
+        load_tile<RPT, DK, DV>(s, present ? P.state + (static_cast<size_t>(slot) * P.H + h) * DK * DV : P.state,
+                               present, rg, c0);
+        float qf[RPT];
+        qrow.to_float(qf);
+        f4 sa = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < RPT; ++j) sa += s[j] * qf[j];
+        *reinterpret_cast<f4*>(red + rg * DV + c0) = sa;
+    }
+    __syncthreads();
+    if (s_bad) {
+        report(P, s_bad);
+        return;  // the whole request is skipped by all of its workgroups
+    }
+
+    // ---- output: e^{b_t} scale (S0^T q) + buffered part ---------------------------
+    if (tid < DV) {
+        float sum = 0.f;
+#pragma unroll
+        for (int g2 = 0; g2 < RG; ++g2) sum += red[g2 * DV + tid];
+        P.out[in_row * DV + tid] = sum * (P.scale * s_es) + obuf[tid];
+    }
+
+    // ---- eager fold: the buffer reached m tokens ---------------------------------
+    if (s_fold && !token_wave) {
+        const float e0 = s_e0;
+#pragma unroll
+        for (int j = 0; j < RPT; ++j) s[j] *= e0;
+        for (int ii = 0; ii < P.m; ++ii) {
+            const f4 x = load4(vrs + ii * DV + c0);
+            RawChunk<IO, RPT> krow;
+            float kf[RPT];
+            krow.load(krs + ii * DK + rg * RPT);
+            krow.to_float(kf);
+            const float w = fw[ii];
+#pragma unroll
+            for (int j = 0; j < RPT; ++j) s[j] += (w * kf[j]) * x;
+        }
+        float* wt = P.state + (static_cast<size_t>(slot) * P.H + h) * DK * DV;
+#pragma unroll
+        for (int j = 0; j < RPT; ++j)
+            __builtin_nontemporal_store(s[j], reinterpret_cast<f4*>(wt + (rg * RPT + j) * DV + c0));
+    }
+}
+
+template <int RULE, int D, typename IO>
+hipError_t launch_decode_t(const TileParams& p, int batch, hipStream_t s) {
+    using G = Geo<D, D>;
+    const size_t lds = sizeof(float) * decode_lds(D, D, G::RG, p.fold_chunk, static_cast<int>(sizeof(IO))).total;
+    decode_kernel<RULE, D, D, IO><<<dim3(static_cast<unsigned>(batch) * p.H), dim3(G::NTHREADS), lds, s>>>(p);
+    return hipGetLastError();
+}
+
+template <int RULE, typename IO>
+hipError_t launch_decode_d(const TileParams& p, int d, int batch, hipStream_t s) {
+    switch (d) {
+        case 16: return launch_decode_t<RULE, 16, IO>(p, batch, s);
+        case 64: return launch_decode_t<RULE, 64, IO>(p, batch, s);
+        default: return launch_decode_t<RULE, 128, IO>(p, batch, s);
+    }
+}
+
+}  // namespace
+
+// Largest m a decode launch of this kernel folds itself: the keys and values
+// of the m positions are staged in LDS (at most 32 KiB of them).
+int decode_fold_limit(int d, int io) {
+    const int bytes_per_pos = 2 * d * (io == KVBUF_BF16 ? 2 : 4);
+    return 32768 / bytes_per_pos;
+}
+
+bool decode_eligible(int rule, int n, int cap) {
+    return rule != KVBUF_RULE_DELTA && n == 1 && cap <= 64;
+}
+
+hipError_t launch_decode(const TileParams& p, int rule, int d, int io, int batch, hipStream_t s) {
+    if (rule == KVBUF_RULE_LINEAR)
+        return io == KVBUF_BF16 ? launch_decode_d<KVBUF_RULE_LINEAR, bf16_bits>(p, d, batch, s)
+                                : launch_decode_d<KVBUF_RULE_LINEAR, float>(p, d, batch, s);
+    return io == KVBUF_BF16 ? launch_decode_d<KVBUF_RULE_GATED, bf16_bits>(p, d, batch, s)
+                            : launch_decode_d<KVBUF_RULE_GATED, float>(p, d, batch, s);
+}
+
+}  // namespace kvbuf

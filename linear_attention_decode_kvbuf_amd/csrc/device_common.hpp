@@ -159,6 +159,27 @@ struct RawChunk {
     }
 };
 
+// q . k over one 16-lane share of a row, from raw chunks (bf16 pairs through
+// the packed bf16 dot instruction: the products are exact in fp32).
+template <typename T, int E>
+__device__ __forceinline__ float chunk_dot(const RawChunk<T, E>& a, const RawChunk<T, E>& b) {
+    float acc = 0.f;
+    if constexpr (sizeof(T) == 2 && E >= 2) {
+        typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+        for (int w = 0; w < RawChunk<T, E>::WORDS; ++w)
+            acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, a.w[w]), __builtin_bit_cast(bf2, b.w[w]),
+                                                  acc, false);
+    } else {
+        float x[E], y[E];
+        a.to_float(x);
+        b.to_float(y);
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc += x[e] * y[e];
+    }
+    return acc;
+}
+
 // Issues the RPT 128-bit loads of a thread's share of a d_k x d_v fp32
 // state tile (rows rg*RPT .. rg*RPT+RPT-1, columns c0 .. c0+3) as buffer
 // loads through a range-checked resource.  A request without a state passes

@@ -67,8 +67,8 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void fold_kernel(TileParam
         a = P.accepted[b];
         if (a < 0 || a > P.n) bad |= KVBUF_DEVERR_ACCEPT;
     }
-    const int pn = p + a;
-    if (p < 0 || pn > cap) bad |= KVBUF_DEVERR_OVERFLOW;
+    const int pn = (p < 0 || p > cap) ? -1 : p + a;
+    if (pn < 0 || pn > cap) bad |= KVBUF_DEVERR_OVERFLOW;
     if (slot >= P.num_slots) bad |= KVBUF_DEVERR_SLOT;
     const bool has_state = slot >= 0;
     const bool fold = !materialize && has_state && P.m > 0 && pn >= P.m &&

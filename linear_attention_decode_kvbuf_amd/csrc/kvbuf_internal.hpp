@@ -49,11 +49,18 @@ struct TileParams {
 
 // Launchers: each picks the template instance for (rule, d, io dtype) and
 // enqueues one grid of B * H workgroups.  Return hipSuccess or the launch error.
+// launch_chunk serves decode, direct and verify; one-token calls of the
+// linear and gated rules with table rows of at most 64 positions go to the
+// split-role kernel (launch_decode), the rest to the general chunk kernel.
 hipError_t launch_chunk(const TileParams& p, int rule, int d, int io, int batch, hipStream_t s);
+hipError_t launch_decode(const TileParams& p, int rule, int d, int io, int batch, hipStream_t s);
+bool decode_eligible(int rule, int n, int cap);
+int decode_fold_limit(int d, int io);
 hipError_t launch_fold(const TileParams& p, int rule, int d, int io, int batch, hipStream_t s);
-int chunk_fold_limit(int d);
+// Largest m that a decode launch of n tokens folds itself (eager policy).
+int chunk_fold_limit(int rule, int d, int io, int n, int cap);
 // Bookkeeping of a decode / direct / flush / commit launch (p.mode, p.n,
-// p.fold_chunk as that launch had them); one thread per request.
+// p.fold_chunk as that launch had them); one wave per request.
 hipError_t launch_advance(const TileParams& p, hipStream_t s);
 hipError_t launch_recurrent(const TileParams& p, int rule, int d, int io, int batch, hipStream_t s);
 
