@@ -32,33 +32,34 @@ if ROOT not in sys.path:
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, published
 
 
-# Algorithmic bytes per (request, head) tile, scalar-gated rule, 2-byte
-# q/k/v, 4-byte state, gates and outputs.
-def decode_bytes(j, dk, dv, io=2):
-    return (4 * dk * dv            # state tile read
-            + io * (2 * dk + dv)   # q, k, v of the new token
-            + io * (dk + dv)       # append of k, v to the pool
-            + io * j * (dk + dv)   # buffered keys and values
-            + 4 * dv               # output
-            + 4 * (j + 2))         # gates: buffered, new, appended
+# Algorithmic bytes per (request, head) tile: 2-byte q/k/v, 4-byte state,
+# gates and outputs; `gated` = the scalar-gated rule (the linear rule has no
+# gates).
+def decode_bytes(j, dk, dv, io=2, gated=True):
+    return (4 * dk * dv                        # state tile read
+            + io * (2 * dk + dv)               # q, k, v of the new token
+            + io * (dk + dv)                   # append of k, v to the pool
+            + io * j * (dk + dv)               # buffered keys and values
+            + 4 * dv                           # output
+            + (4 * (j + 2) if gated else 0))   # gates: buffered, new, appended
 
 
-def flush_bytes(m, dk, dv, io=2):
-    return 8 * dk * dv + m * (io * (dk + dv) + 4)
+def flush_bytes(m, dk, dv, io=2, gated=True):
+    return 8 * dk * dv + m * (io * (dk + dv) + (4 if gated else 0))
 
 
-def recurrent_bytes(dk, dv, io=2):
-    return 8 * dk * dv + io * (2 * dk + dv) + 4 * dv + 4
+def recurrent_bytes(dk, dv, io=2, gated=True):
+    return 8 * dk * dv + io * (2 * dk + dv) + 4 * dv + (4 if gated else 0)
 
 
-def cycle_bytes_fused(m, dk, dv, io=2):
+def cycle_bytes_fused(m, dk, dv, io=2, gated=True):
     """Decodes at occupancy 0 .. m-1 plus one state write (the fold reads the
     state and the buffered tokens the last decode already reads)."""
-    return sum(decode_bytes(j, dk, dv, io) for j in range(m)) + 4 * dk * dv
+    return sum(decode_bytes(j, dk, dv, io, gated) for j in range(m)) + 4 * dk * dv
 
 
-def cycle_bytes_separate(m, dk, dv, io=2):
-    return sum(decode_bytes(j, dk, dv, io) for j in range(m)) + flush_bytes(m, dk, dv, io)
+def cycle_bytes_separate(m, dk, dv, io=2, gated=True):
+    return sum(decode_bytes(j, dk, dv, io, gated) for j in range(m)) + flush_bytes(m, dk, dv, io, gated)
 
 
 def _traffic_file(m):
@@ -169,6 +170,65 @@ def cpu_baseline(synth, oracle, np, torch, w, ring, max_tiles=None):
     }
 
 
+def cycle_leg(kb, synth, torch, dev, w, cycles, warmup):
+    """Full buffer cycles (eager policy, fold fused into the filling decode)
+    of workload w, or decode steps of the recurrent kernel when w.m = 0.
+    Returns tokens/s, time per cycle, algorithmic HBM GB/s and bytes per
+    token (all H tiles of a request)."""
+    gated = w.rule != 0
+    m = max(w.m, 1)
+    kv = build_kv(kb, synth, torch, w, kb.FLUSH_EAGER, dev)
+    ring = make_ring(synth, w, dev, 2 * m)
+    out = torch.empty((w.B, w.H, w.dv), dtype=torch.float32, device=dev)
+
+    def cycle(i):
+        for j in range(m):
+            r = ring[(i * m + j) % len(ring)]
+            kv.decode(r["q"], r["k"], r["v"], r["g"] if gated else None, out=out)
+
+    wall = time_loop(torch, cycle, cycles, warmup)
+    torch.cuda.synchronize()
+    assert int(kv.error.item()) == 0
+    del kv
+    tiles = w.B * w.H
+    per_tile = (cycle_bytes_fused(w.m, w.dk, w.dv, gated=gated) if w.m > 0
+                else recurrent_bytes(w.dk, w.dv, gated=gated))
+    cyc_s = wall / cycles
+    return {"m": w.m, "tokens_per_s": w.B * m / cyc_s, "ms_per_cycle": cyc_s * 1e3,
+            "hbm_gbps": per_tile * tiles / cyc_s / 1e9,
+            "hbm_frac_of_peak": per_tile * tiles / cyc_s / 1e9 / PEAK_HBM_GBPS,
+            "bytes_per_token": per_tile * w.H / m}
+
+
+def sweep_leg(kb, synth, torch, dev, args):
+    """The Figure 3 analogue: buffer sizes m = 4, 16, 32 of the metric
+    workload (blocks of m, two per request), about as many decode launches
+    each as the headline run; m = 0 and m = 8 are the recurrent and headline
+    legs."""
+    out = {}
+    for m in (4, 16, 32):
+        w = synth.workload(3, m=m)
+        cycles = max(5, args.steps * 8 // m)
+        out["m%d" % m] = cycle_leg(kb, synth, torch, dev, w, cycles, max(2, args.warmup * 8 // m))
+    return out
+
+
+def linear_leg(kb, synth, torch, dev, args):
+    """Linear rule (no gates), B=64 H=32 d=128: buffered m=8 against the
+    recurrent m=0 kernel at the same shape."""
+    w = synth.workload(2)
+    buf = cycle_leg(kb, synth, torch, dev, w, args.steps, args.warmup)
+    rec = cycle_leg(kb, synth, torch, dev, synth.workload(2, m=0, blocks_per_req=1), args.steps, args.warmup)
+    return {"m8": buf, "m0": rec, "speedup_vs_m0": buf["tokens_per_s"] / rec["tokens_per_s"]}
+
+
+def head_share_leg(kb, synth, torch, dev, args):
+    """One GPU's share when the 32 heads are split over 8 GPUs: B=256 H=4
+    (1024 tiles, 4 workgroups per CU), m=8, fold fused."""
+    w = synth.workload(3, H=4)
+    return cycle_leg(kb, synth, torch, dev, w, args.steps, args.warmup)
+
+
 def verify_leg(kb, synth, torch, dev, args):
     """B=128 H=32 d=128 m=8 gated: per n, one kvbuf_verify of n drafts then
     one kvbuf_commit of the accepted prefixes (the fold, when a commit fills
@@ -201,11 +261,55 @@ def verify_leg(kb, synth, torch, dev, args):
         accepted = float(sum(int(a.sum()) for a in accs[:4]) / 4)
         # one state read serves all n drafts
         vbytes = tiles * (4 * w.dk * w.dv + 2 * n * (2 * w.dk + w.dv) + 4 * n * w.dv)
-        out["n%d" % n] = {"verify_ms": ver, "commit_ms": com,
-                          "verify_hbm_gbps": vbytes / (ver * 1e-3) / 1e9,
-                          "accepted_tokens_per_s": accepted / ((ver + com) * 1e-3)}
+        res = {"verify_ms": ver, "commit_ms": com,
+               "verify_hbm_gbps": vbytes / (ver * 1e-3) / 1e9,
+               "accepted_tokens_per_s": accepted / ((ver + com) * 1e-3)}
         del kv
+        res["recurrent_baseline"] = verify_baseline(kb, synth, torch, dev, w, n, drafts, accs)
+        # state memory per request: KVBuffer keeps one state and a buffer of
+        # capacity block_size * blocks_per_req; the baseline keeps the state
+        # and one temporary state per draft (Figure 2 caption)
+        s_bytes = w.H * 4 * w.dk * w.dv
+        cap = w.block_size * w.blocks_per_req
+        kvb = s_bytes + w.H * cap * (2 * (w.dk + w.dv) + 4)
+        base = (1 + n) * s_bytes
+        res["state_memory_per_request_bytes"] = {"kvbuffer": kvb, "recurrent_temporaries": base,
+                                                 "requests_ratio": base / kvb}
+        out["n%d" % n] = res
     return out
+
+
+def verify_baseline(kb, synth, torch, dev, w, n, drafts, accs):
+    """The verification KVBuffer replaces: recurrent form with a temporary
+    state per draft (m = 0), then the commit that copies the last accepted
+    draft's temporary state into the request's slot."""
+    w0 = synth.workload(4, m=0, blocks_per_req=1)
+    kv = build_kv(kb, synth, torch, w0, kb.FLUSH_EAGER, dev)
+    temp = torch.empty((n, w.B, w.H, w.dk, w.dv), dtype=torch.float32, device=dev)
+    obuf = torch.empty((w.B, n, w.H, w.dv), dtype=torch.float32, device=dev)
+
+    def call(c):
+        d = drafts[c % 4]
+        return [lambda: kv.verify_recurrent(d["q"], d["k"], d["v"], d["g"], out=obuf, temp=temp),
+                lambda: kv.commit_recurrent(n, accs[c % 4], temp)]
+
+    for c in range(4):
+        for f in call(c):
+            f()
+    launches = []
+    for c in range(8):
+        launches += call(c)
+    per = per_launch_ms(torch, launches, 10)
+    torch.cuda.synchronize()
+    assert int(kv.error.item()) == 0
+    del kv, temp
+    ver = sum(per[0::2]) / 8
+    com = sum(per[1::2]) / 8
+    tiles = w.B * w.H
+    vbytes = tiles * (4 * w.dk * w.dv * (1 + n) + 2 * n * (2 * w.dk + w.dv) + 4 * n * (w.dv + 1))
+    accepted = float(sum(int(a.sum()) for a in accs[:4]) / 4)
+    return {"verify_ms": ver, "commit_ms": com, "verify_hbm_gbps": vbytes / (ver * 1e-3) / 1e9,
+            "accepted_tokens_per_s": accepted / ((ver + com) * 1e-3)}
 
 
 def delta_leg(kb, synth, torch, dev, args):
@@ -252,7 +356,8 @@ def main():
     ap.add_argument("--m", type=int, default=8, help="buffer size")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing on the host")
     ap.add_argument("--no-extras", action="store_true", help="skip the m=0 / separate-flush / copy legs")
-    ap.add_argument("--only", choices=["fused", "recurrent", "separate", "copy", "verify", "delta"], default=None,
+    ap.add_argument("--only", choices=["fused", "recurrent", "separate", "copy", "verify", "delta", "sweep",
+                                       "linear", "heads4"], default=None,
                     help="run one leg only (for profiling)")
     args = ap.parse_args()
 
@@ -374,6 +479,14 @@ def main():
     if not args.no_extras and args.only in (None, "delta"):
         result["delta_mixed"] = delta_leg(kb, synth, torch, dev, args)
 
+    # ---- buffer-size sweep, linear rule at B=64, one GPU's head share ---------
+    if not args.no_extras and args.only in (None, "sweep"):
+        result["m_sweep"] = sweep_leg(kb, synth, torch, dev, args)
+    if not args.no_extras and args.only in (None, "linear"):
+        result["linear_B64"] = linear_leg(kb, synth, torch, dev, args)
+    if not args.no_extras and args.only in (None, "heads4"):
+        result["head_share_H4"] = head_share_leg(kb, synth, torch, dev, args)
+
     if args.only not in (None, "fused"):
         print(json.dumps(result))
         return
@@ -411,7 +524,7 @@ def main():
         "cpu_baseline": cpu,
     }
     for key in ("per_occupancy_ms", "m0_recurrent", "separate_flush", "copy_ceiling_gbps", "verify",
-                "delta_mixed"):
+                "delta_mixed", "m_sweep", "linear_B64", "head_share_H4"):
         if key in result:
             line[key] = result[key]
     print(json.dumps(line))

@@ -188,6 +188,35 @@ kvbuf_status kvbuf_commit(const kvbuf_layout* layout, const kvbuf_pools* pools,
                           hipStream_t stream);
 
 /*
+ * kvbuf_verify_recurrent -- the verification that kvbuf_verify replaces
+ * (Figure 2 caption: a system with only a state pool verifies drafts with the
+ * recurrent form and keeps a temporary state for every draft).  Recurrent
+ * mode only (m = 0).  For every request, drafts 0..n-1 are applied one at a
+ * time to a copy of its state: draft d's output goes to out [B][n][H][d_v]
+ * fp32 and the state after draft d to temp [n][B][H][d_k][d_v] fp32
+ * (caller-owned device memory, n states per request).  The state pool is not
+ * modified.  Inputs as kvbuf_verify.  Requires 1 <= n <= 8; a request
+ * without a valid state slot sets KVBUF_DEVERR_SLOT and is skipped.
+ */
+kvbuf_status kvbuf_verify_recurrent(const kvbuf_layout* layout, const kvbuf_pools* pools,
+                                    const kvbuf_batch* batch, int32_t n, const void* q,
+                                    const void* k, const void* v, const float* g,
+                                    const float* beta, float* out, float* temp,
+                                    hipStream_t stream);
+
+/*
+ * kvbuf_commit_recurrent -- completes kvbuf_verify_recurrent: a request with
+ * accepted[b] = a > 0 takes temp[a-1] as its state (Figure 2 caption: the
+ * request's state is replaced by the temporary state of its last accepted
+ * draft); a = 0 leaves it unchanged.  accepted: [B] int32, device memory;
+ * a value outside [0, n] sets KVBUF_DEVERR_ACCEPT and skips the request.
+ */
+kvbuf_status kvbuf_commit_recurrent(const kvbuf_layout* layout, const kvbuf_pools* pools,
+                                    const kvbuf_batch* batch, int32_t n,
+                                    const int32_t* accepted, const float* temp,
+                                    hipStream_t stream);
+
+/*
  * kvbuf_direct -- decode from the buffer alone for every request, whatever its
  * state slot (abstract: for short contexts the output is computed directly
  * from the buffered keys and values, without creating or updating a state).

@@ -27,7 +27,8 @@ OK, EINVAL, EUNSUPPORTED, ECAPACITY, EHIP = 0, -1, -2, -3, -4
 DEVERR_BLOCK, DEVERR_SLOT, DEVERR_OVERFLOW, DEVERR_ACCEPT = 1, 2, 4, 8
 
 EXPORTED = ("kvbuf_decode", "kvbuf_flush", "kvbuf_verify", "kvbuf_commit", "kvbuf_direct",
-            "kvbuf_materialize", "kvbuf_strerror", "kvbuf_abi_version")
+            "kvbuf_verify_recurrent", "kvbuf_commit_recurrent", "kvbuf_materialize", "kvbuf_strerror",
+            "kvbuf_abi_version")
 
 
 class Layout(ctypes.Structure):
@@ -76,8 +77,11 @@ def load():
         lib.kvbuf_flush.argtypes = [L, PO, B, P]
         lib.kvbuf_commit.argtypes = [L, PO, B, i32, P, P]
         lib.kvbuf_materialize.argtypes = [L, PO, B, P, P]
+        lib.kvbuf_verify_recurrent.argtypes = [L, PO, B, i32, P, P, P, P, P, P, P, P]
+        lib.kvbuf_commit_recurrent.argtypes = [L, PO, B, i32, P, P, P]
         for name in ("kvbuf_decode", "kvbuf_direct", "kvbuf_verify", "kvbuf_flush",
-                     "kvbuf_commit", "kvbuf_materialize"):
+                     "kvbuf_commit", "kvbuf_materialize", "kvbuf_verify_recurrent",
+                     "kvbuf_commit_recurrent"):
             getattr(lib, name).restype = ctypes.c_int
         lib.kvbuf_strerror.argtypes = [ctypes.c_int]
         lib.kvbuf_strerror.restype = ctypes.c_char_p
@@ -152,6 +156,20 @@ def kvbuf_materialize(layout, pools, batch, states, stream=None, raise_on_error=
     st = load().kvbuf_materialize(_ref(layout), _ref(pools), _ref(batch), _ptr(states),
                                   _stream(stream))
     return _check(st, "kvbuf_materialize", raise_on_error)
+
+
+def kvbuf_verify_recurrent(layout, pools, batch, n, q, k, v, g, beta, out, temp, stream=None,
+                           raise_on_error=True):
+    st = load().kvbuf_verify_recurrent(_ref(layout), _ref(pools), _ref(batch), int(n), _ptr(q), _ptr(k),
+                                       _ptr(v), _ptr(g), _ptr(beta), _ptr(out), _ptr(temp),
+                                       _stream(stream))
+    return _check(st, "kvbuf_verify_recurrent", raise_on_error)
+
+
+def kvbuf_commit_recurrent(layout, pools, batch, n, accepted, temp, stream=None, raise_on_error=True):
+    st = load().kvbuf_commit_recurrent(_ref(layout), _ref(pools), _ref(batch), int(n), _ptr(accepted),
+                                       _ptr(temp), _stream(stream))
+    return _check(st, "kvbuf_commit_recurrent", raise_on_error)
 
 
 def kvbuf_abi_version() -> int:
@@ -234,6 +252,20 @@ class KVBuffer:
 
     def commit(self, n, accepted, stream=None):
         kvbuf_commit(self.layout, self.pools, self.batch, n, accepted, stream)
+
+    def verify_recurrent(self, q, k, v, g=None, beta=None, out=None, temp=None, stream=None):
+        """Temporary-state verification (m = 0 only): returns (out, temp)."""
+        n = q.shape[1]
+        if out is None:
+            out = self.torch.empty((self.B, n, self.H, self.d), dtype=self.torch.float32, device=q.device)
+        if temp is None:
+            temp = self.torch.empty((n, self.B, self.H, self.d, self.d), dtype=self.torch.float32,
+                                    device=q.device)
+        kvbuf_verify_recurrent(self.layout, self.pools, self.batch, n, q, k, v, g, beta, out, temp, stream)
+        return out, temp
+
+    def commit_recurrent(self, n, accepted, temp, stream=None):
+        kvbuf_commit_recurrent(self.layout, self.pools, self.batch, n, accepted, temp, stream)
 
     def flush(self, stream=None):
         kvbuf_flush(self.layout, self.pools, self.batch, stream)

@@ -210,6 +210,51 @@ kvbuf_status kvbuf_commit(const kvbuf_layout* layout, const kvbuf_pools* pools,
     return fold_then_advance(t, layout, stream);
 }
 
+kvbuf_status kvbuf_verify_recurrent(const kvbuf_layout* layout, const kvbuf_pools* pools,
+                                    const kvbuf_batch* batch, int32_t n, const void* q,
+                                    const void* k, const void* v, const float* g,
+                                    const float* beta, float* out, float* temp,
+                                    hipStream_t stream) {
+    KVBUF_TRY(check_layout(layout, false));
+    if (layout->m != 0) return KVBUF_EUNSUPPORTED;  // the baseline has no buffer
+    KVBUF_TRY(check_batch(layout, batch));
+    KVBUF_TRY(check_pools(layout, pools, true));
+    if (batch->size == 0) return KVBUF_OK;
+    KVBUF_TRY(check_tokens(layout, q, k, v, g, beta, out));
+    if (!temp) return KVBUF_EINVAL;
+    if (n < 1 || n > kvbuf::kMaxDrafts) return KVBUF_EUNSUPPORTED;
+    KVBUF_TRY(check_grid(layout, batch));
+    TileParams t = make_params(layout, pools, batch);
+    t.mode = kvbuf::MODE_VERIFY;
+    t.n = n;
+    t.q = q;
+    t.k = k;
+    t.v = v;
+    t.g = g;
+    t.beta = beta;
+    t.out = out;
+    return from_hip(kvbuf::launch_verify_recurrent(t, layout->rule, layout->d_k, layout->io_dtype, temp, stream));
+}
+
+kvbuf_status kvbuf_commit_recurrent(const kvbuf_layout* layout, const kvbuf_pools* pools,
+                                    const kvbuf_batch* batch, int32_t n,
+                                    const int32_t* accepted, const float* temp,
+                                    hipStream_t stream) {
+    KVBUF_TRY(check_layout(layout, false));
+    if (layout->m != 0) return KVBUF_EUNSUPPORTED;
+    KVBUF_TRY(check_batch(layout, batch));
+    KVBUF_TRY(check_pools(layout, pools, true));
+    if (batch->size == 0) return KVBUF_OK;
+    if (!accepted || !temp) return KVBUF_EINVAL;
+    if (n < 1 || n > kvbuf::kMaxDrafts) return KVBUF_EUNSUPPORTED;
+    KVBUF_TRY(check_grid(layout, batch));
+    TileParams t = make_params(layout, pools, batch);
+    t.mode = kvbuf::MODE_COMMIT;
+    t.n = n;
+    t.accepted = accepted;
+    return from_hip(kvbuf::launch_commit_recurrent(t, layout->d_k, temp, stream));
+}
+
 kvbuf_status kvbuf_materialize(const kvbuf_layout* layout, const kvbuf_pools* pools,
                                const kvbuf_batch* batch, float* states, hipStream_t stream) {
     KVBUF_TRY(check_layout(layout, true));

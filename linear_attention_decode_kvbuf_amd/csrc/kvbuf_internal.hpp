@@ -63,6 +63,10 @@ int chunk_fold_limit(int rule, int d, int io, int n, int cap);
 // p.fold_chunk as that launch had them); one wave per request.
 hipError_t launch_advance(const TileParams& p, hipStream_t s);
 hipError_t launch_recurrent(const TileParams& p, int rule, int d, int io, int batch, hipStream_t s);
+// Verification with temporary states (m = 0) and its commit, temp
+// [n][B][H][d][d] fp32.
+hipError_t launch_verify_recurrent(const TileParams& p, int rule, int d, int io, float* temp, hipStream_t s);
+hipError_t launch_commit_recurrent(const TileParams& p, int d, const float* temp, hipStream_t s);
 
 // Head dims with compiled kernels (d_k == d_v).
 inline bool supported_dim(int d) { return d == 16 || d == 64 || d == 128; }

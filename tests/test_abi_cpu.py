@@ -112,3 +112,21 @@ def test_mode_specific_validation(lib):
     empty = kb.Batch(0, None, None, None, None)
     assert _decode(L, batch=empty) == kb.OK
     assert kb.kvbuf_flush(L0, POOLS, BATCH, 0, False) == kb.OK
+
+
+def test_recurrent_verification_validation(lib):
+    L0 = _layout(m=0)
+    vr = lambda L, n, temp=FAKE: kb.kvbuf_verify_recurrent(L, POOLS, BATCH, n, FAKE, FAKE, FAKE, FAKE, None,
+                                                           FAKE, temp, 0, False)
+    cr = lambda L, n, acc=FAKE, temp=FAKE: kb.kvbuf_commit_recurrent(L, POOLS, BATCH, n, acc, temp, 0, False)
+    assert vr(_layout(), 2) == kb.EUNSUPPORTED      # the baseline has no buffer: m = 0 only
+    assert vr(L0, 0) == kb.EUNSUPPORTED
+    assert vr(L0, 9) == kb.EUNSUPPORTED
+    assert vr(L0, 2, temp=None) == kb.EINVAL
+    assert cr(_layout(), 2) == kb.EUNSUPPORTED
+    assert cr(L0, 2, acc=None) == kb.EINVAL
+    assert cr(L0, 2, temp=None) == kb.EINVAL
+    assert cr(L0, 9) == kb.EUNSUPPORTED
+    empty = kb.Batch(0, None, None, None, None)
+    assert kb.kvbuf_verify_recurrent(L0, POOLS, empty, 2, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, 0,
+                                     False) == kb.OK

@@ -324,3 +324,61 @@ def test_workload5_mixed_delta():
     run.check_pool()
     run.check_bookkeeping()
     _say("retired %d; max out err %.2e, max state err %.2e" % (retired, run.max_out, run.max_state))
+
+
+# ---------------------------------------------------------------------------
+# The verification that the buffered one replaces: recurrent form with one
+# temporary state per draft (m = 0), and its commit by state replacement.
+# ---------------------------------------------------------------------------
+
+def _tile_rel(a, b):
+    a = np.asarray(a, np.float64).reshape(a.shape[0], -1)
+    b = np.asarray(b, np.float64).reshape(b.shape[0], -1)
+    return np.max(np.abs(a - b), axis=1) / np.maximum(np.max(np.abs(b), axis=1), 1e-30)
+
+
+@pytest.mark.parametrize("rule", [0, 1, 2])
+@pytest.mark.parametrize("n,d", [(1, 64), (4, 128), (8, 64), (3, 16)])
+def test_verify_recurrent_baseline(rule, n, d):
+    import oracle
+
+    w = synth.workload(1, B=5, H=2, dk=d, dv=d, m=0, block_size=1, blocks_per_req=1, steps=3,
+                       rule=rule, io="bf16", state_std=0.02)
+    _say("recurrent verify", w, "n", n)
+    run = Run(w)
+    for t in range(2):  # move the states away from their initial values
+        run.decode(t)
+    inp = run.inputs(0, n=n, stream_base=100)
+    out, temp = run.kv.verify_recurrent(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"])
+    torch.cuda.synchronize()
+    assert int(run.kv.error.item()) == 0
+    q, k, v, g, beta = (run._sampled(inp[x], drafts=True) for x in ("q", "k", "v", "g", "beta"))
+    o_gpu = run._sampled(out, drafts=True)
+    tmp = temp.detach()
+    for dd in range(n):
+        sl = slice(0, dd + 1)
+        o_ref, S_ref = oracle.recurrent(rule, run.S, q[:, sl].transpose(1, 0, 2), k[:, sl].transpose(1, 0, 2),
+                                        v[:, sl].transpose(1, 0, 2),
+                                        None if g is None else g[:, sl].T,
+                                        None if beta is None else beta[:, sl].T)
+        assert np.max(_tile_rel(o_gpu[:, dd], o_ref[dd])) <= 2e-3, dd
+        t_gpu = tmp[dd][run.sb, run.sh].double().cpu().numpy()
+        assert np.max(_tile_rel(t_gpu, S_ref)) <= 1e-5, dd
+    # commit: the state of a request becomes its last accepted draft's temporary state
+    acc = synth.accepted_lengths(w, 0, w.B, n)
+    before = run.kv.state.detach().clone()
+    run.kv.commit_recurrent(n, torch.from_numpy(acc).to("cuda"), temp)
+    torch.cuda.synchronize()
+    assert int(run.kv.error.item()) == 0
+    after = run.kv.state.detach()
+    for b in range(w.B):
+        want = before[run.slots[b]] if acc[b] == 0 else tmp[acc[b] - 1, b]
+        assert torch.equal(after[run.slots[b]], want), b
+    # an accepted count outside [0, n] is reported and changes nothing
+    bad = torch.from_numpy(acc).to("cuda")
+    bad[0] = n + 1
+    snap = run.kv.state.detach().clone()
+    run.kv.commit_recurrent(n, bad, temp)
+    torch.cuda.synchronize()
+    assert int(run.kv.error.item()) & kb.DEVERR_ACCEPT
+    assert torch.equal(run.kv.state[run.slots[0]], snap[run.slots[0]])
