@@ -63,14 +63,14 @@ def cycle_bytes_separate(m, dk, dv, io=2, gated=True):
 
 
 def _traffic_file(m):
-    return os.path.join(ROOT, "profiles", "traffic_chunk_kernel_B256_H32_d128_m%d.txt" % m)
+    return os.path.join(ROOT, "profiles", "traffic_decode_kernel_B256_H32_d128_m%d.txt" % m)
 
 
 def _kernel_source_digest():
     import hashlib
 
     h = hashlib.sha256()
-    for name in ("chunk.hip", "device_common.hpp", "kvbuf_internal.hpp"):
+    for name in ("decode.hip", "device_common.hpp", "kvbuf_internal.hpp"):
         with open(os.path.join(ROOT, "linear_attention_decode_kvbuf_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -102,7 +102,7 @@ def build_kv(kb, synth, torch, w, flush, device):
                      num_state_slots=w.B, rule=w.rule, io_dtype=kb.BF16, flush=flush, device=device)
     if w.m > 0:
         perm = synth.block_permutation(w, w.B * w.blocks_per_req)
-        kv.block_table.copy_(torch.from_numpy(perm.reshape(w.B, w.blocks_per_req)))
+        kv.set_block_table(perm.reshape(w.B, w.blocks_per_req))
     kv.state_slot.copy_(torch.from_numpy(synth.slot_permutation(w, w.B)))
     kv.state.copy_(synth.device_initial_state(w, w.B, device))
     return kv
@@ -112,15 +112,26 @@ def make_ring(synth, w, device, size):
     return [synth.device_token_inputs(w, t, device) for t in range(size)]
 
 
-def time_loop(torch, fn, cycles, warmup):
+def time_loop(torch, fn, cycles, warmup, events=False):
+    """Wall time of ``cycles`` calls of fn after ``warmup`` untimed ones; with
+    events=True also the time between HIP events recorded on the current
+    stream (the one the kernels are launched on) around the same region."""
     for i in range(warmup):
         fn(i)
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    e0.record(stream)
     for i in range(cycles):
         fn(warmup + i)
+    e1.record(stream)
     torch.cuda.synchronize()
-    return time.perf_counter() - t0
+    wall = time.perf_counter() - t0
+    if events:
+        return wall, e0.elapsed_time(e1) * 1e-3
+    return wall
 
 
 def per_launch_ms(torch, launches, reps):
@@ -323,7 +334,7 @@ def delta_leg(kb, synth, torch, dev, args):
                      num_state_slots=w.B - w.n_short, rule=kb.RULE_DELTA, io_dtype=kb.BF16,
                      flush=kb.FLUSH_EAGER, device=dev)
     perm = synth.block_permutation(w, w.B * w.blocks_per_req)
-    kv.block_table.copy_(torch.from_numpy(perm.reshape(w.B, w.blocks_per_req)))
+    kv.set_block_table(perm.reshape(w.B, w.blocks_per_req))
     slots = torch.full((w.B,), -1, dtype=torch.int32)
     slots[: w.B - w.n_short] = torch.arange(w.B - w.n_short, dtype=torch.int32)
     kv.state_slot.copy_(slots)
@@ -393,16 +404,19 @@ def main():
             for j in range(m):
                 decode_fn(kv, i * m + j)()
 
-        wall = time_loop(torch, cycle, args.steps, args.warmup)
+        wall, ev = time_loop(torch, cycle, args.steps, args.warmup, events=True)
         ms_per_step = wall / args.steps * 1e3
         tok_s = w.B * m * args.steps / wall
-        # per-launch durations (events on the launch stream) over the cycle
+        # each decode call is one decode_kernel launch: the average launch
+        # duration is the event time of the timed region over its launches
+        avg_launch_ms = ev * 1e3 / (args.steps * m)
+        # per-occupancy durations, one event pair per launch (each adds an
+        # event record to the launch it brackets)
         reps = max(10, min(args.steps, 50))
         per = per_launch_ms(torch, [decode_fn(kv, j) for j in range(m)], reps)
         torch.cuda.synchronize()
         assert int(kv.error.item()) == 0
         cyc_bytes = cycle_bytes_fused(m, w.dk, w.dv) * tiles
-        avg_launch_ms = sum(per) / m
         achieved = cyc_bytes / m / (avg_launch_ms * 1e-3) / 1e9
         traffic = read_traffic(m, m)
         result.update(
@@ -413,7 +427,7 @@ def main():
             per_occupancy_ms=[round(x, 5) for x in per],
             roofline={"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                       "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
-                      "kernel": "chunk_kernel (decode; the last launch of a cycle folds)",
+                      "kernel": "decode_kernel (one-token decode; the last launch of a cycle folds)",
                       "avg_launch_ms": avg_launch_ms,
                       "algorithmic_bytes_per_launch": cyc_bytes / m},
         )
@@ -423,15 +437,15 @@ def main():
     if not args.no_extras and args.only in (None, "recurrent"):
         w0 = synth.workload(3, m=0, block_size=1, blocks_per_req=1)
         kv0 = build_kv(kb, synth, torch, w0, kb.FLUSH_EAGER, dev)
-        wall0 = time_loop(torch, lambda i: [decode_fn(kv0, i * m + j)() for j in range(m)],
-                          args.steps, args.warmup)
-        per0 = per_launch_ms(torch, [decode_fn(kv0, j) for j in range(m)], 20)
+        wall0, ev0 = time_loop(torch, lambda i: [decode_fn(kv0, i * m + j)() for j in range(m)],
+                               args.steps, args.warmup, events=True)
+        avg0 = ev0 * 1e3 / (args.steps * m)
         b0 = recurrent_bytes(w.dk, w.dv) * tiles
         result["m0_recurrent"] = {
             "tokens_per_s": w.B * m * args.steps / wall0,
             "ms_per_token_step": wall0 / (args.steps * m) * 1e3,
-            "avg_launch_ms": sum(per0) / m,
-            "hbm_gbps": b0 / (sum(per0) / m * 1e-3) / 1e9,
+            "avg_launch_ms": avg0,
+            "hbm_gbps": b0 / (avg0 * 1e-3) / 1e9,
             "bytes_per_token": b0 / w.B,
         }
         del kv0

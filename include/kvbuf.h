@@ -24,9 +24,9 @@
  * buffer below (for example as PyTorch tensors).  Argument validation happens
  * on the host before anything is enqueued, so a call that returns an error
  * has changed nothing.  Metadata that lives on the device (occupancy, block
- * ids, state slots, accepted counts) is checked by the kernels: a request whose
- * metadata is out of range is skipped entirely (no memory outside the pools is
- * touched) and a bit is set in the optional device error word.
+ * ids, state slots, accepted counts) is checked by the kernels: a (request,
+ * head) tile whose metadata is out of range is skipped (no memory outside the
+ * pools is touched) and a bit is set in the optional device error word.
  *
  * Concurrency: calls on one stream are ordered; two calls that overlap in time
  * (different streams) must not touch the same requests, blocks or state slots.
@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define KVBUF_ABI_VERSION 2
+#define KVBUF_ABI_VERSION 3
 
 typedef enum kvbuf_status {
     KVBUF_OK = 0,
@@ -110,15 +110,21 @@ typedef struct kvbuf_pools {
 
 /* The batch: B requests.  All arrays are int32 in device memory, caller-owned,
  * and updated by the library in stream order.
- *   state_slot  [B]                  slot in the state pool; -1 = no state (the
- *                                    request is served from its buffer alone and
- *                                    never folds)
- *   block_table [B][blocks_per_req]  pool block ids, in buffer order: buffer
- *                                    position p is block_table[b][p / block_size],
- *                                    offset p % block_size.  A fold moves the
- *                                    m / block_size leading blocks to the back.
- *   occupancy   [B]                  tokens buffered since the last fold
- *   error       [1] or NULL          KVBUF_DEVERR_* bits are OR-ed into it */
+ *   state_slot  [B]                     slot in the state pool; -1 = no state (the
+ *                                       request is served from its buffer alone
+ *                                       and never folds).  Never written.
+ *   block_table [B][H][blocks_per_req]  pool block ids, in buffer order: buffer
+ *                                       position p of head h is
+ *                                       block_table[b][h][p / block_size], offset
+ *                                       p % block_size.  A fold moves the
+ *                                       m / block_size leading blocks to the back.
+ *   occupancy   [B][H]                  tokens buffered since the last fold
+ *   error       [1] or NULL             KVBUF_DEVERR_* bits are OR-ed into it
+ * The table and occupancy are kept per (request, head): the H copies of a
+ * request hold the same values (the caller writes all of them), and each is
+ * read and advanced in place by the one workgroup that serves that head, so
+ * a call needs no cross-workgroup synchronisation.  A tile whose metadata
+ * fails a device check is skipped and its copy left unchanged. */
 typedef struct kvbuf_batch {
     int32_t size;
     int32_t* state_slot;
@@ -139,8 +145,8 @@ typedef struct kvbuf_batch {
  *         else NULL).
  * Output  out [B][H][d_v] fp32, o = S_t^T (scale q) with S_t the state after
  *         this token.
- * m > 0:  appends the token at buffer position occupancy[b] and advances the
- *         occupancy.  A request with a state slot computes its output from the
+ * m > 0:  appends the token at buffer position occupancy[b][h] and advances
+ *         the occupancy.  A request with a state slot computes its output from the
  *         state at its last fold plus the buffer; one without (slot -1) from
  *         the buffer alone.  With KVBUF_FLUSH_EAGER a request with a state
  *         whose buffer reaches m folds in the same kernel.

@@ -184,7 +184,9 @@ class KVBuffer:
     key        [num_blocks, H, block_size, d_k] io dtype
     value      [num_blocks, H, block_size, d_v] io dtype (fp32 for the delta rule)
     gate       [num_blocks, H, block_size] fp32 (None for the linear rule)
-    state_slot, occupancy [B] int32; block_table [B, blocks_per_req] int32
+    state_slot [B] int32
+    block_table [B, H, blocks_per_req] int32, occupancy [B, H] int32 (one copy
+               per head, all equal; ``set_block_table`` writes every head)
     error      [1] int32
     """
 
@@ -216,9 +218,10 @@ class KVBuffer:
             self.key = self.value = self.gate = None
         i32 = torch.int32
         self.state_slot = torch.arange(batch, dtype=i32, device=dev) % max(num_state_slots, 1)
-        self.block_table = torch.arange(batch * blocks_per_req, dtype=i32, device=dev).reshape(
-            batch, blocks_per_req) % max(num_blocks, 1)
-        self.occupancy = torch.zeros(batch, dtype=i32, device=dev)
+        self.block_table = torch.empty((batch, heads, blocks_per_req), dtype=i32, device=dev)
+        self.set_block_table(torch.arange(batch * blocks_per_req, dtype=i32).reshape(
+            batch, blocks_per_req) % max(num_blocks, 1))
+        self.occupancy = torch.zeros((batch, heads), dtype=i32, device=dev)
         self.error = torch.zeros(1, dtype=i32, device=dev)
         self._refresh()
 
@@ -226,6 +229,11 @@ class KVBuffer:
         self.pools = Pools(_ptr(self.state), _ptr(self.key), _ptr(self.value), _ptr(self.gate))
         self.batch = Batch(self.B, _ptr(self.state_slot), _ptr(self.block_table), _ptr(self.occupancy),
                            _ptr(self.error))
+
+    def set_block_table(self, table):
+        """Every head's copy of the block table <- table [B, blocks_per_req]."""
+        t = self.torch.as_tensor(table, dtype=self.torch.int32).to(self.block_table.device)
+        self.block_table.copy_(t.reshape(self.B, 1, -1).expand(self.B, self.H, t.shape[-1]))
 
     @property
     def capacity(self):

@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libkvbuf.so")
 OBJ_DIR = os.path.join(PKG, "_build")
 
-SOURCES = ["abi.cpp", "chunk.hip", "fold.hip", "recurrent.hip", "bookkeeping.hip", "decode.hip"]
+SOURCES = ["abi.cpp", "chunk.hip", "fold.hip", "recurrent.hip", "decode.hip"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 instructions.

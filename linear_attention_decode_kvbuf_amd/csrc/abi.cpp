@@ -1,7 +1,7 @@
-// The C ABI of libkvbuf: argument validation on the host, then the compute
-// launch and (for calls that move the buffer) a small bookkeeping launch on
-// the caller's stream.  No allocation, no synchronisation, no global mutable
-// state.
+// The C ABI of libkvbuf: argument validation on the host, then one kernel
+// launch on the caller's stream (two for an eager decode whose m exceeds what
+// the decode kernel folds itself).  No allocation, no synchronisation, no
+// global mutable state.
 #include <hip/hip_runtime.h>
 
 #include "kvbuf.h"
@@ -101,14 +101,6 @@ kvbuf_status from_hip(hipError_t e) { return e == hipSuccess ? KVBUF_OK : KVBUF_
         if (st_ != KVBUF_OK) return st_;   \
     } while (0)
 
-// Flush and commit: the fold launch, then the bookkeeping launch that
-// advances occupancies and rotates table rows.
-kvbuf_status fold_then_advance(const TileParams& t, const kvbuf_layout* L, hipStream_t stream) {
-    hipError_t e = kvbuf::launch_fold(t, L->rule, L->d_k, L->io_dtype, t.batch, stream);
-    if (e == hipSuccess) e = kvbuf::launch_advance(t, stream);
-    return from_hip(e);
-}
-
 kvbuf_status chunk_call(const kvbuf_layout* layout, const kvbuf_pools* pools,
                         const kvbuf_batch* batch, int mode, int n, const void* q,
                         const void* k, const void* v, const float* g, const float* beta,
@@ -144,12 +136,10 @@ kvbuf_status chunk_call(const kvbuf_layout* layout, const kvbuf_pools* pools,
         return from_hip(kvbuf::launch_recurrent(t, layout->rule, layout->d_k, layout->io_dtype,
                                                 batch->size, stream));
     hipError_t e = kvbuf::launch_chunk(t, layout->rule, layout->d_k, layout->io_dtype, batch->size, stream);
-    if (e == hipSuccess && mode != kvbuf::MODE_VERIFY) e = kvbuf::launch_advance(t, stream);
     if (e == hipSuccess && eager_decode && !fused) {
         t.mode = kvbuf::MODE_FLUSH;
         t.fold_chunk = fold_chunk(layout->m);
         e = kvbuf::launch_fold(t, layout->rule, layout->d_k, layout->io_dtype, batch->size, stream);
-        if (e == hipSuccess) e = kvbuf::launch_advance(t, stream);
     }
     return from_hip(e);
 }
@@ -189,7 +179,7 @@ kvbuf_status kvbuf_flush(const kvbuf_layout* layout, const kvbuf_pools* pools,
     TileParams t = make_params(layout, pools, batch);
     t.mode = kvbuf::MODE_FLUSH;
     t.fold_chunk = fold_chunk(layout->m);
-    return fold_then_advance(t, layout, stream);
+    return from_hip(kvbuf::launch_fold(t, layout->rule, layout->d_k, layout->io_dtype, batch->size, stream));
 }
 
 kvbuf_status kvbuf_commit(const kvbuf_layout* layout, const kvbuf_pools* pools,
@@ -207,7 +197,7 @@ kvbuf_status kvbuf_commit(const kvbuf_layout* layout, const kvbuf_pools* pools,
     t.n = n;
     t.fold_chunk = fold_chunk(layout->m);
     t.accepted = accepted;
-    return fold_then_advance(t, layout, stream);
+    return from_hip(kvbuf::launch_fold(t, layout->rule, layout->d_k, layout->io_dtype, batch->size, stream));
 }
 
 kvbuf_status kvbuf_verify_recurrent(const kvbuf_layout* layout, const kvbuf_pools* pools,

@@ -89,6 +89,7 @@ void chunk_kernel(TileParams P) {
 
     extern __shared__ float lds[];
     __shared__ unsigned s_bad;
+    __shared__ int s_p;
 
     const TileIndex ti = tile_index(P);
     const int b = ti.b;
@@ -102,8 +103,7 @@ void chunk_kernel(TileParams P) {
     const int cap = P.block_size * P.blocks_per_req;
     const bool direct = P.mode == MODE_DIRECT;
 
-    // ---- request metadata -----------------------------------------------------
-    const int p = P.occ[b];
+    // ---- tile metadata (read by wave 0 only, which also updates it) -----------
     const int slot = direct ? -1 : P.slot[b];
     const ChunkLds L = chunk_lds(RULE, DK, DV, NQ, RG, NG, cap, P.m, P.fold_chunk > 0,
                                  static_cast<int>(sizeof(IO)), static_cast<int>(sizeof(XIO)));
@@ -118,15 +118,20 @@ void chunk_kernel(TileParams P) {
     XIO* vrs = reinterpret_cast<XIO*>(lds + L.vr);
     float* fw = lds + L.fw;
     if (tid < 64) {
-        unsigned bad = stage_row(P, b, h, (p < 0 || p > cap) ? -1 : p + n, spos, tid);
+        const int p0 = P.occ[meta_index(P, b, h)];
+        unsigned bad = stage_row(P, b, h, (p0 < 0 || p0 > cap) ? -1 : p0 + n, spos, tid);
         if (slot >= P.num_slots) bad |= KVBUF_DEVERR_SLOT;
-        if (tid == 0) s_bad = bad;
+        if (tid == 0) {
+            s_bad = bad;
+            s_p = p0;
+        }
     }
-    __syncthreads();  // every wave has read the metadata; spos and s_bad are complete
+    __syncthreads();  // spos, s_p and s_bad are complete
     if (s_bad) {
         report(P, s_bad);
-        return;  // the whole request is skipped by all of its workgroups
+        return;  // the tile is skipped and its metadata left unchanged
     }
+    const int p = s_p;  // occupancy before this call
     const bool has_state = slot >= 0;
     const int T = p + n;                       // positions touched by this call
     const bool fold = P.fold_chunk > 0 && has_state && T >= P.m;  // launcher: fold_chunk >= m
@@ -392,8 +397,9 @@ void chunk_kernel(TileParams P) {
             __builtin_nontemporal_store(s[j], reinterpret_cast<f4*>(wt + (rg * RPT + j) * DV + c0));
     }
 
-    // The occupancy and table row are updated by the bookkeeping launch that
-    // follows this one (decode, direct), once every workgroup is done with them.
+    // ---- 8. metadata: occupancy over the appended tokens, table rotation -----
+    if (tid < 64 && P.mode != MODE_VERIFY)  // drafts do not advance the occupancy
+        update_meta(P, b, h, fold ? T - P.m : T, fold ? P.m / P.block_size : 0, tid);
 }
 
 template <int RULE, int D, typename IO>

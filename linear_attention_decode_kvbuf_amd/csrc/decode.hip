@@ -23,9 +23,9 @@
 //   staging and the appends -- all in registers and wave shuffles.
 // The roles meet at one barrier; then the row-group partials are reduced into
 // the output and, when the buffer fills, the state waves fold the staged
-// tokens into the tile still held in registers and write it back.  The
-// occupancy and table row are updated by the bookkeeping launch that follows
-// (decode, direct).
+// tokens into the tile still held in registers and write it back.  The token
+// wave, the tile's only reader of its occupancy and table row, advances them
+// in place (decode, direct).
 #include "device_common.hpp"
 
 namespace kvbuf {
@@ -88,9 +88,9 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void decode_kernel(TilePar
         const int bs = P.block_size;
         const int bpr = P.blocks_per_req;  // bs * bpr <= 64 (launcher)
         const int cap = bs * bpr;
-        const int p = P.occ[b];
+        const int p = P.occ[meta_index(P, b, h)];
         int blk = 0;
-        if (lane < bpr) blk = P.table[static_cast<size_t>(b) * bpr + lane];
+        if (lane < bpr) blk = P.table[meta_index(P, b, h) * bpr + lane];
         const int T = p + 1;  // positions after the append
         unsigned bad = 0;
         if (p < 0 || p >= cap) bad |= KVBUF_DEVERR_OVERFLOW;
@@ -205,6 +205,9 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void decode_kernel(TilePar
             s_fold = fold ? 1 : 0;
             s_es = GATED ? exp_gate(bt) : 1.0f;
         }
+        // this wave read the tile's metadata above; advance it in place
+        if (!bad && P.mode != MODE_VERIFY)
+            update_meta(P, b, h, fold ? Tl - P.m : Tl, fold ? P.m / bs : 0, lane);
     }
 
     // ---- state waves: query rows, then the tile; S0^T q per row group ----------
@@ -225,7 +228,7 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void decode_kernel(TilePar
     __syncthreads();
     if (s_bad) {
         report(P, s_bad);
-        return;  // the whole request is skipped by all of its workgroups
+        return;  // the tile is skipped and its metadata left unchanged
     }
 
     // ---- output: e^{b_t} scale (S0^T q) + buffered part ---------------------------

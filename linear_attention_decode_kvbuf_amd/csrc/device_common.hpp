@@ -336,7 +336,33 @@ __device__ __forceinline__ void report(const TileParams& P, unsigned bits) {
     if (bits && P.err && threadIdx.x == 0) atomicOr(reinterpret_cast<unsigned*>(P.err), bits);
 }
 
-// One wave (lane = 0..63) reads the request's whole table row with a single
+// Buffer metadata is kept per tile: occupancy [B][H] and block table
+// [B][H][blocks_per_req], every head of a request holding the same values.
+// The workgroup serving tile (b, h) is the only one that reads or writes its
+// copy, so it updates them in place once it is done reading them -- with no
+// atomics, fences or second launch.  Within a workgroup one wave does all the
+// reads and the update, so program order alone separates them.
+__device__ __forceinline__ size_t meta_index(const TileParams& P, int b, int h) {
+    return static_cast<size_t>(b) * P.H + h;
+}
+
+// By the wave that read the metadata (lane = 0..63): occupancy <- p_new and,
+// when k > 0, the first k table entries move to the back (the blocks a fold
+// consumed).  Every lane reads its source entry in one instruction before any
+// lane writes.
+__device__ __forceinline__ void update_meta(const TileParams& P, int b, int h, int p_new, int k, int lane) {
+    const size_t t = meta_index(P, b, h);
+    if (k > 0) {
+        const int bpr = P.blocks_per_req;
+        int32_t* row = P.table + t * bpr;
+        const int src = lane + k < bpr ? lane + k : lane + k - bpr;
+        const int v = lane < bpr ? row[src] : 0;
+        if (lane < bpr) row[lane] = v;
+    }
+    if (lane == 0) P.occ[t] = p_new;
+}
+
+// One wave (lane = 0..63) reads the tile's whole table row with a single
 // vector load -- it does not wait for the occupancy, so the row and the
 // occupancy arrive in the same round trip -- and writes, for every buffer
 // position i < capacity, its pool row (block * H + h) * block_size + i mod
@@ -349,7 +375,7 @@ __device__ __forceinline__ unsigned stage_row(const TileParams& P, int b, int h,
     const int bpr = P.blocks_per_req;  // <= 64 (host-checked)
     const int bs = P.block_size;
     int blk = 0;
-    if (lane < bpr) blk = P.table[static_cast<size_t>(b) * bpr + lane];
+    if (lane < bpr) blk = P.table[meta_index(P, b, h) * bpr + lane];
     const int cap = bs * bpr;
     for (int i = lane; i < cap; i += 64) {
         const int q = i / bs;

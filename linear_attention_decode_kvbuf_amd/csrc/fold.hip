@@ -47,6 +47,7 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void fold_kernel(TileParam
 
     extern __shared__ float lds[];
     __shared__ unsigned s_bad;
+    __shared__ int s_T, s_fold;
 
     const TileIndex ti = tile_index(P);
     const int b = ti.b;
@@ -59,31 +60,41 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void fold_kernel(TileParam
     const int cap = P.block_size * P.blocks_per_req;
     const bool materialize = P.mode == MODE_MATERIALIZE;
 
-    const int p = P.occ[b];
+    // The token wave reads the tile's metadata, checks it, and -- being its
+    // only reader -- advances it in place (flush, commit) before the barrier.
     const int slot = P.slot[b];
-    unsigned bad = 0;
-    int a = 0;
-    if (P.mode == MODE_COMMIT) {
-        a = P.accepted[b];
-        if (a < 0 || a > P.n) bad |= KVBUF_DEVERR_ACCEPT;
-    }
-    const int pn = (p < 0 || p > cap) ? -1 : p + a;
-    if (pn < 0 || pn > cap) bad |= KVBUF_DEVERR_OVERFLOW;
-    if (slot >= P.num_slots) bad |= KVBUF_DEVERR_SLOT;
     const bool has_state = slot >= 0;
-    const bool fold = !materialize && has_state && P.m > 0 && pn >= P.m &&
-                      (P.mode == MODE_FLUSH || P.fuse);
-    const int T = materialize ? p : (fold ? P.m : 0);  // positions applied
     if (token_wave) {
-        const unsigned bb = bad | stage_row(P, b, h, T, reinterpret_cast<uint32_t*>(lds), lane);
-        if (lane == 0) s_bad = bb;
+        const int p = P.occ[meta_index(P, b, h)];
+        unsigned bad = 0;
+        int a = 0;
+        if (P.mode == MODE_COMMIT) {
+            a = P.accepted[b];
+            if (a < 0 || a > P.n) bad |= KVBUF_DEVERR_ACCEPT;
+        }
+        const int pn = (p < 0 || p > cap) ? -1 : p + a;  // occupancy after the kept drafts
+        if (pn < 0 || pn > cap) bad |= KVBUF_DEVERR_OVERFLOW;
+        if (slot >= P.num_slots) bad |= KVBUF_DEVERR_SLOT;
+        const bool fold0 = !materialize && has_state && P.m > 0 && pn >= P.m &&
+                           (P.mode == MODE_FLUSH || P.fuse);
+        const int T0 = materialize ? p : (fold0 ? P.m : 0);  // positions applied
+        bad |= stage_row(P, b, h, T0, reinterpret_cast<uint32_t*>(lds), lane);
+        if (lane == 0) {
+            s_bad = bad;
+            s_T = T0;
+            s_fold = fold0 ? 1 : 0;
+        }
+        if (!bad && !materialize && (fold0 || a != 0))
+            update_meta(P, b, h, fold0 ? pn - P.m : pn, fold0 ? P.m / P.block_size : 0, lane);
     }
-    __syncthreads();  // every wave has read the metadata; the position table and s_bad are complete
+    __syncthreads();  // the position table, s_T, s_fold and s_bad are complete
     if (s_bad) {
         report(P, s_bad);
         return;
     }
-    if (!materialize && !fold) return;  // no state change for this request
+    const bool fold = s_fold != 0;
+    const int T = s_T;
+    if (!materialize && !fold) return;  // no state change for this tile
 
     const int fc = P.fold_chunk;
     float* bl = lds + ((cap + 3) & ~3);
@@ -158,8 +169,6 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void fold_kernel(TileParam
         for (int j = 0; j < RPT; ++j)
             __builtin_nontemporal_store(s[j], reinterpret_cast<f4*>(dst + (rg * RPT + j) * DV + c0));
     }
-    // The occupancy and table row are updated by the bookkeeping launch that
-    // follows this one (flush, commit).
 }
 
 template <int RULE, int D, typename IO>

@@ -33,9 +33,9 @@ struct TileParams {
     void* key;
     void* value;
     float* gate;
-    const int32_t* slot;
-    int32_t* table;
-    int32_t* occ;
+    const int32_t* slot;  // [B]
+    int32_t* table;       // [B][H][blocks_per_req]
+    int32_t* occ;         // [B][H]
     int32_t* err;
     const void* q;
     const void* k;
@@ -59,9 +59,6 @@ int decode_fold_limit(int d, int io);
 hipError_t launch_fold(const TileParams& p, int rule, int d, int io, int batch, hipStream_t s);
 // Largest m that a decode launch of n tokens folds itself (eager policy).
 int chunk_fold_limit(int rule, int d, int io, int n, int cap);
-// Bookkeeping of a decode / direct / flush / commit launch (p.mode, p.n,
-// p.fold_chunk as that launch had them); one wave per request.
-hipError_t launch_advance(const TileParams& p, hipStream_t s);
 hipError_t launch_recurrent(const TileParams& p, int rule, int d, int io, int batch, hipStream_t s);
 // Verification with temporary states (m = 0) and its commit, temp
 // [n][B][H][d][d] fp32.

@@ -73,7 +73,7 @@ class Run:
         self.stateless = np.zeros(B, bool) if stateless is None else np.asarray(stateless, bool)
         slots[self.stateless] = -1
         self.slots = slots
-        self.kv.block_table.copy_(torch.from_numpy(table))
+        self.kv.set_block_table(table)
         self.kv.state_slot.copy_(torch.from_numpy(slots))
         if self.device_gen:
             self.kv.state.copy_(synth.device_initial_state(w, nslots, self.dev))
@@ -192,7 +192,7 @@ class Run:
         new = [self.free.pop(0) for _ in range(bpr)]
         self.free.extend(old)
         self.model.replace_request(b, new, 0, has_state=False)
-        self.kv.block_table[b].copy_(torch.tensor(new, dtype=torch.int32))
+        self.kv.block_table[b].copy_(torch.tensor(new, dtype=torch.int32))  # every head
         self.kv.occupancy[b] = 0
         for j, (bb, _) in enumerate(self.sample):
             if bb == b:
@@ -237,8 +237,11 @@ class Run:
             return
         torch.cuda.synchronize()
         assert int(self.kv.error.item()) == 0, "device error flags %d" % int(self.kv.error.item())
-        np.testing.assert_array_equal(self.kv.block_table.cpu().numpy(), self.model.tables())
-        np.testing.assert_array_equal(self.kv.occupancy.cpu().numpy(), self.model.occupancies())
+        # every head's copy of the table and occupancy equals the model's
+        bt = self.kv.block_table.cpu().numpy()
+        occ = self.kv.occupancy.cpu().numpy()
+        np.testing.assert_array_equal(bt, np.broadcast_to(self.model.tables()[:, None, :], bt.shape))
+        np.testing.assert_array_equal(occ, np.broadcast_to(self.model.occupancies()[:, None], occ.shape))
 
     def check_pool(self):
         """Buffered keys, gates and (linear / gated rules) values of the sampled

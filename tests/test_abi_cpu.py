@@ -44,7 +44,7 @@ def test_struct_sizes_match_header(lib):
 
 
 def test_abi_version_and_strerror(lib):
-    assert kb.kvbuf_abi_version() == 2
+    assert kb.kvbuf_abi_version() == 3
     for st in (kb.OK, kb.EINVAL, kb.EUNSUPPORTED, kb.ECAPACITY, kb.EHIP):
         assert len(kb.strerror(st)) > 5
     assert "unknown" in kb.strerror(-99)

@@ -198,19 +198,26 @@ def test_device_errors_skip_the_request():
     run = Run(w)
     kv = run.kv
     before_state = kv.state.clone()
-    # request 1: a block id outside the pool
-    kv.block_table[1, 0] = 10_000
+    # request 1: a block id outside the pool (every head's copy)
+    kv.block_table[1, :, 0] = 10_000
     inp = run.inputs(0)
     out = kv.decode(inp["q"], inp["k"], inp["v"], inp["g"])
     assert _errors(kv) & kb.DEVERR_BLOCK
-    assert kv.occupancy.cpu().tolist() == [1, 0, 1]  # request 1 was skipped
+    assert kv.occupancy.cpu().tolist() == [[1, 1], [0, 0], [1, 1]]  # request 1 was skipped
     kv.error.zero_()
     # request 0: occupancy at capacity -> overflow, nothing written
-    kv.occupancy[0] = run.kv.capacity
-    kv.block_table[1, 0] = run.model.requests[1].table[0]
+    cap = run.kv.capacity
+    kv.occupancy[0] = cap
+    kv.block_table[1, :, 0] = run.model.requests[1].table[0]
     kv.decode(inp["q"], inp["k"], inp["v"], inp["g"], out=out)
     assert _errors(kv) & kb.DEVERR_OVERFLOW
-    assert kv.occupancy.cpu().tolist() == [run.kv.capacity, 1, 2]
+    assert kv.occupancy.cpu().tolist() == [[cap, cap], [1, 1], [2, 2]]
+    kv.error.zero_()
+    # a bad copy in one head skips that tile only; the other head advances
+    kv.block_table[2, 1, 0] = -3
+    kv.decode(inp["q"], inp["k"], inp["v"], inp["g"], out=out)
+    assert _errors(kv) & kb.DEVERR_BLOCK
+    assert kv.occupancy[2].cpu().tolist() == [3, 2]
     kv.error.zero_()
     # accepted count beyond n
     kv.occupancy[0] = 0
@@ -235,10 +242,10 @@ def test_validation_errors_touch_nothing():
     assert kb.kvbuf_verify(kv.layout, kv.pools, kv.batch, 9, z, z, z, g, None, z,
                            raise_on_error=False) == kb.EUNSUPPORTED
     torch.cuda.synchronize()
-    assert kv.occupancy.cpu().tolist() == [0, 0]
+    assert kv.occupancy.cpu().tolist() == [[0, 0], [0, 0]]
     kb.kvbuf_decode(kv.layout, kv.pools, kv.batch, z, z, z, g, None, z)
     torch.cuda.synchronize()
-    assert kv.occupancy.cpu().tolist() == [1, 1]
+    assert kv.occupancy.cpu().tolist() == [[1, 1], [1, 1]]
 
 
 # ---------------------------------------------------------------------------
