@@ -240,6 +240,79 @@ def head_share_leg(kb, synth, torch, dev, args):
     return cycle_leg(kb, synth, torch, dev, w, args.steps, args.warmup)
 
 
+def context_leg(kb, synth, torch, dev, args):
+    """A request's first L tokens, L = 16 .. 256, served three ways at the
+    metric shape (B=256 H=32 d=128, gated): recurrent (m = 0: the state is
+    read and written every token), chunkwise (m = 8, fold fused) and
+    buffer-only (kvbuf_direct with a buffer of capacity >= L: no state at
+    all).  Then the promotion of the buffer-only requests: a zeroed state
+    slot and one kvbuf_flush folding all L buffered tokens (the page's
+    Figure 5 compares the three decoding forms over context lengths 16-256;
+    the abstract: short contexts are served from the buffer alone)."""
+    out = {}
+    reps = 3
+    for L in (16, 32, 64, 128, 256):
+        w = synth.workload(3, steps=L)
+        ring = make_ring(synth, w, dev, 16)
+        obuf = torch.empty((w.B, w.H, w.dv), dtype=torch.float32, device=dev)
+
+        def run(kv, direct):
+            fn = kv.direct if direct else kv.decode
+            for t in range(L):
+                r = ring[t % len(ring)]
+                fn(r["q"], r["k"], r["v"], r["g"], out=obuf)
+
+        res = {}
+        for name, wl, direct in (("recurrent", synth.workload(3, m=0, blocks_per_req=1), False),
+                                 ("chunkwise_m8", synth.workload(3, m=8), False),
+                                 ("buffer_only", synth.workload(3, m=L, block_size=min(L, 16),
+                                                                blocks_per_req=max(L // 16, 1)), True)):
+            kv = build_kv(kb, synth, torch, wl, kb.FLUSH_EAGER, dev)
+            if direct:
+                kv.state_slot.fill_(-1)
+            times = []
+            for _ in range(reps):
+                kv.occupancy.zero_()
+                torch.cuda.synchronize()
+                stream = torch.cuda.current_stream()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                run(kv, direct)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                times.append(e0.elapsed_time(e1))
+            assert int(kv.error.item()) == 0
+            res[name] = {"ms_per_token_step": min(times) / L}
+            if direct:
+                # promotion: every request gets a zeroed slot, then one fold of
+                # its L tokens.  m = capacity, so the fold's table rotation is
+                # the identity and the same buffer can be promoted again: the
+                # second promotion is timed.
+                kv.state_slot.copy_(torch.from_numpy(synth.slot_permutation(w, w.B)).to(dev))
+                pt = []
+                for _ in range(2):
+                    kv.occupancy.fill_(L)
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    torch.cuda.synchronize()
+                    e0.record(torch.cuda.current_stream())
+                    kv.state.zero_()
+                    kv.flush()
+                    e1.record(torch.cuda.current_stream())
+                    torch.cuda.synchronize()
+                    assert int(kv.error.item()) == 0
+                    assert int(kv.occupancy.max().item()) == 0
+                    pt.append(e0.elapsed_time(e1))
+                res[name]["promotion_ms"] = pt[-1]
+            del kv
+        rec = res["recurrent"]["ms_per_token_step"]
+        for v in res.values():
+            v["normalized_to_recurrent"] = v["ms_per_token_step"] / rec
+        out["L%d" % L] = res
+    return out
+
+
 def verify_leg(kb, synth, torch, dev, args):
     """B=128 H=32 d=128 m=8 gated: per n, one kvbuf_verify of n drafts then
     one kvbuf_commit of the accepted prefixes (the fold, when a commit fills
@@ -368,7 +441,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing on the host")
     ap.add_argument("--no-extras", action="store_true", help="skip the m=0 / separate-flush / copy legs")
     ap.add_argument("--only", choices=["fused", "recurrent", "separate", "copy", "verify", "delta", "sweep",
-                                       "linear", "heads4"], default=None,
+                                       "linear", "heads4", "context"], default=None,
                     help="run one leg only (for profiling)")
     args = ap.parse_args()
 
@@ -500,6 +573,8 @@ def main():
         result["linear_B64"] = linear_leg(kb, synth, torch, dev, args)
     if not args.no_extras and args.only in (None, "heads4"):
         result["head_share_H4"] = head_share_leg(kb, synth, torch, dev, args)
+    if not args.no_extras and args.only in (None, "context"):
+        result["context_sweep"] = context_leg(kb, synth, torch, dev, args)
 
     if args.only not in (None, "fused"):
         print(json.dumps(result))
@@ -538,7 +613,7 @@ def main():
         "cpu_baseline": cpu,
     }
     for key in ("per_occupancy_ms", "m0_recurrent", "separate_flush", "copy_ceiling_gbps", "verify",
-                "delta_mixed", "m_sweep", "linear_B64", "head_share_H4"):
+                "delta_mixed", "m_sweep", "linear_B64", "head_share_H4", "context_sweep"):
         if key in result:
             line[key] = result[key]
     print(json.dumps(line))

@@ -66,18 +66,8 @@ __host__ __device__ inline ChunkLds chunk_lds(int rule, int DK, int DV, int NQ, 
     return L;
 }
 
-// Waves per SIMD the register allocation must allow.  The one-token bf16
-// decode of the linear and gated rules fits 96 VGPRs without spilling, which
-// lets five 4-wave workgroups share a CU instead of four; the other variants
-// keep the compiler's choice (forcing them spills).
-template <int RULE, int NQ, typename IO>
-constexpr int chunk_waves_per_eu() {
-    return (RULE != KVBUF_RULE_DELTA && NQ == 1 && sizeof(IO) == 2) ? 5 : 1;
-}
-
 template <int RULE, int DK, int DV, int NQ, typename IO>
-__global__ __launch_bounds__((Geo<DK, DV>::NT)) __attribute__((amdgpu_waves_per_eu(chunk_waves_per_eu<RULE, NQ, IO>())))
-void chunk_kernel(TileParams P) {
+__global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) {
     using G = Geo<DK, DV>;
     constexpr int NT = G::NT, TPR = G::TPR, RG = G::RG, RPT = G::RPT;
     constexpr int E = DK / 16, EV = DV / 16;
