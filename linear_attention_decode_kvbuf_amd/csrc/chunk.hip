@@ -59,7 +59,7 @@ __host__ __device__ inline ChunkLds chunk_lds(int rule, int DK, int DV, int NQ, 
     L.kr = o; o += round4(NG * DK * io / 4);            // keys of one pass of positions (raw)
     L.vr = o; o += round4(NG * DV * xo / 4);            // their values (raw)
     L.fw = o; o += fold ? round4(m) : 0;                // fold weights
-    L.red = o; o += RG * DV * (delta ? 2 : 1);          // row-group partial sums
+    L.red = o; o += RG * DV * (delta ? 2 : NQ);         // row-group partial sums
     L.sq = o; o += delta ? NQ * DV : 0;                 // reduced outputs before the new tokens
     L.sk = o; o += delta ? NQ * DV : 0;                 // reduced e^{b_t} S0^T k_t + buffer part
     L.total = o;
@@ -291,52 +291,72 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
     float* red = lds + L.red;
     float* outp = P.out + in_row * DV;
     const size_t out_stride = static_cast<size_t>(P.H) * DV;
+    if constexpr (!DELTA) {
+        // every query's row-group partials at once, then one reduction
 #pragma unroll
-    for (int d = 0; d < NQ; ++d) {
-        if (d < n) {
-            f4 a = acc[d];
-            f4 ak = DELTA ? acck[d] : f4{0.f, 0.f, 0.f, 0.f};
-            if (has_state) {
-                f4 sa = f4{0.f, 0.f, 0.f, 0.f};
-                f4 sk = f4{0.f, 0.f, 0.f, 0.f};
-                {
+        for (int d = 0; d < NQ; ++d) {
+            if (d < n) {
+                f4 a = acc[d];
+                if (has_state) {
                     RawChunk<IO, RPT> qrow;
                     float qf[RPT];
                     qrow.load(qr + d * DK + rg * RPT);
                     qrow.to_float(qf);
+                    f4 sa = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int j = 0; j < RPT; ++j) sa += s[j] * qf[j];
+                    a += sa * (P.scale * es[d]);
                 }
-                if constexpr (DELTA) {
-                    RawChunk<IO, RPT> krow;
-                    float kf[RPT];
+                *reinterpret_cast<f4*>(red + (d * RG + rg) * DV + c0) = a;
+            }
+        }
+        __syncthreads();
+        for (int idx = tid; idx < n * DV; idx += NT) {
+            const int d = idx / DV;
+            const int c = idx - d * DV;
+            float sum = 0.f;
+#pragma unroll
+            for (int g2 = 0; g2 < RG; ++g2) sum += red[(d * RG + g2) * DV + c];
+            outp[d * out_stride + c] = sum;
+        }
+    } else {
+#pragma unroll
+        for (int d = 0; d < NQ; ++d) {
+            if (d < n) {
+                f4 a = acc[d];
+                f4 ak = acck[d];
+                if (has_state) {
+                    f4 sa = f4{0.f, 0.f, 0.f, 0.f};
+                    f4 sk = f4{0.f, 0.f, 0.f, 0.f};
+                    RawChunk<IO, RPT> qrow, krow;
+                    float qf[RPT], kf[RPT];
+                    qrow.load(qr + d * DK + rg * RPT);
+                    qrow.to_float(qf);
                     krow.load(kdr + d * DK + rg * RPT);
                     krow.to_float(kf);
 #pragma unroll
-                    for (int j = 0; j < RPT; ++j) sk += s[j] * kf[j];
+                    for (int j = 0; j < RPT; ++j) {
+                        sa += s[j] * qf[j];
+                        sk += s[j] * kf[j];
+                    }
+                    a += sa * (P.scale * es[d]);
+                    ak += sk * es[d];
                 }
-                a += sa * (P.scale * es[d]);
-                if constexpr (DELTA) ak += sk * es[d];
-            }
-            *reinterpret_cast<f4*>(red + rg * DV + c0) = a;
-            if constexpr (DELTA) *reinterpret_cast<f4*>(red + (RG + rg) * DV + c0) = ak;
-            __syncthreads();
-            for (int c = tid; c < DV; c += NT) {
-                float sum = 0.f, sumk = 0.f;
+                *reinterpret_cast<f4*>(red + rg * DV + c0) = a;
+                *reinterpret_cast<f4*>(red + (RG + rg) * DV + c0) = ak;
+                __syncthreads();
+                for (int c = tid; c < DV; c += NT) {
+                    float sum = 0.f, sumk = 0.f;
 #pragma unroll
-                for (int g2 = 0; g2 < RG; ++g2) {
-                    sum += red[g2 * DV + c];
-                    if constexpr (DELTA) sumk += red[(RG + g2) * DV + c];
-                }
-                if constexpr (DELTA) {
+                    for (int g2 = 0; g2 < RG; ++g2) {
+                        sum += red[g2 * DV + c];
+                        sumk += red[(RG + g2) * DV + c];
+                    }
                     lds[L.sq + d * DV + c] = sum;
                     lds[L.sk + d * DV + c] = sumk;
-                } else {
-                    outp[d * out_stride + c] = sum;
                 }
+                __syncthreads();  // `red` is reused by the next query; step 6 reads sq / sk
             }
-            // `red` is reused by the next query; the delta rule reads sq / sk
-            if (DELTA || d + 1 < NQ) __syncthreads();
         }
     }
 
