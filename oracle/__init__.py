@@ -26,7 +26,7 @@ Readings of points the pages leave open (the pages give no equation, no layout
 and no API) are the plainest ones and are listed in the design doc of the repository.
 
 Functions whose results have a pin (a test that checks them against closed
-forms, exact rational arithmetic or invariants): ``recurrent`` for all three
+forms, exact rational arithmetic or invariants): ``recurrent`` for all four
 rules, ``BufferModel`` (conservation, rotation, occupancy range).  Nothing here
 is "parity unpinned".
 """
@@ -48,6 +48,7 @@ _lib = None
 RULE_LINEAR = 0  # S_t = S_{t-1} + k v^T
 RULE_GATED = 1  # S_t = exp(g) S_{t-1} + k v^T
 RULE_DELTA = 2  # S_t = exp(g) (I - beta k k^T) S_{t-1} + beta k v^T
+RULE_CHANNEL = 3  # S_t = diag(exp(g)) S_{t-1} + k v^T, g over the d_k key channels
 
 
 def build(force: bool = True) -> str:
@@ -101,7 +102,8 @@ def recurrent(rule, S0, q, k, v, g=None, beta=None, scale=1.0, nthreads=1):
       S0   [ntiles, dk, dv]    state before the first token (not modified)
       q, k [nsteps, ntiles, dk]
       v    [nsteps, ntiles, dv]
-      g    [nsteps, ntiles]    log-gate, gamma = exp(g) (rules 1 and 2)
+      g    [nsteps, ntiles]    log-gate, gamma = exp(g) (rules 1 and 2);
+           [nsteps, ntiles, dk] one log-gate per key channel (rule 3)
       beta [nsteps, ntiles]    delta-rule step size (rule 2)
     Returns (out [nsteps, ntiles, dv], S [ntiles, dk, dv]): every token's output
     o_t = S_t^T (scale q_t) and the state after the last token, both fp64.
@@ -115,7 +117,10 @@ def recurrent(rule, S0, q, k, v, g=None, beta=None, scale=1.0, nthreads=1):
     q = _f64(q, (nsteps, ntiles, dk))
     k = _f64(k, (nsteps, ntiles, dk))
     v = _f64(v, (nsteps, ntiles, dv))
-    g = _f64(g, (nsteps, ntiles)) if rule >= 1 else None
+    if rule == 3:
+        g = _f64(g, (nsteps, ntiles, dk))
+    else:
+        g = _f64(g, (nsteps, ntiles)) if rule >= 1 else None
     beta = _f64(beta, (nsteps, ntiles)) if rule == 2 else None
     out = np.zeros((nsteps, ntiles, dv), dtype=np.float64)
     rc = _load().oracle_recurrent(int(rule), ntiles, nsteps, dk, dv, float(scale), _ptr(S),

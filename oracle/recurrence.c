@@ -18,6 +18,13 @@
  *   rule 1, scalar-gated:              S_t = exp(g_t) S_{t-1} + k_t v_t^T
  *   rule 2, gated delta rule:          S_t = exp(g_t) (I - beta_t k_t k_t^T) S_{t-1}
  *                                            + beta_t k_t v_t^T
+ *   rule 3, per-channel gate:          S_t = diag(exp(g_t)) S_{t-1} + k_t v_t^T,
+ *                                      g_t a vector over the d_k key channels
+ *
+ * Rule 3 is the diagonal decay of the gated linear attention and matrix-state
+ * RNN families the same page lists among its references ([20] gated linear
+ * attention, [13] RWKV with matrix-valued states): row r of the state (key
+ * channel r) decays by exp(g_t[r]).
  *
  * and the output of token t is o_t = S_t^T (scale * q_t): the state after the
  * token's own update is the one that is read (the current token attends to
@@ -33,6 +40,7 @@
  *   q, k  [nsteps][ntiles][dk]
  *   v     [nsteps][ntiles][dv]
  *   g, beta [nsteps][ntiles]     (g may be NULL for rule 0; beta only for rule 2)
+ *   g       [nsteps][ntiles][dk] for rule 3
  *   out   [nsteps][ntiles][dv]
  */
 #include <math.h>
@@ -53,7 +61,7 @@ static void oracle_one_tile(int rule, long tile, long ntiles, int nsteps, int dk
         const double* vt = v + ((size_t)t * ntiles + tile) * dv;
         double* ot = out + ((size_t)t * ntiles + tile) * dv;
         double gamma = 1.0;
-        if (rule >= 1) gamma = exp(g[(size_t)t * ntiles + tile]);
+        if (rule == 1 || rule == 2) gamma = exp(g[(size_t)t * ntiles + tile]);
 
         if (rule == 2) {
             double b = beta[(size_t)t * ntiles + tile];
@@ -67,6 +75,16 @@ static void oracle_one_tile(int rule, long tile, long ntiles, int nsteps, int dk
                     double* s = &S[(size_t)r * dv + c];
                     *s = gamma * (*s - b * kt[r] * work[c]) + b * kt[r] * vt[c];
                 }
+        } else if (rule == 3) {
+            /* S = diag(exp(g_t)) S + k v^T: row r decays with its own gate */
+            const double* gt = g + ((size_t)t * ntiles + tile) * dk;
+            for (int r = 0; r < dk; ++r) {
+                const double gr = exp(gt[r]);
+                for (int c = 0; c < dv; ++c) {
+                    double* s = &S[(size_t)r * dv + c];
+                    *s = gr * *s + kt[r] * vt[c];
+                }
+            }
         } else {
             /* S = gamma S + k v^T   (gamma = 1 for rule 0) */
             for (int r = 0; r < dk; ++r)
@@ -92,7 +110,7 @@ int oracle_recurrent(int rule, long ntiles, int nsteps, int dk, int dv, double s
                      double* S, const double* q, const double* k, const double* v,
                      const double* g, const double* beta, double* out, int nthreads)
 {
-    if (rule < 0 || rule > 2 || ntiles < 0 || nsteps < 0 || dk <= 0 || dv <= 0) return -1;
+    if (rule < 0 || rule > 3 || ntiles < 0 || nsteps < 0 || dk <= 0 || dv <= 0) return -1;
     if (!S || !q || !k || !v || !out) return -1;
     if (rule >= 1 && !g) return -1;
     if (rule == 2 && !beta) return -1;

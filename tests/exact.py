@@ -20,6 +20,9 @@ W(t, i) = gamma_{i+1} ... gamma_t (the product over the tokens after i, up to t)
 
 where x_i = v_i for rules 0 and 1 and, for the delta rule,
   x_t = u_t = beta_t (v_t - W(t, -1) S_0^T k_t - sum_{i<t} W(t, i) (k_i . k_t) u_i).
+For rule 3 (one decay per key channel) gamma_s and W(t, i) are vectors over
+the d_k channels and act on the rows: W(t, -1) S_0 scales row r by W(t, -1)[r],
+and W(t, i) (q_t . k_i) becomes sum_r q_t[r] W(t, i)[r] k_i[r].
 
 Both are pure Python and only meant for d <= 4 and a few dozen tokens.
 """
@@ -42,7 +45,8 @@ def dot(a, b):
 
 def exact_recurrent(rule, S0, q, k, v, gam, beta, scale=F(1)):
     """Token-by-token recurrence.  q/k/v are lists of vectors, gam/beta lists of
-    scalars (gam = 1 and beta unused for rule 0).  Returns (outputs, states)."""
+    scalars (gam = 1 and beta unused for rule 0; for rule 3 gam[t] is a vector
+    over the key channels).  Returns (outputs, states)."""
     S = [row[:] for row in S0]
     dk, dv = len(S), len(S[0])
     outs, states = [], []
@@ -53,6 +57,8 @@ def exact_recurrent(rule, S0, q, k, v, gam, beta, scale=F(1)):
             P = [[(F(1) if r == s else F(0)) - b * k[t][r] * k[t][s] for s in range(dk)] for r in range(dk)]
             PS = [[sum((P[r][s] * S[s][c] for s in range(dk)), F(0)) for c in range(dv)] for r in range(dk)]
             S = [[g * PS[r][c] + b * k[t][r] * v[t][c] for c in range(dv)] for r in range(dk)]
+        elif rule == 3:
+            S = [[g[r] * S[r][c] + k[t][r] * v[t][c] for c in range(dv)] for r in range(dk)]
         else:
             S = [[g * S[r][c] + k[t][r] * v[t][c] for c in range(dv)] for r in range(dk)]
         outs.append(matT_vec(S, [scale * x for x in q[t]]))
@@ -70,8 +76,17 @@ class ExactKVBuffer:
 
     def _weights(self, gammas):
         """W(t, i) for the token list: decay[i] = product of gammas after i up to the
-        last token; decay_s = product of all of them (the weight of S_0)."""
+        last token; decay_s = product of all of them (the weight of S_0).  For
+        rule 3 every gamma and every weight is a vector over the key channels."""
         n = len(gammas)
+        if self.rule == 3:
+            dk = len(self.S)
+            after = [[F(1)] * dk for _ in range(n)]
+            acc = [F(1)] * dk
+            for i in range(n - 1, -1, -1):
+                after[i] = acc[:]
+                acc = [a * g for a, g in zip(acc, gammas[i])]
+            return after, acc
         after = [F(1)] * n
         acc = F(1)
         for i in range(n - 1, -1, -1):
@@ -96,6 +111,12 @@ class ExactKVBuffer:
         gammas = [p[2] for p in toks]
         after, w0 = self._weights(gammas)
         qs = [self.scale * x for x in qt]
+        if self.rule == 3:
+            o = matT_vec(self.S, [w * x for w, x in zip(w0, qs)])
+            for i, (ki, xi, _) in enumerate(toks):
+                s = sum((a * x * y for a, x, y in zip(after[i], qs, ki)), F(0))
+                o = [o[c] + s * xi[c] for c in range(len(o))]
+            return o
         o = [w0 * x for x in matT_vec(self.S, qs)]
         for i, (ki, xi, _) in enumerate(toks):
             s = after[i] * dot(qs, ki)
@@ -105,6 +126,13 @@ class ExactKVBuffer:
     def effective_state(self):
         gammas = [p[2] for p in self.buf]
         after, w0 = self._weights(gammas)
+        if self.rule == 3:
+            S = [[w0[r] * x for x in row] for r, row in enumerate(self.S)]
+            for i, (ki, xi, _) in enumerate(self.buf):
+                for r in range(len(S)):
+                    for c in range(len(S[0])):
+                        S[r][c] += after[i][r] * ki[r] * xi[c]
+            return S
         S = [[w0 * x for x in row] for row in self.S]
         for i, (ki, xi, _) in enumerate(self.buf):
             for r in range(len(S)):

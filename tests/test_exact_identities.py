@@ -28,12 +28,15 @@ def _seq(seed, T, dk, dv, rule, zero_state=False):
     q = [[fr(-3, 3, 2) for _ in range(dk)] for _ in range(T)]
     k = [[fr(-3, 3, 4) for _ in range(dk)] for _ in range(T)]
     v = [[fr(-3, 3, 2) for _ in range(dv)] for _ in range(T)]
-    gam = [fr(5, 8, 8) if rule >= 1 else F(1) for _ in range(T)]
+    if rule == 3:  # one decay per key channel
+        gam = [[fr(4, 8, 8) for _ in range(dk)] for _ in range(T)]
+    else:
+        gam = [fr(5, 8, 8) if rule >= 1 else F(1) for _ in range(T)]
     beta = [fr(0, 4, 4) if rule == 2 else F(0) for _ in range(T)]
     return S0, q, k, v, gam, beta
 
 
-@pytest.mark.parametrize("rule", [0, 1, 2])
+@pytest.mark.parametrize("rule", [0, 1, 2, 3])
 @pytest.mark.parametrize("m", [1, 2, 3, 4])
 def test_buffered_decode_equals_recurrent(rule, m):
     T, dk, dv = 12, 3, 2
@@ -48,7 +51,7 @@ def test_buffered_decode_equals_recurrent(rule, m):
             assert ex.buf == [] and ex.S == ref_S[t]  # folded state written back exactly
 
 
-@pytest.mark.parametrize("rule", [0, 1, 2])
+@pytest.mark.parametrize("rule", [0, 1, 2, 3])
 @pytest.mark.parametrize("n", [1, 2, 4])
 def test_verify_then_commit_equals_serial_prefix(rule, n):
     m, pre, dk, dv = 4, 3, 2, 3
@@ -84,7 +87,7 @@ def test_commit_nothing_is_a_no_op():
     assert (ex.S, ex.buf) == before
 
 
-@pytest.mark.parametrize("rule", [0, 1, 2])
+@pytest.mark.parametrize("rule", [0, 1, 2, 3])
 def test_direct_equals_recurrence_from_zero(rule):
     """Buffer-only attention with no state at all (S = 0, never folded) equals
     the recurrence started from a zero state."""

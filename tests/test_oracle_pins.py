@@ -73,6 +73,51 @@ def test_gated_parallel_form():
         _close(S[j], np.exp(b[-1]) * S0[j] + K.T @ (np.exp(b[-1] - b)[:, None] * V))
 
 
+def test_channel_gate_parallel_form():
+    """One log-gate per key channel: with B = cumsum(g) over the tokens (a
+    vector per token), O[t] = (e^{B_t} * q_t) S0 + sum_{i<=t} (q_t * e^{B_t - B_i}) . k_i  v_i
+    and S_T = diag(e^{B_T}) S0 + sum_i (e^{B_T - B_i} * k_i) v_i^T (the decayed
+    parallel form of gated linear attention, reference [20] of the page).
+    d_k != d_v, so decaying columns instead of rows fails."""
+    T, ntiles, dk, dv = 8, 2, 4, 3
+    S0 = _rand(50, ntiles, dk, dv)
+    q, k, v = _rand(51, T, ntiles, dk), _unit_rows(_rand(52, T, ntiles, dk)), _rand(53, T, ntiles, dv)
+    g = np.random.default_rng(54).uniform(-0.4, 0.0, size=(T, ntiles, dk))
+    out, S = oracle.recurrent(3, S0, q, k, v, g=g, scale=0.5)
+    for j in range(ntiles):
+        Q, K, V = 0.5 * q[:, j], k[:, j], v[:, j]
+        B = np.cumsum(g[:, j], axis=0)  # [T, dk]
+        W = np.exp(B[:, None, :] - B[None, :, :])  # [t, i, dk]
+        A = np.einsum("tr,tir,ir->ti", Q, W, K) * np.tri(T)
+        _close(out[:, j], (np.exp(B) * Q) @ S0[j] + A @ V)
+        _close(S[j], np.exp(B[-1])[:, None] * S0[j] + (np.exp(B[-1] - B) * K).T @ V)
+
+
+def test_channel_gate_equal_channels_is_scalar_gate():
+    T, ntiles, dk, dv = 6, 3, 3, 5
+    S0 = _rand(55, ntiles, dk, dv)
+    q, k, v = _rand(56, T, ntiles, dk), _rand(57, T, ntiles, dk), _rand(58, T, ntiles, dv)
+    g = np.random.default_rng(59).uniform(-0.3, 0.0, size=(T, ntiles))
+    o1, S1 = oracle.recurrent(1, S0, q, k, v, g=g)
+    o3, S3 = oracle.recurrent(3, S0, q, k, v, g=np.repeat(g[:, :, None], dk, axis=2))
+    _close(o3, o1, 1e-14)
+    _close(S3, S1, 1e-14)
+
+
+def test_channel_gate_closes_one_channel():
+    """A very negative gate on channel r wipes row r of the state each step:
+    after any token, row r is exactly k_t[r] v_t, and the other rows are
+    untouched by that channel's gate."""
+    T, ntiles, dk, dv = 4, 1, 3, 2
+    S0 = _rand(60, ntiles, dk, dv)
+    q, k, v = _rand(61, T, ntiles, dk), _rand(62, T, ntiles, dk), _rand(63, T, ntiles, dv)
+    g = np.zeros((T, ntiles, dk))
+    g[:, :, 1] = -800.0  # exp underflows to 0
+    _, S = oracle.recurrent(3, S0, q, k, v, g=g)
+    _close(S[0, 1], k[-1, 0, 1] * v[-1, 0], 1e-15)
+    _close(S[0, [0, 2]], S0[0, [0, 2]] + k[:, 0, [0, 2]].T @ v[:, 0])
+
+
 def test_gate_zero_is_ungated():
     T, ntiles, dk, dv = 6, 2, 3, 4
     S0 = _rand(10, ntiles, dk, dv)
@@ -157,12 +202,22 @@ def _exact_inputs(seed, T, dk, dv, rule):
     q = rs.integers(-4, 5, size=(T, dk)) / 4.0
     k = rs.integers(-4, 5, size=(T, dk)) / 8.0
     v = rs.integers(-4, 5, size=(T, dv)) / 4.0
-    g = rs.uniform(-0.2, 0.0, size=T) if rule >= 1 else np.zeros(T)
+    if rule == 3:
+        g = rs.uniform(-0.2, 0.0, size=(T, dk))
+    else:
+        g = rs.uniform(-0.2, 0.0, size=T) if rule >= 1 else np.zeros(T)
     beta = rs.integers(0, 5, size=T) / 4.0 if rule == 2 else np.zeros(T)
     return S0, q, k, v, g, beta
 
 
-@pytest.mark.parametrize("rule", [0, 1, 2])
+def _gam(rule, g):
+    """exp(g) as exact Fractions: a scalar, or a vector for rule 3."""
+    if rule == 3:
+        return [F(math.exp(x)) for x in g]
+    return F(math.exp(g)) if rule >= 1 else F(1)
+
+
+@pytest.mark.parametrize("rule", [0, 1, 2, 3])
 @pytest.mark.parametrize("m", [1, 3, 4])
 def test_oracle_equals_exact_buffered_form(rule, m):
     """Exact (Fraction) buffered evaluation -- fold every m tokens, outputs from
@@ -177,12 +232,12 @@ def test_oracle_equals_exact_buffered_form(rule, m):
     ex = ExactKVBuffer(rule, [[F(x) for x in row] for row in S0], m, scale=F(1, 2))
     for t in range(T):
         o = ex.decode([F(x) for x in q[t]], [F(x) for x in k[t]], [F(x) for x in v[t]],
-                      F(math.exp(g[t])) if rule >= 1 else F(1), F(beta[t]))
+                      _gam(rule, g[t]), F(beta[t]))
         _close(out[t, 0], [float(x) for x in o])
     _close(S[0], [[float(x) for x in row] for row in ex.effective_state()])
 
 
-@pytest.mark.parametrize("rule", [0, 1, 2])
+@pytest.mark.parametrize("rule", [0, 1, 2, 3])
 def test_oracle_serial_decode_equals_exact_parallel_verify(rule):
     """Drafts verified in parallel from the buffer (exact) equal the oracle's
     serial decode of the drafts from the current state."""
@@ -193,10 +248,10 @@ def test_oracle_serial_decode_equals_exact_parallel_verify(rule):
     Fr = lambda a: [F(x) for x in a]
     ex = ExactKVBuffer(rule, [Fr(row) for row in S0], m=8)
     for t in range(T):
-        ex.decode(Fr(q[t]), Fr(k[t]), Fr(v[t]), F(math.exp(g[t])) if rule else F(1), F(beta[t]))
+        ex.decode(Fr(q[t]), Fr(k[t]), Fr(v[t]), _gam(rule, g[t]), F(beta[t]))
     outs = ex.verify([Fr(q[t]) for t in range(T, T + n)], [Fr(k[t]) for t in range(T, T + n)],
                      [Fr(v[t]) for t in range(T, T + n)],
-                     [F(math.exp(g[t])) if rule else F(1) for t in range(T, T + n)],
+                     [_gam(rule, g[t]) for t in range(T, T + n)],
                      [F(beta[t]) for t in range(T, T + n)])
     out, _ = oracle.recurrent(rule, S0[None], q[:, None], k[:, None], v[:, None],
                               g=g[:, None], beta=beta[:, None])
