@@ -33,33 +33,39 @@ PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, published
 
 
 # Algorithmic bytes per (request, head) tile: 2-byte q/k/v, 4-byte state,
-# gates and outputs; `gated` = the scalar-gated rule (the linear rule has no
-# gates).
-def decode_bytes(j, dk, dv, io=2, gated=True):
+# gates and outputs; `gated` = a gate per token (4 bytes; the linear rule has
+# none); `gate` overrides the bytes of one token's gates (4 d_k for the
+# per-channel rule).
+def _gate(gated, gate):
+    return gate if gate is not None else (4 if gated else 0)
+
+
+def decode_bytes(j, dk, dv, io=2, gated=True, gate=None):
     return (4 * dk * dv                        # state tile read
             + io * (2 * dk + dv)               # q, k, v of the new token
             + io * (dk + dv)                   # append of k, v to the pool
             + io * j * (dk + dv)               # buffered keys and values
             + 4 * dv                           # output
-            + (4 * (j + 2) if gated else 0))   # gates: buffered, new, appended
+            + _gate(gated, gate) * (j + 2))    # gates: buffered, new, appended
 
 
-def flush_bytes(m, dk, dv, io=2, gated=True):
-    return 8 * dk * dv + m * (io * (dk + dv) + (4 if gated else 0))
+def flush_bytes(m, dk, dv, io=2, gated=True, gate=None):
+    return 8 * dk * dv + m * (io * (dk + dv) + _gate(gated, gate))
 
 
-def recurrent_bytes(dk, dv, io=2, gated=True):
-    return 8 * dk * dv + io * (2 * dk + dv) + 4 * dv + (4 if gated else 0)
+def recurrent_bytes(dk, dv, io=2, gated=True, gate=None):
+    return 8 * dk * dv + io * (2 * dk + dv) + 4 * dv + _gate(gated, gate)
 
 
-def cycle_bytes_fused(m, dk, dv, io=2, gated=True):
+def cycle_bytes_fused(m, dk, dv, io=2, gated=True, gate=None):
     """Decodes at occupancy 0 .. m-1 plus one state write (the fold reads the
     state and the buffered tokens the last decode already reads)."""
-    return sum(decode_bytes(j, dk, dv, io, gated) for j in range(m)) + 4 * dk * dv
+    return sum(decode_bytes(j, dk, dv, io, gated, gate) for j in range(m)) + 4 * dk * dv
 
 
-def cycle_bytes_separate(m, dk, dv, io=2, gated=True):
-    return sum(decode_bytes(j, dk, dv, io, gated) for j in range(m)) + flush_bytes(m, dk, dv, io, gated)
+def cycle_bytes_separate(m, dk, dv, io=2, gated=True, gate=None):
+    return (sum(decode_bytes(j, dk, dv, io, gated, gate) for j in range(m))
+            + flush_bytes(m, dk, dv, io, gated, gate))
 
 
 def _traffic_file(m):
@@ -187,6 +193,7 @@ def cycle_leg(kb, synth, torch, dev, w, cycles, warmup):
     Returns tokens/s, time per cycle, algorithmic HBM GB/s and bytes per
     token (all H tiles of a request)."""
     gated = w.rule != 0
+    gate = 4 * w.dk if w.rule == 3 else None  # per-channel rule: d_k gates per token
     m = max(w.m, 1)
     kv = build_kv(kb, synth, torch, w, kb.FLUSH_EAGER, dev)
     ring = make_ring(synth, w, dev, 2 * m)
@@ -202,8 +209,8 @@ def cycle_leg(kb, synth, torch, dev, w, cycles, warmup):
     assert int(kv.error.item()) == 0
     del kv
     tiles = w.B * w.H
-    per_tile = (cycle_bytes_fused(w.m, w.dk, w.dv, gated=gated) if w.m > 0
-                else recurrent_bytes(w.dk, w.dv, gated=gated))
+    per_tile = (cycle_bytes_fused(w.m, w.dk, w.dv, gated=gated, gate=gate) if w.m > 0
+                else recurrent_bytes(w.dk, w.dv, gated=gated, gate=gate))
     cyc_s = wall / cycles
     return {"m": w.m, "tokens_per_s": w.B * m / cyc_s, "ms_per_cycle": cyc_s * 1e3,
             "hbm_gbps": per_tile * tiles / cyc_s / 1e9,
@@ -230,6 +237,15 @@ def linear_leg(kb, synth, torch, dev, args):
     w = synth.workload(2)
     buf = cycle_leg(kb, synth, torch, dev, w, args.steps, args.warmup)
     rec = cycle_leg(kb, synth, torch, dev, synth.workload(2, m=0, blocks_per_req=1), args.steps, args.warmup)
+    return {"m8": buf, "m0": rec, "speedup_vs_m0": buf["tokens_per_s"] / rec["tokens_per_s"]}
+
+
+def channel_leg(kb, synth, torch, dev, args):
+    """Per-channel gates (one log-gate per key channel) at the metric shape:
+    buffered m = 8 against the recurrent m = 0 kernel of the same rule."""
+    buf = cycle_leg(kb, synth, torch, dev, synth.workload(3, rule=3), args.steps, args.warmup)
+    rec = cycle_leg(kb, synth, torch, dev, synth.workload(3, rule=3, m=0, blocks_per_req=1),
+                    args.steps, args.warmup)
     return {"m8": buf, "m0": rec, "speedup_vs_m0": buf["tokens_per_s"] / rec["tokens_per_s"]}
 
 
@@ -441,7 +457,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing on the host")
     ap.add_argument("--no-extras", action="store_true", help="skip the m=0 / separate-flush / copy legs")
     ap.add_argument("--only", choices=["fused", "recurrent", "separate", "copy", "verify", "delta", "sweep",
-                                       "linear", "heads4", "context"], default=None,
+                                       "linear", "heads4", "context", "channel"], default=None,
                     help="run one leg only (for profiling)")
     args = ap.parse_args()
 
@@ -575,6 +591,8 @@ def main():
         result["head_share_H4"] = head_share_leg(kb, synth, torch, dev, args)
     if not args.no_extras and args.only in (None, "context"):
         result["context_sweep"] = context_leg(kb, synth, torch, dev, args)
+    if not args.no_extras and args.only in (None, "channel"):
+        result["channel_gates"] = channel_leg(kb, synth, torch, dev, args)
 
     if args.only not in (None, "fused"):
         print(json.dumps(result))
@@ -613,7 +631,7 @@ def main():
         "cpu_baseline": cpu,
     }
     for key in ("per_occupancy_ms", "m0_recurrent", "separate_flush", "copy_ceiling_gbps", "verify",
-                "delta_mixed", "m_sweep", "linear_B64", "head_share_H4", "context_sweep"):
+                "delta_mixed", "m_sweep", "linear_B64", "head_share_H4", "context_sweep", "channel_gates"):
         if key in result:
             line[key] = result[key]
     print(json.dumps(line))

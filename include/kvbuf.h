@@ -17,6 +17,9 @@
  *   KVBUF_RULE_LINEAR  S <- S + k v^T
  *   KVBUF_RULE_GATED   S <- exp(g) S + k v^T
  *   KVBUF_RULE_DELTA   S <- exp(g) (I - beta k k^T) S + beta k v^T
+ *   KVBUF_RULE_CHANNEL S <- diag(exp(g)) S + k v^T, one log-gate per key channel
+ *                      (the diagonal decay of the gated linear attention and
+ *                      matrix-state RNN works in the page's reference list)
  * and the token's output is o = S^T (scale q), read after the token's own update.
  *
  * Everything is asynchronous on the caller's HIP stream.  The library
@@ -54,7 +57,12 @@ typedef enum kvbuf_status {
 typedef enum kvbuf_rule {
     KVBUF_RULE_LINEAR = 0,
     KVBUF_RULE_GATED = 1,
-    KVBUF_RULE_DELTA = 2
+    KVBUF_RULE_DELTA = 2,
+    /* One log-gate per key channel.  Served by decode, direct, flush, commit,
+     * materialize, one-draft verify and the recurrent (m = 0) entry points for
+     * table rows of at most 64 positions; kvbuf_verify with n > 1 and longer
+     * rows return KVBUF_EUNSUPPORTED. */
+    KVBUF_RULE_CHANNEL = 3
 } kvbuf_rule;
 
 typedef enum kvbuf_dtype {
@@ -99,7 +107,8 @@ typedef struct kvbuf_layout {
  *   value [num_blocks][H][block_size][d_v] io_dtype for the linear and gated rules;
  *         fp32 for the delta rule, where it holds each token's pseudo-value
  *         u = beta (v - exp(g) S_prev^T k), so that S = exp(g) S_prev + k u^T
- *   gate  [num_blocks][H][block_size]      fp32 log-gates (NULL for the linear rule)
+ *   gate  [num_blocks][H][block_size]      fp32 log-gates (NULL for the linear rule);
+ *         [num_blocks][H][block_size][d_k] for the per-channel rule
  * In recurrent mode (m = 0) only `state` is used. */
 typedef struct kvbuf_pools {
     float* state;
@@ -141,8 +150,8 @@ typedef struct kvbuf_batch {
  * Figure 3 caption: the buffer size m = 0 case is the recurrent form.)
  *
  * Inputs  q, k [B][H][d_k] and v [B][H][d_v] in io_dtype; g [B][H] fp32
- *         log-gates (rules GATED, DELTA; else NULL); beta [B][H] fp32 (DELTA;
- *         else NULL).
+ *         log-gates (rules GATED, DELTA; [B][H][d_k] for CHANNEL; NULL for
+ *         LINEAR); beta [B][H] fp32 (DELTA; else NULL).
  * Output  out [B][H][d_v] fp32, o = S_t^T (scale q) with S_t the state after
  *         this token.
  * m > 0:  appends the token at buffer position occupancy[b][h] and advances
@@ -171,7 +180,8 @@ kvbuf_status kvbuf_flush(const kvbuf_layout* layout, const kvbuf_pools* pools,
  * kvbuf_verify -- parallel verification of n draft tokens per request
  * (Figure 2 caption: the drafts' keys and values are buffered and verified
  * together, without a temporary state per draft).
- * Inputs  q, k [B][n][H][d_k], v [B][n][H][d_v] (io_dtype); g, beta [B][n][H].
+ * Inputs  q, k [B][n][H][d_k], v [B][n][H][d_v] (io_dtype); g, beta [B][n][H]
+ *         (g [B][n][H][d_k] for the per-channel rule).
  * Output  out [B][n][H][d_v] fp32: draft d attends to the state, the buffer and
  *         drafts 0..d (causal within the drafts).
  * The drafts are written at buffer positions occupancy .. occupancy+n-1; the

@@ -19,7 +19,7 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkvbuf.so")
 
-RULE_LINEAR, RULE_GATED, RULE_DELTA = 0, 1, 2
+RULE_LINEAR, RULE_GATED, RULE_DELTA, RULE_CHANNEL = 0, 1, 2, 3
 BF16, F32 = 0, 1
 FLUSH_EAGER, FLUSH_DEFERRED = 0, 1
 
@@ -183,7 +183,8 @@ class KVBuffer:
     state      [num_state_slots, H, d_k, d_v] fp32
     key        [num_blocks, H, block_size, d_k] io dtype
     value      [num_blocks, H, block_size, d_v] io dtype (fp32 for the delta rule)
-    gate       [num_blocks, H, block_size] fp32 (None for the linear rule)
+    gate       [num_blocks, H, block_size] fp32 (None for the linear rule;
+               [num_blocks, H, block_size, d_k] for the per-channel rule)
     state_slot [B] int32
     block_table [B, H, blocks_per_req] int32, occupancy [B, H] int32 (one copy
                per head, all equal; ``set_block_table`` writes every head)
@@ -212,8 +213,8 @@ class KVBuffer:
             self.key = torch.zeros((num_blocks, heads, block_size, d), dtype=io, device=dev)
             vdt = torch.float32 if rule == RULE_DELTA else io
             self.value = torch.zeros((num_blocks, heads, block_size, d), dtype=vdt, device=dev)
-            self.gate = (torch.zeros((num_blocks, heads, block_size), dtype=torch.float32, device=dev)
-                         if rule != RULE_LINEAR else None)
+            gshape = (num_blocks, heads, block_size, d) if rule == RULE_CHANNEL else (num_blocks, heads, block_size)
+            self.gate = torch.zeros(gshape, dtype=torch.float32, device=dev) if rule != RULE_LINEAR else None
         else:
             self.key = self.value = self.gate = None
         i32 = torch.int32

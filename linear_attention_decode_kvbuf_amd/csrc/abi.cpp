@@ -15,7 +15,7 @@ kvbuf_status check_layout(const kvbuf_layout* L, bool need_buffer) {
     if (!L) return KVBUF_EINVAL;
     if (L->num_heads <= 0 || L->d_k <= 0 || L->d_v <= 0 || L->m < 0) return KVBUF_EINVAL;
     if (L->num_state_slots < 0 || L->num_blocks < 0) return KVBUF_EINVAL;
-    if (L->rule < KVBUF_RULE_LINEAR || L->rule > KVBUF_RULE_DELTA) return KVBUF_EUNSUPPORTED;
+    if (L->rule < KVBUF_RULE_LINEAR || L->rule > KVBUF_RULE_CHANNEL) return KVBUF_EUNSUPPORTED;
     if (L->io_dtype != KVBUF_BF16 && L->io_dtype != KVBUF_F32) return KVBUF_EUNSUPPORTED;
     if (L->flush != KVBUF_FLUSH_EAGER && L->flush != KVBUF_FLUSH_DEFERRED) return KVBUF_EINVAL;
     if (L->d_k != L->d_v || !kvbuf::supported_dim(L->d_k)) return KVBUF_EUNSUPPORTED;
@@ -116,6 +116,10 @@ kvbuf_status chunk_call(const kvbuf_layout* layout, const kvbuf_pools* pools,
         if (n < 1 || n > kvbuf::kMaxDrafts) return KVBUF_EUNSUPPORTED;
         if (n > layout->block_size * layout->blocks_per_req) return KVBUF_ECAPACITY;
     }
+    // the per-channel rule is served by the one-token decode kernel only
+    if (layout->rule == KVBUF_RULE_CHANNEL && layout->m > 0 &&
+        !kvbuf::decode_eligible(layout->rule, n, layout->block_size * layout->blocks_per_req))
+        return KVBUF_EUNSUPPORTED;
     TileParams t = make_params(layout, pools, batch);
     t.mode = mode;
     t.n = n;

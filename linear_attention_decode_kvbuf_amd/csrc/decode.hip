@@ -8,6 +8,10 @@
 // log-gate since the last fold and t = p the new token's position:
 //   o_t = e^{b_t} S0^T (scale q_t) + sum_{i<=t} e^{b_t - b_i} scale (q_t . k_i) v_i
 //   fold (t = m - 1):  S <- e^{b_{m-1}} S0 + sum_{i<m} e^{b_{m-1} - b_i} k_i v_i^T
+// With one log-gate per key channel (B_i the per-channel cumulative gate)
+// every decay is a vector acting on the key channels:
+//   o_t = S0^T (e^{B_t} scale q_t) + sum_{i<=t} scale (sum_r q_t[r] k_i[r] e^{B_t[r] - B_i[r]}) v_i
+//   fold: row r of S0 scales by e^{B_{m-1}[r]}, k_i[r] by e^{B_{m-1}[r] - B_i[r]}.
 //
 // Serves kvbuf_decode, kvbuf_direct and a one-draft kvbuf_verify when the
 // table row covers at most 64 positions (one lane of the token wave per
@@ -34,11 +38,13 @@ namespace {
 __host__ __device__ inline int round4d(int x) { return (x + 3) & ~3; }
 
 // LDS layout in 4-byte words.  mf = positions staged for a fold in this
-// launch (0: it never folds); io = bytes per key / value element.
+// launch (0: it never folds); io = bytes per key / value element; for the
+// per-channel rule, cap rows of gates (turned into per-channel suffix sums)
+// and the cumulative gate of the new token.
 struct DecodeLds {
-    int obuf, red, fw, kr, vr, total;
+    int obuf, red, fw, kr, vr, dg, bt, total;
 };
-__host__ __device__ inline DecodeLds decode_lds(int DK, int DV, int RG, int mf, int io) {
+__host__ __device__ inline DecodeLds decode_lds(int DK, int DV, int RG, int mf, int io, bool ch, int cap) {
     DecodeLds L;
     int o = 0;
     L.obuf = o; o += DV;                        // weighted sum of buffered values (token wave)
@@ -46,8 +52,24 @@ __host__ __device__ inline DecodeLds decode_lds(int DK, int DV, int RG, int mf, 
     L.fw = o; o += round4d(mf);                 // fold weights e^{b_{m-1} - b_i}
     L.kr = o; o += round4d(mf * DK * io / 4);   // keys to fold (raw bits)
     L.vr = o; o += round4d(mf * DV * io / 4);   // values to fold (raw bits)
+    L.dg = o; o += ch ? cap * DK : 0;           // per-channel rule: B_t - B_i per position (fp32)
+    L.bt = o; o += ch ? DK : 0;                 // per-channel rule: B_t
     L.total = o;
     return L;
+}
+
+// q . k over a lane's E channels with per-channel weights e^{d[e]}.
+template <typename T, int E>
+__device__ __forceinline__ float chunk_dot_decayed(const RawChunk<T, E>& a, const RawChunk<T, E>& b,
+                                                   const float* d) {
+    float x[E], y[E], dd[E];
+    a.to_float(x);
+    b.to_float(y);
+    loadE<E>(d, dd);
+    float acc = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc += (x[e] * y[e]) * exp_gate(dd[e]);
+    return acc;
 }
 
 template <int RULE, int DK, int DV, typename IO>
@@ -56,9 +78,11 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void decode_kernel(TilePar
     constexpr int NT = G::NT, TPR = G::TPR, RG = G::RG, RPT = G::RPT;
     constexpr int E = DK / 16, EV = DV / 16;
     constexpr int NB = 4;  // rounds of 4 positions whose loads are in flight together
-    constexpr bool GATED = RULE != KVBUF_RULE_LINEAR;
+    constexpr bool CH = RULE == KVBUF_RULE_CHANNEL;   // one gate per key channel
+    constexpr bool GATED = RULE == KVBUF_RULE_GATED;  // one gate per token
+    constexpr int CPL = (DK + 63) / 64;               // key channels per token-wave lane
 
-    extern __shared__ float lds[];
+    extern __shared__ __attribute__((aligned(16))) float lds[];  // 16-byte rows for the LDS copies
     __shared__ unsigned s_bad;
     __shared__ int s_fold;
     __shared__ float s_es, s_e0;
@@ -72,7 +96,10 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void decode_kernel(TilePar
     const int c0 = (tid % TPR) * 4;
     const bool direct = P.mode == MODE_DIRECT;
     const int mf = P.fold_chunk;  // = m when this launch may fold
-    const DecodeLds L = decode_lds(DK, DV, RG, mf, static_cast<int>(sizeof(IO)));
+    const DecodeLds L = decode_lds(DK, DV, RG, mf, static_cast<int>(sizeof(IO)), CH,
+                                   P.block_size * P.blocks_per_req);
+    float* dg = lds + L.dg;
+    float* btv = lds + L.bt;
     float* obuf = lds + L.obuf;
     float* red = lds + L.red;
     float* fw = lds + L.fw;
@@ -144,6 +171,29 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void decode_kernel(TilePar
             }
         };
         issue(0);
+        if constexpr (CH) {
+            // gate rows of every position straight into LDS, then in place
+            // gate row i -> B_t - B_i (the gates after i up to t), per channel
+            const float* gin = P.g + in_row * DK;
+            lds_copy_rows<DK * 4>(reinterpret_cast<char*>(dg), Tl, [&](int i) {
+                const uint32_t pri = static_cast<uint32_t>(__shfl(static_cast<int>(prow), i & 63, 64));
+                return reinterpret_cast<const char*>(i < pc ? P.gate + static_cast<size_t>(pri) * DK : gin);
+            }, lane);
+            wait_lds_copies();
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+                const int ch = lane + 64 * c;
+                if (ch < DK) {
+                    float run = 0.0f;
+                    for (int i = Tl - 1; i >= 0; --i) {
+                        const float gi = dg[i * DK + ch];
+                        dg[i * DK + ch] = run;
+                        run += gi;
+                    }
+                    btv[ch] = run;
+                }
+            }
+        }
 
         // cumulative log-gates b_i of positions 0 .. T-1, lane i holds b_i
         float bcum = 0.0f;
@@ -165,7 +215,12 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void decode_kernel(TilePar
 #pragma unroll
             for (int r = 0; r < NB; ++r) {
                 const int i = i0 + 4 * r + gl;
-                const float dot = group16_sum(chunk_dot(qc, kc[r]));
+                float dot;
+                if constexpr (CH) {
+                    dot = group16_sum(chunk_dot_decayed(qc, kc[r], dg + (i < Tl ? i : 0) * DK + cl * E));
+                } else {
+                    dot = group16_sum(chunk_dot(qc, kc[r]));
+                }
                 const float bi_ = __shfl(bcum, i & 63, 64);
                 const float w = i < Tl ? (GATED ? exp_gate(bt - bi_) : 1.0f) * P.scale * dot : 0.0f;
                 float vf[EV];
@@ -195,7 +250,12 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void decode_kernel(TilePar
         if constexpr (GATED) {
             if (!bad && lane == pc) P.gate[prow] = P.g[in_row];
         }
-        if (fold) {
+        if constexpr (CH) {  // the new token's gate row
+            const uint32_t prow_t = static_cast<uint32_t>(__shfl(static_cast<int>(prow), pc, 64));
+            for (int ch = lane; !bad && ch < DK; ch += 64)
+                P.gate[static_cast<size_t>(prow_t) * DK + ch] = P.g[in_row * DK + ch];
+        }
+        if (fold && !CH) {
             const float bm = __shfl(bcum, P.m - 1, 64);
             if (lane < P.m) fw[lane] = GATED ? exp_gate(bm - bcum) : 1.0f;
             if (lane == 0) s_e0 = GATED ? exp_gate(bm) : 1.0f;
@@ -212,18 +272,32 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void decode_kernel(TilePar
 
     // ---- state waves: query rows, then the tile; S0^T q per row group ----------
     f4 s[RPT];
+    RawChunk<IO, RPT> qrow;
     if (!token_wave) {
-        RawChunk<IO, RPT> qrow;
         qrow.load(qin + rg * RPT);
         const bool present = slot >= 0 && slot < P.num_slots;
         load_tile<RPT, DK, DV>(s, present ? P.state + (static_cast<size_t>(slot) * P.H + h) * DK * DV : P.state,
                                present, rg, c0);
-        float qf[RPT];
-        qrow.to_float(qf);
-        f4 sa = f4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (!CH) {
+            float qf[RPT];
+            qrow.to_float(qf);
+            f4 sa = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int j = 0; j < RPT; ++j) sa += s[j] * qf[j];
-        *reinterpret_cast<f4*>(red + rg * DV + c0) = sa;
+            for (int j = 0; j < RPT; ++j) sa += s[j] * qf[j];
+            *reinterpret_cast<f4*>(red + rg * DV + c0) = sa;
+        }
+    }
+    if constexpr (CH) {
+        // S0^T (e^{B_t} q) needs the token wave's B_t: one more barrier
+        __syncthreads();
+        if (!token_wave) {
+            float qf[RPT];
+            qrow.to_float(qf);
+            f4 sa = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < RPT; ++j) sa += s[j] * (qf[j] * exp_gate(btv[rg * RPT + j]));
+            *reinterpret_cast<f4*>(red + rg * DV + c0) = sa;
+        }
     }
     __syncthreads();
     if (s_bad) {
@@ -236,23 +310,40 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void decode_kernel(TilePar
         float sum = 0.f;
 #pragma unroll
         for (int g2 = 0; g2 < RG; ++g2) sum += red[g2 * DV + tid];
-        P.out[in_row * DV + tid] = sum * (P.scale * s_es) + obuf[tid];
+        P.out[in_row * DV + tid] = sum * (CH ? P.scale : P.scale * s_es) + obuf[tid];
     }
 
     // ---- eager fold: the buffer reached m tokens ---------------------------------
     if (s_fold && !token_wave) {
-        const float e0 = s_e0;
+        if constexpr (CH) {
+            // decays relative to position m-1: B_{m-1} - B_i = dg[i] - dg[m-1]
+            const float* dm = dg + (P.m - 1) * DK + rg * RPT;
 #pragma unroll
-        for (int j = 0; j < RPT; ++j) s[j] *= e0;
-        for (int ii = 0; ii < P.m; ++ii) {
-            const f4 x = load4(vrs + ii * DV + c0);
-            RawChunk<IO, RPT> krow;
-            float kf[RPT];
-            krow.load(krs + ii * DK + rg * RPT);
-            krow.to_float(kf);
-            const float w = fw[ii];
+            for (int j = 0; j < RPT; ++j) s[j] *= exp_gate(btv[rg * RPT + j] - dm[j]);
+            for (int ii = 0; ii < P.m; ++ii) {
+                const f4 x = load4(vrs + ii * DV + c0);
+                RawChunk<IO, RPT> krow;
+                float kf[RPT];
+                krow.load(krs + ii * DK + rg * RPT);
+                krow.to_float(kf);
+                const float* di = dg + ii * DK + rg * RPT;
 #pragma unroll
-            for (int j = 0; j < RPT; ++j) s[j] += (w * kf[j]) * x;
+                for (int j = 0; j < RPT; ++j) s[j] += (kf[j] * exp_gate(di[j] - dm[j])) * x;
+            }
+        } else {
+            const float e0 = s_e0;
+#pragma unroll
+            for (int j = 0; j < RPT; ++j) s[j] *= e0;
+            for (int ii = 0; ii < P.m; ++ii) {
+                const f4 x = load4(vrs + ii * DV + c0);
+                RawChunk<IO, RPT> krow;
+                float kf[RPT];
+                krow.load(krs + ii * DK + rg * RPT);
+                krow.to_float(kf);
+                const float w = fw[ii];
+#pragma unroll
+                for (int j = 0; j < RPT; ++j) s[j] += (w * kf[j]) * x;
+            }
         }
         float* wt = P.state + (static_cast<size_t>(slot) * P.H + h) * DK * DV;
 #pragma unroll
@@ -264,7 +355,8 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void decode_kernel(TilePar
 template <int RULE, int D, typename IO>
 hipError_t launch_decode_t(const TileParams& p, int batch, hipStream_t s) {
     using G = Geo<D, D>;
-    const size_t lds = sizeof(float) * decode_lds(D, D, G::RG, p.fold_chunk, static_cast<int>(sizeof(IO))).total;
+    const size_t lds = sizeof(float) * decode_lds(D, D, G::RG, p.fold_chunk, static_cast<int>(sizeof(IO)),
+                                                  RULE == KVBUF_RULE_CHANNEL, p.block_size * p.blocks_per_req).total;
     decode_kernel<RULE, D, D, IO><<<dim3(static_cast<unsigned>(batch) * p.H), dim3(G::NTHREADS), lds, s>>>(p);
     return hipGetLastError();
 }
@@ -292,6 +384,9 @@ bool decode_eligible(int rule, int n, int cap) {
 }
 
 hipError_t launch_decode(const TileParams& p, int rule, int d, int io, int batch, hipStream_t s) {
+    if (rule == KVBUF_RULE_CHANNEL)
+        return io == KVBUF_BF16 ? launch_decode_d<KVBUF_RULE_CHANNEL, bf16_bits>(p, d, batch, s)
+                                : launch_decode_d<KVBUF_RULE_CHANNEL, float>(p, d, batch, s);
     if (rule == KVBUF_RULE_LINEAR)
         return io == KVBUF_BF16 ? launch_decode_d<KVBUF_RULE_LINEAR, bf16_bits>(p, d, batch, s)
                                 : launch_decode_d<KVBUF_RULE_LINEAR, float>(p, d, batch, s);

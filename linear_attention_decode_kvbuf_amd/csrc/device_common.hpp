@@ -320,6 +320,35 @@ __device__ __forceinline__ void stage_rows(const TileTokens<DK, DV, IO, XIO>& to
     }
 }
 
+// Direct-to-LDS copy of `rows` rows of RB bytes (RB a multiple of 16, at
+// most 1 KiB) by one wave: row i is read from src(i) and lands at dst + i RB.
+// One instruction carries 1 KiB, 16 bytes per lane: lane L writes dst + 16 L
+// of its window, holding bytes 16 (L mod RB/16) .. of row L / (RB/16).  dst
+// must be 16-byte aligned.  src may use wave shuffles: every lane calls it.
+template <int RB, typename SrcOf>
+__device__ __forceinline__ void lds_copy_rows(char* dst, int rows, SrcOf src, int lane) {
+    static_assert(RB % 16 == 0 && RB <= 1024, "whole 16-byte lanes of a 1 KiB copy");
+    constexpr int LPR = RB / 16;   // lanes per row
+    constexpr int RPI = 64 / LPR;  // rows per instruction
+    const int rr = lane / LPR;
+    const int off = (lane % LPR) * 16;
+    for (int r0 = 0; r0 < rows; r0 += RPI) {
+        const int row = r0 + rr;
+        const char* a = src(row < rows ? row : r0) + off;
+        if (row < rows)
+            __builtin_amdgcn_global_load_lds(a, (__attribute__((address_space(3))) void*)(dst + r0 * RB), 16, 0, 0);
+    }
+}
+
+// The copies count on the wave's vector-memory counter and land in LDS
+// asynchronously; the compiler does not reliably order LDS reads of the rows
+// after them, so the wave waits for the counter to drain (vmcnt(0) in the
+// gfx9 encoding) and keeps the scheduler from moving anything across.
+__device__ __forceinline__ void wait_lds_copies() {
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 // Workgroups are numbered head-major: workgroup w serves request w % B and
 // head w / B, so consecutive workgroups stream different requests' state
 // slots and buffer blocks.

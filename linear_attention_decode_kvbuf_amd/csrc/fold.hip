@@ -12,7 +12,9 @@
 // into the state S0 at the last fold:
 //   S <- e^{b_{T-1}} S0 + sum_{i<T} e^{b_{T-1} - b_i} k_i x_i^T
 // a rank-T update of the d_k x d_v tile (x_i = v_i, or the delta rule's
-// pseudo-value u_i).  One workgroup per (request, head): the state waves put
+// pseudo-value u_i).  With one log-gate per key channel the decays are
+// vectors and act on rows: row r of S0 is scaled by e^{B_{T-1}[r]} and k_i[r]
+// by e^{B_{T-1}[r] - B_i[r]} (B the per-channel cumulative log-gate).  One workgroup per (request, head): the state waves put
 // the 64 KiB tile in flight while the token wave forms the decay weights and
 // stages the keys and values in LDS (double-buffered rounds of up to 32
 // tokens); the state waves apply the update from registers and write the tile
@@ -25,12 +27,13 @@ namespace kvbuf {
 namespace {
 
 // LDS: pool row of each buffer position, cumulative log-gates, two staging
-// buffers of fc tokens (keys, values, weights), the state weight e^{b_{T-1}}.
+// buffers of fc tokens (keys, values, weights), the state weight e^{b_{T-1}}
+// (per key channel for the per-channel rule: DK of them).
 __host__ __device__ inline int fold_stage_floats(int DK, int DV, int fc) {
     return fc * (DK + DV) + ((fc + 3) & ~3);
 }
-__host__ __device__ inline int fold_lds_floats(int DK, int DV, int cap, int fc) {
-    return 2 * ((cap + 3) & ~3) + 2 * fold_stage_floats(DK, DV, fc) + 4;
+__host__ __device__ inline int fold_lds_floats(int DK, int DV, int cap, int fc, bool ch) {
+    return 2 * ((cap + 3) & ~3) + 2 * fold_stage_floats(DK, DV, fc) + (ch ? DK : 4);
 }
 
 // MULTI: the fold may take more than one staging round (then the token wave
@@ -42,7 +45,9 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void fold_kernel(TileParam
     using G = Geo<DK, DV>;
     constexpr int NT = G::NT, TPR = G::TPR, RPT = G::RPT;
     constexpr bool DELTA = RULE == KVBUF_RULE_DELTA;
-    constexpr bool GATED = RULE != KVBUF_RULE_LINEAR;
+    constexpr bool CH = RULE == KVBUF_RULE_CHANNEL;
+    constexpr bool SGATE = RULE == KVBUF_RULE_GATED || DELTA;  // one scalar gate per token
+    constexpr int CPL = (DK + 63) / 64;                        // key channels per token-wave lane
     using XIO = typename std::conditional<DELTA, float, IO>::type;
 
     extern __shared__ float lds[];
@@ -110,6 +115,13 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void fold_kernel(TileParam
     tok.H = P.H;
     tok.p = cap;  // every position read here is in the pool
 
+    // Per-channel rule: the token wave holds, for its key channels
+    // ch = lane + 64 c, the running sum of the gates of the positions staged
+    // so far (prefix) and their total over all T positions (e0p[ch]).
+    float prefix[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) prefix[c] = 0.0f;
+
     // Token wave: stage round r (tokens r*fc ..) into buffer r % 2.
     auto stage = [&](int r) {
         float* fk = stage0 + (r & 1) * stage_floats;
@@ -118,13 +130,40 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void fold_kernel(TileParam
         const int i0 = r * fc;
         const int cnt = min(fc, T - i0);
         stage_rows(tok, i0, cnt, fk, fx, nullptr, lane);
-        for (int ii = lane; ii < cnt; ii += 64)
-            fw[ii] = GATED ? exp_gate(bl[T - 1] - bl[i0 + ii]) : 1.0f;
+        if constexpr (CH) {
+            // k_i[ch] e^{B_{T-1}[ch] - B_i[ch]}, positions in order
+            for (int ii = 0; ii < cnt; ++ii) {
+                const size_t row = static_cast<size_t>(tok.pos[i0 + ii]) * DK;
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) {
+                    const int ch = lane + 64 * c;
+                    if (ch < DK) {
+                        prefix[c] += P.gate[row + ch];
+                        fk[ii * DK + ch] *= exp_gate(e0p[ch] - prefix[c]);
+                    }
+                }
+            }
+            for (int ii = lane; ii < cnt; ii += 64) fw[ii] = 1.0f;
+        } else {
+            for (int ii = lane; ii < cnt; ii += 64)
+                fw[ii] = SGATE ? exp_gate(bl[T - 1] - bl[i0 + ii]) : 1.0f;
+        }
     };
 
     if (token_wave) {
-        if constexpr (GATED) gate_prefix(bl, T, lane, [&](int i) { return tok.gate(i); });
-        if (lane == 0) *e0p = (GATED && T > 0) ? exp_gate(bl[T - 1]) : 1.0f;
+        if constexpr (SGATE) gate_prefix(bl, T, lane, [&](int i) { return tok.gate(i); });
+        if constexpr (CH) {
+            // total log-gate of each key channel over the T positions
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+                const int ch = lane + 64 * c;
+                float tot = 0.0f;
+                for (int i = 0; ch < DK && i < T; ++i) tot += P.gate[static_cast<size_t>(tok.pos[i]) * DK + ch];
+                if (ch < DK) e0p[ch] = tot;
+            }
+        } else {
+            if (lane == 0) *e0p = (SGATE && T > 0) ? exp_gate(bl[T - 1]) : 1.0f;
+        }
         if (T > 0) stage(0);
     }
     f4 s[RPT];
@@ -133,9 +172,14 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void fold_kernel(TileParam
                                has_state, rg, c0);
     __syncthreads();
     if (!token_wave) {
-        const float e0 = *e0p;
+        if constexpr (CH) {
 #pragma unroll
-        for (int j = 0; j < RPT; ++j) s[j] *= e0;
+            for (int j = 0; j < RPT; ++j) s[j] *= exp_gate(e0p[rg * RPT + j]);
+        } else {
+            const float e0 = *e0p;
+#pragma unroll
+            for (int j = 0; j < RPT; ++j) s[j] *= e0;
+        }
     }
     auto apply = [&](int r) {
         const float* fk = stage0 + (r & 1) * stage_floats;
@@ -175,7 +219,7 @@ template <int RULE, int D, typename IO>
 hipError_t launch_fold_t(const TileParams& p, int batch, hipStream_t s) {
     using G = Geo<D, D>;
     const int cap = p.block_size * p.blocks_per_req;
-    const size_t lds = sizeof(float) * fold_lds_floats(D, D, cap, p.fold_chunk);
+    const size_t lds = sizeof(float) * fold_lds_floats(D, D, cap, p.fold_chunk, RULE == KVBUF_RULE_CHANNEL);
     const int most = p.mode == MODE_MATERIALIZE ? cap : p.m;  // most positions one tile applies
     const dim3 grid(static_cast<unsigned>(batch) * p.H), block(G::NTHREADS);
     if (most <= p.fold_chunk)
@@ -199,6 +243,7 @@ hipError_t launch_fold_r(const TileParams& p, int rule, int d, int batch, hipStr
     switch (rule) {
         case KVBUF_RULE_LINEAR: return launch_fold_d<KVBUF_RULE_LINEAR, IO>(p, d, batch, s);
         case KVBUF_RULE_GATED: return launch_fold_d<KVBUF_RULE_GATED, IO>(p, d, batch, s);
+        case KVBUF_RULE_CHANNEL: return launch_fold_d<KVBUF_RULE_CHANNEL, IO>(p, d, batch, s);
         default: return launch_fold_d<KVBUF_RULE_DELTA, IO>(p, d, batch, s);
     }
 }

@@ -8,6 +8,7 @@
 //   gated    S <- e^g S + k v^T
 //   delta    S <- e^g S + k u^T,  u = beta (v - e^g S^T k)
 //            (the same as e^g (I - beta k k^T) S + beta k v^T)
+//   channel  S <- diag(e^g) S + k v^T, one log-gate per key channel (row)
 //   output   o = S^T (scale q) with the updated S.
 // One workgroup per tile reads the 64 KiB state once and writes it once:
 // 2 |S| bytes of HBM traffic per token, which is what the buffered path avoids.
@@ -23,6 +24,7 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void recurrent_kernel(Tile
     using G = Geo<DK, DV>;
     constexpr int NT = G::NT, TPR = G::TPR, RG = G::RG, RPT = G::RPT;
     constexpr bool DELTA = RULE == KVBUF_RULE_DELTA;
+    constexpr bool CH = RULE == KVBUF_RULE_CHANNEL;
     constexpr bool GATED = RULE != KVBUF_RULE_LINEAR;
 
     __shared__ float qs[DK];
@@ -30,7 +32,8 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void recurrent_kernel(Tile
     __shared__ float vf[DV];
     __shared__ float red[RG * DV];
     __shared__ float sk[DELTA ? DV : 1];
-    __shared__ float gb[2];  // gamma, beta
+    __shared__ float gb[2];           // gamma, beta
+    __shared__ float gv[CH ? DK : 1];  // per-channel decay e^{g[r]}
 
     const TileIndex ti = tile_index(P);
     const int b = ti.b;
@@ -57,8 +60,11 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void recurrent_kernel(Tile
             kf[r] = load1(k + r);
         }
         for (int c = lane; c < DV; c += 64) vf[c] = load1(v + c);
+        if constexpr (CH) {
+            for (int r = lane; r < DK; r += 64) gv[r] = exp_gate(P.g[in_row * DK + r]);
+        }
         if (lane == 0) {
-            gb[0] = GATED ? exp_gate(P.g[in_row]) : 1.0f;
+            gb[0] = (GATED && !CH) ? exp_gate(P.g[in_row]) : 1.0f;
             gb[1] = DELTA ? P.beta[in_row] : 0.0f;
         }
     }
@@ -98,7 +104,7 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void recurrent_kernel(Tile
 #pragma unroll
         for (int j = 0; j < RPT; ++j) {
             const int r = rg * RPT + j;
-            s[j] = gamma * s[j] + kf[r] * x;
+            s[j] = (CH ? gv[r] : gamma) * s[j] + kf[r] * x;
             o += s[j] * qs[r];
         }
 #pragma unroll
@@ -126,12 +132,14 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void verify_recurrent_kern
     constexpr int NT = G::NT, TPR = G::TPR, RG = G::RG, RPT = G::RPT;
     constexpr int NMAX = kMaxDrafts;
     constexpr bool DELTA = RULE == KVBUF_RULE_DELTA;
+    constexpr bool CH = RULE == KVBUF_RULE_CHANNEL;
     constexpr bool GATED = RULE != KVBUF_RULE_LINEAR;
 
     __shared__ float qs[NMAX][DK];
     __shared__ float kf[NMAX][DK];
     __shared__ float vf[NMAX][DV];
     __shared__ float gb[NMAX][2];  // gamma, beta
+    __shared__ float gv[CH ? NMAX : 1][CH ? DK : 1];  // per-channel decays of each draft
     __shared__ float red[2][RG * DV];
     __shared__ float sk[DELTA ? DV : 1];
 
@@ -162,8 +170,11 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void verify_recurrent_kern
                 kf[d][r] = load1(k + r);
             }
             for (int c = lane; c < DV; c += 64) vf[d][c] = load1(v + c);
+            if constexpr (CH) {
+                for (int r = lane; r < DK; r += 64) gv[d][r] = exp_gate(P.g[row * DK + r]);
+            }
             if (lane == 0) {
-                gb[d][0] = GATED ? exp_gate(P.g[row]) : 1.0f;
+                gb[d][0] = (GATED && !CH) ? exp_gate(P.g[row]) : 1.0f;
                 gb[d][1] = DELTA ? P.beta[row] : 0.0f;
             }
         }
@@ -203,7 +214,7 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void verify_recurrent_kern
 #pragma unroll
             for (int j = 0; j < RPT; ++j) {
                 const int r = rg * RPT + j;
-                s[j] = gamma * s[j] + kf[d][r] * x;
+                s[j] = (CH ? gv[d][r] : gamma) * s[j] + kf[d][r] * x;
                 o += s[j] * qs[d][r];
             }
             float* tt = temp + ((static_cast<size_t>(d) * P.batch + b) * P.H + h) * DK * DV;
@@ -279,6 +290,7 @@ hipError_t launch_rec_r(const TileParams& p, int rule, int d, int batch, hipStre
     switch (rule) {
         case KVBUF_RULE_LINEAR: return launch_rec_d<KVBUF_RULE_LINEAR, IO>(p, d, batch, s);
         case KVBUF_RULE_GATED: return launch_rec_d<KVBUF_RULE_GATED, IO>(p, d, batch, s);
+        case KVBUF_RULE_CHANNEL: return launch_rec_d<KVBUF_RULE_CHANNEL, IO>(p, d, batch, s);
         default: return launch_rec_d<KVBUF_RULE_DELTA, IO>(p, d, batch, s);
     }
 }
@@ -304,6 +316,7 @@ hipError_t launch_verify_rec_r(const TileParams& p, int rule, int d, float* temp
     switch (rule) {
         case KVBUF_RULE_LINEAR: return launch_verify_rec_d<KVBUF_RULE_LINEAR, IO>(p, d, temp, s);
         case KVBUF_RULE_GATED: return launch_verify_rec_d<KVBUF_RULE_GATED, IO>(p, d, temp, s);
+        case KVBUF_RULE_CHANNEL: return launch_verify_rec_d<KVBUF_RULE_CHANNEL, IO>(p, d, temp, s);
         default: return launch_verify_rec_d<KVBUF_RULE_DELTA, IO>(p, d, temp, s);
     }
 }

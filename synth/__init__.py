@@ -113,7 +113,8 @@ def token_inputs(w: Workload, step: int, B: int | None = None, n: int | None = N
     v = rng(w.ident, step, V + s).standard_normal(lead + (w.H, w.dv), dtype=np.float32)
     g = beta = None
     if w.rule >= 1:
-        g = rng(w.ident, step, G + s).uniform(-0.1, 0.0, size=lead + (w.H,)).astype(np.float32)
+        gshape = lead + (w.H, w.dk) if w.rule == 3 else lead + (w.H,)  # rule 3: one gate per key channel
+        g = rng(w.ident, step, G + s).uniform(-0.1, 0.0, size=gshape).astype(np.float32)
     if w.rule == 2:
         beta = rng(w.ident, step, BETA + s).uniform(0.0, 1.0, size=lead + (w.H,)).astype(np.float32)
     return dict(q=_store(q, w.io), k=_store(k, w.io), v=_store(v, w.io), g=g, beta=beta)
@@ -184,7 +185,8 @@ def device_token_inputs(w: Workload, step: int, device, B: int | None = None, n:
     v = torch.randn(lead + (w.H, w.dv), generator=_torch_gen(device, w.ident, step, V + s), **f)
     g = beta = None
     if w.rule >= 1:
-        g = -0.1 * torch.rand(lead + (w.H,), generator=_torch_gen(device, w.ident, step, G + s), **f)
+        gshape = lead + (w.H, w.dk) if w.rule == 3 else lead + (w.H,)  # rule 3: one gate per key channel
+        g = -0.1 * torch.rand(gshape, generator=_torch_gen(device, w.ident, step, G + s), **f)
     if w.rule == 2:
         beta = torch.rand(lead + (w.H,), generator=_torch_gen(device, w.ident, step, BETA + s), **f)
     return dict(q=q.to(io), k=k.to(io), v=v.to(io), g=g, beta=beta)

@@ -71,7 +71,7 @@ def _decode(layout, pools=POOLS, batch=BATCH, q=FAKE, g=FAKE, beta=None):
     (dict(num_heads=0), kb.EINVAL),
     (dict(d_k=32, d_v=32), kb.EUNSUPPORTED),
     (dict(d_k=128, d_v=64), kb.EUNSUPPORTED),
-    (dict(rule=3), kb.EUNSUPPORTED),
+    (dict(rule=4), kb.EUNSUPPORTED),
     (dict(io_dtype=7), kb.EUNSUPPORTED),
     (dict(flush=5), kb.EINVAL),
     (dict(m=6), kb.ECAPACITY),             # not a multiple of block_size
@@ -130,3 +130,13 @@ def test_recurrent_verification_validation(lib):
     empty = kb.Batch(0, None, None, None, None)
     assert kb.kvbuf_verify_recurrent(L0, POOLS, empty, 2, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, 0,
                                      False) == kb.OK
+
+
+def test_channel_rule_limits(lib):
+    """The per-channel rule is served by the one-token kernel: drafts beyond
+    one and table rows beyond 64 positions are refused on the host."""
+    L = _layout(rule=kb.RULE_CHANNEL)
+    assert kb.kvbuf_verify(L, POOLS, BATCH, 2, FAKE, FAKE, FAKE, FAKE, None, FAKE, 0, False) == kb.EUNSUPPORTED
+    long_rows = _layout(rule=kb.RULE_CHANNEL, block_size=4, blocks_per_req=17, num_blocks=40)
+    assert _decode(long_rows) == kb.EUNSUPPORTED
+    assert kb.kvbuf_direct(long_rows, POOLS, BATCH, FAKE, FAKE, FAKE, FAKE, None, FAKE, 0, False) == kb.EUNSUPPORTED

@@ -42,7 +42,7 @@ def test_tiny_every_step(flush):
     _say("max out err %.2e, max state err %.2e" % (run.max_out, run.max_state))
 
 
-@pytest.mark.parametrize("rule", [0, 1, 2])
+@pytest.mark.parametrize("rule", [0, 1, 2, 3])
 @pytest.mark.parametrize("d,io", [(16, "f32"), (64, "bf16"), (128, "bf16"), (128, "f32")])
 @pytest.mark.parametrize("m,bs,bpr", [(4, 4, 2), (4, 2, 3), (1, 1, 3), (6, 3, 3)])
 def test_small_rules(rule, d, io, m, bs, bpr):
@@ -76,7 +76,7 @@ def test_long_table_rows(m, bs, bpr, flush):
     run.check_bookkeeping()
 
 
-@pytest.mark.parametrize("rule", [0, 1, 2])
+@pytest.mark.parametrize("rule", [0, 1, 2, 3])
 def test_deferred_flush_with_tail(rule):
     """Decode past m before folding: the fold takes the first m tokens and
     leaves the rest buffered in the rotated table."""
@@ -95,7 +95,7 @@ def test_deferred_flush_with_tail(rule):
     run.check_bookkeeping()
 
 
-@pytest.mark.parametrize("rule", [0, 1, 2])
+@pytest.mark.parametrize("rule", [0, 1, 2, 3])
 def test_recurrent_m0(rule):
     w = synth.workload(1, B=3, H=4, dk=128, dv=128, m=0, block_size=1, blocks_per_req=1, steps=9,
                        rule=rule, io="bf16", state_std=0.02)
@@ -109,8 +109,7 @@ def test_recurrent_m0(rule):
         assert np.max(np.abs(gpu - ref)) / np.max(np.abs(ref)) <= 1e-5
 
 
-@pytest.mark.parametrize("rule", [0, 1, 2])
-@pytest.mark.parametrize("n", [1, 3, 8])
+@pytest.mark.parametrize("rule,n", [(r, n) for r in (0, 1, 2) for n in (1, 3, 8)] + [(3, 1)])
 def test_verify_commit_small(rule, n):
     w = synth.workload(1, B=4, H=2, dk=64, dv=64, m=4, block_size=4, blocks_per_req=4, steps=6,
                        rule=rule, io="bf16", state_std=0.02)
@@ -141,7 +140,7 @@ def test_staggered_occupancies(rule):
     run.check_pool()
 
 
-@pytest.mark.parametrize("rule", [0, 1, 2])
+@pytest.mark.parametrize("rule", [0, 1, 2, 3])
 def test_direct_and_promotion(rule):
     """Buffer-only decode equals the recurrence from a zero state; giving the
     request a zeroed state slot afterwards and folding creates its state."""
@@ -344,7 +343,7 @@ def _tile_rel(a, b):
     return np.max(np.abs(a - b), axis=1) / np.maximum(np.max(np.abs(b), axis=1), 1e-30)
 
 
-@pytest.mark.parametrize("rule", [0, 1, 2])
+@pytest.mark.parametrize("rule", [0, 1, 2, 3])
 @pytest.mark.parametrize("n,d", [(1, 64), (4, 128), (8, 64), (3, 16)])
 def test_verify_recurrent_baseline(rule, n, d):
     import oracle
@@ -366,7 +365,7 @@ def test_verify_recurrent_baseline(rule, n, d):
         sl = slice(0, dd + 1)
         o_ref, S_ref = oracle.recurrent(rule, run.S, q[:, sl].transpose(1, 0, 2), k[:, sl].transpose(1, 0, 2),
                                         v[:, sl].transpose(1, 0, 2),
-                                        None if g is None else g[:, sl].T,
+                                        None if g is None else np.swapaxes(g[:, sl], 0, 1),
                                         None if beta is None else beta[:, sl].T)
         assert np.max(_tile_rel(o_gpu[:, dd], o_ref[dd])) <= 2e-3, dd
         t_gpu = tmp[dd][run.sb, run.sh].double().cpu().numpy()
