@@ -230,6 +230,19 @@ class BufferModel:
             return self.flush(b)
         return False
 
+    def commit_path(self, b, path, eager=True) -> bool:
+        """Tree drafts: keep the drafts on one root-to-node path (indices into
+        the verified drafts, in path order).  Draft path[k] moves from
+        position occupancy + path[k] to occupancy + k, then the occupancy
+        advances over the path (a chain tree with path [0 .. a-1] is
+        ``commit(b, a)``).  The pages' reference list includes tree
+        speculative decoding; the accepted path is what the request keeps."""
+        r = self.requests[b]
+        moved = [self.physical.get(self.position(b, r.occupancy + d)) for d in path]
+        for k, tok in enumerate(moved):
+            self._write(b, r.occupancy + k, tok)
+        return self.commit(b, len(path), eager)
+
     def buffered_tokens(self, b):
         """Token ids at logical positions 0 .. occupancy-1 of request b."""
         r = self.requests[b]

@@ -166,6 +166,29 @@ class ExactKVBuffer:
         self._drafts = drafts
         return outs
 
+    def verify_tree(self, qs, ks, vs, gs, bs, parent):
+        """Tree drafts: draft d attends to the buffer, its ancestors (parent[d],
+        parent[parent[d]], ... up to -1 = the buffer) and itself, with the
+        decay accumulated along that path."""
+        drafts, outs = [], []
+        for d in range(len(qs)):
+            anc, a = [], parent[d]
+            while a >= 0:
+                anc.append(a)
+                a = parent[a]
+            prev = self.buf + [drafts[a] for a in reversed(anc)]
+            x = self._pseudo_value(ks[d], vs[d], gs[d], bs[d], prev)
+            drafts.append((list(ks[d]), x, gs[d]))
+            outs.append(self._output(qs[d], prev + [drafts[d]]))
+        self._drafts = drafts
+        return outs
+
+    def commit_path(self, path):
+        self.buf.extend(self._drafts[d] for d in path)
+        self._drafts = []
+        if self.m > 0 and len(self.buf) >= self.m:
+            self.fold()
+
     def commit(self, accepted):
         self.buf.extend(self._drafts[:accepted])
         self._drafts = []

@@ -97,3 +97,30 @@ def test_random_operations_conserve_blocks_and_bound_occupancy():
         assert all(0 <= o < m for o in bm.occupancies())
     owned = sorted(x for row in bm.tables().tolist() for x in row)
     assert owned == sorted(pool[: B * bpr])
+
+
+def test_commit_path_compacts_the_accepted_drafts():
+    """Tree drafts: the accepted root-to-node path moves to consecutive
+    positions after the buffered tokens; other drafts stay as dead data."""
+    bm = BufferModel(m=8, block_size=4, blocks_per_req=3)
+    bm.add_request([4, 0, 2])
+    for t in range(3):
+        bm.decode(0, ("d", t))
+    bm.verify(0, [("v", i) for i in range(6)])  # positions 3 .. 8
+    bm.commit_path(0, [1, 3, 5])  # drafts 1, 3, 5 -> positions 3, 4, 5
+    assert bm.occupancies().tolist() == [6]
+    assert bm.buffered_tokens(0) == [("d", 0), ("d", 1), ("d", 2), ("v", 1), ("v", 3), ("v", 5)]
+    assert bm.physical[bm.position(0, 8)] == ("v", 5)  # the source stays as dead data
+
+
+def test_commit_chain_path_is_commit():
+    a = BufferModel(m=4, block_size=2, blocks_per_req=4)
+    b = BufferModel(m=4, block_size=2, blocks_per_req=4)
+    for bm in (a, b):
+        bm.add_request([3, 1, 0, 2])
+        bm.decode(0, "x")
+        bm.verify(0, ["p", "q", "r", "s"])
+    assert a.commit(0, 3) == b.commit_path(0, [0, 1, 2])
+    assert a.tables().tolist() == b.tables().tolist()
+    assert a.occupancies().tolist() == b.occupancies().tolist()
+    assert a.buffered_tokens(0) == b.buffered_tokens(0)

@@ -110,3 +110,60 @@ def test_m1_is_recurrent():
     for t in range(5):
         assert ex.decode(q[t], k[t], v[t], gam[t], beta[t]) == ref_o[t]
         assert ex.S == ref_S[t] and ex.buf == []
+
+
+def _tree(seed, n):
+    """A random draft tree: parent[d] in {-1 (the buffer), 0 .. d-1}."""
+    r = random.Random(seed)
+    return [r.randint(-1, d - 1) for d in range(n)]
+
+
+def _path_to(parent, d):
+    path = []
+    while d >= 0:
+        path.append(d)
+        d = parent[d]
+    return path[::-1]
+
+
+@pytest.mark.parametrize("rule", [0, 1, 2, 3])
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_tree_verify_equals_serial_path_and_commit_keeps_it(rule, seed):
+    """Every node of a draft tree, verified from the buffer, equals the serial
+    decode of its root-to-node path; committing one path leaves the request
+    exactly where a serial decode of that path would (the page's reference
+    list includes tree speculative decoding for state-space models)."""
+    m, pre, n, dk, dv = 5, 3, 6, 2, 3
+    parent = _tree(600 + seed, n)
+    S0, q, k, v, gam, beta = _seq(700 + 10 * rule + seed, pre + n + 3, dk, dv, rule)
+    ex = ExactKVBuffer(rule, S0, m)
+    for t in range(pre):
+        ex.decode(q[t], k[t], v[t], gam[t], beta[t])
+    sl = slice(pre, pre + n)
+    outs = ex.verify_tree(q[sl], k[sl], v[sl], gam[sl], beta[sl], parent)
+    for d in range(n):
+        idx = list(range(pre)) + [pre + a for a in _path_to(parent, d)]
+        pick = lambda xs: [xs[i] for i in idx]
+        ref_o, _ = exact_recurrent(rule, S0, pick(q), pick(k), pick(v), pick(gam), pick(beta))
+        assert outs[d] == ref_o[-1], d
+    leaf = max(range(n), key=lambda d: len(_path_to(parent, d)))
+    path = _path_to(parent, leaf)
+    ex.commit_path(path)
+    idx = list(range(pre)) + [pre + a for a in path] + list(range(pre + n, pre + n + 3))
+    pick = lambda xs: [xs[i] for i in idx]
+    ref_o, ref_S = exact_recurrent(rule, S0, pick(q), pick(k), pick(v), pick(gam), pick(beta))
+    assert ex.effective_state() == ref_S[pre + len(path) - 1]
+    for j, t in enumerate(range(pre + n, pre + n + 3)):
+        assert ex.decode(q[t], k[t], v[t], gam[t], beta[t]) == ref_o[pre + len(path) + j]
+
+
+def test_chain_tree_is_parallel_verify():
+    n = 4
+    S0, q, k, v, gam, beta = _seq(800, 2 + n, 2, 2, 1)
+    a, b = ExactKVBuffer(1, S0, 8), ExactKVBuffer(1, S0, 8)
+    for t in range(2):
+        a.decode(q[t], k[t], v[t], gam[t], beta[t])
+        b.decode(q[t], k[t], v[t], gam[t], beta[t])
+    sl = slice(2, 2 + n)
+    assert a.verify(q[sl], k[sl], v[sl], gam[sl], beta[sl]) == \
+        b.verify_tree(q[sl], k[sl], v[sl], gam[sl], beta[sl], [d - 1 for d in range(n)])
