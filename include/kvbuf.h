@@ -204,6 +204,35 @@ kvbuf_status kvbuf_commit(const kvbuf_layout* layout, const kvbuf_pools* pools,
                           hipStream_t stream);
 
 /*
+ * kvbuf_verify_tree -- verification of n draft tokens that form a tree (the
+ * page's reference list includes tree speculative decoding for state-space
+ * models): parent [B][n] int32, device memory, parent[b][d] in {-1, 0 .. d-1};
+ * -1 makes draft d follow the buffer directly.  Draft d attends to the state,
+ * the buffer, its ancestors and itself, with the gates accumulated along that
+ * path -- the output a serial decode of its root-to-node path would give.
+ * Drafts are written at buffer positions occupancy + d as with kvbuf_verify;
+ * the occupancy does not change.  A chain (parent[d] = d - 1) is kvbuf_verify.
+ * Requires m > 0, 1 <= n <= 8, rules LINEAR, GATED, DELTA.  A parent outside
+ * its range sets KVBUF_DEVERR_ACCEPT and skips the tile.
+ */
+kvbuf_status kvbuf_verify_tree(const kvbuf_layout* layout, const kvbuf_pools* pools,
+                               const kvbuf_batch* batch, int32_t n, const int32_t* parent,
+                               const void* q, const void* k, const void* v, const float* g,
+                               const float* beta, float* out, hipStream_t stream);
+
+/*
+ * kvbuf_commit_tree -- keep the drafts on the path from the root to leaf[b]
+ * ([B] int32, device memory; -1 keeps none) of the preceding
+ * kvbuf_verify_tree with the same parent array: they move to consecutive
+ * buffer positions after the buffered tokens (other drafts stay behind as
+ * dead data) and the occupancy advances over them; with KVBUF_FLUSH_EAGER a
+ * request whose buffer reaches m folds in the same kernel.
+ */
+kvbuf_status kvbuf_commit_tree(const kvbuf_layout* layout, const kvbuf_pools* pools,
+                               const kvbuf_batch* batch, int32_t n, const int32_t* parent,
+                               const int32_t* leaf, hipStream_t stream);
+
+/*
  * kvbuf_verify_recurrent -- the verification that kvbuf_verify replaces
  * (Figure 2 caption: a system with only a state pool verifies drafts with the
  * recurrent form and keeps a temporary state for every draft).  Recurrent

@@ -27,7 +27,7 @@ OK, EINVAL, EUNSUPPORTED, ECAPACITY, EHIP = 0, -1, -2, -3, -4
 DEVERR_BLOCK, DEVERR_SLOT, DEVERR_OVERFLOW, DEVERR_ACCEPT = 1, 2, 4, 8
 
 EXPORTED = ("kvbuf_decode", "kvbuf_flush", "kvbuf_verify", "kvbuf_commit", "kvbuf_direct",
-            "kvbuf_verify_recurrent", "kvbuf_commit_recurrent", "kvbuf_materialize", "kvbuf_strerror",
+            "kvbuf_verify_tree", "kvbuf_commit_tree", "kvbuf_verify_recurrent", "kvbuf_commit_recurrent", "kvbuf_materialize", "kvbuf_strerror",
             "kvbuf_abi_version")
 
 
@@ -77,10 +77,13 @@ def load():
         lib.kvbuf_flush.argtypes = [L, PO, B, P]
         lib.kvbuf_commit.argtypes = [L, PO, B, i32, P, P]
         lib.kvbuf_materialize.argtypes = [L, PO, B, P, P]
+        lib.kvbuf_verify_tree.argtypes = [L, PO, B, i32, P, P, P, P, P, P, P, P]
+        lib.kvbuf_commit_tree.argtypes = [L, PO, B, i32, P, P, P]
         lib.kvbuf_verify_recurrent.argtypes = [L, PO, B, i32, P, P, P, P, P, P, P, P]
         lib.kvbuf_commit_recurrent.argtypes = [L, PO, B, i32, P, P, P]
         for name in ("kvbuf_decode", "kvbuf_direct", "kvbuf_verify", "kvbuf_flush",
-                     "kvbuf_commit", "kvbuf_materialize", "kvbuf_verify_recurrent",
+                     "kvbuf_commit", "kvbuf_materialize", "kvbuf_verify_tree", "kvbuf_commit_tree",
+                     "kvbuf_verify_recurrent",
                      "kvbuf_commit_recurrent"):
             getattr(lib, name).restype = ctypes.c_int
         lib.kvbuf_strerror.argtypes = [ctypes.c_int]
@@ -156,6 +159,18 @@ def kvbuf_materialize(layout, pools, batch, states, stream=None, raise_on_error=
     st = load().kvbuf_materialize(_ref(layout), _ref(pools), _ref(batch), _ptr(states),
                                   _stream(stream))
     return _check(st, "kvbuf_materialize", raise_on_error)
+
+
+def kvbuf_verify_tree(layout, pools, batch, n, parent, q, k, v, g, beta, out, stream=None, raise_on_error=True):
+    st = load().kvbuf_verify_tree(_ref(layout), _ref(pools), _ref(batch), int(n), _ptr(parent), _ptr(q),
+                                  _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(out), _stream(stream))
+    return _check(st, "kvbuf_verify_tree", raise_on_error)
+
+
+def kvbuf_commit_tree(layout, pools, batch, n, parent, leaf, stream=None, raise_on_error=True):
+    st = load().kvbuf_commit_tree(_ref(layout), _ref(pools), _ref(batch), int(n), _ptr(parent), _ptr(leaf),
+                                  _stream(stream))
+    return _check(st, "kvbuf_commit_tree", raise_on_error)
 
 
 def kvbuf_verify_recurrent(layout, pools, batch, n, q, k, v, g, beta, out, temp, stream=None,
@@ -261,6 +276,18 @@ class KVBuffer:
 
     def commit(self, n, accepted, stream=None):
         kvbuf_commit(self.layout, self.pools, self.batch, n, accepted, stream)
+
+    def verify_tree(self, parent, q, k, v, g=None, beta=None, out=None, stream=None):
+        """Tree drafts: parent [B, n] int32 on the device (-1 = follows the buffer)."""
+        n = q.shape[1]
+        if out is None:
+            out = self.torch.empty((self.B, n, self.H, self.d), dtype=self.torch.float32, device=q.device)
+        kvbuf_verify_tree(self.layout, self.pools, self.batch, n, parent, q, k, v, g, beta, out, stream)
+        return out
+
+    def commit_tree(self, parent, leaf, stream=None):
+        """Keep the path from the root to leaf [B] int32 (-1 = none) of the last tree verify."""
+        kvbuf_commit_tree(self.layout, self.pools, self.batch, parent.shape[1], parent, leaf, stream)
 
     def verify_recurrent(self, q, k, v, g=None, beta=None, out=None, temp=None, stream=None):
         """Temporary-state verification (m = 0 only): returns (out, temp)."""

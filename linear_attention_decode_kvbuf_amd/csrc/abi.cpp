@@ -104,7 +104,7 @@ kvbuf_status from_hip(hipError_t e) { return e == hipSuccess ? KVBUF_OK : KVBUF_
 kvbuf_status chunk_call(const kvbuf_layout* layout, const kvbuf_pools* pools,
                         const kvbuf_batch* batch, int mode, int n, const void* q,
                         const void* k, const void* v, const float* g, const float* beta,
-                        float* out, hipStream_t stream) {
+                        float* out, hipStream_t stream, const int32_t* parent = nullptr) {
     const bool direct = mode == kvbuf::MODE_DIRECT;
     KVBUF_TRY(check_layout(layout, mode != kvbuf::MODE_DECODE));
     KVBUF_TRY(check_batch(layout, batch));
@@ -118,11 +118,12 @@ kvbuf_status chunk_call(const kvbuf_layout* layout, const kvbuf_pools* pools,
     }
     // the per-channel rule is served by the one-token decode kernel only
     if (layout->rule == KVBUF_RULE_CHANNEL && layout->m > 0 &&
-        !kvbuf::decode_eligible(layout->rule, n, layout->block_size * layout->blocks_per_req))
+        (parent || !kvbuf::decode_eligible(layout->rule, n, layout->block_size * layout->blocks_per_req)))
         return KVBUF_EUNSUPPORTED;
     TileParams t = make_params(layout, pools, batch);
     t.mode = mode;
     t.n = n;
+    t.parent = parent;
     // A decode under the eager policy folds inside the decode kernel when the
     // m tokens fit its first staging pass; otherwise a fold launch follows it.
     const bool eager_decode = mode == kvbuf::MODE_DECODE && t.fuse && layout->m > 0;
@@ -201,6 +202,34 @@ kvbuf_status kvbuf_commit(const kvbuf_layout* layout, const kvbuf_pools* pools,
     t.n = n;
     t.fold_chunk = fold_chunk(layout->m);
     t.accepted = accepted;
+    return from_hip(kvbuf::launch_fold(t, layout->rule, layout->d_k, layout->io_dtype, batch->size, stream));
+}
+
+kvbuf_status kvbuf_verify_tree(const kvbuf_layout* layout, const kvbuf_pools* pools,
+                               const kvbuf_batch* batch, int32_t n, const int32_t* parent,
+                               const void* q, const void* k, const void* v, const float* g,
+                               const float* beta, float* out, hipStream_t stream) {
+    if (!parent) return KVBUF_EINVAL;
+    return chunk_call(layout, pools, batch, kvbuf::MODE_VERIFY, n, q, k, v, g, beta, out, stream, parent);
+}
+
+kvbuf_status kvbuf_commit_tree(const kvbuf_layout* layout, const kvbuf_pools* pools,
+                               const kvbuf_batch* batch, int32_t n, const int32_t* parent,
+                               const int32_t* leaf, hipStream_t stream) {
+    KVBUF_TRY(check_layout(layout, true));
+    KVBUF_TRY(check_batch(layout, batch));
+    KVBUF_TRY(check_pools(layout, pools, true));
+    if (batch->size == 0) return KVBUF_OK;
+    if (!parent || !leaf) return KVBUF_EINVAL;
+    if (n < 1 || n > kvbuf::kMaxDrafts) return KVBUF_EUNSUPPORTED;
+    if (layout->rule == KVBUF_RULE_CHANNEL) return KVBUF_EUNSUPPORTED;
+    KVBUF_TRY(check_grid(layout, batch));
+    TileParams t = make_params(layout, pools, batch);
+    t.mode = kvbuf::MODE_COMMIT;
+    t.n = n;
+    t.fold_chunk = fold_chunk(layout->m);
+    t.parent = parent;
+    t.leaf = leaf;
     return from_hip(kvbuf::launch_fold(t, layout->rule, layout->d_k, layout->io_dtype, batch->size, stream));
 }
 

@@ -80,6 +80,11 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
     extern __shared__ float lds[];
     __shared__ unsigned s_bad;
     __shared__ int s_p;
+    // New token d of this call attends to position p + e iff bit e of s_anc[d]
+    // is set: every e <= d for a chain of drafts (and the one token of a
+    // decode); d and its ancestors for a tree of drafts (parent -1 = the
+    // buffered context).
+    __shared__ uint32_t s_anc[kMaxDrafts];
 
     const TileIndex ti = tile_index(P);
     const int b = ti.b;
@@ -111,6 +116,19 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
         const int p0 = P.occ[meta_index(P, b, h)];
         unsigned bad = stage_row(P, b, h, (p0 < 0 || p0 > cap) ? -1 : p0 + n, spos, tid);
         if (slot >= P.num_slots) bad |= KVBUF_DEVERR_SLOT;
+        int par = tid - 1;  // a chain
+        if (P.parent && tid < n) par = P.parent[static_cast<size_t>(b) * n + tid];
+        const bool bad_par = tid < n && (par < -1 || par >= tid);  // parents precede children
+        if (__ballot(bad_par)) bad |= KVBUF_DEVERR_ACCEPT;
+        // ancestor mask of draft `tid`: follow the parents (at most n steps)
+        uint32_t anc = 0;
+        int cur = (tid < n && !bad_par) ? tid : -1;
+        for (int step = 0; step < n; ++step) {
+            if (cur >= 0) anc |= 1u << cur;
+            const int up = __shfl(par, cur >= 0 ? cur : 0, 64);
+            cur = (cur > 0 && up >= 0 && up < cur) ? up : -1;
+        }
+        if (tid < n) s_anc[tid] = anc;
         if (tid == 0) {
             s_bad = bad;
             s_p = p0;
@@ -208,7 +226,19 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
     // ---- 3. cumulative log-gates (wave 0), decay weights of S0 -----------------
     if (tid < 64) {
         if constexpr (GATED) {
+            const float graw_d = tid < n ? bl[p + tid] : 0.0f;  // log-gate of draft tid
             gate_prefix(bl, T, tid, [&](int i) { return bl[i]; });
+            if (P.parent) {
+                // tree drafts: the decay of draft d runs along its own path,
+                // b_{p+d} = b_{p-1} + the log-gates of d and its ancestors
+                const uint32_t anc = tid < n ? s_anc[tid] : 0u;
+                float acc = p > 0 ? bl[p - 1] : 0.0f;
+                for (int e = 0; e < n; ++e) {
+                    const float ge = __shfl(graw_d, e, 64);
+                    if ((anc >> e) & 1u) acc += ge;
+                }
+                if (tid < n) bl[p + tid] = acc;
+            }
         } else {
             for (int i = tid; i < T; i += 64) bl[i] = 0.0f;
         }
@@ -243,15 +273,18 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
         for (int d = 0; d < NQ; ++d) {
             if (d < n) {
                 const int t = p + d;
+                // the buffered context, then the new tokens on d's path
+                const uint32_t anc = s_anc[d];
+                const bool seen = i < p || (i < T && ((anc >> (i - p)) & 1u));
                 RawChunk<IO, E> qc;
                 qc.load(qr + d * DK + cl * E);
                 const float dot = group16_sum(chunk_dot(qc, kc));
-                const float wq = (i <= t) ? (GATED ? exp_gate(bl[t] - bl[ic]) : 1.0f) * P.scale * dot : 0.f;
+                const float wq = seen ? (GATED ? exp_gate(bl[t] - bl[ic]) : 1.0f) * P.scale * dot : 0.f;
                 if (cl == 0 && i < T) cq[d * ldc + i] = wq;
                 if constexpr (DELTA) {
                     qc.load(kdr + d * DK + cl * E);
                     const float dk = group16_sum(chunk_dot(qc, kc));
-                    const float wk = (i < t) ? (GATED ? exp_gate(bl[t] - bl[ic]) : 1.0f) * dk : 0.f;
+                    const float wk = (seen && i != t) ? (GATED ? exp_gate(bl[t] - bl[ic]) : 1.0f) * dk : 0.f;
                     if (cl == 0 && i < T) ck[d * ldc + i] = wk;
                 }
             }
@@ -463,7 +496,8 @@ int chunk_fold_limit(int rule, int d, int io, int n, int cap) {
 }
 
 hipError_t launch_chunk(const TileParams& p, int rule, int d, int io, int batch, hipStream_t s) {
-    if (decode_eligible(rule, p.n, p.block_size * p.blocks_per_req)) return launch_decode(p, rule, d, io, batch, s);
+    if (!p.parent && decode_eligible(rule, p.n, p.block_size * p.blocks_per_req))
+        return launch_decode(p, rule, d, io, batch, s);
     return io == KVBUF_BF16 ? launch_chunk_r<bf16_bits>(p, rule, d, batch, s)
                             : launch_chunk_r<float>(p, rule, d, batch, s);
 }

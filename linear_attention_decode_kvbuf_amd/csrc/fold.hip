@@ -36,6 +36,30 @@ __host__ __device__ inline int fold_lds_floats(int DK, int DV, int cap, int fc, 
     return 2 * ((cap + 3) & ~3) + 2 * fold_stage_floats(DK, DV, fc) + (ch ? DK : 4);
 }
 
+// Copies rows src[k] -> dst[k], k < a (U 16-byte units per row) with one
+// wave: all loads first (at most four per lane, held in named registers),
+// then the stores in the same order.
+template <int U>
+__device__ __forceinline__ void move_rows(char* plane, const uint32_t* src, const uint32_t* dst, int a,
+                                          int lane) {
+    constexpr int N = (kMaxDrafts * U + 63) / 64;
+    static_assert(N <= 4, "rows of at most 512 bytes");
+    auto at = [&](const uint32_t* rows, int r) {
+        const int u = lane + 64 * r;
+        return reinterpret_cast<uint4*>(plane + (static_cast<size_t>(rows[u / U]) * U + u % U) * 16);
+    };
+    auto live = [&](int r) { return (lane + 64 * r) / U < a; };
+    uint4 v0{}, v1{}, v2{}, v3{};
+    if (live(0)) v0 = *at(src, 0);
+    if (N > 1 && live(1)) v1 = *at(src, 1);
+    if (N > 2 && live(2)) v2 = *at(src, 2);
+    if (N > 3 && live(3)) v3 = *at(src, 3);
+    if (live(0)) *at(dst, 0) = v0;
+    if (N > 1 && live(1)) *at(dst, 1) = v1;
+    if (N > 2 && live(2)) *at(dst, 2) = v2;
+    if (N > 3 && live(3)) *at(dst, 3) = v3;
+}
+
 // MULTI: the fold may take more than one staging round (then the token wave
 // stages round r+1 while the state waves apply round r).  Without it every
 // position is staged before the state loads are issued, which keeps the
@@ -53,6 +77,9 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void fold_kernel(TileParam
     extern __shared__ float lds[];
     __shared__ unsigned s_bad;
     __shared__ int s_T, s_fold;
+    // tree commit: pool rows of the k-th kept draft before (src) and after
+    // (dst) its move to buffer position p + k
+    __shared__ uint32_t s_src[kMaxDrafts], s_dst[kMaxDrafts];
 
     const TileIndex ti = tile_index(P);
     const int b = ti.b;
@@ -69,13 +96,30 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void fold_kernel(TileParam
     // only reader -- advances it in place (flush, commit) before the barrier.
     const int slot = P.slot[b];
     const bool has_state = slot >= 0;
+    const bool tree = P.leaf != nullptr;
+    int a = 0;  // drafts kept
     if (token_wave) {
         const int p = P.occ[meta_index(P, b, h)];
         unsigned bad = 0;
-        int a = 0;
-        if (P.mode == MODE_COMMIT) {
+        uint32_t path = 0;  // tree commit: bit d set = draft d is kept
+        if (P.mode == MODE_COMMIT && !tree) {
             a = P.accepted[b];
             if (a < 0 || a > P.n) bad |= KVBUF_DEVERR_ACCEPT;
+        } else if (P.mode == MODE_COMMIT) {
+            // the path from the root to the leaf, walked up through the parents
+            const int n = P.n;
+            const int leaf = P.leaf[b];
+            const int par = lane < n ? P.parent[static_cast<size_t>(b) * n + lane] : -1;
+            if (__ballot(lane < n && (par < -1 || par >= lane)) || leaf < -1 || leaf >= n)
+                bad |= KVBUF_DEVERR_ACCEPT;
+            int cur = bad ? -1 : leaf;
+            for (int step = 0; step < n; ++step) {
+                if (cur >= 0) path |= 1u << cur;
+                const int up = __shfl(par, cur >= 0 ? cur : 0, 64);
+                cur = (cur > 0 && up < cur) ? up : -1;
+            }
+            a = __popc(path);
+            if (p + n > cap) bad |= KVBUF_DEVERR_OVERFLOW;  // the drafts sit at p .. p + n - 1
         }
         const int pn = (p < 0 || p > cap) ? -1 : p + a;  // occupancy after the kept drafts
         if (pn < 0 || pn > cap) bad |= KVBUF_DEVERR_OVERFLOW;
@@ -83,7 +127,26 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void fold_kernel(TileParam
         const bool fold0 = !materialize && has_state && P.m > 0 && pn >= P.m &&
                            (P.mode == MODE_FLUSH || P.fuse);
         const int T0 = materialize ? p : (fold0 ? P.m : 0);  // positions applied
-        bad |= stage_row(P, b, h, T0, reinterpret_cast<uint32_t*>(lds), lane);
+        uint32_t* pos = reinterpret_cast<uint32_t*>(lds);
+        bad |= stage_row(P, b, h, (tree && pn >= 0) ? max(T0, p + P.n) : T0, pos, lane);
+        if (tree && !bad) {
+            // kept draft d (rank k on the path) moves from position p + d to
+            // p + k: the fold below reads it from its draft row, and its rows
+            // are copied once the fold's reads are done
+            const bool kept = lane < P.n && ((path >> lane) & 1u);
+            const int k = kept ? __popc(path & ((1u << lane) - 1u)) : 0;
+            uint32_t src = 0, dst = 0;
+            if (kept) {
+                src = pos[p + lane];
+                dst = pos[p + k];
+            }
+            __builtin_amdgcn_wave_barrier();
+            if (kept) {
+                pos[p + k] = src;
+                s_src[k] = src;
+                s_dst[k] = dst;
+            }
+        }
         if (lane == 0) {
             s_bad = bad;
             s_T = T0;
@@ -99,7 +162,27 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void fold_kernel(TileParam
     }
     const bool fold = s_fold != 0;
     const int T = s_T;
-    if (!materialize && !fold) return;  // no state change for this tile
+
+    // Token wave, tree commit: copy the kept drafts' key, value and gate rows
+    // to their new positions.  Every load is issued before the first store and
+    // a row's destination is never the source of a later row (kept draft k
+    // comes from position p + d with d >= k), so no row is overwritten before
+    // it is read.
+    auto move_kept = [&]() __attribute__((always_inline)) {
+        if (!tree || a == 0) return;
+        move_rows<DK * sizeof(IO) / 16>(static_cast<char*>(P.key), s_src, s_dst, a, lane);
+        move_rows<DV * sizeof(XIO) / 16>(static_cast<char*>(P.value), s_src, s_dst, a, lane);
+        if constexpr (CH) {
+            move_rows<DK * 4 / 16>(reinterpret_cast<char*>(P.gate), s_src, s_dst, a, lane);
+        } else if constexpr (SGATE) {
+            const float gk = lane < a ? P.gate[s_src[lane]] : 0.0f;
+            if (lane < a) P.gate[s_dst[lane]] = gk;
+        }
+    };
+    if (!materialize && !fold) {  // no state change for this tile
+        if (token_wave) move_kept();
+        return;
+    }
 
     const int fc = P.fold_chunk;
     float* bl = lds + ((cap + 3) & ~3);
@@ -165,6 +248,7 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void fold_kernel(TileParam
             if (lane == 0) *e0p = (SGATE && T > 0) ? exp_gate(bl[T - 1]) : 1.0f;
         }
         if (T > 0) stage(0);
+        if (!MULTI) move_kept();  // the fold's rows are staged
     }
     f4 s[RPT];
     if (!token_wave)
@@ -205,6 +289,7 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void fold_kernel(TileParam
             }
             __syncthreads();
         }
+        if (token_wave) move_kept();  // every round is staged
     }
     if (!token_wave) {
         float* dst = materialize ? P.states_out + (static_cast<size_t>(b) * P.H + h) * DK * DV

@@ -45,6 +45,8 @@ struct TileParams {
     float* out;
     const int32_t* accepted;
     float* states_out;
+    const int32_t* parent;  // tree drafts: [B][n] parent of each draft (-1 = the buffer), else null
+    const int32_t* leaf;    // tree commit: [B] accepted leaf (-1 = none), else null
 };
 
 // Launchers: each picks the template instance for (rule, d, io dtype) and

@@ -24,7 +24,7 @@ from dataclasses import dataclass, replace
 import numpy as np
 
 # Stream ids of the seed tuple.
-Q, K, V, G, BETA, ACCEPT, LENGTHS, STATE, PERM, SLOTS = range(1, 11)
+Q, K, V, G, BETA, ACCEPT, LENGTHS, STATE, PERM, SLOTS, TREE = range(1, 12)
 
 
 def rng(workload: int, step: int, stream: int) -> np.random.Generator:
@@ -144,6 +144,17 @@ def slot_permutation(w: Workload, nslots: int) -> np.ndarray:
 def accepted_lengths(w: Workload, call: int, B: int, n: int) -> np.ndarray:
     """Accepted-prefix lengths a ~ U{0..n}, one per request, for one verify call."""
     return rng(w.ident, call, ACCEPT).integers(0, n + 1, size=B).astype(np.int32)
+
+
+def draft_tree(w: Workload, call: int, B: int, n: int):
+    """A random tree of n drafts per request for one verify call and the leaf
+    whose root-to-leaf path is accepted: parent[b][d] ~ U{-1 .. d-1} (-1 = the
+    draft follows the buffer), leaf[b] ~ U{-1 .. n-1} (-1 = none kept).
+    Returns (parent [B, n], leaf [B]) int32."""
+    r = rng(w.ident, call, TREE)
+    parent = np.floor(r.random((B, n)) * (np.arange(n) + 1)).astype(np.int32) - 1
+    leaf = r.integers(-1, n, size=B).astype(np.int32)
+    return parent, leaf
 
 
 def short_lengths(w: Workload, draw: int, count: int) -> np.ndarray:

@@ -184,6 +184,51 @@ class Run:
         self._after(folded)
         return out
 
+    def verify_tree_commit(self, call, parent, leaf):
+        """One tree verify (parent [B, n]) per request, then keep the path from
+        the root to leaf[b].  Each draft's reference output is the recurrence
+        run over its root-to-node path."""
+        w = self.w
+        n = parent.shape[1]
+        inp = self.inputs(call, n=n, stream_base=200)
+        par = torch.from_numpy(np.ascontiguousarray(parent, np.int32)).to(self.dev)
+        out = self.kv.verify_tree(par, inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"])
+        for b in range(w.B):
+            self.model.verify(b, [("t", call, b, d) for d in range(n)])
+        q, k, v, g, beta = (self._sampled(inp[x], drafts=True) for x in ("q", "k", "v", "g", "beta"))
+        o_gpu = self._sampled(out, drafts=True)  # [ns, n, d]
+
+        def path_to(b, d):
+            path = []
+            while d >= 0:
+                path.append(d)
+                d = int(parent[b][d])
+            return path[::-1]
+
+        for j, (b, h) in enumerate(self.sample):
+            for dd in range(n):
+                self.tokens[(("t", call, b, dd), j)] = (k[j, dd].copy(), v[j, dd].copy(),
+                                                        None if g is None else np.array(g[j, dd], np.float32))
+            sel = lambda x, path: None if x is None else np.swapaxes(x[j:j + 1, path], 0, 1)  # [len, 1, ...]
+            for dd in range(n):
+                path = path_to(b, dd)
+                o_ref, _ = oracle.recurrent(w.rule, self.S[j:j + 1], sel(q, path), sel(k, path), sel(v, path),
+                                            sel(g, path), sel(beta, path))
+                err = rel_err_tiles(o_gpu[j, dd][None], o_ref[-1], axes=-1)
+                self.max_out = max(self.max_out, err)
+                assert err <= TOL_OUT, "tree verify %d tile %s draft %d: output error %.3e" % (call, (b, h), dd, err)
+            path = path_to(b, int(leaf[b]))
+            if path:
+                _, S1 = oracle.recurrent(w.rule, self.S[j:j + 1], sel(q, path), sel(k, path), sel(v, path),
+                                         sel(g, path), sel(beta, path))
+                self.S[j] = S1[0]
+        lf = torch.from_numpy(np.ascontiguousarray(leaf, np.int32)).to(self.dev)
+        self.kv.commit_tree(par, lf)
+        eager = self.flush_policy == kb.FLUSH_EAGER
+        folded = {b for b in range(w.B) if self.model.commit_path(b, path_to(b, int(leaf[b])), eager=eager)}
+        self._after(folded)
+        return out
+
     def retire_and_admit(self, b):
         """Request b ends; a new buffer-only request takes its batch entry with
         fresh blocks from the free list (the old ones go to its end)."""

@@ -140,3 +140,25 @@ def test_channel_rule_limits(lib):
     long_rows = _layout(rule=kb.RULE_CHANNEL, block_size=4, blocks_per_req=17, num_blocks=40)
     assert _decode(long_rows) == kb.EUNSUPPORTED
     assert kb.kvbuf_direct(long_rows, POOLS, BATCH, FAKE, FAKE, FAKE, FAKE, None, FAKE, 0, False) == kb.EUNSUPPORTED
+
+
+def test_tree_entry_validation(lib):
+    """Tree drafts need a buffer (m > 0), 1 <= n <= 8, parent (and leaf)
+    arrays, and one of the rules with a scalar or no gate."""
+    L = _layout()
+    vt = lambda L, n, parent=FAKE: kb.kvbuf_verify_tree(L, POOLS, BATCH, n, parent, FAKE, FAKE, FAKE, FAKE, None,
+                                                        FAKE, 0, False)
+    ct = lambda L, n, parent=FAKE, leaf=FAKE: kb.kvbuf_commit_tree(L, POOLS, BATCH, n, parent, leaf, 0, False)
+    assert vt(L, 2, parent=None) == kb.EINVAL
+    assert vt(L, 0) == kb.EUNSUPPORTED
+    assert vt(L, 9) == kb.EUNSUPPORTED
+    assert vt(_layout(m=0), 2) == kb.EUNSUPPORTED
+    assert vt(_layout(rule=kb.RULE_CHANNEL), 1) == kb.EUNSUPPORTED
+    assert ct(L, 2, parent=None) == kb.EINVAL
+    assert ct(L, 2, leaf=None) == kb.EINVAL
+    assert ct(L, 0) == kb.EUNSUPPORTED
+    assert ct(L, 9) == kb.EUNSUPPORTED
+    assert ct(_layout(m=0), 2) == kb.EUNSUPPORTED
+    assert ct(_layout(rule=kb.RULE_CHANNEL), 2) == kb.EUNSUPPORTED
+    empty = kb.Batch(0, None, None, None, None)
+    assert kb.kvbuf_commit_tree(L, POOLS, empty, 2, FAKE, FAKE, 0, False) == kb.OK

@@ -125,6 +125,79 @@ def test_verify_commit_small(rule, n):
         run.check_bookkeeping()
 
 
+@pytest.mark.parametrize("rule,d,io", [(0, 64, "bf16"), (1, 128, "bf16"), (2, 64, "bf16"), (1, 16, "f32"),
+                                       (2, 128, "f32")])
+@pytest.mark.parametrize("n", [1, 5, 8])
+def test_tree_verify_commit(rule, d, io, n):
+    """Random draft trees: every draft's output is the recurrence over its
+    root-to-node path; committing a path moves its rows to consecutive
+    positions (pool bits and bookkeeping exact) and, when the buffer fills,
+    folds them (states within tolerance)."""
+    w = synth.workload(1, B=6, H=2, dk=d, dv=d, m=8, block_size=4, blocks_per_req=5, steps=8,
+                       rule=rule, io=io, state_std=0.02)
+    _say("tree", w, "n", n)
+    run = Run(w)
+    t = 0
+    for call in range(8):
+        run.decode(t)
+        t += 1
+        parent, leaf = synth.draft_tree(w, call, w.B, n)
+        run.verify_tree_commit(call, parent, leaf)
+        run.check_effective_states()
+        run.check_pool()
+        run.check_bookkeeping()
+
+
+@pytest.mark.parametrize("flush", [kb.FLUSH_EAGER, kb.FLUSH_DEFERRED])
+def test_tree_chain_matches_verify(flush):
+    """A chain-shaped tree gives kvbuf_verify's outputs, and committing its
+    first a drafts leaves the same pools as kvbuf_commit(a)."""
+    w = synth.workload(1, B=4, H=2, dk=128, dv=128, m=8, block_size=4, blocks_per_req=4, steps=4,
+                       rule=1, io="bf16", state_std=0.02)
+    runs = [Run(w, flush=flush), Run(w, flush=flush)]
+    n = 6
+    chain = np.tile(np.arange(-1, n - 1, dtype=np.int32), (w.B, 1))
+    for call in range(4):
+        acc = synth.accepted_lengths(w, call, w.B, n)
+        o_chain = runs[0].verify_commit(call, n, acc)
+        inp = runs[1].inputs(call, n=n, stream_base=100)
+        par = torch.from_numpy(chain).to(runs[1].dev)
+        o_tree = runs[1].kv.verify_tree(par, inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"])
+        runs[1].kv.commit_tree(par, torch.from_numpy(acc - 1).to(runs[1].dev))
+        torch.cuda.synchronize()
+        # the tree path sums the drafts' gates one by one, the chain path by a
+        # parallel scan: equal up to rounding
+        torch.testing.assert_close(o_tree, o_chain, rtol=0, atol=1e-5 * float(o_chain.abs().max()))
+        for name in ("state", "key", "value", "gate", "block_table", "occupancy"):
+            assert torch.equal(getattr(runs[0].kv, name), getattr(runs[1].kv, name)), name
+        if flush == kb.FLUSH_DEFERRED:
+            runs[0].flush()
+            runs[1].kv.flush()
+
+
+def test_tree_invalid_parent_or_leaf_skips_the_tile():
+    """A parent outside {-1 .. d-1} or a leaf outside {-1 .. n-1} sets the
+    draft-range error bit and leaves that request untouched."""
+    w = synth.workload(1, B=3, H=2, dk=64, dv=64, m=4, block_size=4, blocks_per_req=3, steps=1,
+                       rule=1, io="bf16", state_std=0.02)
+    run = Run(w)
+    inp = run.inputs(0, n=3, stream_base=200)
+    parent = torch.tensor([[-1, 0, 1], [-1, 2, 0], [-1, -1, 0]], dtype=torch.int32, device=run.dev)
+    out = torch.full((w.B, 3, w.H, w.dk), 7.0, device=run.dev)
+    run.kv.verify_tree(parent, inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], out=out)
+    torch.cuda.synchronize()
+    assert int(run.kv.error.item()) == kb.DEVERR_ACCEPT
+    assert torch.all(out[1] == 7.0) and not torch.all(out[0] == 7.0)
+    run.kv.error.zero_()
+    good = torch.tensor([[-1, 0, 1], [-1, 0, 0], [-1, -1, 0]], dtype=torch.int32, device=run.dev)
+    occ0 = run.kv.occupancy.clone()
+    run.kv.commit_tree(good, torch.tensor([2, 3, -2], dtype=torch.int32, device=run.dev))
+    torch.cuda.synchronize()
+    assert int(run.kv.error.item()) == kb.DEVERR_ACCEPT
+    occ = run.kv.occupancy
+    assert torch.equal(occ[1:], occ0[1:]) and torch.all(occ[0] == occ0[0] + 3)
+
+
 @pytest.mark.parametrize("rule", [0, 1, 2])
 def test_staggered_occupancies(rule):
     """Commits of different lengths desynchronise the requests' occupancies,
