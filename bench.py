@@ -364,6 +364,7 @@ def verify_leg(kb, synth, torch, dev, args):
         res = {"verify_ms": ver, "commit_ms": com,
                "verify_hbm_gbps": vbytes / (ver * 1e-3) / 1e9,
                "accepted_tokens_per_s": accepted / ((ver + com) * 1e-3)}
+        res["tree"] = tree_verify(kb, synth, torch, kv, w, n, drafts, obuf, vbytes)
         del kv
         res["recurrent_baseline"] = verify_baseline(kb, synth, torch, dev, w, n, drafts, accs)
         # state memory per request: KVBuffer keeps one state and a buffer of
@@ -377,6 +378,44 @@ def verify_leg(kb, synth, torch, dev, args):
                                                  "requests_ratio": base / kvb}
         out["n%d" % n] = res
     return out
+
+
+def tree_verify(kb, synth, torch, kv, w, n, drafts, obuf, vbytes):
+    """The same drafts arranged as random trees (kvbuf_verify_tree: each draft
+    attends to its ancestors only, decays along its path), then
+    kvbuf_commit_tree of a random root-to-leaf path per request."""
+    dev = obuf.device
+    trees = [synth.draft_tree(w, c, w.B, n) for c in range(4)]
+    par = [torch.from_numpy(p).to(dev) for p, _ in trees]
+    leaf = [torch.from_numpy(lf).to(dev) for _, lf in trees]
+
+    def depth(p, d):
+        k = 0
+        while d >= 0:
+            k, d = k + 1, int(p[d])
+        return k
+
+    kept = [sum(depth(p[b], int(lf[b])) for b in range(w.B)) for p, lf in trees]
+
+    def call(c):
+        d = drafts[c % 4]
+        return [lambda: kv.verify_tree(par[c % 4], d["q"], d["k"], d["v"], d["g"], out=obuf),
+                lambda: kv.commit_tree(par[c % 4], leaf[c % 4])]
+
+    for c in range(4):
+        for f in call(c):
+            f()
+    launches = []
+    for c in range(8):
+        launches += call(c)
+    per = per_launch_ms(torch, launches, 20)
+    torch.cuda.synchronize()
+    assert int(kv.error.item()) == 0
+    ver = sum(per[0::2]) / 8
+    com = sum(per[1::2]) / 8
+    accepted = sum(kept) / 4
+    return {"verify_ms": ver, "commit_ms": com, "verify_hbm_gbps": vbytes / (ver * 1e-3) / 1e9,
+            "accepted_tokens_per_s": accepted / ((ver + com) * 1e-3)}
 
 
 def verify_baseline(kb, synth, torch, dev, w, n, drafts, accs):
