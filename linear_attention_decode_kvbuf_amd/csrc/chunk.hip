@@ -487,7 +487,7 @@ hipError_t launch_chunk_r(const TileParams& p, int rule, int d, int batch, hipSt
 // that kernel stages (the one-token kernel: an LDS budget; this kernel: the
 // first staging pass of NT / 16 positions); otherwise a fold launch follows.
 int chunk_fold_limit(int rule, int d, int io, int n, int cap) {
-    if (decode_eligible(rule, n, cap)) return decode_fold_limit(d, io);
+    if (decode_eligible(rule, n, cap)) return decode_fold_limit(rule, d, io);
     switch (d) {
         case 16: return Geo<16, 16>::NT / 16;
         case 64: return Geo<64, 64>::NT / 16;

@@ -39,10 +39,11 @@ __host__ __device__ inline int round4d(int x) { return (x + 3) & ~3; }
 
 // LDS layout in 4-byte words.  mf = positions staged for a fold in this
 // launch (0: it never folds); io = bytes per key / value element; for the
-// per-channel rule, cap rows of gates (turned into per-channel suffix sums)
-// and the cumulative gate of the new token.
+// per-channel rule, cap rows of gates (turned into per-channel suffix sums),
+// the cumulative gate of the new token and the fold's per-row state decay;
+// its fold keys are staged as fp32, already multiplied by their decays.
 struct DecodeLds {
-    int obuf, red, fw, kr, vr, dg, bt, total;
+    int obuf, red, fw, kr, vr, dg, bt, qd, fr, total;
 };
 __host__ __device__ inline DecodeLds decode_lds(int DK, int DV, int RG, int mf, int io, bool ch, int cap) {
     DecodeLds L;
@@ -50,26 +51,14 @@ __host__ __device__ inline DecodeLds decode_lds(int DK, int DV, int RG, int mf, 
     L.obuf = o; o += DV;                        // weighted sum of buffered values (token wave)
     L.red = o; o += RG * DV;                    // S0^T q partials, one row per row group
     L.fw = o; o += round4d(mf);                 // fold weights e^{b_{m-1} - b_i}
-    L.kr = o; o += round4d(mf * DK * io / 4);   // keys to fold (raw bits)
+    L.kr = o; o += round4d(mf * DK * (ch ? 4 : io) / 4);  // keys to fold (raw bits; weighted fp32)
     L.vr = o; o += round4d(mf * DV * io / 4);   // values to fold (raw bits)
     L.dg = o; o += ch ? cap * DK : 0;           // per-channel rule: B_t - B_i per position (fp32)
-    L.bt = o; o += ch ? DK : 0;                 // per-channel rule: B_t
+    L.bt = o; o += ch ? DK : 0;                 // per-channel rule: e^{B_t}
+    L.qd = o; o += ch ? DK : 0;                 // per-channel rule: e^{B_t} q_t
+    L.fr = o; o += ch ? DK : 0;                 // per-channel rule: e^{B_{m-1} - B_t} per state row
     L.total = o;
     return L;
-}
-
-// q . k over a lane's E channels with per-channel weights e^{d[e]}.
-template <typename T, int E>
-__device__ __forceinline__ float chunk_dot_decayed(const RawChunk<T, E>& a, const RawChunk<T, E>& b,
-                                                   const float* d) {
-    float x[E], y[E], dd[E];
-    a.to_float(x);
-    b.to_float(y);
-    loadE<E>(d, dd);
-    float acc = 0.f;
-#pragma unroll
-    for (int e = 0; e < E; ++e) acc += (x[e] * y[e]) * exp_gate(dd[e]);
-    return acc;
 }
 
 template <int RULE, int DK, int DV, typename IO>
@@ -77,8 +66,10 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void decode_kernel(TilePar
     using G = Geo<DK, DV>;
     constexpr int NT = G::NT, TPR = G::TPR, RG = G::RG, RPT = G::RPT;
     constexpr int E = DK / 16, EV = DV / 16;
-    constexpr int NB = 4;  // rounds of 4 positions whose loads are in flight together
     constexpr bool CH = RULE == KVBUF_RULE_CHANNEL;   // one gate per key channel
+    // rounds of 4 positions whose loads are in flight together (the
+    // per-channel rule's decayed dots need more registers per round)
+    constexpr int NB = CH ? 2 : 4;
     constexpr bool GATED = RULE == KVBUF_RULE_GATED;  // one gate per token
     constexpr int CPL = (DK + 63) / 64;               // key channels per token-wave lane
 
@@ -100,6 +91,9 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void decode_kernel(TilePar
                                    P.block_size * P.blocks_per_req);
     float* dg = lds + L.dg;
     float* btv = lds + L.bt;
+    float* qdv = lds + L.qd;
+    float* frow = lds + L.fr;
+    float* krf = lds + L.kr;  // per-channel rule: weighted fp32 fold keys
     float* obuf = lds + L.obuf;
     float* red = lds + L.red;
     float* fw = lds + L.fw;
@@ -190,7 +184,10 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void decode_kernel(TilePar
                         dg[i * DK + ch] = run;
                         run += gi;
                     }
-                    btv[ch] = run;
+                    const float ebt = exp_gate(run);
+                    btv[ch] = ebt;                              // e^{B_t}
+                    qdv[ch] = load1(qin + ch) * ebt;            // e^{B_t} q
+                    if (fold) frow[ch] = exp_gate(-dg[(P.m - 1) * DK + ch]);  // e^{B_{m-1} - B_t}
                 }
             }
         }
@@ -217,7 +214,23 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void decode_kernel(TilePar
                 const int i = i0 + 4 * r + gl;
                 float dot;
                 if constexpr (CH) {
-                    dot = group16_sum(chunk_dot_decayed(qc, kc[r], dg + (i < Tl ? i : 0) * DK + cl * E));
+                    // sum_r q[r] (k_i[r] e^{B_t[r] - B_i[r]}); the decayed key is
+                    // also the fold's key, up to the row factor e^{B_{m-1} - B_t}
+                    float qf[E], kf[E], dd[E];
+                    qc.to_float(qf);
+                    kc[r].to_float(kf);
+                    loadE<E>(dg + (i < Tl ? i : 0) * DK + cl * E, dd);
+                    float acc = 0.f;
+#pragma unroll
+                    for (int e = 0; e < E; ++e) {
+                        kf[e] *= exp_gate(dd[e]);
+                        acc += qf[e] * kf[e];
+                    }
+                    dot = group16_sum(acc);
+                    if (fold && i < P.m) {
+#pragma unroll
+                        for (int e = 0; e < E; ++e) krf[i * DK + cl * E + e] = kf[e];
+                    }
                 } else {
                     dot = group16_sum(chunk_dot(qc, kc[r]));
                 }
@@ -228,7 +241,7 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void decode_kernel(TilePar
 #pragma unroll
                 for (int e = 0; e < EV; ++e) ob[e] += w * vf[e];
                 if (fold && i < P.m) {
-                    kc[r].store(krs + i * DK + cl * E);
+                    if constexpr (!CH) kc[r].store(krs + i * DK + cl * E);
                     vc[r].store(vrs + i * DV + cl * EV);
                 }
                 if (i == pc && i < Tl) {  // append the new token to the pool
@@ -274,7 +287,7 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void decode_kernel(TilePar
     f4 s[RPT];
     RawChunk<IO, RPT> qrow;
     if (!token_wave) {
-        qrow.load(qin + rg * RPT);
+        if constexpr (!CH) qrow.load(qin + rg * RPT);
         const bool present = slot >= 0 && slot < P.num_slots;
         load_tile<RPT, DK, DV>(s, present ? P.state + (static_cast<size_t>(slot) * P.H + h) * DK * DV : P.state,
                                present, rg, c0);
@@ -292,10 +305,10 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void decode_kernel(TilePar
         __syncthreads();
         if (!token_wave) {
             float qf[RPT];
-            qrow.to_float(qf);
+            loadE<RPT>(qdv + rg * RPT, qf);
             f4 sa = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int j = 0; j < RPT; ++j) sa += s[j] * (qf[j] * exp_gate(btv[rg * RPT + j]));
+            for (int j = 0; j < RPT; ++j) sa += s[j] * qf[j];
             *reinterpret_cast<f4*>(red + rg * DV + c0) = sa;
         }
     }
@@ -316,20 +329,19 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void decode_kernel(TilePar
     // ---- eager fold: the buffer reached m tokens ---------------------------------
     if (s_fold && !token_wave) {
         if constexpr (CH) {
-            // decays relative to position m-1: B_{m-1} - B_i = dg[i] - dg[m-1]
-            const float* dm = dg + (P.m - 1) * DK + rg * RPT;
+            // e^{B_{m-1} - B_t} (e^{B_t} S0 + sum_i k_i e^{B_t - B_i} v_i^T), row by
+            // row; the staged keys carry their decays e^{B_t - B_i}
 #pragma unroll
-            for (int j = 0; j < RPT; ++j) s[j] *= exp_gate(btv[rg * RPT + j] - dm[j]);
+            for (int j = 0; j < RPT; ++j) s[j] *= btv[rg * RPT + j];
             for (int ii = 0; ii < P.m; ++ii) {
                 const f4 x = load4(vrs + ii * DV + c0);
-                RawChunk<IO, RPT> krow;
                 float kf[RPT];
-                krow.load(krs + ii * DK + rg * RPT);
-                krow.to_float(kf);
-                const float* di = dg + ii * DK + rg * RPT;
+                loadE<RPT>(krf + ii * DK + rg * RPT, kf);
 #pragma unroll
-                for (int j = 0; j < RPT; ++j) s[j] += (kf[j] * exp_gate(di[j] - dm[j])) * x;
+                for (int j = 0; j < RPT; ++j) s[j] += kf[j] * x;
             }
+#pragma unroll
+            for (int j = 0; j < RPT; ++j) s[j] *= frow[rg * RPT + j];
         } else {
             const float e0 = s_e0;
 #pragma unroll
@@ -373,9 +385,11 @@ hipError_t launch_decode_d(const TileParams& p, int d, int batch, hipStream_t s)
 }  // namespace
 
 // Largest m a decode launch of this kernel folds itself: the keys and values
-// of the m positions are staged in LDS (at most 32 KiB of them).
-int decode_fold_limit(int d, int io) {
-    const int bytes_per_pos = 2 * d * (io == KVBUF_BF16 ? 2 : 4);
+// of the m positions are staged in LDS (at most 32 KiB of them; fp32 keys for
+// the per-channel rule).
+int decode_fold_limit(int rule, int d, int io) {
+    const int e = io == KVBUF_BF16 ? 2 : 4;
+    const int bytes_per_pos = d * e + d * (rule == KVBUF_RULE_CHANNEL ? 4 : e);
     return 32768 / bytes_per_pos;
 }
 

@@ -57,7 +57,7 @@ struct TileParams {
 hipError_t launch_chunk(const TileParams& p, int rule, int d, int io, int batch, hipStream_t s);
 hipError_t launch_decode(const TileParams& p, int rule, int d, int io, int batch, hipStream_t s);
 bool decode_eligible(int rule, int n, int cap);
-int decode_fold_limit(int d, int io);
+int decode_fold_limit(int rule, int d, int io);
 hipError_t launch_fold(const TileParams& p, int rule, int d, int io, int batch, hipStream_t s);
 // Largest m that a decode launch of n tokens folds itself (eager policy).
 int chunk_fold_limit(int rule, int d, int io, int n, int cap);
