@@ -66,7 +66,8 @@ __host__ __device__ inline ChunkLds chunk_lds(int rule, int DK, int DV, int NQ, 
     return L;
 }
 
-template <int RULE, int DK, int DV, int NQ, typename IO>
+// TREE: the new tokens are tree drafts (parent array); otherwise a chain.
+template <int RULE, int DK, int DV, int NQ, typename IO, bool TREE>
 __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) {
     using G = Geo<DK, DV>;
     constexpr int NT = G::NT, TPR = G::TPR, RG = G::RG, RPT = G::RPT;
@@ -80,11 +81,10 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
     extern __shared__ float lds[];
     __shared__ unsigned s_bad;
     __shared__ int s_p;
-    // New token d of this call attends to position p + e iff bit e of s_anc[d]
-    // is set: every e <= d for a chain of drafts (and the one token of a
-    // decode); d and its ancestors for a tree of drafts (parent -1 = the
-    // buffered context).
-    __shared__ uint32_t s_anc[kMaxDrafts];
+    // Tree drafts: draft d attends to position p + e iff bit e of s_anc[d] is
+    // set -- d and its ancestors (parent -1 = the buffered context).  A chain
+    // (and the one token of a decode) attends to every e <= d.
+    __shared__ uint32_t s_anc[TREE ? kMaxDrafts : 1];
 
     const TileIndex ti = tile_index(P);
     const int b = ti.b;
@@ -116,19 +116,20 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
         const int p0 = P.occ[meta_index(P, b, h)];
         unsigned bad = stage_row(P, b, h, (p0 < 0 || p0 > cap) ? -1 : p0 + n, spos, tid);
         if (slot >= P.num_slots) bad |= KVBUF_DEVERR_SLOT;
-        int par = tid - 1;  // a chain
-        if (P.parent && tid < n) par = P.parent[static_cast<size_t>(b) * n + tid];
-        const bool bad_par = tid < n && (par < -1 || par >= tid);  // parents precede children
-        if (__ballot(bad_par)) bad |= KVBUF_DEVERR_ACCEPT;
-        // ancestor mask of draft `tid`: follow the parents (at most n steps)
-        uint32_t anc = 0;
-        int cur = (tid < n && !bad_par) ? tid : -1;
-        for (int step = 0; step < n; ++step) {
-            if (cur >= 0) anc |= 1u << cur;
-            const int up = __shfl(par, cur >= 0 ? cur : 0, 64);
-            cur = (cur > 0 && up >= 0 && up < cur) ? up : -1;
+        if constexpr (TREE) {
+            const int par = tid < n ? P.parent[static_cast<size_t>(b) * n + tid] : -1;
+            const bool bad_par = tid < n && (par < -1 || par >= tid);  // parents precede children
+            if (__ballot(bad_par)) bad |= KVBUF_DEVERR_ACCEPT;
+            // ancestor mask of draft `tid`: follow the parents (at most n steps)
+            uint32_t anc = 0;
+            int cur = (tid < n && !bad_par) ? tid : -1;
+            for (int step = 0; step < n; ++step) {
+                if (cur >= 0) anc |= 1u << cur;
+                const int up = __shfl(par, cur >= 0 ? cur : 0, 64);
+                cur = (cur > 0 && up >= 0 && up < cur) ? up : -1;
+            }
+            if (tid < n) s_anc[tid] = anc;
         }
-        if (tid < n) s_anc[tid] = anc;
         if (tid == 0) {
             s_bad = bad;
             s_p = p0;
@@ -226,9 +227,10 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
     // ---- 3. cumulative log-gates (wave 0), decay weights of S0 -----------------
     if (tid < 64) {
         if constexpr (GATED) {
-            const float graw_d = tid < n ? bl[p + tid] : 0.0f;  // log-gate of draft tid
+            float graw_d = 0.0f;  // tree drafts: log-gate of draft tid
+            if constexpr (TREE) graw_d = tid < n ? bl[p + tid] : 0.0f;
             gate_prefix(bl, T, tid, [&](int i) { return bl[i]; });
-            if (P.parent) {
+            if constexpr (TREE) {
                 // tree drafts: the decay of draft d runs along its own path,
                 // b_{p+d} = b_{p-1} + the log-gates of d and its ancestors
                 const uint32_t anc = tid < n ? s_anc[tid] : 0u;
@@ -274,8 +276,7 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
             if (d < n) {
                 const int t = p + d;
                 // the buffered context, then the new tokens on d's path
-                const uint32_t anc = s_anc[d];
-                const bool seen = i < p || (i < T && ((anc >> (i - p)) & 1u));
+                const bool seen = TREE ? (i < p || (i < T && ((s_anc[TREE ? d : 0] >> (i - p)) & 1u))) : i <= t;
                 RawChunk<IO, E> qc;
                 qc.load(qr + d * DK + cl * E);
                 const float dot = group16_sum(chunk_dot(qc, kc));
@@ -284,7 +285,7 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
                 if constexpr (DELTA) {
                     qc.load(kdr + d * DK + cl * E);
                     const float dk = group16_sum(chunk_dot(qc, kc));
-                    const float wk = (seen && i != t) ? (GATED ? exp_gate(bl[t] - bl[ic]) : 1.0f) * dk : 0.f;
+                    const float wk = (TREE ? (seen && i != t) : i < t) ? (GATED ? exp_gate(bl[t] - bl[ic]) : 1.0f) * dk : 0.f;
                     if (cl == 0 && i < T) ck[d * ldc + i] = wk;
                 }
             }
@@ -445,8 +446,8 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
         update_meta(P, b, h, fold ? T - P.m : T, fold ? P.m / P.block_size : 0, tid);
 }
 
-template <int RULE, int D, typename IO>
-hipError_t launch_chunk_t(const TileParams& p, int batch, hipStream_t s) {
+template <int RULE, int D, typename IO, bool TREE>
+hipError_t launch_chunk_q(const TileParams& p, int batch, hipStream_t s) {
     using G = Geo<D, D>;
     const int cap = p.block_size * p.blocks_per_req;
     const int nq = p.n <= 1 ? 1 : p.n <= 2 ? 2 : p.n <= 4 ? 4 : 8;
@@ -455,12 +456,17 @@ hipError_t launch_chunk_t(const TileParams& p, int batch, hipStream_t s) {
                                                  static_cast<int>(sizeof(IO)), static_cast<int>(sizeof(XIO))).total;
     const dim3 grid(static_cast<unsigned>(batch) * p.H), block(G::NT);
     switch (nq) {
-        case 1: chunk_kernel<RULE, D, D, 1, IO><<<grid, block, lds, s>>>(p); break;
-        case 2: chunk_kernel<RULE, D, D, 2, IO><<<grid, block, lds, s>>>(p); break;
-        case 4: chunk_kernel<RULE, D, D, 4, IO><<<grid, block, lds, s>>>(p); break;
-        default: chunk_kernel<RULE, D, D, 8, IO><<<grid, block, lds, s>>>(p); break;
+        case 1: chunk_kernel<RULE, D, D, 1, IO, TREE><<<grid, block, lds, s>>>(p); break;
+        case 2: chunk_kernel<RULE, D, D, 2, IO, TREE><<<grid, block, lds, s>>>(p); break;
+        case 4: chunk_kernel<RULE, D, D, 4, IO, TREE><<<grid, block, lds, s>>>(p); break;
+        default: chunk_kernel<RULE, D, D, 8, IO, TREE><<<grid, block, lds, s>>>(p); break;
     }
     return hipGetLastError();
+}
+
+template <int RULE, int D, typename IO>
+hipError_t launch_chunk_t(const TileParams& p, int batch, hipStream_t s) {
+    return p.parent ? launch_chunk_q<RULE, D, IO, true>(p, batch, s) : launch_chunk_q<RULE, D, IO, false>(p, batch, s);
 }
 
 template <int RULE, typename IO>

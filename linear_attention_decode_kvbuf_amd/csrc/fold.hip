@@ -64,7 +64,8 @@ __device__ __forceinline__ void move_rows(char* plane, const uint32_t* src, cons
 // stages round r+1 while the state waves apply round r).  Without it every
 // position is staged before the state loads are issued, which keeps the
 // token wave's registers out of the tile's live range.
-template <int RULE, int DK, int DV, typename IO, bool MULTI>
+// TREE: a commit of a root-to-leaf path of tree drafts.
+template <int RULE, int DK, int DV, typename IO, bool MULTI, bool TREE>
 __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void fold_kernel(TileParams P) {
     using G = Geo<DK, DV>;
     constexpr int NT = G::NT, TPR = G::TPR, RPT = G::RPT;
@@ -79,7 +80,7 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void fold_kernel(TileParam
     __shared__ int s_T, s_fold;
     // tree commit: pool rows of the k-th kept draft before (src) and after
     // (dst) its move to buffer position p + k
-    __shared__ uint32_t s_src[kMaxDrafts], s_dst[kMaxDrafts];
+    __shared__ uint32_t s_src[TREE ? kMaxDrafts : 1], s_dst[TREE ? kMaxDrafts : 1];
 
     const TileIndex ti = tile_index(P);
     const int b = ti.b;
@@ -96,16 +97,16 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void fold_kernel(TileParam
     // only reader -- advances it in place (flush, commit) before the barrier.
     const int slot = P.slot[b];
     const bool has_state = slot >= 0;
-    const bool tree = P.leaf != nullptr;
+    constexpr bool tree = TREE;
     int a = 0;  // drafts kept
     if (token_wave) {
         const int p = P.occ[meta_index(P, b, h)];
         unsigned bad = 0;
         uint32_t path = 0;  // tree commit: bit d set = draft d is kept
-        if (P.mode == MODE_COMMIT && !tree) {
+        if (!tree && P.mode == MODE_COMMIT) {
             a = P.accepted[b];
             if (a < 0 || a > P.n) bad |= KVBUF_DEVERR_ACCEPT;
-        } else if (P.mode == MODE_COMMIT) {
+        } else if (tree) {
             // the path from the root to the leaf, walked up through the parents
             const int n = P.n;
             const int leaf = P.leaf[b];
@@ -169,7 +170,7 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void fold_kernel(TileParam
     // comes from position p + d with d >= k), so no row is overwritten before
     // it is read.
     auto move_kept = [&]() __attribute__((always_inline)) {
-        if (!tree || a == 0) return;
+        if (a == 0) return;
         move_rows<DK * sizeof(IO) / 16>(static_cast<char*>(P.key), s_src, s_dst, a, lane);
         move_rows<DV * sizeof(XIO) / 16>(static_cast<char*>(P.value), s_src, s_dst, a, lane);
         if constexpr (CH) {
@@ -180,7 +181,7 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void fold_kernel(TileParam
         }
     };
     if (!materialize && !fold) {  // no state change for this tile
-        if (token_wave) move_kept();
+        if (tree && token_wave) move_kept();
         return;
     }
 
@@ -248,7 +249,7 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void fold_kernel(TileParam
             if (lane == 0) *e0p = (SGATE && T > 0) ? exp_gate(bl[T - 1]) : 1.0f;
         }
         if (T > 0) stage(0);
-        if (!MULTI) move_kept();  // the fold's rows are staged
+        if (tree && !MULTI) move_kept();  // the fold's rows are staged
     }
     f4 s[RPT];
     if (!token_wave)
@@ -289,7 +290,7 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void fold_kernel(TileParam
             }
             __syncthreads();
         }
-        if (token_wave) move_kept();  // every round is staged
+        if (tree && token_wave) move_kept();  // every round is staged
     }
     if (!token_wave) {
         float* dst = materialize ? P.states_out + (static_cast<size_t>(b) * P.H + h) * DK * DV
@@ -307,10 +308,14 @@ hipError_t launch_fold_t(const TileParams& p, int batch, hipStream_t s) {
     const size_t lds = sizeof(float) * fold_lds_floats(D, D, cap, p.fold_chunk, RULE == KVBUF_RULE_CHANNEL);
     const int most = p.mode == MODE_MATERIALIZE ? cap : p.m;  // most positions one tile applies
     const dim3 grid(static_cast<unsigned>(batch) * p.H), block(G::NTHREADS);
-    if (most <= p.fold_chunk)
-        fold_kernel<RULE, D, D, IO, false><<<grid, block, lds, s>>>(p);
-    else
-        fold_kernel<RULE, D, D, IO, true><<<grid, block, lds, s>>>(p);
+    const bool tree = p.leaf != nullptr;
+    if (most <= p.fold_chunk) {
+        if (tree) fold_kernel<RULE, D, D, IO, false, true><<<grid, block, lds, s>>>(p);
+        else fold_kernel<RULE, D, D, IO, false, false><<<grid, block, lds, s>>>(p);
+    } else {
+        if (tree) fold_kernel<RULE, D, D, IO, true, true><<<grid, block, lds, s>>>(p);
+        else fold_kernel<RULE, D, D, IO, true, false><<<grid, block, lds, s>>>(p);
+    }
     return hipGetLastError();
 }
 
