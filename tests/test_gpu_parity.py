@@ -148,6 +148,28 @@ def test_tree_verify_commit(rule, d, io, n):
         run.check_bookkeeping()
 
 
+@pytest.mark.parametrize("rule", [1, 2])
+def test_tree_deferred_with_flush_and_stars(rule):
+    """Deferred policy: tree commits only append; kvbuf_flush after each call
+    folds the first m positions once the buffer holds m (leaving the rest of
+    a commit buffered behind them).  Every third call is a star (every draft
+    follows the buffer directly), whose paths keep at most one draft."""
+    w = synth.workload(1, B=5, H=2, dk=64, dv=64, m=8, block_size=4, blocks_per_req=6, steps=9,
+                       rule=rule, io="bf16", state_std=0.02)
+    run = Run(w, flush=kb.FLUSH_DEFERRED)
+    n = 6
+    for call in range(9):
+        parent, leaf = synth.draft_tree(w, call, w.B, n)
+        if call % 3 == 2:
+            parent[:] = -1
+        run.verify_tree_commit(call, parent, leaf)
+        run.check_effective_states()
+        run.flush()
+        run.check_effective_states()
+        run.check_pool()
+        run.check_bookkeeping()
+
+
 @pytest.mark.parametrize("flush", [kb.FLUSH_EAGER, kb.FLUSH_DEFERRED])
 def test_tree_chain_matches_verify(flush):
     """A chain-shaped tree gives kvbuf_verify's outputs, and committing its
