@@ -66,6 +66,99 @@ __host__ __device__ inline ChunkLds chunk_lds(int rule, int DK, int DV, int NQ, 
     return L;
 }
 
+// S0^T q for up to eight queries on the matrix cores (bf16, d_k = d_v = 128,
+// 256 threads: thread t holds rows 16 (t / 32) + j, j < 16, columns
+// 4 (t % 32) .. + 3 of the tile).  Wave w multiplies its 32 rows with
+// v_mfma_f32_16x16x16_bf16: K = 16 = four lane groups g of four rows, B[k][n]
+// = S[32w + 16 (g / 2) + 4 q + i][64 (g % 2) + 4 n + e] straight from the
+// state registers (component e of s[4q + i]), M = 16 = two column halves x
+// eight queries, A[8 h + d][k] = q_d[row of k] where g % 2 = h and 0 otherwise.
+// The fp32 state goes in as two bf16 terms, hi = bf16(S) and lo = bf16(S -
+// hi), so each product is exact and S is represented to about 2^-17 of its
+// size; the bf16 queries are exact.  The wave's partial sums over its 32 rows
+// are added (times scale e^{b_t}) into the row-group-2w slots of `red`, which
+// already hold this wave's value sums.
+template <int DK, int DV, int RG>
+__device__ __forceinline__ void state_products_mfma(const f4 (&s)[16], const bf16_bits* qr, float* red,
+                                                    const float* es, float scale, int n, int tid) {
+    typedef short s4 __attribute__((ext_vector_type(4)));
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+    const int w = tid >> 6, l = tid & 63, g = l >> 4, nn = l & 15;
+    // A operands, one per quad of rows
+    s4 a[4];
+    const int da = l & 7;
+    const bool live_a = ((g & 1) == ((l & 15) >> 3)) && da < n;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int row0 = 32 * w + 16 * (g >> 1) + 4 * q;
+        a[q] = live_a ? *reinterpret_cast<const s4*>(qr + da * DK + row0) : s4{0, 0, 0, 0};
+    }
+    f4 d[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        d[e] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const f2 x01 = {s[4 * q][e], s[4 * q + 1][e]};
+            const f2 x23 = {s[4 * q + 2][e], s[4 * q + 3][e]};
+            const uint32_t h01 = __builtin_bit_cast(uint32_t, __builtin_convertvector(x01, bf2));
+            const uint32_t h23 = __builtin_bit_cast(uint32_t, __builtin_convertvector(x23, bf2));
+            const f2 r01 = x01 - f2{__uint_as_float(h01 << 16), __uint_as_float(h01 & 0xffff0000u)};
+            const f2 r23 = x23 - f2{__uint_as_float(h23 << 16), __uint_as_float(h23 & 0xffff0000u)};
+            const uint32_t l01 = __builtin_bit_cast(uint32_t, __builtin_convertvector(r01, bf2));
+            const uint32_t l23 = __builtin_bit_cast(uint32_t, __builtin_convertvector(r23, bf2));
+            const s4 bh = __builtin_bit_cast(s4, make_uint2(h01, h23));
+            const s4 bl = __builtin_bit_cast(s4, make_uint2(l01, l23));
+            d[e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a[q], bh, d[e], 0, 0, 0);
+            d[e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a[q], bl, d[e], 0, 0, 0);
+        }
+    }
+    // lane l holds D[4 g + i][nn]: query 4 (g % 2) + i, column 64 (g / 2) + 4 nn + e
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int dq = 4 * (g & 1) + i;
+        if (dq < n) {
+            f4* dst = reinterpret_cast<f4*>(red + (dq * RG + 2 * w) * DV + 64 * (g >> 1) + 4 * nn);
+            *dst += f4{d[0][i], d[1][i], d[2][i], d[3][i]} * (scale * es[dq]);
+        }
+    }
+}
+
+// Scores of one pass (16 buffer positions i0 .. i0+15) against up to eight
+// bf16 queries of d_k = 128, by one wave: D[d][j] = q_d . k_{i0+j} with
+// v_mfma_f32_16x16x16_bf16 over eight K-slices of 16 channels (A[m][k] =
+// q_m[16 c + k] from the raw query rows, zero for m >= n; B[k][j] = the raw
+// key row of position i0 + j).  bf16 products are exact in fp32.  Lane l then
+// holds D[4 (l / 16) + i][l % 16] and writes the decayed, scaled, masked
+// score of query 4 (l / 16) + i (l < 32) at position i0 + l % 16 to cq.
+template <int DK, bool TREE, bool GATED>
+__device__ __forceinline__ void scores_mfma(const bf16_bits* qr, const bf16_bits* krs, float* cq, const float* bl,
+                                            const uint32_t* anc, int i0, int p, int T, int n, int ldc, float scale,
+                                            int lane) {
+    typedef short s4 __attribute__((ext_vector_type(4)));
+    const int g = lane >> 4, j = lane & 15;
+    const int m = lane & 15;
+    f4 dacc = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < DK / 16; ++c) {
+        const s4 a = m < n ? *reinterpret_cast<const s4*>(qr + m * DK + 16 * c + 4 * g) : s4{0, 0, 0, 0};
+        const s4 b = *reinterpret_cast<const s4*>(krs + j * DK + 16 * c + 4 * g);
+        dacc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, dacc, 0, 0, 0);
+    }
+    const int i = i0 + j;
+    const int ic = min(i, T - 1);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int d = 4 * g + r;
+        if (g < 2 && d < n && i < T) {
+            const int t = p + d;
+            const bool seen = TREE ? (i < p || ((anc[TREE ? d : 0] >> (i - p)) & 1u)) : i <= t;
+            cq[d * ldc + i] = seen ? (GATED ? exp_gate(bl[t] - bl[ic]) : 1.0f) * scale * dacc[r] : 0.f;
+        }
+    }
+}
+
 // TREE: the new tokens are tree drafts (parent array); otherwise a chain.
 template <int RULE, int DK, int DV, int NQ, typename IO, bool TREE>
 __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) {
@@ -77,6 +170,10 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
     constexpr bool DELTA = RULE == KVBUF_RULE_DELTA;
     constexpr bool GATED = RULE != KVBUF_RULE_LINEAR;
     using XIO = typename std::conditional<DELTA, float, IO>::type;
+    // four or eight bf16 queries of d = 128: the scores and the state products
+    // run on the matrix cores, and the value sums go straight to LDS
+    constexpr bool MF = !DELTA && NQ >= 4 && DK == 128 && DV == 128 && std::is_same<IO, bf16_bits>::value;
+    constexpr bool MFS = MF;
 
     extern __shared__ float lds[];
     __shared__ unsigned s_bad;
@@ -250,10 +347,10 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
     __syncthreads();
 
     // ---- 4. per pass: scores of its positions, weighted value sums -------------
-    f4 acc[NQ];
+    f4 acc[MF ? 1 : NQ];
     f4 acck[DELTA ? NQ : 1];
 #pragma unroll
-    for (int d = 0; d < NQ; ++d) {
+    for (int d = 0; d < (MF ? 1 : NQ); ++d) {
         acc[d] = f4{0.f, 0.f, 0.f, 0.f};
         if constexpr (DELTA) acck[d] = f4{0.f, 0.f, 0.f, 0.f};
     }
@@ -269,11 +366,15 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
         }
         const int i = i0 + gp;
         const int ic = min(i, T - 1);
+        if constexpr (MFS) {
+            // wave 0: the pass's 16 positions x the queries on the matrix cores
+            if (tid < 64) scores_mfma<DK, TREE, GATED>(qr, krs, cq, bl, s_anc, i0, p, T, n, ldc, P.scale, tid);
+        }
         RawChunk<IO, E> kc;
-        kc.load(krs + gp * DK + cl * E);
+        if (!MFS) kc.load(krs + gp * DK + cl * E);
 #pragma unroll
         for (int d = 0; d < NQ; ++d) {
-            if (d < n) {
+            if (!MFS && d < n) {
                 const int t = p + d;
                 // the buffered context, then the new tokens on d's path
                 const bool seen = TREE ? (i < p || (i < T && ((s_anc[TREE ? d : 0] >> (i - p)) & 1u))) : i <= t;
@@ -293,13 +394,28 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
         __syncthreads();
         // weighted sums: row group rg takes the pass positions ii = rg, rg+RG, ...
         const int cnt = min(NG, tacc - i0);
-        for (int ii = rg; ii < cnt; ii += RG) {
-            const f4 x = load4(vrs + ii * DV + c0);
+        if constexpr (MF) {
+            // one query at a time, straight into this thread's slot of `red`
+            // (no accumulator stays live next to the tile)
+            float* red = lds + L.red;
 #pragma unroll
             for (int d = 0; d < NQ; ++d) {
                 if (d < n) {
-                    acc[d] += cq[d * ldc + i0 + ii] * x;
-                    if constexpr (DELTA) acck[d] += ck[d * ldc + i0 + ii] * x;
+                    f4* own = reinterpret_cast<f4*>(red + (d * RG + rg) * DV + c0);
+                    f4 a = i0 > 0 ? *own : f4{0.f, 0.f, 0.f, 0.f};
+                    for (int ii = rg; ii < cnt; ii += RG) a += cq[d * ldc + i0 + ii] * load4(vrs + ii * DV + c0);
+                    *own = a;
+                }
+            }
+        } else {
+            for (int ii = rg; ii < cnt; ii += RG) {
+                const f4 x = load4(vrs + ii * DV + c0);
+#pragma unroll
+                for (int d = 0; d < NQ; ++d) {
+                    if (d < n) {
+                        acc[d] += cq[d * ldc + i0 + ii] * x;
+                        if constexpr (DELTA) acck[d] += ck[d * ldc + i0 + ii] * x;
+                    }
                 }
             }
         }
@@ -325,11 +441,14 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
     float* red = lds + L.red;
     float* outp = P.out + in_row * DV;
     const size_t out_stride = static_cast<size_t>(P.H) * DV;
+    if constexpr (MF) {  // the value sums are in `red` already
+        if (has_state) state_products_mfma<DK, DV, RG>(s, qr, red, es, P.scale, n, tid);
+    }
     if constexpr (!DELTA) {
         // every query's row-group partials at once, then one reduction
 #pragma unroll
         for (int d = 0; d < NQ; ++d) {
-            if (d < n) {
+            if (!MF && d < n) {
                 f4 a = acc[d];
                 if (has_state) {
                     RawChunk<IO, RPT> qrow;

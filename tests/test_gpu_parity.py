@@ -220,6 +220,30 @@ def test_tree_invalid_parent_or_leaf_skips_the_tile():
     assert torch.equal(occ[1:], occ0[1:]) and torch.all(occ[0] == occ0[0] + 3)
 
 
+@pytest.mark.parametrize("rule", [0, 1])
+@pytest.mark.parametrize("n", [3, 5, 6, 7])
+@pytest.mark.parametrize("tree", [False, True])
+def test_verify_partial_query_blocks(rule, n, tree):
+    """d = 128 bf16 verifies of 4 or 8 queries per launch with only n of them
+    used (the matrix-core path pads the rest with zeros), across folds and
+    buffers of every occupancy."""
+    w = synth.workload(1, B=5, H=3, dk=128, dv=128, m=8, block_size=4, blocks_per_req=5, steps=10,
+                       rule=rule, io="bf16", state_std=0.02)
+    run = Run(w)
+    t = 0
+    for call in range(7):
+        run.decode(t)
+        t += 1
+        if tree:
+            parent, leaf = synth.draft_tree(w, call, w.B, n)
+            run.verify_tree_commit(call, parent, leaf)
+        else:
+            run.verify_commit(call, n, synth.accepted_lengths(w, call, w.B, n))
+        run.check_effective_states()
+        run.check_pool()
+        run.check_bookkeeping()
+
+
 @pytest.mark.parametrize("rule", [0, 1, 2])
 def test_staggered_occupancies(rule):
     """Commits of different lengths desynchronise the requests' occupancies,
