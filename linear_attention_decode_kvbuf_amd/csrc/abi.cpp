@@ -144,6 +144,7 @@ kvbuf_status chunk_call(const kvbuf_layout* layout, const kvbuf_pools* pools,
     if (e == hipSuccess && eager_decode && !fused) {
         t.mode = kvbuf::MODE_FLUSH;
         t.fold_chunk = fold_chunk(layout->m);
+        t.sparse = 1;
         e = kvbuf::launch_fold(t, layout->rule, layout->d_k, layout->io_dtype, batch->size, stream);
     }
     return from_hip(e);

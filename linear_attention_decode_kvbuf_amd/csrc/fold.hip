@@ -66,7 +66,7 @@ __device__ __forceinline__ void move_rows(char* plane, const uint32_t* src, cons
 // token wave's registers out of the tile's live range.
 // TREE: a commit of a root-to-leaf path of tree drafts.
 template <int RULE, int DK, int DV, typename IO, bool MULTI, bool TREE>
-__global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void fold_kernel(TileParams P) {
+__device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h) {
     using G = Geo<DK, DV>;
     constexpr int NT = G::NT, TPR = G::TPR, RPT = G::RPT;
     constexpr bool DELTA = RULE == KVBUF_RULE_DELTA;
@@ -82,9 +82,6 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void fold_kernel(TileParam
     // (dst) its move to buffer position p + k
     __shared__ uint32_t s_src[TREE ? kMaxDrafts : 1], s_dst[TREE ? kMaxDrafts : 1];
 
-    const TileIndex ti = tile_index(P);
-    const int b = ti.b;
-    const int h = ti.h;
     const int tid = threadIdx.x;
     const bool token_wave = tid >= NT;
     const int lane = tid - NT;
@@ -301,6 +298,56 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void fold_kernel(TileParam
     }
 }
 
+// One workgroup per tile.
+template <int RULE, int DK, int DV, typename IO, bool MULTI, bool TREE>
+__global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void fold_kernel(TileParams P) {
+    const TileIndex ti = tile_index(P);
+    fold_tile<RULE, DK, DV, IO, MULTI, TREE>(P, ti.b, ti.h);
+}
+
+// The flush that follows a decode launch whose eager fold does not fit the
+// decode kernel: at any step only the tiles whose buffer just filled have
+// work.  A workgroup takes kSparseTiles consecutive tiles, reads their slots
+// and occupancies in one round trip, and runs the flush of a tile only if it
+// is full (or its metadata is out of range, to report it); the flush of any
+// other tile changes nothing.  Launching a workgroup per tile instead costs a
+// dispatch, a metadata round trip and a barrier for every tile at every step.
+constexpr int kSparseTiles = 8;
+template <int RULE, int DK, int DV, typename IO, bool MULTI>
+__global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void fold_sparse_kernel(TileParams P) {
+    constexpr int NT = Geo<DK, DV>::NT;
+    __shared__ uint32_t s_mask;
+    const int ntiles = P.batch * P.H;
+    const int first = blockIdx.x * kSparseTiles;
+    if (threadIdx.x >= NT) {
+        const int lane = threadIdx.x - NT;
+        const int t = first + lane;
+        bool need = false;
+        if (lane < kSparseTiles && t < ntiles) {
+            const int h = t / P.batch;
+            const int b = t - h * P.batch;
+            const int slot = P.slot[b];
+            const int p = P.occ[meta_index(P, b, h)];
+            const int cap = P.block_size * P.blocks_per_req;
+            need = p < 0 || p > cap || slot >= P.num_slots || (slot >= 0 && p >= P.m);
+        }
+        const uint64_t m = __ballot(need);
+        if (lane == 0) s_mask = static_cast<uint32_t>(m);
+    }
+    __syncthreads();
+    uint32_t mask = s_mask;
+    bool later = false;
+    while (mask != 0u) {
+        const int k = __builtin_ctz(mask);
+        mask &= mask - 1u;
+        if (later) __syncthreads();  // the previous tile's LDS has been consumed
+        later = true;
+        const int t = first + k;
+        const int h = t / P.batch;
+        fold_tile<RULE, DK, DV, IO, MULTI, false>(P, t - h * P.batch, h);
+    }
+}
+
 template <int RULE, int D, typename IO>
 hipError_t launch_fold_t(const TileParams& p, int batch, hipStream_t s) {
     using G = Geo<D, D>;
@@ -309,6 +356,12 @@ hipError_t launch_fold_t(const TileParams& p, int batch, hipStream_t s) {
     const int most = p.mode == MODE_MATERIALIZE ? cap : p.m;  // most positions one tile applies
     const dim3 grid(static_cast<unsigned>(batch) * p.H), block(G::NTHREADS);
     const bool tree = p.leaf != nullptr;
+    if (p.sparse) {  // a flush after a decode launch (never a tree commit)
+        const dim3 sgrid((static_cast<unsigned>(batch) * p.H + kSparseTiles - 1) / kSparseTiles);
+        if (most <= p.fold_chunk) fold_sparse_kernel<RULE, D, D, IO, false><<<sgrid, block, lds, s>>>(p);
+        else fold_sparse_kernel<RULE, D, D, IO, true><<<sgrid, block, lds, s>>>(p);
+        return hipGetLastError();
+    }
     if (most <= p.fold_chunk) {
         if (tree) fold_kernel<RULE, D, D, IO, false, true><<<grid, block, lds, s>>>(p);
         else fold_kernel<RULE, D, D, IO, false, false><<<grid, block, lds, s>>>(p);

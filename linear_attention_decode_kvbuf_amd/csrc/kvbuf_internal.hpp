@@ -47,6 +47,7 @@ struct TileParams {
     float* states_out;
     const int32_t* parent;  // tree drafts: [B][n] parent of each draft (-1 = the buffer), else null
     const int32_t* leaf;    // tree commit: [B] accepted leaf (-1 = none), else null
+    int sparse;             // flush after a decode launch: fold only the full tiles of each group
 };
 
 // Launchers: each picks the template instance for (rule, d, io dtype) and
