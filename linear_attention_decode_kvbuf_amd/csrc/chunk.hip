@@ -56,8 +56,9 @@ __host__ __device__ inline ChunkLds chunk_lds(int rule, int DK, int DV, int NQ, 
     L.cq = o; o += NQ * round4(cap);                    // e^{b_t - b_i} scale (q_t . k_i)
     L.ck = o; o += delta ? NQ * round4(cap) : 0;        // e^{b_t - b_i} (k_t . k_i)
     L.es = o; o += round4(NQ + 1);                      // e^{b_t} per new token; [NQ]: e^{b_{m-1}}
-    L.kr = o; o += round4(NG * DK * io / 4);            // keys of one pass of positions (raw)
-    L.vr = o; o += round4(NG * DV * xo / 4);            // their values (raw)
+    const int slots = delta ? 2 : 1;                    // delta rule: two pass slots (direct-to-LDS ring)
+    L.kr = o; o += round4(slots * NG * DK * io / 4);    // keys of one pass of positions (raw)
+    L.vr = o; o += round4(slots * NG * DV * xo / 4);    // their values (raw)
     L.fw = o; o += fold ? round4(m) : 0;                // fold weights
     L.red = o; o += RG * DV * (delta ? 2 : NQ);         // row-group partial sums
     L.sq = o; o += delta ? NQ * DV : 0;                 // reduced outputs before the new tokens
@@ -174,8 +175,14 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
     // run on the matrix cores, and the value sums go straight to LDS
     constexpr bool MF = !DELTA && NQ >= 4 && DK == 128 && DV == 128 && std::is_same<IO, bf16_bits>::value;
     constexpr bool MFS = MF;
+    // Delta rule: the keys and pseudo-values of each pass are copied straight
+    // into a two-slot LDS ring by direct-to-LDS loads.  The first two passes
+    // are requested before the state tile, so buffers of up to 2 NG positions
+    // cost no round trip after it; a later pass is requested as soon as the
+    // pass two before it has been consumed.
+    constexpr bool DMA = DELTA;
 
-    extern __shared__ float lds[];
+    extern __shared__ __attribute__((aligned(16))) float lds[];  // 16-byte rows for the LDS copies
     __shared__ unsigned s_bad;
     __shared__ int s_p;
     // Tree drafts: draft d attends to position p + e iff bit e of s_anc[d] is
@@ -261,6 +268,27 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
     XIO* xpool = static_cast<XIO*>(P.value);
 
     // ---- 1. token loads of the first pass, then the state tile ----------------
+    // direct-to-LDS copies of the positions i0 .. i0+NG-1 into ring rows
+    // row0 .. row0+NG-1: each wave copies NG / (NT / 64) of them
+    auto dma_pass = [&](int i0, int row0) {
+        constexpr int RW = NG / (NT / 64);
+        const int w = tid >> 6;
+        const int lane = tid & 63;
+        const int r0 = w * RW;
+        const int nk = max(0, min(RW, T - (i0 + r0)));
+        const int nx = max(0, min(RW, p - (i0 + r0)));  // pseudo-values of buffered positions only
+        lds_copy_rows<DK * static_cast<int>(sizeof(IO))>(
+            reinterpret_cast<char*>(krs + (row0 + r0) * DK), nk,
+            [&](int r) { return reinterpret_cast<const char*>(tok.key(i0 + r0 + r)); }, lane);
+        lds_copy_rows<DV * static_cast<int>(sizeof(XIO))>(
+            reinterpret_cast<char*>(vrs + (row0 + r0) * DV), nx,
+            [&](int r) { return reinterpret_cast<const char*>(tok.pooled_value(i0 + r0 + r)); }, lane);
+    };
+    if constexpr (DMA) {
+        dma_pass(0, 0);
+        if (T > NG) dma_pass(NG, NG);
+        __builtin_amdgcn_sched_barrier(0);  // the copies go first
+    }
     RawChunk<IO, E> qraw[NQR], kdraw[DELTA ? NQR : 1];
 #pragma unroll
     for (int r = 0; r < NQR; ++r) {
@@ -289,12 +317,20 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
             }
         }
     };
-    load_pass(0);
+    if constexpr (!DMA) load_pass(0);
     __builtin_amdgcn_sched_barrier(0);  // keep every token load ahead of the state loads
 
     f4 s[RPT];
     load_tile<RPT, DK, DV>(s, has_state ? P.state + (static_cast<size_t>(slot) * P.H + h) * DK * DV : P.state,
                            has_state, rg, c0);
+    if constexpr (DMA) {
+        // Everything but the RPT state loads has landed (a wave's loads retire
+        // in issue order), so the copied rows are in LDS once the barrier
+        // below is passed.  gfx9 encoding of vmcnt(RPT), other counters free.
+        static_assert(RPT < 64, "vmcnt field");
+        __builtin_amdgcn_s_waitcnt((RPT & 15) | ((RPT >> 4) << 14) | 0x0F70);
+        __builtin_amdgcn_sched_barrier(0);
+    }
 
     // ---- 2. token data to LDS as raw bits; appends from the same registers -----
 #pragma unroll
@@ -318,7 +354,16 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
             }
         }
     };
-    stage_pass(0);
+    if constexpr (DMA) {
+        // append this call's keys from the registers they were loaded into
+#pragma unroll
+        for (int r = 0; r < NQR; ++r) {
+            const int d = gp + NG * r;
+            if (d < n) kdraw[r].store(kpool + tok.slot_index(p + d) * DK + cl * E);
+        }
+    } else {
+        stage_pass(0);
+    }
     __syncthreads();
 
     // ---- 3. cumulative log-gates (wave 0), decay weights of S0 -----------------
@@ -356,13 +401,23 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
     }
     const int tacc = DELTA ? p : T;  // positions whose values enter the sums here
     for (int i0 = 0; i0 < T; i0 += NG) {
+        const int rbase = DMA ? ((i0 / NG) & 1) * NG : 0;  // ring slot of this pass's rows
         if (i0 > 0) {
-            // Later passes (buffers longer than NG positions): these loads
-            // follow the state loads, so they wait for them.
-            __syncthreads();  // the previous pass's rows are consumed
-            load_pass(i0);
-            stage_pass(i0);
-            __syncthreads();
+            if constexpr (DMA) {
+                if (i0 >= 2 * NG) {
+                    // requested at the end of the pass two before this one;
+                    // those copies follow the state loads, so this waits for them
+                    wait_lds_copies();
+                    __syncthreads();
+                }
+            } else {
+                // Later passes (buffers longer than NG positions): these loads
+                // follow the state loads, so they wait for them.
+                __syncthreads();  // the previous pass's rows are consumed
+                load_pass(i0);
+                stage_pass(i0);
+                __syncthreads();
+            }
         }
         const int i = i0 + gp;
         const int ic = min(i, T - 1);
@@ -371,7 +426,7 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
             if (tid < 64) scores_mfma<DK, TREE, GATED>(qr, krs, cq, bl, s_anc, i0, p, T, n, ldc, P.scale, tid);
         }
         RawChunk<IO, E> kc;
-        if (!MFS) kc.load(krs + gp * DK + cl * E);
+        if (!MFS) kc.load(krs + (rbase + gp) * DK + cl * E);
 #pragma unroll
         for (int d = 0; d < NQ; ++d) {
             if (!MFS && d < n) {
@@ -409,7 +464,7 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
             }
         } else {
             for (int ii = rg; ii < cnt; ii += RG) {
-                const f4 x = load4(vrs + ii * DV + c0);
+                const f4 x = load4(vrs + (rbase + ii) * DV + c0);
 #pragma unroll
                 for (int d = 0; d < NQ; ++d) {
                     if (d < n) {
@@ -419,8 +474,14 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
                 }
             }
         }
+        if constexpr (DMA) {
+            if (i0 + 2 * NG < T) {
+                __syncthreads();  // every wave is done with this slot
+                dma_pass(i0 + 2 * NG, rbase);
+            }
+        }
     }
-    if (fold && T > NG) {
+    if (fold && T > (DMA ? 2 * NG : NG)) {
         // Rare: the buffer outgrew one pass before an eager fold (only after
         // deferred-policy calls).  The m positions to fold are all in the
         // pool (p >= m); stage them again.
