@@ -17,15 +17,17 @@
 //   x_t = u_t = beta_t (v_t - e^{b_t} S0^T k_t - sum_{i<t} e^{b_t - b_i} (k_i . k_t) u_i),
 // the pseudo-value the pool stores in place of v.
 //
-// One workgroup of NT threads per (request, head).  Each thread first issues
-// its share of the small token loads -- one 16-byte chunk of a buffered key
-// and of its value (16 threads per position), a query chunk, a gate -- and
-// only then its RPT 128-bit non-temporal loads of the 64 KiB state tile.  The
-// memory counter of a wave retires in issue order, so waiting for the token
-// data never waits for the state: the scores, gate prefix sums and decay
-// weights are formed while the tile is in flight, and the tile is consumed
-// last, in one pass over registers.  The state is the only large operand; the
-// kernel is bound by HBM bandwidth.
+// One workgroup of NT threads per (request, head); each thread holds RPT rows
+// x 4 columns of the 64 KiB state tile (RPT 128-bit non-temporal loads) and
+// stages a share of the token rows (16 threads per position, one 16-byte
+// chunk each).  A wave's memory counter retires in issue order, so what is
+// issued before the tile never waits for it.  Delta rule: the first two
+// passes of buffered rows (and the query, key and gate) go first, so their
+// scores, gate prefix sums and decay weights are formed while the tile is in
+// flight.  Linear and gated rules: the tile goes right after the metadata and
+// the token work waits for it (faster for verification, whose vector work
+// is heavier).  The tile is consumed last, in one pass over registers.  The
+// state is the only large operand; the kernel is bound by HBM bandwidth.
 #include "device_common.hpp"
 
 namespace kvbuf {
@@ -181,6 +183,11 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
     // cost no round trip after it; a later pass is requested as soon as the
     // pass two before it has been consumed.
     constexpr bool DMA = DELTA;
+    // Linear / gated rules: the tile is requested right after the metadata,
+    // ahead of the buffer's rows (the scores then wait for the tile, which
+    // measured faster for verification than holding the tile back behind the
+    // metadata chain).  Delta rule: the tile follows the first two passes.
+    constexpr bool EARLY = !DELTA;
 
     extern __shared__ __attribute__((aligned(16))) float lds[];  // 16-byte rows for the LDS copies
     __shared__ unsigned s_bad;
@@ -216,9 +223,21 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
     IO* krs = reinterpret_cast<IO*>(lds + L.kr);
     XIO* vrs = reinterpret_cast<XIO*>(lds + L.vr);
     float* fw = lds + L.fw;
+    int p0 = 0, blk = 0;
+    if (tid < 64) {  // the occupancy and the table row in one round trip
+        p0 = P.occ[meta_index(P, b, h)];
+        blk = load_table_row(P, b, h, tid);
+    }
+    f4 s[RPT];
+    if constexpr (EARLY) {
+        __builtin_amdgcn_sched_barrier(0);  // the metadata loads go first
+        const bool present = slot >= 0 && slot < P.num_slots;
+        load_tile<RPT, DK, DV>(s, present ? P.state + (static_cast<size_t>(slot) * P.H + h) * DK * DV : P.state,
+                               present, rg, c0);
+        __builtin_amdgcn_sched_barrier(0);
+    }
     if (tid < 64) {
-        const int p0 = P.occ[meta_index(P, b, h)];
-        unsigned bad = stage_row(P, b, h, (p0 < 0 || p0 > cap) ? -1 : p0 + n, spos, tid);
+        unsigned bad = stage_row_from(P, h, (p0 < 0 || p0 > cap) ? -1 : p0 + n, spos, tid, blk);
         if (slot >= P.num_slots) bad |= KVBUF_DEVERR_SLOT;
         if constexpr (TREE) {
             const int par = tid < n ? P.parent[static_cast<size_t>(b) * n + tid] : -1;
@@ -320,9 +339,9 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
     if constexpr (!DMA) load_pass(0);
     __builtin_amdgcn_sched_barrier(0);  // keep every token load ahead of the state loads
 
-    f4 s[RPT];
-    load_tile<RPT, DK, DV>(s, has_state ? P.state + (static_cast<size_t>(slot) * P.H + h) * DK * DV : P.state,
-                           has_state, rg, c0);
+    if constexpr (!EARLY)
+        load_tile<RPT, DK, DV>(s, has_state ? P.state + (static_cast<size_t>(slot) * P.H + h) * DK * DV : P.state,
+                               has_state, rg, c0);
     if constexpr (DMA) {
         // Everything but the RPT state loads has landed (a wave's loads retire
         // in issue order), so the copied rows are in LDS once the barrier

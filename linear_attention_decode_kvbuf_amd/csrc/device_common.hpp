@@ -399,12 +399,11 @@ __device__ __forceinline__ void update_meta(const TileParams& P, int b, int h, i
 // lookup.  (The host bounds num_blocks * H * block_size below 2^31.)  Checks
 // the block ids covering positions [0, end).  Returns KVBUF_DEVERR_* bits,
 // the same in every lane (0 = usable).
-__device__ __forceinline__ unsigned stage_row(const TileParams& P, int b, int h, int end, uint32_t* pos,
-                                              int lane) {
-    const int bpr = P.blocks_per_req;  // <= 64 (host-checked)
+// (stage_row_from: the same with the row already loaded, lane i holding entry i.)
+__device__ __forceinline__ unsigned stage_row_from(const TileParams& P, int h, int end, uint32_t* pos, int lane,
+                                                   int blk) {
+    const int bpr = P.blocks_per_req;
     const int bs = P.block_size;
-    int blk = 0;
-    if (lane < bpr) blk = P.table[meta_index(P, b, h) * bpr + lane];
     const int cap = bs * bpr;
     for (int i = lane; i < cap; i += 64) {
         const int q = i / bs;
@@ -416,6 +415,14 @@ __device__ __forceinline__ unsigned stage_row(const TileParams& P, int b, int h,
     const int nblk = (end + bs - 1) / bs;
     const bool badblk = lane < nblk && (blk < 0 || blk >= P.num_blocks);
     return __ballot(badblk) ? KVBUF_DEVERR_BLOCK : 0u;
+}
+__device__ __forceinline__ int load_table_row(const TileParams& P, int b, int h, int lane) {
+    const int bpr = P.blocks_per_req;  // <= 64 (host-checked)
+    return lane < bpr ? P.table[meta_index(P, b, h) * bpr + lane] : 0;
+}
+__device__ __forceinline__ unsigned stage_row(const TileParams& P, int b, int h, int end, uint32_t* pos,
+                                              int lane) {
+    return stage_row_from(P, h, end, pos, lane, load_table_row(P, b, h, lane));
 }
 
 }  // namespace kvbuf

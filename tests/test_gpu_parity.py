@@ -408,6 +408,26 @@ def test_workload3_gated_sweep(m):
     _say("max out err %.2e, max state err %.2e" % (run.max_out, run.max_state))
 
 
+@pytest.mark.parametrize("n", [4, 8])
+def test_workload4_tree_verify_commit(n):
+    """Tree drafts at the verification workload's full size (B=128 H=32
+    d=128 m=8), in the launch configuration the benchmark times; sampled tiles
+    against the recurrence along each draft's path."""
+    w = synth.workload(4)
+    _say("workload 4 trees n=%d" % n, w)
+    run = Run(w)
+    t = 0
+    for call in range(8):
+        run.decode(t)
+        t += 1
+        parent, leaf = synth.draft_tree(w, call + 1000 * n, w.B, n)
+        run.verify_tree_commit(call, parent, leaf)
+    run.check_effective_states()
+    run.check_pool()
+    run.check_bookkeeping()
+    _say("max out err %.2e, max state err %.2e" % (run.max_out, run.max_state))
+
+
 @pytest.mark.parametrize("n", [1, 2, 4, 8])
 def test_workload4_verify_commit(n):
     w = synth.workload(4)
