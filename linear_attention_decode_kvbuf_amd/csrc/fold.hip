@@ -60,12 +60,42 @@ __device__ __forceinline__ void move_rows(char* plane, const uint32_t* src, cons
     if (N > 3 && live(3)) *at(dst, 3) = v3;
 }
 
+// Long folds on the matrix cores (bf16 MFMA, fp32 accumulate).  An fp32 value
+// x enters as three bf16 terms, hi = bf16(x), mid = bf16(x - hi),
+// lo = bf16(x - hi - mid), whose sum carries x to about 2^-27 of its size;
+// products of bf16 terms are exact in fp32.
+typedef short mf_s4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint32_t mf_pack2(float a, float b) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{a, b}, bf2));
+}
+__device__ __forceinline__ float mf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float mf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+// four values exactly representable in bf16
+__device__ __forceinline__ mf_s4 mf_exact(const float (&x)[4]) {
+    return __builtin_bit_cast(mf_s4, make_uint2(mf_pack2(x[0], x[1]), mf_pack2(x[2], x[3])));
+}
+__device__ __forceinline__ void mf_split3(const float (&x)[4], mf_s4& h, mf_s4& m, mf_s4& l) {
+    float r[4];
+    const uint32_t h01 = mf_pack2(x[0], x[1]), h23 = mf_pack2(x[2], x[3]);
+    r[0] = x[0] - mf_lo(h01); r[1] = x[1] - mf_hi(h01); r[2] = x[2] - mf_lo(h23); r[3] = x[3] - mf_hi(h23);
+    const uint32_t m01 = mf_pack2(r[0], r[1]), m23 = mf_pack2(r[2], r[3]);
+    r[0] -= mf_lo(m01); r[1] -= mf_hi(m01); r[2] -= mf_lo(m23); r[3] -= mf_hi(m23);
+    h = __builtin_bit_cast(mf_s4, make_uint2(h01, h23));
+    m = __builtin_bit_cast(mf_s4, make_uint2(m01, m23));
+    l = __builtin_bit_cast(mf_s4, make_uint2(mf_pack2(r[0], r[1]), mf_pack2(r[2], r[3])));
+}
+__device__ __forceinline__ f4 mf_mac(mf_s4 a, mf_s4 b, f4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
 // MULTI: the fold may take more than one staging round (then the token wave
 // stages round r+1 while the state waves apply round r).  Without it every
 // position is staged before the state loads are issued, which keeps the
 // token wave's registers out of the tile's live range.
 // TREE: a commit of a root-to-leaf path of tree drafts.
-template <int RULE, int DK, int DV, typename IO, bool MULTI, bool TREE>
+template <int RULE, int DK, int DV, typename IO, bool MULTI, bool TREE, bool MFT>
 __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h) {
     using G = Geo<DK, DV>;
     constexpr int NT = G::NT, TPR = G::TPR, RPT = G::RPT;
@@ -74,6 +104,15 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h) {
     constexpr bool SGATE = RULE == KVBUF_RULE_GATED || DELTA;  // one scalar gate per token
     constexpr int CPL = (DK + 63) / 64;                        // key channels per token-wave lane
     using XIO = typename std::conditional<DELTA, float, IO>::type;
+    // Folds that may exceed 16 positions (MFT, d = 128): the rank-T update
+    // runs on the matrix cores (shorter ones are cheaper on the vector ALUs).  The tile is then held in the MFMA accumulator
+    // layout -- 16 x 16 blocks of S^T, wave w owning rows 32w .. 32w+31: lane l
+    // holds row 32w + 16 rb + l % 16, columns 16 cb + 4 (l / 16) .. +3 of block
+    // (rb, cb) in s[8 rb + cb] -- and block (rb, cb) of S^T gains
+    // sum_k x_k[c] (w_k k_k[r]) as A (x rows, M = columns) times B (weighted
+    // keys, N = rows) over K-chunks of 16 positions.
+    constexpr bool MF = MFT && DK == 128 && DV == 128;
+    constexpr bool XEXACT = std::is_same<XIO, bf16_bits>::value;  // values exact in bf16
 
     extern __shared__ float lds[];
     __shared__ unsigned s_bad;
@@ -249,12 +288,31 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h) {
         if (tree && !MULTI) move_kept();  // the fold's rows are staged
     }
     f4 s[RPT];
-    if (!token_wave)
-        load_tile<RPT, DK, DV>(s, has_state ? P.state + (static_cast<size_t>(slot) * P.H + h) * DK * DV : P.state,
-                               has_state, rg, c0);
+    const int mw = tid >> 6, ml = tid & 63;  // MF: wave and lane
+    auto mf_offset = [&](int j) {            // MF: float offset of s[j] in the tile
+        const int row = 32 * mw + 16 * (j >> 3) + (ml & 15);
+        return row * DV + 16 * (j & 7) + 4 * (ml >> 4);
+    };
+    if (!token_wave) {
+        const float* tile = has_state ? P.state + (static_cast<size_t>(slot) * P.H + h) * DK * DV : P.state;
+        if constexpr (MF) {
+            static_assert(RPT == 16, "16 blocks of 16 x 16 per wave");
+            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<float*>(tile), 0, has_state ? DK * DV * static_cast<int>(sizeof(float)) : 0, kBufferFlags);
+#pragma unroll
+            for (int j = 0; j < RPT; ++j)
+                s[j] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(rs, mf_offset(j) * 4, 0,
+                                                                                   kCachePolicyNT));
+        } else {
+            load_tile<RPT, DK, DV>(s, tile, has_state, rg, c0);
+        }
+    }
     __syncthreads();
     if (!token_wave) {
-        if constexpr (CH) {
+        if constexpr (CH && MF) {
+#pragma unroll
+            for (int j = 0; j < RPT; ++j) s[j] *= exp_gate(e0p[32 * mw + 16 * (j >> 3) + (ml & 15)]);
+        } else if constexpr (CH) {
 #pragma unroll
             for (int j = 0; j < RPT; ++j) s[j] *= exp_gate(e0p[rg * RPT + j]);
         } else {
@@ -268,6 +326,59 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h) {
         const float* fx = fk + fc * DK;
         const float* fw = fx + fc * DV;
         const int cnt = min(fc, T - r * fc);
+        if constexpr (MF) {
+            const int g = ml >> 4, nn = ml & 15;
+            for (int k0 = 0; k0 < cnt; k0 += 16) {
+                // B: weighted keys w_p k_p[r], positions k0 + 4g + i, row r of block rb
+                mf_s4 bh[2], bm[2], bo[2];
+#pragma unroll
+                for (int rb = 0; rb < 2; ++rb) {
+                    float v[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int pp = k0 + 4 * g + i;
+                        v[i] = pp < cnt ? fw[pp] * fk[pp * DK + 32 * mw + 16 * rb + nn] : 0.0f;
+                    }
+                    mf_split3(v, bh[rb], bm[rb], bo[rb]);
+                }
+#pragma unroll
+                for (int cb = 0; cb < 8; ++cb) {
+                    // A: values x_p[c], column c = 16 cb + nn
+                    float x[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int pp = k0 + 4 * g + i;
+                        x[i] = pp < cnt ? fx[pp * DV + 16 * cb + nn] : 0.0f;
+                    }
+                    if constexpr (XEXACT) {
+                        const mf_s4 a = mf_exact(x);
+#pragma unroll
+                        for (int rb = 0; rb < 2; ++rb) {
+                            f4 d = s[8 * rb + cb];
+                            d = mf_mac(a, bh[rb], d);
+                            d = mf_mac(a, bm[rb], d);
+                            d = mf_mac(a, bo[rb], d);
+                            s[8 * rb + cb] = d;
+                        }
+                    } else {
+                        mf_s4 ah, am, ao;
+                        mf_split3(x, ah, am, ao);
+#pragma unroll
+                        for (int rb = 0; rb < 2; ++rb) {
+                            f4 d = s[8 * rb + cb];
+                            d = mf_mac(ah, bh[rb], d);
+                            d = mf_mac(ah, bm[rb], d);
+                            d = mf_mac(am, bh[rb], d);
+                            d = mf_mac(ah, bo[rb], d);
+                            d = mf_mac(ao, bh[rb], d);
+                            d = mf_mac(am, bm[rb], d);
+                            s[8 * rb + cb] = d;
+                        }
+                    }
+                }
+            }
+            return;
+        }
         for (int ii = 0; ii < cnt; ++ii) {
             const f4 x = *reinterpret_cast<const f4*>(fx + ii * DV + c0);
             const float w = fw[ii];
@@ -294,15 +405,16 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h) {
                                  : P.state + (static_cast<size_t>(slot) * P.H + h) * DK * DV;
 #pragma unroll
         for (int j = 0; j < RPT; ++j)
-            __builtin_nontemporal_store(s[j], reinterpret_cast<f4*>(dst + (rg * RPT + j) * DV + c0));
+            __builtin_nontemporal_store(
+                s[j], reinterpret_cast<f4*>(dst + (MF ? mf_offset(j) : (rg * RPT + j) * DV + c0)));
     }
 }
 
 // One workgroup per tile.
-template <int RULE, int DK, int DV, typename IO, bool MULTI, bool TREE>
+template <int RULE, int DK, int DV, typename IO, bool MULTI, bool TREE, bool MFT>
 __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void fold_kernel(TileParams P) {
     const TileIndex ti = tile_index(P);
-    fold_tile<RULE, DK, DV, IO, MULTI, TREE>(P, ti.b, ti.h);
+    fold_tile<RULE, DK, DV, IO, MULTI, TREE, MFT>(P, ti.b, ti.h);
 }
 
 // The flush that follows a decode launch whose eager fold does not fit the
@@ -313,7 +425,7 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void fold_kernel(TileParam
 // other tile changes nothing.  Launching a workgroup per tile instead costs a
 // dispatch, a metadata round trip and a barrier for every tile at every step.
 constexpr int kSparseTiles = 8;
-template <int RULE, int DK, int DV, typename IO, bool MULTI>
+template <int RULE, int DK, int DV, typename IO, bool MULTI, bool MFT>
 __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void fold_sparse_kernel(TileParams P) {
     constexpr int NT = Geo<DK, DV>::NT;
     __shared__ uint32_t s_mask;
@@ -344,7 +456,7 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void fold_sparse_kernel(Ti
         later = true;
         const int t = first + k;
         const int h = t / P.batch;
-        fold_tile<RULE, DK, DV, IO, MULTI, false>(P, t - h * P.batch, h);
+        fold_tile<RULE, DK, DV, IO, MULTI, false, MFT>(P, t - h * P.batch, h);
     }
 }
 
@@ -356,18 +468,25 @@ hipError_t launch_fold_t(const TileParams& p, int batch, hipStream_t s) {
     const int most = p.mode == MODE_MATERIALIZE ? cap : p.m;  // most positions one tile applies
     const dim3 grid(static_cast<unsigned>(batch) * p.H), block(G::NTHREADS);
     const bool tree = p.leaf != nullptr;
+    // multi-round folds always exceed 16 positions (fold_chunk >= 16 when m > 16)
+    const bool multi = most > p.fold_chunk;
+    const bool mf = most > 16;
     if (p.sparse) {  // a flush after a decode launch (never a tree commit)
         const dim3 sgrid((static_cast<unsigned>(batch) * p.H + kSparseTiles - 1) / kSparseTiles);
-        if (most <= p.fold_chunk) fold_sparse_kernel<RULE, D, D, IO, false><<<sgrid, block, lds, s>>>(p);
-        else fold_sparse_kernel<RULE, D, D, IO, true><<<sgrid, block, lds, s>>>(p);
+        if (multi) fold_sparse_kernel<RULE, D, D, IO, true, true><<<sgrid, block, lds, s>>>(p);
+        else if (mf) fold_sparse_kernel<RULE, D, D, IO, false, true><<<sgrid, block, lds, s>>>(p);
+        else fold_sparse_kernel<RULE, D, D, IO, false, false><<<sgrid, block, lds, s>>>(p);
         return hipGetLastError();
     }
-    if (most <= p.fold_chunk) {
-        if (tree) fold_kernel<RULE, D, D, IO, false, true><<<grid, block, lds, s>>>(p);
-        else fold_kernel<RULE, D, D, IO, false, false><<<grid, block, lds, s>>>(p);
+    if (multi) {
+        if (tree) fold_kernel<RULE, D, D, IO, true, true, true><<<grid, block, lds, s>>>(p);
+        else fold_kernel<RULE, D, D, IO, true, false, true><<<grid, block, lds, s>>>(p);
+    } else if (mf) {
+        if (tree) fold_kernel<RULE, D, D, IO, false, true, true><<<grid, block, lds, s>>>(p);
+        else fold_kernel<RULE, D, D, IO, false, false, true><<<grid, block, lds, s>>>(p);
     } else {
-        if (tree) fold_kernel<RULE, D, D, IO, true, true><<<grid, block, lds, s>>>(p);
-        else fold_kernel<RULE, D, D, IO, true, false><<<grid, block, lds, s>>>(p);
+        if (tree) fold_kernel<RULE, D, D, IO, false, true, false><<<grid, block, lds, s>>>(p);
+        else fold_kernel<RULE, D, D, IO, false, false, false><<<grid, block, lds, s>>>(p);
     }
     return hipGetLastError();
 }

@@ -77,6 +77,30 @@ def test_long_table_rows(m, bs, bpr, flush):
 
 
 @pytest.mark.parametrize("rule", [0, 1, 2, 3])
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+@pytest.mark.parametrize("flush", [kb.FLUSH_EAGER, kb.FLUSH_DEFERRED])
+def test_long_folds(rule, io, flush):
+    """Folds and materialisations of more than 32 positions at d = 128 (the
+    rank-T update on the matrix cores): eager folds of m = 48 where they do
+    not fit the decode kernel (per-channel and delta rules, fp32 rows),
+    deferred flushes of 48 with a tail behind them, and effective states of
+    up to 50 buffered positions."""
+    w = synth.workload(1, B=3, H=2, dk=128, dv=128, m=48, block_size=16, blocks_per_req=4, steps=150,
+                       rule=rule, io=io, state_std=0.02)
+    _say("long folds", w, "flush", flush)
+    run = Run(w, flush=flush)
+    for t in range(w.steps):
+        run.decode(t)
+        if flush == kb.FLUSH_DEFERRED and t % 50 == 49:
+            run.flush()
+        if t % 25 == 24:
+            run.check_effective_states()
+    run.check_effective_states()
+    run.check_pool()
+    run.check_bookkeeping()
+
+
+@pytest.mark.parametrize("rule", [0, 1, 2, 3])
 def test_deferred_flush_with_tail(rule):
     """Decode past m before folding: the fold takes the first m tokens and
     leaves the rest buffered in the rotated table."""
