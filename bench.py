@@ -140,10 +140,10 @@ def time_loop(torch, fn, cycles, warmup, events=False):
     return wall
 
 
-def per_launch_ms(torch, launches, reps):
-    """Average duration (ms) of each launch in ``launches`` (a list of
-    callables issued back to back), from HIP events recorded on the stream
-    the kernels run on, over ``reps`` repetitions."""
+def per_launch_ms(torch, launches, reps, median=False):
+    """Duration (ms) of each launch in ``launches`` (a list of callables
+    issued back to back), from HIP events recorded on the stream the kernels
+    run on, over ``reps`` repetitions: the mean, or the median."""
     stream = torch.cuda.current_stream()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(launches) + 1)] for _ in range(reps)]
     for r in range(reps):
@@ -152,11 +152,10 @@ def per_launch_ms(torch, launches, reps):
             fn()
             evs[r][i + 1].record(stream)
     torch.cuda.synchronize()
-    out = [0.0] * len(launches)
-    for r in range(reps):
-        for i in range(len(launches)):
-            out[i] += evs[r][i].elapsed_time(evs[r][i + 1]) / reps
-    return out
+    times = [[evs[r][i].elapsed_time(evs[r][i + 1]) for r in range(reps)] for i in range(len(launches))]
+    if median:
+        return [sorted(t)[len(t) // 2] for t in times]
+    return [sum(t) / reps for t in times]
 
 
 def cpu_baseline(synth, oracle, np, torch, w, ring, max_tiles=None):
@@ -177,6 +176,11 @@ def cpu_baseline(synth, oracle, np, torch, w, ring, max_tiles=None):
     oracle.recurrent(1, S0, q, k, v, g=g, nthreads=ncores)
     dt = time.perf_counter() - t0
     tile_tokens_per_s = tiles * steps / dt
+    # the same on one thread, over the first 1/16 of the tiles
+    t1 = max(1, tiles // 16)
+    t0 = time.perf_counter()
+    oracle.recurrent(1, S0[:t1], q[:, :t1], k[:, :t1], v[:, :t1], g=g[:, :t1], nthreads=1)
+    dt1 = time.perf_counter() - t0
     return {
         "value": tile_tokens_per_s / w.H,  # a token of one request = H tiles
         "unit": "tokens/s",
@@ -184,6 +188,8 @@ def cpu_baseline(synth, oracle, np, torch, w, ring, max_tiles=None):
         "kind": "oracle",
         "sample": "fp64 recurrent oracle (C, OpenMP over tiles), %d consecutive tokens of %d of the %d "
                   "(request, head) tiles of the same workload, %.1f s" % (steps, tiles, w.B * w.H, dt),
+        "one_thread": {"value": t1 * steps / dt1 / w.H, "unit": "tokens/s",
+                       "sample": "%d tokens of %d tiles, %.2f s" % (steps, t1, dt1)},
     }
 
 
@@ -451,6 +457,43 @@ def verify_baseline(kb, synth, torch, dev, w, n, drafts, accs):
             "accepted_tokens_per_s": accepted / ((ver + com) * 1e-3)}
 
 
+def long_fold_leg(kb, synth, torch, dev, args):
+    """kvbuf_flush of m = 32, 64, 128 buffered tokens at B=256 H=32 d=128
+    (deferred policy, scalar-gated and delta rules): one state read and write
+    plus the m rows per tile; folds of more than 16 positions run their rank-m
+    update on the matrix cores."""
+    out = {}
+    for rule, name in ((kb.RULE_GATED, "gated"), (kb.RULE_DELTA, "delta")):
+        for m in (32, 64, 128):
+            w = synth.workload(3, m=m, block_size=m, blocks_per_req=1, rule=rule)
+            kv = kb.KVBuffer(batch=w.B, heads=w.H, d=w.dk, m=m, block_size=m, blocks_per_req=1, num_blocks=w.B,
+                             num_state_slots=w.B, rule=rule, io_dtype=kb.BF16, flush=kb.FLUSH_DEFERRED,
+                             device=dev)
+            kv.state.normal_(0.0, 0.02)
+            kv.key.normal_()
+            kv.value.normal_()
+            kv.gate.uniform_(-0.1, 0.0)
+
+            def fill():
+                kv.occupancy.fill_(m)
+
+            launches = []
+            for _ in range(4):
+                launches += [fill, kv.flush]
+            for f in launches:
+                f()
+            per = per_launch_ms(torch, launches, 5)
+            torch.cuda.synchronize()
+            assert int(kv.error.item()) == 0
+            ms = sum(per[1::2]) / 4
+            xb = 4 * w.dv if rule == kb.RULE_DELTA else 2 * w.dv  # pseudo-values are fp32
+            tile_bytes = 8 * w.dk * w.dv + m * (2 * w.dk + xb + 4)
+            out["%s_m%d" % (name, m)] = {"flush_ms": ms,
+                                         "hbm_gbps": tile_bytes * w.B * w.H / (ms * 1e-3) / 1e9}
+            del kv
+    return out
+
+
 def delta_leg(kb, synth, torch, dev, args):
     """Gated delta rule, B=512 (256 requests with a state, 256 served from the
     buffer alone), H=32 d=128 m=64: one decode launch per step (plus the fold
@@ -496,7 +539,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing on the host")
     ap.add_argument("--no-extras", action="store_true", help="skip the m=0 / separate-flush / copy legs")
     ap.add_argument("--only", choices=["fused", "recurrent", "separate", "copy", "verify", "delta", "sweep",
-                                       "linear", "heads4", "context", "channel"], default=None,
+                                       "linear", "heads4", "context", "channel", "longfold"], default=None,
                     help="run one leg only (for profiling)")
     args = ap.parse_args()
 
@@ -538,10 +581,10 @@ def main():
         # each decode call is one decode_kernel launch: the average launch
         # duration is the event time of the timed region over its launches
         avg_launch_ms = ev * 1e3 / (args.steps * m)
-        # per-occupancy durations, one event pair per launch (each adds an
-        # event record to the launch it brackets)
+        # per-occupancy durations, medians over the cycles, one event pair per
+        # launch (each adds an event record to the launch it brackets)
         reps = max(10, min(args.steps, 50))
-        per = per_launch_ms(torch, [decode_fn(kv, j) for j in range(m)], reps)
+        per = per_launch_ms(torch, [decode_fn(kv, j) for j in range(m)], reps, median=True)
         torch.cuda.synchronize()
         assert int(kv.error.item()) == 0
         cyc_bytes = cycle_bytes_fused(m, w.dk, w.dv) * tiles
@@ -632,6 +675,8 @@ def main():
         result["context_sweep"] = context_leg(kb, synth, torch, dev, args)
     if not args.no_extras and args.only in (None, "channel"):
         result["channel_gates"] = channel_leg(kb, synth, torch, dev, args)
+    if not args.no_extras and args.only in (None, "longfold"):
+        result["long_folds"] = long_fold_leg(kb, synth, torch, dev, args)
 
     if args.only not in (None, "fused"):
         print(json.dumps(result))
@@ -670,7 +715,8 @@ def main():
         "cpu_baseline": cpu,
     }
     for key in ("per_occupancy_ms", "m0_recurrent", "separate_flush", "copy_ceiling_gbps", "verify",
-                "delta_mixed", "m_sweep", "linear_B64", "head_share_H4", "context_sweep", "channel_gates"):
+                "delta_mixed", "m_sweep", "linear_B64", "head_share_H4", "context_sweep", "channel_gates",
+                "long_folds"):
         if key in result:
             line[key] = result[key]
     print(json.dumps(line))
