@@ -58,7 +58,7 @@ __host__ __device__ inline ChunkLds chunk_lds(int rule, int DK, int DV, int NQ, 
     L.cq = o; o += NQ * round4(cap);                    // e^{b_t - b_i} scale (q_t . k_i)
     L.ck = o; o += delta ? NQ * round4(cap) : 0;        // e^{b_t - b_i} (k_t . k_i)
     L.es = o; o += round4(NQ + 1);                      // e^{b_t} per new token; [NQ]: e^{b_{m-1}}
-    const int slots = delta ? 2 : 1;                    // delta rule: two pass slots (direct-to-LDS ring)
+    const int slots = (delta || NQ == 1) ? 2 : 1;       // two pass slots for the direct-to-LDS ring
     L.kr = o; o += round4(slots * NG * DK * io / 4);    // keys of one pass of positions (raw)
     L.vr = o; o += round4(slots * NG * DV * xo / 4);    // their values (raw)
     L.fw = o; o += fold ? round4(m) : 0;                // fold weights
@@ -177,12 +177,15 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
     // run on the matrix cores, and the value sums go straight to LDS
     constexpr bool MF = !DELTA && NQ >= 4 && DK == 128 && DV == 128 && std::is_same<IO, bf16_bits>::value;
     constexpr bool MFS = MF;
-    // Delta rule: the keys and pseudo-values of each pass are copied straight
-    // into a two-slot LDS ring by direct-to-LDS loads.  The first two passes
-    // are requested before the state tile, so buffers of up to 2 NG positions
-    // cost no round trip after it; a later pass is requested as soon as the
-    // pass two before it has been consumed.
-    constexpr bool DMA = DELTA;
+    // One new token (decode / direct with long rows) and the delta rule: the
+    // keys and values (pseudo-values) of each pass are copied straight into a
+    // two-slot LDS ring by direct-to-LDS loads.  The first two passes are
+    // requested together (before the state tile for the delta rule), so
+    // buffers of up to 2 NG positions cost one round trip; a later pass is
+    // requested as soon as the pass two before it has been consumed.
+    // Verification of 2-8 drafts stages its rows through registers (measured
+    // faster there).
+    constexpr bool DMA = DELTA || NQ == 1;
     // Linear / gated rules: the tile is requested right after the metadata,
     // ahead of the buffer's rows (the scores then wait for the tile, which
     // measured faster for verification than holding the tile back behind the
@@ -295,28 +298,37 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
         const int lane = tid & 63;
         const int r0 = w * RW;
         const int nk = max(0, min(RW, T - (i0 + r0)));
-        const int nx = max(0, min(RW, p - (i0 + r0)));  // pseudo-values of buffered positions only
+        // values of every position; delta rule: pseudo-values of buffered positions only
+        const int nx = max(0, min(RW, (DELTA ? p : T) - (i0 + r0)));
         lds_copy_rows<DK * static_cast<int>(sizeof(IO))>(
             reinterpret_cast<char*>(krs + (row0 + r0) * DK), nk,
             [&](int r) { return reinterpret_cast<const char*>(tok.key(i0 + r0 + r)); }, lane);
         lds_copy_rows<DV * static_cast<int>(sizeof(XIO))>(
-            reinterpret_cast<char*>(vrs + (row0 + r0) * DV), nx,
-            [&](int r) { return reinterpret_cast<const char*>(tok.pooled_value(i0 + r0 + r)); }, lane);
+            reinterpret_cast<char*>(vrs + (row0 + r0) * DV), nx, [&](int r) {
+                const int i = i0 + r0 + r;
+                if constexpr (DELTA) return reinterpret_cast<const char*>(tok.pooled_value(i));
+                else return reinterpret_cast<const char*>(i < p ? tok.pooled_value(i) : tok.new_value(i - p));
+            }, lane);
     };
     if constexpr (DMA) {
         dma_pass(0, 0);
         if (T > NG) dma_pass(NG, NG);
         __builtin_amdgcn_sched_barrier(0);  // the copies go first
     }
-    RawChunk<IO, E> qraw[NQR], kdraw[DELTA ? NQR : 1];
+    // this call's queries, and its keys (and values, linear / gated rules) for
+    // the appends
+    RawChunk<IO, E> qraw[NQR], kdraw[NQR];
+    RawChunk<IO, EV> vdraw[DELTA ? 1 : NQR];
 #pragma unroll
     for (int r = 0; r < NQR; ++r) {
         const int d = gp + NG * r;
         qraw[r].zero();
-        if constexpr (DELTA) kdraw[r].zero();
+        kdraw[r].zero();
+        if constexpr (!DELTA) vdraw[r].zero();
         if (d < n) {
             qraw[r].load(static_cast<const IO*>(P.q) + (in_row + d * P.H) * DK + cl * E);
-            if constexpr (DELTA) kdraw[r].load(tok.kin + d * tok.in_stride_k + cl * E);
+            kdraw[r].load(tok.kin + d * tok.in_stride_k + cl * E);
+            if constexpr (!DELTA) vdraw[r].load(tok.new_value(d) + cl * EV);
         }
     }
     float graw = 0.f;  // log-gate of position tid
@@ -342,13 +354,15 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
     if constexpr (!EARLY)
         load_tile<RPT, DK, DV>(s, has_state ? P.state + (static_cast<size_t>(slot) * P.H + h) * DK * DV : P.state,
                                has_state, rg, c0);
-    if constexpr (DMA) {
+    if constexpr (DMA && !EARLY) {
         // Everything but the RPT state loads has landed (a wave's loads retire
         // in issue order), so the copied rows are in LDS once the barrier
         // below is passed.  gfx9 encoding of vmcnt(RPT), other counters free.
         static_assert(RPT < 64, "vmcnt field");
         __builtin_amdgcn_s_waitcnt((RPT & 15) | ((RPT >> 4) << 14) | 0x0F70);
         __builtin_amdgcn_sched_barrier(0);
+    } else if constexpr (DMA) {
+        wait_lds_copies();  // the copies follow the tile here
     }
 
     // ---- 2. token data to LDS as raw bits; appends from the same registers -----
@@ -374,11 +388,15 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
         }
     };
     if constexpr (DMA) {
-        // append this call's keys from the registers they were loaded into
+        // append this call's keys (and values) from the registers they were
+        // loaded into; delta-rule pseudo-values are appended once formed
 #pragma unroll
         for (int r = 0; r < NQR; ++r) {
             const int d = gp + NG * r;
-            if (d < n) kdraw[r].store(kpool + tok.slot_index(p + d) * DK + cl * E);
+            if (d < n) {
+                kdraw[r].store(kpool + tok.slot_index(p + d) * DK + cl * E);
+                if constexpr (!DELTA) vdraw[r].store(xpool + tok.slot_index(p + d) * DV + cl * EV);
+            }
         }
     } else {
         stage_pass(0);
@@ -442,7 +460,8 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
         const int ic = min(i, T - 1);
         if constexpr (MFS) {
             // wave 0: the pass's 16 positions x the queries on the matrix cores
-            if (tid < 64) scores_mfma<DK, TREE, GATED>(qr, krs, cq, bl, s_anc, i0, p, T, n, ldc, P.scale, tid);
+            if (tid < 64)
+                scores_mfma<DK, TREE, GATED>(qr, krs + rbase * DK, cq, bl, s_anc, i0, p, T, n, ldc, P.scale, tid);
         }
         RawChunk<IO, E> kc;
         if (!MFS) kc.load(krs + (rbase + gp) * DK + cl * E);
@@ -477,7 +496,8 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
                 if (d < n) {
                     f4* own = reinterpret_cast<f4*>(red + (d * RG + rg) * DV + c0);
                     f4 a = i0 > 0 ? *own : f4{0.f, 0.f, 0.f, 0.f};
-                    for (int ii = rg; ii < cnt; ii += RG) a += cq[d * ldc + i0 + ii] * load4(vrs + ii * DV + c0);
+                    for (int ii = rg; ii < cnt; ii += RG)
+                        a += cq[d * ldc + i0 + ii] * load4(vrs + (rbase + ii) * DV + c0);
                     *own = a;
                 }
             }
