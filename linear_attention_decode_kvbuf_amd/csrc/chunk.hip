@@ -176,7 +176,6 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
     // four or eight bf16 queries of d = 128: the scores and the state products
     // run on the matrix cores, and the value sums go straight to LDS
     constexpr bool MF = !DELTA && NQ >= 4 && DK == 128 && DV == 128 && std::is_same<IO, bf16_bits>::value;
-    constexpr bool MFS = MF;
     // One new token (decode / direct with long rows) and the delta rule: the
     // keys and values (pseudo-values) of each pass are copied straight into a
     // two-slot LDS ring by direct-to-LDS loads.  The first two passes are
@@ -458,16 +457,16 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
         }
         const int i = i0 + gp;
         const int ic = min(i, T - 1);
-        if constexpr (MFS) {
+        if constexpr (MF) {
             // wave 0: the pass's 16 positions x the queries on the matrix cores
             if (tid < 64)
                 scores_mfma<DK, TREE, GATED>(qr, krs + rbase * DK, cq, bl, s_anc, i0, p, T, n, ldc, P.scale, tid);
         }
         RawChunk<IO, E> kc;
-        if (!MFS) kc.load(krs + (rbase + gp) * DK + cl * E);
+        if (!MF) kc.load(krs + (rbase + gp) * DK + cl * E);
 #pragma unroll
         for (int d = 0; d < NQ; ++d) {
-            if (!MFS && d < n) {
+            if (!MF && d < n) {
                 const int t = p + d;
                 // the buffered context, then the new tokens on d's path
                 const bool seen = TREE ? (i < p || (i < T && ((s_anc[TREE ? d : 0] >> (i - p)) & 1u))) : i <= t;
@@ -521,9 +520,9 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
         }
     }
     if (fold && T > (DMA ? 2 * NG : NG)) {
-        // Rare: the buffer outgrew one pass before an eager fold (only after
-        // deferred-policy calls).  The m positions to fold are all in the
-        // pool (p >= m); stage them again.
+        // Rare: the buffer outgrew the passes still staged before an eager
+        // fold (only after deferred-policy calls).  The m positions to fold
+        // are all in the pool (p >= m); stage them again.
         __syncthreads();
         kr.zero();
         xr.zero();
