@@ -134,7 +134,8 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h) {
     const int slot = P.slot[b];
     const bool has_state = slot >= 0;
     constexpr bool tree = TREE;
-    int a = 0;  // drafts kept
+    int a = 0;        // drafts kept
+    int a_moves = 0;  // tree commit: kept drafts whose rows move
     if (token_wave) {
         const int p = P.occ[meta_index(P, b, h)];
         unsigned bad = 0;
@@ -169,20 +170,25 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h) {
         if (tree && !bad) {
             // kept draft d (rank k on the path) moves from position p + d to
             // p + k: the fold below reads it from its draft row, and its rows
-            // are copied once the fold's reads are done
+            // are copied once the fold's reads are done (drafts already in
+            // place, d = k, are not copied)
             const bool kept = lane < P.n && ((path >> lane) & 1u);
             const int k = kept ? __popc(path & ((1u << lane) - 1u)) : 0;
+            const bool moves = kept && k != lane;
+            const uint64_t mv = __ballot(moves);
+            const int slot_k = moves ? __popc(static_cast<uint32_t>(mv) & ((1u << lane) - 1u)) : 0;
             uint32_t src = 0, dst = 0;
             if (kept) {
                 src = pos[p + lane];
                 dst = pos[p + k];
             }
             __builtin_amdgcn_wave_barrier();
-            if (kept) {
-                pos[p + k] = src;
-                s_src[k] = src;
-                s_dst[k] = dst;
+            if (kept) pos[p + k] = src;
+            if (moves) {
+                s_src[slot_k] = src;
+                s_dst[slot_k] = dst;
             }
+            a_moves = __popcll(mv);
         }
         if (lane == 0) {
             s_bad = bad;
@@ -206,14 +212,15 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h) {
     // comes from position p + d with d >= k), so no row is overwritten before
     // it is read.
     auto move_kept = [&]() __attribute__((always_inline)) {
-        if (a == 0) return;
-        move_rows<DK * sizeof(IO) / 16>(static_cast<char*>(P.key), s_src, s_dst, a, lane);
-        move_rows<DV * sizeof(XIO) / 16>(static_cast<char*>(P.value), s_src, s_dst, a, lane);
+        const int nm = a_moves;
+        if (nm == 0) return;
+        move_rows<DK * sizeof(IO) / 16>(static_cast<char*>(P.key), s_src, s_dst, nm, lane);
+        move_rows<DV * sizeof(XIO) / 16>(static_cast<char*>(P.value), s_src, s_dst, nm, lane);
         if constexpr (CH) {
-            move_rows<DK * 4 / 16>(reinterpret_cast<char*>(P.gate), s_src, s_dst, a, lane);
+            move_rows<DK * 4 / 16>(reinterpret_cast<char*>(P.gate), s_src, s_dst, nm, lane);
         } else if constexpr (SGATE) {
-            const float gk = lane < a ? P.gate[s_src[lane]] : 0.0f;
-            if (lane < a) P.gate[s_dst[lane]] = gk;
+            const float gk = lane < nm ? P.gate[s_src[lane]] : 0.0f;
+            if (lane < nm) P.gate[s_dst[lane]] = gk;
         }
     };
     if (!materialize && !fold) {  // no state change for this tile
