@@ -113,8 +113,12 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h) {
     // keys, N = rows) over K-chunks of 16 positions.
     constexpr bool MF = MFT && DK == 128 && DV == 128;
     constexpr bool XEXACT = std::is_same<XIO, bf16_bits>::value;  // values exact in bf16
+    // ... and their rows are staged as loaded, by direct-to-LDS copies (one
+    // round trip per staging round; the per-channel rule keeps fp32 rows,
+    // whose keys carry per-channel decays)
+    constexpr bool RAW = MF && !CH;
 
-    extern __shared__ float lds[];
+    extern __shared__ __attribute__((aligned(16))) float lds[];  // 16-byte rows for the LDS copies
     __shared__ unsigned s_bad;
     __shared__ int s_T, s_fold;
     // tree commit: pool rows of the k-th kept draft before (src) and after
@@ -256,7 +260,16 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h) {
         float* fw = fx + fc * DV;
         const int i0 = r * fc;
         const int cnt = min(fc, T - i0);
-        stage_rows(tok, i0, cnt, fk, fx, nullptr, lane);
+        if constexpr (RAW) {
+            lds_copy_rows<DK * static_cast<int>(sizeof(IO))>(
+                reinterpret_cast<char*>(fk), cnt,
+                [&](int ii) { return reinterpret_cast<const char*>(tok.key(i0 + ii)); }, lane);
+            lds_copy_rows<DV * static_cast<int>(sizeof(XIO))>(
+                reinterpret_cast<char*>(fx), cnt,
+                [&](int ii) { return reinterpret_cast<const char*>(tok.pooled_value(i0 + ii)); }, lane);
+        } else {
+            stage_rows(tok, i0, cnt, fk, fx, nullptr, lane);
+        }
         if constexpr (CH) {
             // k_i[ch] e^{B_{T-1}[ch] - B_i[ch]}, positions in order
             for (int ii = 0; ii < cnt; ++ii) {
@@ -275,6 +288,7 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h) {
             for (int ii = lane; ii < cnt; ii += 64)
                 fw[ii] = SGATE ? exp_gate(bl[T - 1] - bl[i0 + ii]) : 1.0f;
         }
+        if constexpr (RAW) wait_lds_copies();  // the token wave holds no other loads
     };
 
     if (token_wave) {
@@ -344,7 +358,9 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int pp = k0 + 4 * g + i;
-                        v[i] = pp < cnt ? fw[pp] * fk[pp * DK + 32 * mw + 16 * rb + nn] : 0.0f;
+                        const int at = pp * DK + 32 * mw + 16 * rb + nn;
+                        const float kv = RAW ? load1(reinterpret_cast<const IO*>(fk) + at) : fk[at];
+                        v[i] = pp < cnt ? fw[pp] * kv : 0.0f;
                     }
                     mf_split3(v, bh[rb], bm[rb], bo[rb]);
                 }
@@ -352,13 +368,21 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h) {
                 for (int cb = 0; cb < 8; ++cb) {
                     // A: values x_p[c], column c = 16 cb + nn
                     float x[4];
+                    mf_s4 xb;  // raw bf16 rows: the bits themselves
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int pp = k0 + 4 * g + i;
-                        x[i] = pp < cnt ? fx[pp * DV + 16 * cb + nn] : 0.0f;
+                        const int at = pp * DV + 16 * cb + nn;
+                        if constexpr (RAW && XEXACT) {
+                            xb[i] = pp < cnt ? static_cast<short>(reinterpret_cast<const bf16_bits*>(fx)[at]) : 0;
+                        } else if constexpr (RAW) {
+                            x[i] = pp < cnt ? load1(reinterpret_cast<const XIO*>(fx) + at) : 0.0f;
+                        } else {
+                            x[i] = pp < cnt ? fx[at] : 0.0f;
+                        }
                     }
                     if constexpr (XEXACT) {
-                        const mf_s4 a = mf_exact(x);
+                        const mf_s4 a = RAW ? xb : mf_exact(x);
 #pragma unroll
                         for (int rb = 0; rb < 2; ++rb) {
                             f4 d = s[8 * rb + cb];
