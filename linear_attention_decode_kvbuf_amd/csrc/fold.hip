@@ -26,14 +26,33 @@
 namespace kvbuf {
 namespace {
 
-// LDS: pool row of each buffer position, cumulative log-gates, two staging
-// buffers of fc tokens (keys, values, weights), the state weight e^{b_{T-1}}
-// (per key channel for the per-channel rule: DK of them).
-__host__ __device__ inline int fold_stage_floats(int DK, int DV, int fc) {
-    return fc * (DK + DV) + ((fc + 3) & ~3);
+// LDS: pool row of each buffer position, cumulative log-gates, the weight
+// of every position (raw staging), nb staging buffers of fc tokens (keys,
+// values and -- fp32 staging -- weights), the state weight e^{b_{T-1}} (per
+// key channel for the per-channel rule: DK of them).  Keys and values are
+// staged as fp32 (kb = xb = 4) or, for the matrix-core folds, raw: as stored
+// in the pool (kb, xb = element bytes), by direct-to-LDS copies.
+__host__ __device__ inline int fold_stage_floats(int DK, int DV, int fc, int kb, int xb, bool raw) {
+    return (fc * (DK * kb + DV * xb)) / 4 + (raw ? 0 : ((fc + 3) & ~3));
 }
-__host__ __device__ inline int fold_lds_floats(int DK, int DV, int cap, int fc, bool ch) {
-    return 2 * ((cap + 3) & ~3) + 2 * fold_stage_floats(DK, DV, fc) + (ch ? DK : 4);
+__host__ __device__ inline int fold_lds_floats(int DK, int DV, int cap, int stage_floats, int nb, bool ch) {
+    return 2 * ((cap + 3) & ~3) + ((cap + 31) & ~31) + nb * stage_floats + (ch ? DK : 4);
+}
+// raw multi-round folds of bf16 rows keep this many staging buffers: the
+// copies of round r + 2 are in flight while round r is applied
+constexpr int kFoldRing = 3;
+
+// The barrier between ring rounds.  __syncthreads() makes every wave wait for
+// all of its outstanding memory operations, the direct-to-LDS copies of later
+// rounds included; here the token wave has already waited for the round that
+// is read next, and each wave only completes its LDS accesses (lgkmcnt(0))
+// before the barrier.  The signal fences keep the compiler from moving memory
+// accesses across it.
+__device__ __forceinline__ void ring_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
 // Copies rows src[k] -> dst[k], k < a (U 16-byte units per row) with one
@@ -90,6 +109,40 @@ __device__ __forceinline__ f4 mf_mac(mf_s4 a, mf_s4 b, f4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 
+// bf16 rows of 128 (256 bytes) staged for the 16 x 16 x 32 products.
+// v_mfma_f32_16x16x32_bf16 takes, in lane l (group G = l / 16, t = l % 16),
+// A[t][8G + i] and B[8G + i][t] for i < 8 and returns D[4G + j][t], j < 4;
+// ds_read_b64_tr_b16 gives lane t of a 16-lane group element j of source lane
+// 4j + t / 4, word t % 4.  So when the 16 lanes of group G point at rows
+// 8G + t / 4 (+ 4), columns c0 + 4 (t % 4) of a row-major tile, lane t
+// receives column c0 + t of rows 8G .. 8G + 3 (+ 4): the K-major operand
+// that the product wants, from rows as they were copied.  The 16-byte chunk
+// cc of row r sits at slot 16 r + (cc ^ f(r)), f(r) = 2 ((r & 3) | (((r >> 3)
+// & 1) << 2)), which spreads the 16 rows that one such read touches over all
+// LDS banks.
+typedef short tr_s4 __attribute__((ext_vector_type(4)));
+typedef __bf16 mf_b8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ int tr_swz(int r) { return 2 * ((r & 3) | (((r >> 3) & 1) << 2)); }
+template <typename SrcOf>
+__device__ __forceinline__ void lds_copy_swz(char* dst, int rows, SrcOf src, int lane) {
+    for (int r0 = 0; r0 < rows; r0 += 4) {
+        const int r = r0 + (lane >> 4);
+        const char* a = src(r < rows ? r : r0) + 16 * ((lane & 15) ^ tr_swz(r));
+        if (r < rows)
+            __builtin_amdgcn_global_load_lds(a, (__attribute__((address_space(3))) void*)(dst + r0 * 256), 16, 0, 0);
+    }
+}
+__device__ __forceinline__ tr_s4 tr_read(const char* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) tr_s4*)(p));
+}
+__device__ __forceinline__ mf_b8 tr_join(tr_s4 a, tr_s4 b) {
+    typedef short s8 __attribute__((ext_vector_type(8)));
+    return __builtin_bit_cast(mf_b8, s8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]});
+}
+__device__ __forceinline__ f4 mf_mac32(mf_b8 a, mf_b8 b, f4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
 // MULTI: the fold may take more than one staging round (then the token wave
 // stages round r+1 while the state waves apply round r).  Without it every
 // position is staged before the state loads are issued, which keeps the
@@ -117,6 +170,13 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h) {
     // round trip per staging round; the per-channel rule keeps fp32 rows,
     // whose keys carry per-channel decays)
     constexpr bool RAW = MF && !CH;
+    // (three buffers of fp32 rows would cost a workgroup per CU)
+    constexpr bool RING = RAW && MULTI && sizeof(XIO) == 2;
+    // multi-round folds of bf16 keys and values: 16 x 16 x 32 products on
+    // transposing LDS reads (their wider operands cost a wave per SIMD, which
+    // a single round does not win back)
+    constexpr bool TR = RAW && MULTI && sizeof(IO) == 2 && sizeof(XIO) == 2;
+    constexpr int NBUF = RING ? kFoldRing : 2;
 
     extern __shared__ __attribute__((aligned(16))) float lds[];  // 16-byte rows for the LDS copies
     __shared__ unsigned s_bad;
@@ -232,11 +292,16 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h) {
         return;
     }
 
-    const int fc = P.fold_chunk;
-    float* bl = lds + ((cap + 3) & ~3);
-    float* stage0 = bl + ((cap + 3) & ~3);
-    const int stage_floats = fold_stage_floats(DK, DV, fc);
-    float* e0p = stage0 + 2 * stage_floats;
+    // multi-round raw folds always take the full raw chunk (the launcher)
+    const int fc = RING ? kRawFoldChunk : P.fold_chunk;
+    const int cap4 = (cap + 3) & ~3;
+    float* bl = lds + cap4;
+    float* fwa = bl + cap4;  // raw staging: the weight of every position (0 up to a multiple of 32)
+    float* stage0 = fwa + ((cap + 31) & ~31);
+    constexpr int KB = RAW ? static_cast<int>(sizeof(IO)) : 4, XB = RAW ? static_cast<int>(sizeof(XIO)) : 4;
+    const int srows = TR ? 32 : fc;  // rows of a staging buffer (TR: a whole product chunk)
+    const int stage_floats = fold_stage_floats(DK, DV, srows, KB, XB, RAW);
+    float* e0p = stage0 + NBUF * stage_floats;
 
     TileTokens<DK, DV, IO, XIO> tok;
     tok.kpool = static_cast<const IO*>(P.key);
@@ -253,20 +318,39 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h) {
 #pragma unroll
     for (int c = 0; c < CPL; ++c) prefix[c] = 0.0f;
 
-    // Token wave: stage round r (tokens r*fc ..) into buffer r % 2.
+    // Token wave: stage round r (tokens r*fc ..) into buffer r % NBUF.  Raw
+    // rows are only issued here: stage() waits for them, a ring fold
+    // (ring_wait) counts them.
+    auto issue = [&](int r) {
+        char* fk = reinterpret_cast<char*>(stage0 + (r % NBUF) * stage_floats);
+        char* fx = fk + srows * DK * KB;
+        const int i0 = r * fc;
+        const int cnt = min(fc, T - i0);
+        auto key_row = [&](int ii) { return reinterpret_cast<const char*>(tok.key(i0 + ii)); };
+        auto value_row = [&](int ii) { return reinterpret_cast<const char*>(tok.pooled_value(i0 + ii)); };
+        if constexpr (TR) {
+            lds_copy_swz(fk, cnt, key_row, lane);
+            lds_copy_swz(fx, cnt, value_row, lane);
+            // rows past the end of a short round read as zeros
+            for (int q = cnt * 16 + lane; q < 32 * 16; q += 64) {
+                reinterpret_cast<uint4*>(fk)[q] = make_uint4(0u, 0u, 0u, 0u);
+                reinterpret_cast<uint4*>(fx)[q] = make_uint4(0u, 0u, 0u, 0u);
+            }
+        } else {
+            lds_copy_rows<DK * KB>(fk, cnt, key_row, lane);
+            lds_copy_rows<DV * XB>(fx, cnt, value_row, lane);
+        }
+    };
     auto stage = [&](int r) {
-        float* fk = stage0 + (r & 1) * stage_floats;
-        float* fx = fk + fc * DK;
-        float* fw = fx + fc * DV;
+        float* fk = stage0 + (r % NBUF) * stage_floats;
+        float* fx = fk + srows * DK * KB / 4;
+        float* fw = fx + srows * DV * XB / 4;
         const int i0 = r * fc;
         const int cnt = min(fc, T - i0);
         if constexpr (RAW) {
-            lds_copy_rows<DK * static_cast<int>(sizeof(IO))>(
-                reinterpret_cast<char*>(fk), cnt,
-                [&](int ii) { return reinterpret_cast<const char*>(tok.key(i0 + ii)); }, lane);
-            lds_copy_rows<DV * static_cast<int>(sizeof(XIO))>(
-                reinterpret_cast<char*>(fx), cnt,
-                [&](int ii) { return reinterpret_cast<const char*>(tok.pooled_value(i0 + ii)); }, lane);
+            issue(r);
+            wait_lds_copies();
+            return;
         } else {
             stage_rows(tok, i0, cnt, fk, fx, nullptr, lane);
         }
@@ -288,7 +372,20 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h) {
             for (int ii = lane; ii < cnt; ii += 64)
                 fw[ii] = SGATE ? exp_gate(bl[T - 1] - bl[i0 + ii]) : 1.0f;
         }
-        if constexpr (RAW) wait_lds_copies();  // the token wave holds no other loads
+    };
+    // Ring: wait until the copies of round r have landed while those of round
+    // r + 1 (if issued) may still be in flight.  The copies retire in order;
+    // a full round is a known number of copy instructions, a short (last)
+    // round waits for everything.
+    auto ring_wait = [&](int r) {
+        constexpr int RPIK = 64 / (DK * KB / 16), RPIX = 64 / (DV * XB / 16);
+        constexpr int FULL = (kRawFoldChunk + RPIK - 1) / RPIK + (kRawFoldChunk + RPIX - 1) / RPIX;
+        static_assert(FULL < 64, "vmcnt holds six bits");
+        if ((r + 2) * fc <= T)
+            __builtin_amdgcn_s_waitcnt((FULL & 15) | ((FULL >> 4) << 14) | 0x0F70);
+        else
+            __builtin_amdgcn_s_waitcnt(0x0F70);
+        __builtin_amdgcn_sched_barrier(0);
     };
 
     if (token_wave) {
@@ -305,7 +402,20 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h) {
         } else {
             if (lane == 0) *e0p = (SGATE && T > 0) ? exp_gate(bl[T - 1]) : 1.0f;
         }
-        if (T > 0) stage(0);
+        if constexpr (RAW) {
+            for (int i = lane; i < ((T + 31) & ~31); i += 64)
+                fwa[i] = i >= T ? 0.0f : SGATE ? exp_gate(bl[T - 1] - bl[i]) : 1.0f;
+        }
+        if constexpr (RING) {
+            // the metadata stores above have completed before any copy is
+            // counted (stores and loads share the counter)
+            __builtin_amdgcn_s_waitcnt(0x0F70);
+            if (T > 0) issue(0);
+            if (T > fc) issue(1);
+            ring_wait(0);
+        } else {
+            if (T > 0) stage(0);
+        }
         if (tree && !MULTI) move_kept();  // the fold's rows are staged
     }
     f4 s[RPT];
@@ -328,7 +438,8 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h) {
             load_tile<RPT, DK, DV>(s, tile, has_state, rg, c0);
         }
     }
-    __syncthreads();
+    if constexpr (RING) ring_barrier();  // round 0 has landed
+    else __syncthreads();
     if (!token_wave) {
         if constexpr (CH && MF) {
 #pragma unroll
@@ -343,10 +454,58 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h) {
         }
     }
     auto apply = [&](int r) {
-        const float* fk = stage0 + (r & 1) * stage_floats;
-        const float* fx = fk + fc * DK;
-        const float* fw = fx + fc * DV;
+        const float* fk = stage0 + (r % NBUF) * stage_floats;
+        const float* fx = fk + srows * DK * KB / 4;
+        const float* fw = RAW ? fwa + r * fc : fx + srows * DV * XB / 4;
         const int cnt = min(fc, T - r * fc);
+        if constexpr (TR) {
+            // lane ml: group G, row-in-group t; its read address inside a
+            // chunk of 32 rows for column block cbx (16 columns) and half h
+            const int G = ml >> 4, t = ml & 15;
+            const int lane_off = (8 * G + (t >> 2)) * 256 + 16 * ((t & 3) >> 1) + 8 * (t & 1);
+            const int f2 = (t >> 2) | ((G & 1) << 2);  // tr_swz of the row, halved
+            auto at = [&](const float* buf, int kb, int h, int cbx) {
+                return reinterpret_cast<const char*>(buf) + kb * 256 + h * 1024 + lane_off + 32 * (cbx ^ f2);
+            };
+            for (int kb = 0; kb < cnt; kb += 32) {
+                // B: w_p k_p[n] for positions kb + 8G + i, rows n = 32 mw + 16 rb + t
+                const f4 w0 = *reinterpret_cast<const f4*>(fw + kb + 8 * G);
+                const f4 w1 = *reinterpret_cast<const f4*>(fw + kb + 8 * G + 4);
+                mf_b8 bh[2], bm[2], bo[2];
+#pragma unroll
+                for (int rb = 0; rb < 2; ++rb) {
+                    const tr_s4 k0 = tr_read(at(fk, kb, 0, 2 * mw + rb));
+                    const tr_s4 k1 = tr_read(at(fk, kb, 1, 2 * mw + rb));
+                    float v0[4], v1[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        v0[i] = w0[i] * __uint_as_float(static_cast<uint32_t>(static_cast<uint16_t>(k0[i])) << 16);
+                        v1[i] = w1[i] * __uint_as_float(static_cast<uint32_t>(static_cast<uint16_t>(k1[i])) << 16);
+                    }
+                    mf_s4 h0, m0, o0, h1, m1, o1;
+                    mf_split3(v0, h0, m0, o0);
+                    mf_split3(v1, h1, m1, o1);
+                    bh[rb] = tr_join(h0, h1);
+                    bm[rb] = tr_join(m0, m1);
+                    bo[rb] = tr_join(o0, o1);
+                }
+                // A: x_p[c], columns c = 16 cb + t; each block takes its
+                // three products in the order hi, mid, lo
+#pragma unroll
+                for (int cb = 0; cb < 8; ++cb) {
+                    const mf_b8 a = tr_join(tr_read(at(fx, kb, 0, cb)), tr_read(at(fx, kb, 1, cb)));
+#pragma unroll
+                    for (int rb = 0; rb < 2; ++rb) {
+                        f4 d = s[8 * rb + cb];
+                        d = mf_mac32(a, bh[rb], d);
+                        d = mf_mac32(a, bm[rb], d);
+                        d = mf_mac32(a, bo[rb], d);
+                        s[8 * rb + cb] = d;
+                    }
+                }
+            }
+            return;
+        }
         if constexpr (MF) {
             const int g = ml >> 4, nn = ml & 15;
             for (int k0 = 0; k0 < cnt; k0 += 16) {
@@ -423,11 +582,18 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h) {
         const int rounds = (T + fc - 1) / fc;
         for (int r = 0; r < rounds; ++r) {
             if (token_wave) {
-                if (r + 1 < rounds) stage(r + 1);
+                if constexpr (RING) {
+                    // buffer (r + 2) % 3 was last read by round r - 1
+                    if (r + 2 < rounds) issue(r + 2);
+                    if (r + 1 < rounds) ring_wait(r + 1);
+                } else {
+                    if (r + 1 < rounds) stage(r + 1);
+                }
             } else {
                 apply(r);
             }
-            __syncthreads();
+            if constexpr (RING) ring_barrier();
+            else __syncthreads();
         }
         if (tree && token_wave) move_kept();  // every round is staged
     }
@@ -495,29 +661,40 @@ template <int RULE, int D, typename IO>
 hipError_t launch_fold_t(const TileParams& p, int batch, hipStream_t s) {
     using G = Geo<D, D>;
     const int cap = p.block_size * p.blocks_per_req;
-    const size_t lds = sizeof(float) * fold_lds_floats(D, D, cap, p.fold_chunk, RULE == KVBUF_RULE_CHANNEL);
     const int most = p.mode == MODE_MATERIALIZE ? cap : p.m;  // most positions one tile applies
     const dim3 grid(static_cast<unsigned>(batch) * p.H), block(G::NTHREADS);
     const bool tree = p.leaf != nullptr;
-    // multi-round folds always exceed 16 positions (fold_chunk >= 16 when m > 16)
-    const bool multi = most > p.fold_chunk;
     const bool mf = most > 16;
-    if (p.sparse) {  // a flush after a decode launch (never a tree commit)
-        const dim3 sgrid((static_cast<unsigned>(batch) * p.H + kSparseTiles - 1) / kSparseTiles);
-        if (multi) fold_sparse_kernel<RULE, D, D, IO, true, true><<<sgrid, block, lds, s>>>(p);
-        else if (mf) fold_sparse_kernel<RULE, D, D, IO, false, true><<<sgrid, block, lds, s>>>(p);
-        else fold_sparse_kernel<RULE, D, D, IO, false, false><<<sgrid, block, lds, s>>>(p);
+    // the matrix-core instances (d = 128) stage pool rows as stored, except
+    // under the per-channel rule
+    constexpr bool CH = RULE == KVBUF_RULE_CHANNEL;
+    const bool raw = mf && D == 128 && !CH;
+    const int kb = raw ? static_cast<int>(sizeof(IO)) : 4;
+    const int xb = raw && RULE != KVBUF_RULE_DELTA ? static_cast<int>(sizeof(IO)) : 4;
+    TileParams q = p;
+    q.fold_chunk = std::min(most, raw ? kRawFoldChunk : kFoldChunk);
+    // multi-round folds always exceed 16 positions (the chunk is at least 16 then)
+    const bool multi = most > q.fold_chunk;
+    const bool tr = raw && multi && kb == 2 && xb == 2;  // staged in whole chunks of 32 rows
+    const size_t lds = sizeof(float) * fold_lds_floats(D, D, cap,
+                                                       fold_stage_floats(D, D, tr ? 32 : q.fold_chunk, kb, xb, raw),
+                                                       raw && multi && xb == 2 ? kFoldRing : 2, CH);
+    if (q.sparse) {  // a flush after a decode launch (never a tree commit)
+        const dim3 sgrid((static_cast<unsigned>(batch) * q.H + kSparseTiles - 1) / kSparseTiles);
+        if (multi) fold_sparse_kernel<RULE, D, D, IO, true, true><<<sgrid, block, lds, s>>>(q);
+        else if (mf) fold_sparse_kernel<RULE, D, D, IO, false, true><<<sgrid, block, lds, s>>>(q);
+        else fold_sparse_kernel<RULE, D, D, IO, false, false><<<sgrid, block, lds, s>>>(q);
         return hipGetLastError();
     }
     if (multi) {
-        if (tree) fold_kernel<RULE, D, D, IO, true, true, true><<<grid, block, lds, s>>>(p);
-        else fold_kernel<RULE, D, D, IO, true, false, true><<<grid, block, lds, s>>>(p);
+        if (tree) fold_kernel<RULE, D, D, IO, true, true, true><<<grid, block, lds, s>>>(q);
+        else fold_kernel<RULE, D, D, IO, true, false, true><<<grid, block, lds, s>>>(q);
     } else if (mf) {
-        if (tree) fold_kernel<RULE, D, D, IO, false, true, true><<<grid, block, lds, s>>>(p);
-        else fold_kernel<RULE, D, D, IO, false, false, true><<<grid, block, lds, s>>>(p);
+        if (tree) fold_kernel<RULE, D, D, IO, false, true, true><<<grid, block, lds, s>>>(q);
+        else fold_kernel<RULE, D, D, IO, false, false, true><<<grid, block, lds, s>>>(q);
     } else {
-        if (tree) fold_kernel<RULE, D, D, IO, false, true, false><<<grid, block, lds, s>>>(p);
-        else fold_kernel<RULE, D, D, IO, false, false, false><<<grid, block, lds, s>>>(p);
+        if (tree) fold_kernel<RULE, D, D, IO, false, true, false><<<grid, block, lds, s>>>(q);
+        else fold_kernel<RULE, D, D, IO, false, false, false><<<grid, block, lds, s>>>(q);
     }
     return hipGetLastError();
 }

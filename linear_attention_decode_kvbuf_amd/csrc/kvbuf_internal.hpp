@@ -73,6 +73,7 @@ inline bool supported_dim(int d) { return d == 16 || d == 64 || d == 128; }
 
 constexpr int kMaxDrafts = 8;
 constexpr int kFoldChunk = 32;  // most tokens staged in LDS per fold round
+constexpr int kRawFoldChunk = 32;  // ... when staged as stored (bf16 rows take half the LDS)
 constexpr int kMaxTableRow = 64;
 
 }  // namespace kvbuf
