@@ -132,8 +132,30 @@ __device__ __forceinline__ void lds_copy_swz(char* dst, int rows, SrcOf src, int
             __builtin_amdgcn_global_load_lds(a, (__attribute__((address_space(3))) void*)(dst + r0 * 256), 16, 0, 0);
     }
 }
+// fp32 rows of 128 (512 bytes, the delta rule's pseudo-values), read one
+// word per lane: chunk cc of row r at slot 32 r + (cc ^ 4 ((r >> 3) & 3)), so
+// that the four rows 8G + i (G < 4) of one read land in different banks.
+template <typename SrcOf>
+__device__ __forceinline__ void lds_copy_swz32(char* dst, int rows, SrcOf src, int lane) {
+    for (int r0 = 0; r0 < rows; r0 += 2) {
+        const int r = r0 + (lane >> 5);
+        const char* a = src(r < rows ? r : r0) + 16 * ((lane & 31) ^ (4 * ((r >> 3) & 3)));
+        if (r < rows)
+            __builtin_amdgcn_global_load_lds(a, (__attribute__((address_space(3))) void*)(dst + r0 * 512), 16, 0, 0);
+    }
+}
+// LDS byte address of a pointer into the workgroup's LDS, and reads at one
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)(p)));
+}
 __device__ __forceinline__ tr_s4 tr_read(const char* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) tr_s4*)(p));
+}
+__device__ __forceinline__ tr_s4 tr_read(uint32_t a) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) tr_s4*)(uintptr_t)(a));
+}
+__device__ __forceinline__ float lds_f32(uint32_t a) {
+    return *(__attribute__((address_space(3))) const float*)(uintptr_t)(a);
 }
 __device__ __forceinline__ mf_b8 tr_join(tr_s4 a, tr_s4 b) {
     typedef short s8 __attribute__((ext_vector_type(8)));
@@ -172,10 +194,15 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h) {
     constexpr bool RAW = MF && !CH;
     // (three buffers of fp32 rows would cost a workgroup per CU)
     constexpr bool RING = RAW && MULTI && sizeof(XIO) == 2;
-    // multi-round folds of bf16 keys and values: 16 x 16 x 32 products on
-    // transposing LDS reads (their wider operands cost a wave per SIMD, which
-    // a single round does not win back)
-    constexpr bool TR = RAW && MULTI && sizeof(IO) == 2 && sizeof(XIO) == 2;
+    // multi-round folds of bf16 keys: 16 x 16 x 32 products on transposing
+    // LDS reads (their wider operands cost a wave per SIMD, which a single
+    // round does not win back).  bf16 values enter as they are and the
+    // weighted keys as three terms; the delta rule's fp32 pseudo-values carry
+    // the weight and enter as three terms against the keys as they are.
+    constexpr bool TR = RAW && MULTI && sizeof(IO) == 2;
+    // ... and then each state wave holds 32 columns of the tile (all rows),
+    // so that it splits only its own columns of the pseudo-values
+    constexpr bool COLS = TR && !XEXACT;
     constexpr int NBUF = RING ? kFoldRing : 2;
 
     extern __shared__ __attribute__((aligned(16))) float lds[];  // 16-byte rows for the LDS copies
@@ -329,13 +356,15 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h) {
         auto key_row = [&](int ii) { return reinterpret_cast<const char*>(tok.key(i0 + ii)); };
         auto value_row = [&](int ii) { return reinterpret_cast<const char*>(tok.pooled_value(i0 + ii)); };
         if constexpr (TR) {
+            constexpr int XC = DV * XB / 16;  // 16-byte chunks of a value row
             lds_copy_swz(fk, cnt, key_row, lane);
-            lds_copy_swz(fx, cnt, value_row, lane);
+            if constexpr (XB == 2) lds_copy_swz(fx, cnt, value_row, lane);
+            else lds_copy_swz32(fx, cnt, value_row, lane);
             // rows past the end of a short round read as zeros
-            for (int q = cnt * 16 + lane; q < 32 * 16; q += 64) {
+            for (int q = cnt * 16 + lane; q < 32 * 16; q += 64)
                 reinterpret_cast<uint4*>(fk)[q] = make_uint4(0u, 0u, 0u, 0u);
+            for (int q = cnt * XC + lane; q < 32 * XC; q += 64)
                 reinterpret_cast<uint4*>(fx)[q] = make_uint4(0u, 0u, 0u, 0u);
-            }
         } else {
             lds_copy_rows<DK * KB>(fk, cnt, key_row, lane);
             lds_copy_rows<DV * XB>(fx, cnt, value_row, lane);
@@ -421,6 +450,10 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h) {
     f4 s[RPT];
     const int mw = tid >> 6, ml = tid & 63;  // MF: wave and lane
     auto mf_offset = [&](int j) {            // MF: float offset of s[j] in the tile
+        if constexpr (COLS) {                // rows 16 (j / 2) + l % 16, columns 32 mw + 16 (j % 2) + 4 (l / 16)
+            const int row = 16 * (j >> 1) + (ml & 15);
+            return row * DV + 32 * mw + 16 * (j & 1) + 4 * (ml >> 4);
+        }
         const int row = 32 * mw + 16 * (j >> 3) + (ml & 15);
         return row * DV + 16 * (j & 7) + 4 * (ml >> 4);
     };
@@ -462,12 +495,63 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h) {
             // lane ml: group G, row-in-group t; its read address inside a
             // chunk of 32 rows for column block cbx (16 columns) and half h
             const int G = ml >> 4, t = ml & 15;
-            const int lane_off = (8 * G + (t >> 2)) * 256 + 16 * ((t & 3) >> 1) + 8 * (t & 1);
             const int f2 = (t >> 2) | ((G & 1) << 2);  // tr_swz of the row, halved
+            const int lane_off = (8 * G + (t >> 2)) * 256 + 16 * ((t & 3) >> 1) + 8 * (t & 1);
             auto at = [&](const float* buf, int kb, int h, int cbx) {
                 return reinterpret_cast<const char*>(buf) + kb * 256 + h * 1024 + lane_off + 32 * (cbx ^ f2);
             };
+            // The same as an LDS address, formed so that the compiler does not
+            // keep the eight column offsets in registers: staging buffers sit
+            // at multiples of 512 bytes from the first, so the swizzle is an
+            // XOR of the offset bits that select the 32-byte column pair.
+            const uint32_t base0 = lds_addr(stage0);
+            auto rel = [&](const float* buf) { return static_cast<uint32_t>((buf - stage0) * 4); };
+            auto at_x = [&](const float* buf, int kb, int h, int cbx) {
+                return base0 + ((rel(buf) + kb * 256 + h * 1024 + lane_off + 32 * f2) ^ static_cast<uint32_t>(32 * cbx));
+            };
             for (int kb = 0; kb < cnt; kb += 32) {
+                if constexpr (COLS) {
+                    // A: w_p u_p[c] in three terms, for this wave's columns
+                    // c = 32 mw + 16 cb + t, read one word per lane from the
+                    // swizzled fp32 rows; B: k_p[n] as stored, n = 16 rb + t
+                    // (read again for the second column block: holding all
+                    // eight would cost a wave per SIMD)
+#pragma unroll
+                    for (int cb = 0; cb < 2; ++cb) {
+                        const uint32_t xr = base0 + ((rel(fx) + (kb + 8 * G) * 512 + 64 * G + 4 * t) ^
+                                                     static_cast<uint32_t>(64 * (2 * mw + cb)));
+                        const f4 w0 = *reinterpret_cast<const f4*>(fw + kb + 8 * G);
+                        const f4 w1 = *reinterpret_cast<const f4*>(fw + kb + 8 * G + 4);
+                        float v0[4], v1[4];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            v0[i] = w0[i] * lds_f32(xr + i * 512);
+                            v1[i] = w1[i] * lds_f32(xr + (i + 4) * 512);
+                        }
+                        mf_s4 h0, m0, o0, h1, m1, o1;
+                        mf_split3(v0, h0, m0, o0);
+                        mf_split3(v1, h1, m1, o1);
+                        const mf_b8 ah = tr_join(h0, h1), am = tr_join(m0, m1), ao = tr_join(o0, o1);
+                        auto keys = [&](int rb) {
+                            return tr_join(tr_read(at_x(fk, kb, 0, rb)), tr_read(at_x(fk, kb, 1, rb)));
+                        };
+                        // one row block's keys at a time: the scheduling
+                        // barriers keep the compiler from hoisting all eight
+                        // (registers); other waves cover the read latency
+#pragma unroll
+                        for (int rb = 0; rb < 8; ++rb) {
+                            const mf_b8 kr = keys(rb);
+                            f4 d = s[2 * rb + cb];
+                            d = mf_mac32(ah, kr, d);
+                            d = mf_mac32(am, kr, d);
+                            d = mf_mac32(ao, kr, d);
+                            s[2 * rb + cb] = d;
+                            __builtin_amdgcn_sched_barrier(0);
+                        }
+                        asm volatile("" ::: "memory");  // the key reads are not merged across column blocks
+                    }
+                    continue;
+                }
                 // B: w_p k_p[n] for positions kb + 8G + i, rows n = 32 mw + 16 rb + t
                 const f4 w0 = *reinterpret_cast<const f4*>(fw + kb + 8 * G);
                 const f4 w1 = *reinterpret_cast<const f4*>(fw + kb + 8 * G + 4);
@@ -609,7 +693,8 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h) {
 
 // One workgroup per tile.
 template <int RULE, int DK, int DV, typename IO, bool MULTI, bool TREE, bool MFT>
-__global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void fold_kernel(TileParams P) {
+__global__ __launch_bounds__((Geo<DK, DV>::NTHREADS))
+__attribute__((amdgpu_waves_per_eu(RULE == KVBUF_RULE_DELTA && MULTI ? 4 : 1))) void fold_kernel(TileParams P) {
     const TileIndex ti = tile_index(P);
     fold_tile<RULE, DK, DV, IO, MULTI, TREE, MFT>(P, ti.b, ti.h);
 }
@@ -675,7 +760,7 @@ hipError_t launch_fold_t(const TileParams& p, int batch, hipStream_t s) {
     q.fold_chunk = std::min(most, raw ? kRawFoldChunk : kFoldChunk);
     // multi-round folds always exceed 16 positions (the chunk is at least 16 then)
     const bool multi = most > q.fold_chunk;
-    const bool tr = raw && multi && kb == 2 && xb == 2;  // staged in whole chunks of 32 rows
+    const bool tr = raw && multi && kb == 2;  // staged in whole chunks of 32 rows
     const size_t lds = sizeof(float) * fold_lds_floats(D, D, cap,
                                                        fold_stage_floats(D, D, tr ? 32 : q.fold_chunk, kb, xb, raw),
                                                        raw && multi && xb == 2 ? kFoldRing : 2, CH);
