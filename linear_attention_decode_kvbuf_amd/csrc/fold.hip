@@ -171,7 +171,7 @@ __device__ __forceinline__ f4 mf_mac32(mf_b8 a, mf_b8 b, f4 c) {
 // token wave's registers out of the tile's live range.
 // TREE: a commit of a root-to-leaf path of tree drafts.
 template <int RULE, int DK, int DV, typename IO, bool MULTI, bool TREE, bool MFT>
-__device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h) {
+__device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h, int tid) {
     using G = Geo<DK, DV>;
     constexpr int NT = G::NT, TPR = G::TPR, RPT = G::RPT;
     constexpr bool DELTA = RULE == KVBUF_RULE_DELTA;
@@ -212,7 +212,6 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h) {
     // (dst) its move to buffer position p + k
     __shared__ uint32_t s_src[TREE ? kMaxDrafts : 1], s_dst[TREE ? kMaxDrafts : 1];
 
-    const int tid = threadIdx.x;
     const bool token_wave = tid >= NT;
     const int lane = tid - NT;
     const int rg = tid / TPR;
@@ -696,7 +695,7 @@ template <int RULE, int DK, int DV, typename IO, bool MULTI, bool TREE, bool MFT
 __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS))
 __attribute__((amdgpu_waves_per_eu(RULE == KVBUF_RULE_DELTA && MULTI ? 4 : 1))) void fold_kernel(TileParams P) {
     const TileIndex ti = tile_index(P);
-    fold_tile<RULE, DK, DV, IO, MULTI, TREE, MFT>(P, ti.b, ti.h);
+    fold_tile<RULE, DK, DV, IO, MULTI, TREE, MFT>(P, ti.b, ti.h, threadIdx.x);
 }
 
 // The flush that follows a decode launch whose eager fold does not fit the
@@ -708,7 +707,8 @@ __attribute__((amdgpu_waves_per_eu(RULE == KVBUF_RULE_DELTA && MULTI ? 4 : 1))) 
 // dispatch, a metadata round trip and a barrier for every tile at every step.
 constexpr int kSparseTiles = 8;
 template <int RULE, int DK, int DV, typename IO, bool MULTI, bool MFT>
-__global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void fold_sparse_kernel(TileParams P) {
+__global__ __launch_bounds__((Geo<DK, DV>::NTHREADS))
+__attribute__((amdgpu_waves_per_eu(MULTI ? 4 : 1))) void fold_sparse_kernel(TileParams P) {
     constexpr int NT = Geo<DK, DV>::NT;
     __shared__ uint32_t s_mask;
     const int ntiles = P.batch * P.H;
@@ -738,7 +738,12 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void fold_sparse_kernel(Ti
         later = true;
         const int t = first + k;
         const int h = t / P.batch;
-        fold_tile<RULE, DK, DV, IO, MULTI, false, MFT>(P, t - h * P.batch, h);
+        // the thread index is made opaque to the compiler in each
+        // iteration, so that it does not keep every lane-derived value of the
+        // tile code live across the loop
+        int tid = threadIdx.x;
+        asm volatile("" : "+v"(tid));
+        fold_tile<RULE, DK, DV, IO, MULTI, false, MFT>(P, t - h * P.batch, h, tid);
     }
 }
 
