@@ -683,10 +683,17 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h, int
     if (!token_wave) {
         float* dst = materialize ? P.states_out + (static_cast<size_t>(b) * P.H + h) * DK * DV
                                  : P.state + (static_cast<size_t>(slot) * P.H + h) * DK * DV;
+        // The matrix-core layout writes 64-byte runs of a row per store;
+        // streaming (non-temporal) stores of such runs reach HBM as partial
+        // lines (22-45% more bytes written, measured), ordinary stores merge
+        // in L2 first.  Whole rows (the vector layout) stream.
 #pragma unroll
-        for (int j = 0; j < RPT; ++j)
-            __builtin_nontemporal_store(
-                s[j], reinterpret_cast<f4*>(dst + (MF ? mf_offset(j) : (rg * RPT + j) * DV + c0)));
+        for (int j = 0; j < RPT; ++j) {
+            if constexpr (MF)
+                *reinterpret_cast<f4*>(dst + mf_offset(j)) = s[j];
+            else
+                __builtin_nontemporal_store(s[j], reinterpret_cast<f4*>(dst + (rg * RPT + j) * DV + c0));
+        }
     }
 }
 
