@@ -172,6 +172,28 @@ def test_tree_verify_commit(rule, d, io, n):
         run.check_bookkeeping()
 
 
+@pytest.mark.parametrize("rule,io", [(1, "bf16"), (2, "bf16"), (0, "f32")])
+def test_tree_commit_long_fold(rule, io):
+    """Tree commits that fill a buffer of m = 48 at d = 128: the commit's fold
+    takes two staging rounds on the matrix cores (bf16 keys: the transposing
+    reads; fp32 rows: the plain ones) while the kept drafts move to their
+    path positions."""
+    w = synth.workload(1, B=3, H=2, dk=128, dv=128, m=48, block_size=16, blocks_per_req=4, steps=60,
+                       rule=rule, io=io, state_std=0.02)
+    _say("tree long fold", w)
+    run = Run(w)
+    t = 0
+    for call in range(12):
+        for _ in range(4):
+            run.decode(t)
+            t += 1
+        parent, leaf = synth.draft_tree(w, call, w.B, 8)
+        run.verify_tree_commit(call, parent, leaf)
+        run.check_effective_states()
+        run.check_pool()
+        run.check_bookkeeping()
+
+
 @pytest.mark.parametrize("rule", [1, 2])
 def test_tree_deferred_with_flush_and_stars(rule):
     """Deferred policy: tree commits only append; kvbuf_flush after each call
@@ -551,3 +573,57 @@ def test_verify_recurrent_baseline(rule, n, d):
     torch.cuda.synchronize()
     assert int(run.kv.error.item()) & kb.DEVERR_ACCEPT
     assert torch.equal(run.kv.state[run.slots[0]], snap[run.slots[0]])
+
+
+@pytest.mark.parametrize("rule,m", [(1, 64), (1, 128), (2, 64), (2, 128)])
+def test_long_fold_full_size(rule, m):
+    """kvbuf_flush of m buffered tokens at B=256 H=32 d=128, bf16, in the
+    launch configuration the benchmark times (a block of m per request):
+    sampled tiles against the recurrence over their m buffered tokens -- for
+    the delta rule over its stored pseudo-values, which a fold applies as the
+    values of the scalar-gated rule."""
+    import oracle
+    from tests.harness import TOL_STATE, rel_err_tiles
+
+    B, H, d = 256, 32, 128
+    dev = torch.device("cuda:0")
+    kv = kb.KVBuffer(batch=B, heads=H, d=d, m=m, block_size=m, blocks_per_req=1, num_blocks=B,
+                     num_state_slots=B, rule=rule, io_dtype=kb.BF16, flush=kb.FLUSH_DEFERRED, device=dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(9100 + 10 * rule + m)
+    kv.state.normal_(0.0, 0.02, generator=gen)
+    kv.key.normal_(generator=gen)
+    kv.value.normal_(generator=gen)
+    kv.gate.uniform_(-0.1, 0.0, generator=gen)
+    # sampled tiles: seeded host data written into their state slots and blocks
+    rs = np.random.default_rng(9200 + 10 * rule + m)
+    flat = [0, B * H - 1] + [int(x) for x in rs.choice(np.arange(1, B * H - 1), 10, replace=False)]
+    tiles = [(f // H, f % H) for f in flat]
+    n = len(tiles)
+    bf16 = lambda a: torch.from_numpy(a).to(torch.bfloat16).float().numpy()
+    S0 = rs.normal(0.0, 0.02, (n, d, d)).astype(np.float32)
+    K = bf16(rs.normal(size=(m, n, d)).astype(np.float32))
+    V = rs.normal(size=(m, n, d)).astype(np.float32)
+    if rule != kb.RULE_DELTA:
+        V = bf16(V)
+    G = rs.uniform(-0.1, 0.0, (m, n)).astype(np.float32)
+    slot = kv.state_slot.cpu().numpy()
+    block = kv.block_table.cpu().numpy()
+    for j, (b, h) in enumerate(tiles):
+        s, blk = int(slot[b]), int(block[b, h, 0])
+        kv.state[s, h] = torch.from_numpy(S0[j]).to(dev)
+        kv.key[blk, h] = torch.from_numpy(K[:, j]).to(dev, kv.key.dtype)
+        kv.value[blk, h] = torch.from_numpy(V[:, j]).to(dev, kv.value.dtype)
+        kv.gate[blk, h] = torch.from_numpy(G[:, j]).to(dev)
+    kv.occupancy.fill_(m)
+    _say("long fold full size rule %d m %d" % (rule, m))
+    kv.flush()
+    torch.cuda.synchronize()
+    assert int(kv.error.item()) == 0
+    assert int(kv.occupancy.abs().sum().item()) == 0
+    assert np.array_equal(kv.block_table.cpu().numpy(), block)  # one block per request rotates onto itself
+    _, S_ref = oracle.recurrent(kb.RULE_GATED, S0, np.zeros((m, n, d)), K, V, G)
+    S_gpu = np.stack([kv.state[int(slot[b]), h].cpu().numpy() for b, h in tiles])
+    err = rel_err_tiles(S_gpu, S_ref, axes=(-2, -1))
+    _say("max state err %.2e" % err)
+    assert err <= TOL_STATE, "state error %.3e" % err
