@@ -145,6 +145,18 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void decode_kernel(TilePar
         }
         RawChunk<IO, E> qc;
         qc.load(qin + cl * E);
+        // per-channel rule: this lane's channels of the query and of the new
+        // token's gate row, loaded with the rest (each later use would
+        // otherwise cost the chain a round trip)
+        float qch[CH ? CPL : 1], gnew[CH ? CPL : 1];
+        if constexpr (CH) {
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+                const int ch = lane + 64 * c;
+                qch[c] = ch < DK ? load1(qin + ch) : 0.0f;
+                gnew[c] = ch < DK ? P.g[in_row * DK + ch] : 0.0f;
+            }
+        }
         RawChunk<IO, E> kc[NB];
         RawChunk<IO, EV> vc[NB];
         uint32_t pr[NB];
@@ -186,7 +198,7 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void decode_kernel(TilePar
                     }
                     const float ebt = exp_gate(run);
                     btv[ch] = ebt;                              // e^{B_t}
-                    qdv[ch] = load1(qin + ch) * ebt;            // e^{B_t} q
+                    qdv[ch] = qch[c] * ebt;                     // e^{B_t} q
                     if (fold) frow[ch] = exp_gate(-dg[(P.m - 1) * DK + ch]);  // e^{B_{m-1} - B_t}
                 }
             }
@@ -265,8 +277,11 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void decode_kernel(TilePar
         }
         if constexpr (CH) {  // the new token's gate row
             const uint32_t prow_t = static_cast<uint32_t>(__shfl(static_cast<int>(prow), pc, 64));
-            for (int ch = lane; !bad && ch < DK; ch += 64)
-                P.gate[static_cast<size_t>(prow_t) * DK + ch] = P.g[in_row * DK + ch];
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+                const int ch = lane + 64 * c;
+                if (!bad && ch < DK) P.gate[static_cast<size_t>(prow_t) * DK + ch] = gnew[c];
+            }
         }
         if (fold && !CH) {
             const float bm = __shfl(bcum, P.m - 1, 64);
