@@ -14,13 +14,16 @@
 // a rank-T update of the d_k x d_v tile (x_i = v_i, or the delta rule's
 // pseudo-value u_i).  With one log-gate per key channel the decays are
 // vectors and act on rows: row r of S0 is scaled by e^{B_{T-1}[r]} and k_i[r]
-// by e^{B_{T-1}[r] - B_i[r]} (B the per-channel cumulative log-gate).  One workgroup per (request, head): the state waves put
-// the 64 KiB tile in flight while the token wave forms the decay weights and
-// stages the keys and values in LDS (double-buffered rounds of up to 32
-// tokens); the state waves apply the update from registers and write the tile
-// back.  For the buffer sizes served here the update costs 2 T flops per 8
-// bytes of state traffic -- below the fp32 vector ridge of the chip -- so it
-// runs on the vector ALUs and the kernel is bound by HBM bandwidth.
+// by e^{B_{T-1}[r] - B_i[r]} (B the per-channel cumulative log-gate).
+//
+// One workgroup per (request, head): the state waves put the 64 KiB tile in
+// flight while the token wave forms the decay weights and stages the keys and
+// values in LDS (rounds of up to 32 tokens); the state waves apply the update
+// from registers and write the tile back.  The update costs 2 T flops per 8
+// bytes of state traffic: short folds (T <= 16) run on the vector ALUs, longer
+// ones on the matrix cores, whose fp32 operands enter as exact bf16 terms --
+// every workgroup of a launch runs the same phases in step, so the arithmetic
+// of a round adds to the time unless it is short.
 #include "device_common.hpp"
 
 namespace kvbuf {
