@@ -332,6 +332,17 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
     }
     float graw = 0.f;  // log-gate of position tid
     if (GATED && tid < T) graw = tok.gate(tid);
+    // delta rule, one new token: its value and step size for this thread's
+    // column (step 6), loaded with the rest rather than after the reductions
+    constexpr bool PRE = DELTA && NQ == 1;
+    float vpre = 0.f, bpre = 0.f;
+    if constexpr (PRE) {
+        static_assert(NT >= DV, "one column per thread");
+        if (n > 0 && tid < DV) {
+            vpre = load1(tok.new_value(0) + tid);
+            bpre = P.beta[in_row];
+        }
+    }
     RawChunk<IO, E> kr;
     RawChunk<XIO, EV> xr;
     auto load_pass = [&](int i0) {
@@ -621,11 +632,11 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
                 u[d] = 0.f;
                 if (d < n) {
                     const int t = p + d;
-                    float x = load1(tok.new_value(d) + c) - lds[L.sk + d * DV + c];
+                    float x = (PRE ? vpre : load1(tok.new_value(d) + c)) - lds[L.sk + d * DV + c];
                     float o = lds[L.sq + d * DV + c];
 #pragma unroll
                     for (int e = 0; e < d; ++e) x -= ck[d * ldc + p + e] * u[e];
-                    x *= P.beta[in_row + static_cast<size_t>(d) * P.H];
+                    x *= PRE ? bpre : P.beta[in_row + static_cast<size_t>(d) * P.H];
                     u[d] = x;
 #pragma unroll
                     for (int e = 0; e <= d; ++e) o += cq[d * ldc + p + e] * u[e];
