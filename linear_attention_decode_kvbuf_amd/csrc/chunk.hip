@@ -384,8 +384,17 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
             if constexpr (DELTA) kdraw[r].store(kdr + d * DK + cl * E);
         }
     }
-    if (GATED && tid < T) bl[tid] = graw;
-    for (int i = NT + tid; GATED && i < T; i += NT) bl[i] = tok.gate(i);  // long buffers only
+    // log-gates of every position; the new tokens' (positions p ..) are also
+    // appended to the pool from here
+    if (GATED && tid < T) {
+        bl[tid] = graw;
+        if (tid >= p) P.gate[tok.slot_index(tid)] = graw;
+    }
+    for (int i = NT + tid; GATED && i < T; i += NT) {  // long buffers only
+        const float gi = tok.gate(i);
+        bl[i] = gi;
+        if (i >= p) P.gate[tok.slot_index(i)] = gi;
+    }
     auto stage_pass = [&](int i0) {
         const int i = i0 + gp;
         if (i < T) {
@@ -544,7 +553,6 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
             xr.store(vrs + gp * DV + cl * EV);
         }
     }
-    if (GATED && tid < n) P.gate[tok.slot_index(p + tid)] = tok.gin[tid * P.H];
     if (fold && tid < P.m) fw[tid] = GATED ? exp_gate(bl[P.m - 1] - bl[tid]) : 1.0f;
 
     // ---- 5. the state tile: S^T q (and S^T k), reduced over row groups --------
