@@ -205,6 +205,7 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void decode_kernel(TilePar
         }
 
         // cumulative log-gates b_i of positions 0 .. T-1, lane i holds b_i
+        const float graw = g;  // the new token's log-gate in lane pc, appended below
         float bcum = 0.0f;
         if constexpr (GATED) {
 #pragma unroll
@@ -273,7 +274,7 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void decode_kernel(TilePar
             for (int e = 0; e < EV; ++e) obuf[cl * EV + e] = ob[e];
         }
         if constexpr (GATED) {
-            if (!bad && lane == pc) P.gate[prow] = P.g[in_row];
+            if (!bad && lane == pc) P.gate[prow] = graw;
         }
         if constexpr (CH) {  // the new token's gate row
             const uint32_t prow_t = static_cast<uint32_t>(__shfl(static_cast<int>(prow), pc, 64));
