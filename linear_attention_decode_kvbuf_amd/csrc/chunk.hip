@@ -680,7 +680,7 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
 
     // ---- 8. metadata: occupancy over the appended tokens, table rotation -----
     if (tid < 64 && P.mode != MODE_VERIFY)  // drafts do not advance the occupancy
-        update_meta(P, b, h, fold ? T - P.m : T, fold ? P.m / P.block_size : 0, tid);
+        update_meta(P, b, h, fold ? T - P.m : T, fold ? P.m / P.block_size : 0, tid, blk);
 }
 
 template <int RULE, int D, typename IO, bool TREE>

@@ -296,7 +296,7 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void decode_kernel(TilePar
         }
         // this wave read the tile's metadata above; advance it in place
         if (!bad && P.mode != MODE_VERIFY)
-            update_meta(P, b, h, fold ? Tl - P.m : Tl, fold ? P.m / bs : 0, lane);
+            update_meta(P, b, h, fold ? Tl - P.m : Tl, fold ? P.m / bs : 0, lane, blk);
     }
 
     // ---- state waves: query rows, then the tile; S0^T q per row group ----------

@@ -375,31 +375,32 @@ __device__ __forceinline__ size_t meta_index(const TileParams& P, int b, int h) 
     return static_cast<size_t>(b) * P.H + h;
 }
 
-// By the wave that read the metadata (lane = 0..63): occupancy <- p_new and,
-// when k > 0, the first k table entries move to the back (the blocks a fold
-// consumed).  Every lane reads its source entry in one instruction before any
-// lane writes.
-__device__ __forceinline__ void update_meta(const TileParams& P, int b, int h, int p_new, int k, int lane) {
+// By the wave that read the metadata (lane = 0..63, all active; blk = table
+// entry `lane` as read, see load_table_row): occupancy <- p_new and, when
+// k > 0, the first k table entries move to the back (the blocks a fold
+// consumed), rotated in registers -- re-reading the row would put a round
+// trip at the end of the wave's chain.
+__device__ __forceinline__ void update_meta(const TileParams& P, int b, int h, int p_new, int k, int lane,
+                                            int blk) {
     const size_t t = meta_index(P, b, h);
     if (k > 0) {
         const int bpr = P.blocks_per_req;
-        int32_t* row = P.table + t * bpr;
         const int src = lane + k < bpr ? lane + k : lane + k - bpr;
-        const int v = lane < bpr ? row[src] : 0;
-        if (lane < bpr) row[lane] = v;
+        const int v = __shfl(blk, src & 63, 64);
+        if (lane < bpr) P.table[t * bpr + lane] = v;
     }
     if (lane == 0) P.occ[t] = p_new;
 }
 
 // One wave (lane = 0..63) reads the tile's whole table row with a single
-// vector load -- it does not wait for the occupancy, so the row and the
-// occupancy arrive in the same round trip -- and writes, for every buffer
-// position i < capacity, its pool row (block * H + h) * block_size + i mod
-// block_size to pos[i] in LDS, so that later address arithmetic is one
-// lookup.  (The host bounds num_blocks * H * block_size below 2^31.)  Checks
-// the block ids covering positions [0, end).  Returns KVBUF_DEVERR_* bits,
-// the same in every lane (0 = usable).
-// (stage_row_from: the same with the row already loaded, lane i holding entry i.)
+// vector load (load_table_row: lane i gets entry i) -- it does not wait for
+// the occupancy, so the row and the occupancy arrive in the same round trip --
+// and stage_row_from writes, for every buffer position i < capacity, its pool
+// row (block * H + h) * block_size + i mod block_size to pos[i] in LDS, so
+// that later address arithmetic is one lookup.  (The host bounds num_blocks *
+// H * block_size below 2^31.)  It checks the block ids covering positions
+// [0, end) and returns KVBUF_DEVERR_* bits, the same in every lane (0 =
+// usable).
 __device__ __forceinline__ unsigned stage_row_from(const TileParams& P, int h, int end, uint32_t* pos, int lane,
                                                    int blk) {
     const int bpr = P.blocks_per_req;
@@ -419,10 +420,6 @@ __device__ __forceinline__ unsigned stage_row_from(const TileParams& P, int h, i
 __device__ __forceinline__ int load_table_row(const TileParams& P, int b, int h, int lane) {
     const int bpr = P.blocks_per_req;  // <= 64 (host-checked)
     return lane < bpr ? P.table[meta_index(P, b, h) * bpr + lane] : 0;
-}
-__device__ __forceinline__ unsigned stage_row(const TileParams& P, int b, int h, int end, uint32_t* pos,
-                                              int lane) {
-    return stage_row_from(P, h, end, pos, lane, load_table_row(P, b, h, lane));
 }
 
 }  // namespace kvbuf

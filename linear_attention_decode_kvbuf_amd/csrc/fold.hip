@@ -259,7 +259,8 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h, int
                            (P.mode == MODE_FLUSH || P.fuse);
         const int T0 = materialize ? p : (fold0 ? P.m : 0);  // positions applied
         uint32_t* pos = reinterpret_cast<uint32_t*>(lds);
-        bad |= stage_row(P, b, h, (tree && pn >= 0) ? max(T0, p + P.n) : T0, pos, lane);
+        const int blk = load_table_row(P, b, h, lane);
+        bad |= stage_row_from(P, h, (tree && pn >= 0) ? max(T0, p + P.n) : T0, pos, lane, blk);
         if (tree && !bad) {
             // kept draft d (rank k on the path) moves from position p + d to
             // p + k: the fold below reads it from its draft row, and its rows
@@ -289,7 +290,7 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h, int
             s_fold = fold0 ? 1 : 0;
         }
         if (!bad && !materialize && (fold0 || a != 0))
-            update_meta(P, b, h, fold0 ? pn - P.m : pn, fold0 ? P.m / P.block_size : 0, lane);
+            update_meta(P, b, h, fold0 ? pn - P.m : pn, fold0 ? P.m / P.block_size : 0, lane, blk);
     }
     __syncthreads();  // the position table, s_T, s_fold and s_bad are complete
     if (s_bad) {
