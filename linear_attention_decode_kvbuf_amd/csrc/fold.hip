@@ -373,6 +373,19 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h, int
             lds_copy_rows<DV * XB>(fx, cnt, value_row, lane);
         }
     };
+    // Per-channel rule: this lane's channels of the log-gates of positions
+    // i0 .. i0 + n - 1 (n <= 8; zero past n), all requested before any is used.
+    auto gate_chunk = [&](int i0, int n, float (&gv)[CPL][8]) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const size_t row = u < n ? static_cast<size_t>(tok.pos[i0 + u]) * DK : 0;
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+                const int ch = lane + 64 * c;
+                gv[c][u] = (u < n && ch < DK) ? P.gate[row + ch] : 0.0f;
+            }
+        }
+    };
     auto stage = [&](int r) {
         float* fk = stage0 + (r % NBUF) * stage_floats;
         float* fx = fk + srows * DK * KB / 4;
@@ -387,15 +400,21 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h, int
             stage_rows(tok, i0, cnt, fk, fx, nullptr, lane);
         }
         if constexpr (CH) {
-            // k_i[ch] e^{B_{T-1}[ch] - B_i[ch]}, positions in order
-            for (int ii = 0; ii < cnt; ++ii) {
-                const size_t row = static_cast<size_t>(tok.pos[i0 + ii]) * DK;
+            // k_i[ch] e^{B_{T-1}[ch] - B_i[ch]}, positions in order; the gates
+            // of 8 positions are requested before any is used
+            for (int ii0 = 0; ii0 < cnt; ii0 += 8) {
+                float gv[CPL][8];
+                gate_chunk(i0 + ii0, min(8, cnt - ii0), gv);
 #pragma unroll
-                for (int c = 0; c < CPL; ++c) {
-                    const int ch = lane + 64 * c;
-                    if (ch < DK) {
-                        prefix[c] += P.gate[row + ch];
-                        fk[ii * DK + ch] *= exp_gate(e0p[ch] - prefix[c]);
+                for (int u = 0; u < 8; ++u) {
+                    const int ii = ii0 + u;
+#pragma unroll
+                    for (int c = 0; c < CPL; ++c) {
+                        const int ch = lane + 64 * c;
+                        if (ch < DK && ii < cnt) {
+                            prefix[c] += gv[c][u];
+                            fk[ii * DK + ch] *= exp_gate(e0p[ch] - prefix[c]);
+                        }
                     }
                 }
             }
@@ -423,14 +442,22 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h, int
     if (token_wave) {
         if constexpr (SGATE) gate_prefix(bl, T, lane, [&](int i) { return tok.gate(i); });
         if constexpr (CH) {
-            // total log-gate of each key channel over the T positions
+            // total log-gate of each key channel over the T positions, summed
+            // in order
+            float tot[CPL];
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) {
-                const int ch = lane + 64 * c;
-                float tot = 0.0f;
-                for (int i = 0; ch < DK && i < T; ++i) tot += P.gate[static_cast<size_t>(tok.pos[i]) * DK + ch];
-                if (ch < DK) e0p[ch] = tot;
+            for (int c = 0; c < CPL; ++c) tot[c] = 0.0f;
+            for (int i0 = 0; i0 < T; i0 += 8) {
+                float gv[CPL][8];
+                gate_chunk(i0, min(8, T - i0), gv);
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+#pragma unroll
+                    for (int c = 0; c < CPL; ++c) tot[c] += gv[c][u];  // zero past the end
             }
+#pragma unroll
+            for (int c = 0; c < CPL; ++c)
+                if (lane + 64 * c < DK) e0p[lane + 64 * c] = tot[c];
         } else {
             if (lane == 0) *e0p = (SGATE && T > 0) ? exp_gate(bl[T - 1]) : 1.0f;
         }
