@@ -198,6 +198,7 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
     // set -- d and its ancestors (parent -1 = the buffered context).  A chain
     // (and the one token of a decode) attends to every e <= d.
     __shared__ uint32_t s_anc[TREE ? kMaxDrafts : 1];
+    __shared__ float s_gnew[NQ];  // log-gates of this call's tokens
 
     const TileIndex ti = tile_index(P);
     const int b = ti.b;
@@ -384,16 +385,17 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
             if constexpr (DELTA) kdraw[r].store(kdr + d * DK + cl * E);
         }
     }
-    // log-gates of every position; the new tokens' (positions p ..) are also
-    // appended to the pool from here
+    // log-gates of every position; the new tokens' are kept aside for their
+    // append at the end (a store here would hold up the next barrier, a
+    // register would be live through the whole kernel)
     if (GATED && tid < T) {
         bl[tid] = graw;
-        if (tid >= p) P.gate[tok.slot_index(tid)] = graw;
+        if (tid >= p) s_gnew[tid - p] = graw;
     }
     for (int i = NT + tid; GATED && i < T; i += NT) {  // long buffers only
         const float gi = tok.gate(i);
         bl[i] = gi;
-        if (i >= p) P.gate[tok.slot_index(i)] = gi;
+        if (i >= p) s_gnew[i - p] = gi;
     }
     auto stage_pass = [&](int i0) {
         const int i = i0 + gp;
@@ -555,6 +557,12 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
     }
     if (fold && tid < P.m) fw[tid] = GATED ? exp_gate(bl[P.m - 1] - bl[tid]) : 1.0f;
 
+    // The new tokens' log-gates go to the pool after the last barrier (a
+    // barrier waits for the stores before it).
+    auto append_gates = [&]() {
+        if (GATED && tid < n) P.gate[tok.slot_index(p + tid)] = s_gnew[tid];
+    };
+
     // ---- 5. the state tile: S^T q (and S^T k), reduced over row groups --------
     float* red = lds + L.red;
     float* outp = P.out + in_row * DV;
@@ -582,6 +590,7 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
             }
         }
         __syncthreads();
+        append_gates();
         for (int idx = tid; idx < n * DV; idx += NT) {
             const int d = idx / DV;
             const int c = idx - d * DV;
@@ -655,6 +664,7 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
             }
         }
         __syncthreads();
+        append_gates();
     }
 
     // ---- 7. eager fold: the buffer reached m tokens ----------------------------
