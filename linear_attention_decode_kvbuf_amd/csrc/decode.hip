@@ -43,7 +43,7 @@ __host__ __device__ inline int round4d(int x) { return (x + 3) & ~3; }
 // the cumulative gate of the new token and the fold's per-row state decay;
 // its fold keys are staged as fp32, already multiplied by their decays.
 struct DecodeLds {
-    int obuf, red, fw, kr, vr, dg, bt, qd, fr, total;
+    int obuf, red, fw, kr, vr, dg, bt, qd, fr, ap, total;
 };
 __host__ __device__ inline DecodeLds decode_lds(int DK, int DV, int RG, int mf, int io, bool ch, int cap) {
     DecodeLds L;
@@ -57,6 +57,7 @@ __host__ __device__ inline DecodeLds decode_lds(int DK, int DV, int RG, int mf, 
     L.bt = o; o += ch ? DK : 0;                 // per-channel rule: e^{B_t}
     L.qd = o; o += ch ? DK : 0;                 // per-channel rule: e^{B_t} q_t
     L.fr = o; o += ch ? DK : 0;                 // per-channel rule: e^{B_{m-1} - B_t} per state row
+    L.ap = o; o += round4d((DK + DV) * io / 4) + (ch ? DK : 0);  // the new token's key, value (, gate row)
     L.total = o;
     return L;
 }
@@ -77,6 +78,11 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void decode_kernel(TilePar
     __shared__ unsigned s_bad;
     __shared__ int s_fold;
     __shared__ float s_es, s_e0;
+    // the token wave's stores, made after the barrier (see its end)
+    __shared__ uint32_t s_arow;  // pool row of the new token
+    __shared__ float s_ag;       // its log-gate (one per token)
+    __shared__ int s_pnew, s_rot;
+    __shared__ int s_blk[64];    // the table row as read
 
     const TileIndex ti = tile_index(P);
     const int b = ti.b;
@@ -99,6 +105,9 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void decode_kernel(TilePar
     float* fw = lds + L.fw;
     IO* krs = reinterpret_cast<IO*>(lds + L.kr);
     IO* vrs = reinterpret_cast<IO*>(lds + L.vr);
+    IO* kap = reinterpret_cast<IO*>(lds + L.ap);  // the new token's key, value and gate row
+    IO* vap = kap + DK;
+    float* gap = lds + L.ap + round4d((DK + DV) * static_cast<int>(sizeof(IO)) / 4);
     const size_t in_row = static_cast<size_t>(b) * P.H + h;  // one new token per request
     const int slot = direct ? -1 : P.slot[b];
     const IO* qin = static_cast<const IO*>(P.q) + in_row * DK;
@@ -257,9 +266,10 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void decode_kernel(TilePar
                     if constexpr (!CH) kc[r].store(krs + i * DK + cl * E);
                     vc[r].store(vrs + i * DV + cl * EV);
                 }
-                if (i == pc && i < Tl) {  // append the new token to the pool
-                    kc[r].store(const_cast<IO*>(kpool) + static_cast<size_t>(pr[r]) * DK + cl * E);
-                    vc[r].store(const_cast<IO*>(vpool) + static_cast<size_t>(pr[r]) * DV + cl * EV);
+                if (i == pc && i < Tl) {  // the new token, appended to the pool after the barrier
+                    kc[r].store(kap + cl * E);
+                    vc[r].store(vap + cl * EV);
+                    if (cl == 0) s_arow = pr[r];
                 }
             }
         }
@@ -274,14 +284,13 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void decode_kernel(TilePar
             for (int e = 0; e < EV; ++e) obuf[cl * EV + e] = ob[e];
         }
         if constexpr (GATED) {
-            if (!bad && lane == pc) P.gate[prow] = graw;
+            if (lane == pc) s_ag = graw;
         }
         if constexpr (CH) {  // the new token's gate row
-            const uint32_t prow_t = static_cast<uint32_t>(__shfl(static_cast<int>(prow), pc, 64));
 #pragma unroll
             for (int c = 0; c < CPL; ++c) {
                 const int ch = lane + 64 * c;
-                if (!bad && ch < DK) P.gate[static_cast<size_t>(prow_t) * DK + ch] = gnew[c];
+                if (ch < DK) gap[ch] = gnew[c];
             }
         }
         if (fold && !CH) {
@@ -294,9 +303,13 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void decode_kernel(TilePar
             s_fold = fold ? 1 : 0;
             s_es = GATED ? exp_gate(bt) : 1.0f;
         }
-        // this wave read the tile's metadata above; advance it in place
-        if (!bad && P.mode != MODE_VERIFY)
-            update_meta(P, b, h, fold ? Tl - P.m : Tl, fold ? P.m / bs : 0, lane, blk);
+        // this wave read the tile's metadata above; it advances it in place
+        // after the barrier
+        s_blk[lane] = blk;
+        if (lane == 0) {
+            s_pnew = fold ? Tl - P.m : Tl;
+            s_rot = fold ? P.m / bs : 0;
+        }
     }
 
     // ---- state waves: query rows, then the tile; S0^T q per row group ----------
@@ -332,6 +345,30 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void decode_kernel(TilePar
     if (s_bad) {
         report(P, s_bad);
         return;  // the tile is skipped and its metadata left unchanged
+    }
+
+    // ---- token wave: its stores, after the barrier (which would wait for
+    // them): the new token's key, value and gate, and the metadata ----------------
+    if (token_wave) {
+        const int lane = tid - NT;
+        const size_t row = s_arow;
+        if (lane < 16) {
+            RawChunk<IO, E> kc;
+            kc.load(kap + lane * E);
+            kc.store(static_cast<IO*>(P.key) + row * DK + lane * E);
+        } else if (lane < 32) {
+            RawChunk<IO, EV> vc;
+            vc.load(vap + (lane - 16) * EV);
+            vc.store(static_cast<IO*>(P.value) + row * DV + (lane - 16) * EV);
+        }
+        if constexpr (GATED) {
+            if (lane == 0) P.gate[row] = s_ag;
+        }
+        if constexpr (CH) {
+            for (int ch = lane; ch < DK; ch += 64) P.gate[row * DK + ch] = gap[ch];
+        }
+        if (P.mode != MODE_VERIFY) update_meta(P, b, h, s_pnew, s_rot, lane, s_blk[lane]);
+        return;
     }
 
     // ---- output: e^{b_t} scale (S0^T q) + buffered part ---------------------------
