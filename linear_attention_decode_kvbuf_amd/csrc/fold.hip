@@ -183,19 +183,22 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h, int
     constexpr int CPL = (DK + 63) / 64;                        // key channels per token-wave lane
     using XIO = typename std::conditional<DELTA, float, IO>::type;
     // Folds that may exceed 16 positions (MFT, d = 128): the rank-T update
-    // runs on the matrix cores (shorter ones are cheaper on the vector ALUs).  The tile is then held in the MFMA accumulator
-    // layout -- 16 x 16 blocks of S^T, wave w owning rows 32w .. 32w+31: lane l
-    // holds row 32w + 16 rb + l % 16, columns 16 cb + 4 (l / 16) .. +3 of block
-    // (rb, cb) in s[8 rb + cb] -- and block (rb, cb) of S^T gains
-    // sum_k x_k[c] (w_k k_k[r]) as A (x rows, M = columns) times B (weighted
-    // keys, N = rows) over K-chunks of 16 positions.
+    // runs on the matrix cores (shorter ones are cheaper on the vector ALUs).
+    // The tile is then held in the MFMA accumulator layout -- 16 x 16 blocks
+    // of S^T, wave w owning rows 32w .. 32w+31: lane l holds row
+    // 32w + 16 rb + l % 16, columns 16 cb + 4 (l / 16) .. +3 of block (rb, cb)
+    // in s[8 rb + cb] -- and block (rb, cb) of S^T gains sum_k x_k[c] (w_k
+    // k_k[r]) as A (x rows, M = columns) times B (weighted keys, N = rows) over
+    // K-chunks of 16 positions (one round) or 32 (several rounds, TR below).
     constexpr bool MF = MFT && DK == 128 && DV == 128;
     constexpr bool XEXACT = std::is_same<XIO, bf16_bits>::value;  // values exact in bf16
     // ... and their rows are staged as loaded, by direct-to-LDS copies (one
     // round trip per staging round; the per-channel rule keeps fp32 rows,
     // whose keys carry per-channel decays)
     constexpr bool RAW = MF && !CH;
-    // (three buffers of fp32 rows would cost a workgroup per CU)
+    // Multi-round folds of bf16 rows keep three staging buffers, the copies of
+    // round r + 2 in flight while round r is applied (three buffers of fp32
+    // rows would cost a workgroup per CU).
     constexpr bool RING = RAW && MULTI && sizeof(XIO) == 2;
     // multi-round folds of bf16 keys: 16 x 16 x 32 products on transposing
     // LDS reads (their wider operands cost a wave per SIMD, which a single
