@@ -227,9 +227,11 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
     XIO* vrs = reinterpret_cast<XIO*>(lds + L.vr);
     float* fw = lds + L.fw;
     int p0 = 0, blk = 0;
-    if (tid < 64) {  // the occupancy and the table row in one round trip
+    int par = -1;  // tree drafts: parent of draft tid
+    if (tid < 64) {  // the occupancy, the table row (and the parents) in one round trip
         p0 = P.occ[meta_index(P, b, h)];
         blk = load_table_row(P, b, h, tid);
+        if (TREE && tid < n) par = P.parent[static_cast<size_t>(b) * n + tid];
     }
     f4 s[RPT];
     if constexpr (EARLY) {
@@ -243,7 +245,6 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
         unsigned bad = stage_row_from(P, h, (p0 < 0 || p0 > cap) ? -1 : p0 + n, spos, tid, blk);
         if (slot >= P.num_slots) bad |= KVBUF_DEVERR_SLOT;
         if constexpr (TREE) {
-            const int par = tid < n ? P.parent[static_cast<size_t>(b) * n + tid] : -1;
             const bool bad_par = tid < n && (par < -1 || par >= tid);  // parents precede children
             if (__ballot(bad_par)) bad |= KVBUF_DEVERR_ACCEPT;
             // ancestor mask of draft `tid`: follow the parents (at most n steps)

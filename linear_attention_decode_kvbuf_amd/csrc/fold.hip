@@ -233,7 +233,10 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h, int
     int a = 0;        // drafts kept
     int a_moves = 0;  // tree commit: kept drafts whose rows move
     if (token_wave) {
+        // occupancy, table row, accepted count / parents and leaf: all
+        // requested before any is used (one round trip)
         const int p = P.occ[meta_index(P, b, h)];
+        const int blk = load_table_row(P, b, h, lane);
         unsigned bad = 0;
         uint32_t path = 0;  // tree commit: bit d set = draft d is kept
         if (!tree && P.mode == MODE_COMMIT) {
@@ -262,7 +265,6 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h, int
                            (P.mode == MODE_FLUSH || P.fuse);
         const int T0 = materialize ? p : (fold0 ? P.m : 0);  // positions applied
         uint32_t* pos = reinterpret_cast<uint32_t*>(lds);
-        const int blk = load_table_row(P, b, h, lane);
         bad |= stage_row_from(P, h, (tree && pn >= 0) ? max(T0, p + P.n) : T0, pos, lane, blk);
         if (tree && !bad) {
             // kept draft d (rank k on the path) moves from position p + d to
