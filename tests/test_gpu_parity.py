@@ -100,6 +100,25 @@ def test_long_folds(rule, io, flush):
     run.check_bookkeeping()
 
 
+@pytest.mark.parametrize("rule,d", [(1, 64), (2, 64), (3, 64), (1, 16), (2, 16)])
+def test_long_folds_small_dims(rule, d):
+    """Folds of 48 positions at d = 64 and 16: several staging rounds of fp32
+    rows on the vector ALUs (the matrix-core instances serve d = 128)."""
+    w = synth.workload(1, B=3, H=2, dk=d, dv=d, m=48, block_size=16, blocks_per_req=4, steps=110,
+                       rule=rule, io="bf16", state_std=0.02)
+    _say("long folds small dims", w)
+    run = Run(w, flush=kb.FLUSH_DEFERRED)
+    for t in range(w.steps):
+        run.decode(t)
+        if t % 50 == 49:
+            run.flush()
+        if t % 25 == 24:
+            run.check_effective_states()
+    run.check_effective_states()
+    run.check_pool()
+    run.check_bookkeeping()
+
+
 @pytest.mark.parametrize("rule", [0, 1, 2, 3])
 def test_deferred_flush_with_tail(rule):
     """Decode past m before folding: the fold takes the first m tokens and
