@@ -594,13 +594,14 @@ def test_verify_recurrent_baseline(rule, n, d):
     assert torch.equal(run.kv.state[run.slots[0]], snap[run.slots[0]])
 
 
-@pytest.mark.parametrize("rule,m", [(1, 64), (1, 128), (2, 64), (2, 128)])
+@pytest.mark.parametrize("rule,m", [(1, 64), (1, 128), (2, 64), (2, 128), (0, 128), (3, 64)])
 def test_long_fold_full_size(rule, m):
     """kvbuf_flush of m buffered tokens at B=256 H=32 d=128, bf16, in the
     launch configuration the benchmark times (a block of m per request):
     sampled tiles against the recurrence over their m buffered tokens -- for
     the delta rule over its stored pseudo-values, which a fold applies as the
-    values of the scalar-gated rule."""
+    values of the scalar-gated rule.  (The per-channel rule keeps buffers of
+    at most 64 positions.)"""
     import oracle
     from tests.harness import TOL_STATE, rel_err_tiles
 
@@ -613,7 +614,8 @@ def test_long_fold_full_size(rule, m):
     kv.state.normal_(0.0, 0.02, generator=gen)
     kv.key.normal_(generator=gen)
     kv.value.normal_(generator=gen)
-    kv.gate.uniform_(-0.1, 0.0, generator=gen)
+    if kv.gate is not None:
+        kv.gate.uniform_(-0.1, 0.0, generator=gen)
     # sampled tiles: seeded host data written into their state slots and blocks
     rs = np.random.default_rng(9200 + 10 * rule + m)
     flat = [0, B * H - 1] + [int(x) for x in rs.choice(np.arange(1, B * H - 1), 10, replace=False)]
@@ -625,7 +627,7 @@ def test_long_fold_full_size(rule, m):
     V = rs.normal(size=(m, n, d)).astype(np.float32)
     if rule != kb.RULE_DELTA:
         V = bf16(V)
-    G = rs.uniform(-0.1, 0.0, (m, n)).astype(np.float32)
+    G = rs.uniform(-0.1, 0.0, (m, n, d) if rule == kb.RULE_CHANNEL else (m, n)).astype(np.float32)
     slot = kv.state_slot.cpu().numpy()
     block = kv.block_table.cpu().numpy()
     for j, (b, h) in enumerate(tiles):
@@ -633,7 +635,8 @@ def test_long_fold_full_size(rule, m):
         kv.state[s, h] = torch.from_numpy(S0[j]).to(dev)
         kv.key[blk, h] = torch.from_numpy(K[:, j]).to(dev, kv.key.dtype)
         kv.value[blk, h] = torch.from_numpy(V[:, j]).to(dev, kv.value.dtype)
-        kv.gate[blk, h] = torch.from_numpy(G[:, j]).to(dev)
+        if kv.gate is not None:
+            kv.gate[blk, h] = torch.from_numpy(G[:, j]).to(dev)
     kv.occupancy.fill_(m)
     _say("long fold full size rule %d m %d" % (rule, m))
     kv.flush()
@@ -641,7 +644,9 @@ def test_long_fold_full_size(rule, m):
     assert int(kv.error.item()) == 0
     assert int(kv.occupancy.abs().sum().item()) == 0
     assert np.array_equal(kv.block_table.cpu().numpy(), block)  # one block per request rotates onto itself
-    _, S_ref = oracle.recurrent(kb.RULE_GATED, S0, np.zeros((m, n, d)), K, V, G)
+    # the fold of the delta rule is the scalar-gated rule's over pseudo-values
+    ref_rule = kb.RULE_GATED if rule == kb.RULE_DELTA else rule
+    _, S_ref = oracle.recurrent(ref_rule, S0, np.zeros((m, n, d)), K, V, G if rule != kb.RULE_LINEAR else None)
     S_gpu = np.stack([kv.state[int(slot[b]), h].cpu().numpy() for b, h in tiles])
     err = rel_err_tiles(S_gpu, S_ref, axes=(-2, -1))
     _say("max state err %.2e" % err)
