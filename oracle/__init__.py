@@ -22,8 +22,9 @@ Two parts:
   full the state is updated with all buffered tokens and written back to the
   request's state slot; Figure 2 caption: draft tokens are buffered too).
 
-Readings of points the pages leave open (the pages give no equation, no layout
-and no API) are the plainest ones and are listed in the design doc of the repository.
+Where the pages leave a point open (they give no equation, no layout and no
+API), the plainest reading that the rest of the pages support is taken, and the
+function that depends on it says which.
 
 Functions whose results have a pin (a test that checks them against closed
 forms, exact rational arithmetic or invariants): ``recurrent`` for all four
