@@ -544,8 +544,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print("bench.py runs on one GPU only: the decode path has no cross-GPU step and this build "
-              "measures the per-GPU kernel (requested --gpus %d)" % args.gpus, file=sys.stderr)
+        print("bench.py runs on one GPU only: the decode path has no cross-GPU step, and what is "
+              "measured is one GPU's kernel (requested --gpus %d)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
