@@ -13,9 +13,10 @@
 //   o_t = S0^T (e^{B_t} scale q_t) + sum_{i<=t} scale (sum_r q_t[r] k_i[r] e^{B_t[r] - B_i[r]}) v_i
 //   fold: row r of S0 scales by e^{B_{m-1}[r]}, k_i[r] by e^{B_{m-1}[r] - B_i[r]}.
 //
-// Serves kvbuf_decode, kvbuf_direct and a one-draft kvbuf_verify when the
-// table row covers at most 64 positions (one lane of the token wave per
-// position).
+// Serves kvbuf_decode and a one-draft kvbuf_verify when the table row covers
+// at most 64 positions (one lane of the token wave per position), and
+// kvbuf_direct of the per-channel rule (the other rules' buffer-only requests
+// go to the chunk kernel).
 //
 // * State waves (NT threads): read the slot, issue the tile's 128-bit loads
 //   at once (after only the query rows they multiply), and form their share

@@ -52,8 +52,9 @@ struct TileParams {
 
 // Launchers: each picks the template instance for (rule, d, io dtype) and
 // enqueues one grid of B * H workgroups.  Return hipSuccess or the launch error.
-// launch_chunk serves decode, direct and verify; one-token calls of the
-// linear and gated rules with table rows of at most 64 positions go to the
+// launch_chunk serves decode, direct and verify; one-token calls with table
+// rows of at most 64 positions (decode and one-draft verify of the linear and
+// gated rules; decode, verify and direct of the per-channel rule) go to the
 // split-role kernel (launch_decode), the rest to the general chunk kernel.
 hipError_t launch_chunk(const TileParams& p, int rule, int d, int io, int batch, hipStream_t s);
 hipError_t launch_decode(const TileParams& p, int rule, int d, int io, int batch, hipStream_t s);
