@@ -325,12 +325,13 @@ def test_staggered_occupancies(rule):
 
 
 @pytest.mark.parametrize("rule,d,io", [(0, 128, "bf16"), (1, 128, "bf16"), (3, 128, "bf16"), (1, 64, "f32"),
-                                       (3, 16, "f32")])
+                                       (0, 16, "f32"), (3, 16, "f32")])
 def test_direct_long_rows(rule, d, io):
     """Buffer-only decode of up to 60 positions (table rows of 64): the
-    positions after the token wave's first round reach LDS by direct copies
-    (a launch that never folds); every output against the recurrence from a
-    zero state, and the pool and bookkeeping exactly."""
+    linear and gated rules on the chunk kernel's direct-to-LDS ring (several
+    passes of positions), the per-channel rule on the one-token kernel (several
+    rounds of 16 positions through its token wave); every output against the
+    recurrence from a zero state, and the pool and bookkeeping exactly."""
     w = synth.workload(1, B=3, H=2, dk=d, dv=d, m=64, block_size=16, blocks_per_req=4, steps=60,
                        rule=rule, io=io, state_std=0.02)
     _say("direct long rows", w)
