@@ -91,7 +91,8 @@ typedef struct kvbuf_layout {
     int32_t d_v;             /* value head dim */
     int32_t m;               /* tokens folded per flush; 0 = recurrent mode (no buffer) */
     int32_t block_size;      /* tokens per pool block; m must be a multiple of it */
-    int32_t blocks_per_req;  /* table row length; capacity = block_size * blocks_per_req >= m, <= 64 entries */
+    int32_t blocks_per_req;  /* table row length, <= 64 entries; capacity = block_size * blocks_per_req,
+                                m <= capacity <= 512 positions */
     int32_t num_blocks;      /* blocks in the pool */
     int32_t num_state_slots; /* slots in the state pool */
     int32_t rule;            /* kvbuf_rule */
@@ -144,10 +145,10 @@ typedef struct kvbuf_batch {
 
 /*
  * kvbuf_decode -- one decode step for every request of the batch.
- * (pith.science page, Figure 1 caption: the state is loaded together with the
- * buffered keys and values to compute the output; once the buffer is full the
- * state is updated with all buffered tokens and written back to its slot.
- * Figure 3 caption: the buffer size m = 0 case is the recurrent form.)
+ * (pith.science page, Figure 1 caption: decode reads the state and the
+ * request's buffer blocks side by side; a full buffer is folded into the
+ * state, which goes back to its slot.  Figure 3 caption: a buffer of size
+ * m = 0 is the recurrent baseline.)
  *
  * Inputs  q, k [B][H][d_k] and v [B][H][d_v] in io_dtype; g [B][H] fp32
  *         log-gates (rules GATED, DELTA; [B][H][d_k] for CHANNEL; NULL for
@@ -170,8 +171,8 @@ kvbuf_status kvbuf_decode(const kvbuf_layout* layout, const kvbuf_pools* pools,
  * kvbuf_flush -- fold the first m buffered tokens of every request that has a
  * state slot and at least m buffered tokens into its state, write the state
  * back, rotate its block table and lower its occupancy by m.  Other requests
- * are left untouched.  (Figure 1 caption, the deferred batched state update;
- * abstract: state updates are deferred and applied in batch.)  No-op when m = 0.
+ * are left untouched.  (Figure 1 caption and abstract: the state changes
+ * once per buffer, in one batched update.)  No-op when m = 0.
  */
 kvbuf_status kvbuf_flush(const kvbuf_layout* layout, const kvbuf_pools* pools,
                          const kvbuf_batch* batch, hipStream_t stream);
@@ -263,8 +264,8 @@ kvbuf_status kvbuf_commit_recurrent(const kvbuf_layout* layout, const kvbuf_pool
 
 /*
  * kvbuf_direct -- decode from the buffer alone for every request, whatever its
- * state slot (abstract: for short contexts the output is computed directly
- * from the buffered keys and values, without creating or updating a state).
+ * state slot (abstract: a short request never gets a state; its buffer alone
+ * yields its outputs).
  * Same arguments as kvbuf_decode; the state pool is never read or written and
  * no request folds.  Requires m > 0.
  */

@@ -255,52 +255,100 @@ class KVBuffer:
     def capacity(self):
         return self.layout.block_size * self.layout.blocks_per_req
 
-    def decode(self, q, k, v, g=None, beta=None, out=None, stream=None):
+    # ---- argument checks: the library reads raw pointers, so a tensor of the
+    # wrong dtype, shape, layout or device would be reinterpreted or read out
+    # of bounds; these raise ValueError before anything is enqueued.
+    def _need(self, x, name, shape, dtype):
+        if not isinstance(x, self.torch.Tensor):
+            raise ValueError("%s must be a tensor" % name)
+        if x.device != self.state.device:
+            raise ValueError("%s is on %s; the pools are on %s" % (name, x.device, self.state.device))
+        if x.dtype != dtype:
+            raise ValueError("%s has dtype %s, expected %s" % (name, x.dtype, dtype))
+        if tuple(x.shape) != tuple(shape):
+            raise ValueError("%s has shape %s, expected %s" % (name, tuple(x.shape), tuple(shape)))
+        if not x.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+
+    def _tokens(self, lead, q, k, v, g, beta, out):
+        """Checks q, k, v [*lead, H, d] (io dtype), g / beta [*lead, H] fp32
+        (g [*lead, H, d] for the per-channel rule) and out [*lead, H, d] fp32;
+        allocates out when it is None."""
+        H, d, f32 = self.H, self.d, self.torch.float32
+        for name, x in (("q", q), ("k", k), ("v", v)):
+            self._need(x, name, lead + (H, d), self.io_torch)
+        if self.rule == RULE_LINEAR:
+            g = None  # unused by the rule
+        else:
+            gshape = lead + (H, d) if self.rule == RULE_CHANNEL else lead + (H,)
+            self._need(g, "g", gshape, f32)
+        if self.rule == RULE_DELTA:
+            self._need(beta, "beta", lead + (H,), f32)
+        else:
+            beta = None
         if out is None:
-            out = self.torch.empty((self.B, self.H, self.d), dtype=self.torch.float32, device=q.device)
+            out = self.torch.empty(lead + (H, d), dtype=f32, device=self.state.device)
+        self._need(out, "out", lead + (H, d), f32)
+        return g, beta, out
+
+    def _drafts(self, q):
+        if not isinstance(q, self.torch.Tensor) or q.dim() != 4:
+            raise ValueError("drafts are [B, n, H, d] tensors")
+        return int(q.shape[1])
+
+    def _ints(self, x, name, shape):
+        self._need(x, name, shape, self.torch.int32)
+
+    def decode(self, q, k, v, g=None, beta=None, out=None, stream=None):
+        g, beta, out = self._tokens((self.B,), q, k, v, g, beta, out)
         kvbuf_decode(self.layout, self.pools, self.batch, q, k, v, g, beta, out, stream)
         return out
 
     def direct(self, q, k, v, g=None, beta=None, out=None, stream=None):
-        if out is None:
-            out = self.torch.empty((self.B, self.H, self.d), dtype=self.torch.float32, device=q.device)
+        g, beta, out = self._tokens((self.B,), q, k, v, g, beta, out)
         kvbuf_direct(self.layout, self.pools, self.batch, q, k, v, g, beta, out, stream)
         return out
 
     def verify(self, q, k, v, g=None, beta=None, out=None, stream=None):
-        n = q.shape[1]
-        if out is None:
-            out = self.torch.empty((self.B, n, self.H, self.d), dtype=self.torch.float32, device=q.device)
+        n = self._drafts(q)
+        g, beta, out = self._tokens((self.B, n), q, k, v, g, beta, out)
         kvbuf_verify(self.layout, self.pools, self.batch, n, q, k, v, g, beta, out, stream)
         return out
 
     def commit(self, n, accepted, stream=None):
+        self._ints(accepted, "accepted", (self.B,))
         kvbuf_commit(self.layout, self.pools, self.batch, n, accepted, stream)
 
     def verify_tree(self, parent, q, k, v, g=None, beta=None, out=None, stream=None):
         """Tree drafts: parent [B, n] int32 on the device (-1 = follows the buffer)."""
-        n = q.shape[1]
-        if out is None:
-            out = self.torch.empty((self.B, n, self.H, self.d), dtype=self.torch.float32, device=q.device)
+        n = self._drafts(q)
+        self._ints(parent, "parent", (self.B, n))
+        g, beta, out = self._tokens((self.B, n), q, k, v, g, beta, out)
         kvbuf_verify_tree(self.layout, self.pools, self.batch, n, parent, q, k, v, g, beta, out, stream)
         return out
 
     def commit_tree(self, parent, leaf, stream=None):
         """Keep the path from the root to leaf [B] int32 (-1 = none) of the last tree verify."""
+        if not isinstance(parent, self.torch.Tensor) or parent.dim() != 2:
+            raise ValueError("parent is a [B, n] tensor")
+        self._ints(parent, "parent", (self.B, parent.shape[1]))
+        self._ints(leaf, "leaf", (self.B,))
         kvbuf_commit_tree(self.layout, self.pools, self.batch, parent.shape[1], parent, leaf, stream)
 
     def verify_recurrent(self, q, k, v, g=None, beta=None, out=None, temp=None, stream=None):
         """Temporary-state verification (m = 0 only): returns (out, temp)."""
-        n = q.shape[1]
-        if out is None:
-            out = self.torch.empty((self.B, n, self.H, self.d), dtype=self.torch.float32, device=q.device)
+        n = self._drafts(q)
+        g, beta, out = self._tokens((self.B, n), q, k, v, g, beta, out)
         if temp is None:
             temp = self.torch.empty((n, self.B, self.H, self.d, self.d), dtype=self.torch.float32,
-                                    device=q.device)
+                                    device=self.state.device)
+        self._need(temp, "temp", (n, self.B, self.H, self.d, self.d), self.torch.float32)
         kvbuf_verify_recurrent(self.layout, self.pools, self.batch, n, q, k, v, g, beta, out, temp, stream)
         return out, temp
 
     def commit_recurrent(self, n, accepted, temp, stream=None):
+        self._ints(accepted, "accepted", (self.B,))
+        self._need(temp, "temp", (n, self.B, self.H, self.d, self.d), self.torch.float32)
         kvbuf_commit_recurrent(self.layout, self.pools, self.batch, n, accepted, temp, stream)
 
     def flush(self, stream=None):
@@ -310,5 +358,6 @@ class KVBuffer:
         if out is None:
             out = self.torch.empty((self.B, self.H, self.d, self.d), dtype=self.torch.float32,
                                    device=self.state.device)
+        self._need(out, "out", (self.B, self.H, self.d, self.d), self.torch.float32)
         kvbuf_materialize(self.layout, self.pools, self.batch, out, stream)
         return out

@@ -26,7 +26,7 @@ kvbuf_status check_layout(const kvbuf_layout* L, bool need_buffer) {
         if (L->blocks_per_req > kvbuf::kMaxTableRow) return KVBUF_ECAPACITY;
         if (L->m % L->block_size != 0) return KVBUF_ECAPACITY;
         if (static_cast<long long>(L->block_size) * L->blocks_per_req < L->m) return KVBUF_ECAPACITY;
-        if (static_cast<long long>(L->block_size) * L->blocks_per_req > 4096) return KVBUF_ECAPACITY;
+        if (static_cast<long long>(L->block_size) * L->blocks_per_req > kvbuf::kMaxCapacity) return KVBUF_ECAPACITY;
         // pool rows (block, head, slot) are indexed with 32-bit integers
         if (static_cast<long long>(L->num_blocks) * L->num_heads * L->block_size > 0x7fffffffLL)
             return KVBUF_ECAPACITY;

@@ -1,13 +1,13 @@
 // Buffered decode, draft verification and buffer-only decode (one kernel).
 //
 // KVBuffer: IO-aware Serving for Linear Attention (pith.science page):
-//  * Figure 1 caption -- the output of a token is computed from the state,
-//    loaded together with the buffered keys and values; once the buffer holds
-//    m tokens the state is updated with all of them and written back;
-//  * Figure 2 caption -- draft tokens are buffered and verified together,
-//    without a temporary state per draft;
-//  * abstract -- short contexts are served from the buffered keys and values
-//    alone, without creating or updating a state.
+//  * Figure 1 caption -- decode reads the state and the request's buffer
+//    blocks side by side; a full buffer is folded into the state, which goes
+//    back to its slot;
+//  * Figure 2 caption -- drafts go into the buffer and are checked in one
+//    pass, so no per-draft copy of the state exists;
+//  * abstract -- a short request never gets a state: its buffer alone
+//    yields its outputs.
 //
 // Unrolling the recurrence from the state S0 at the last fold (positions
 // 0 .. T-1 buffered since then, b_i = g_0 + ... + g_i the cumulative log-gate):

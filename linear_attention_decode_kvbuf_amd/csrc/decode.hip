@@ -2,9 +2,9 @@
 // split between two roles that run at the same time.
 //
 // KVBuffer: IO-aware Serving for Linear Attention (pith.science page,
-// Figure 1 caption: the output of a token is computed from the state loaded
-// together with the buffered keys and values; once the buffer holds m tokens
-// the state absorbs them and is written back).  With b_i the cumulative
+// Figure 1 caption: decode reads the state and the request's buffer blocks
+// side by side; a full buffer is folded into the state, which goes back to
+// its slot).  With b_i the cumulative
 // log-gate since the last fold and t = p the new token's position:
 //   o_t = e^{b_t} S0^T (scale q_t) + sum_{i<=t} e^{b_t - b_i} scale (q_t . k_i) v_i
 //   fold (t = m - 1):  S <- e^{b_{m-1}} S0 + sum_{i<m} e^{b_{m-1} - b_i} k_i v_i^T

@@ -406,11 +406,18 @@ __device__ __forceinline__ unsigned stage_row_from(const TileParams& P, int h, i
     const int bpr = P.blocks_per_req;
     const int bs = P.block_size;
     const int cap = bs * bpr;
-    for (int i = lane; i < cap; i += 64) {
-        const int q = i / bs;
+    // A lane permute reads zero from an inactive source lane, so every pass
+    // runs with all 64 lanes active (a uniform trip count, the source index
+    // clamped into the row) and only the store is guarded: a loop over
+    // i < cap would leave the lanes past the end of the last partial pass
+    // inactive while the lanes before them fetch block ids from them.
+    for (int base = 0; base < cap; base += 64) {
+        const int i = base + lane;
+        const int q = min(i / bs, bpr - 1);
         const uint32_t bi = static_cast<uint32_t>(__shfl(blk, q, 64));
-        pos[i] = (bi * static_cast<uint32_t>(P.H) + static_cast<uint32_t>(h)) * static_cast<uint32_t>(bs) +
-                 static_cast<uint32_t>(i - q * bs);
+        if (i < cap)
+            pos[i] = (bi * static_cast<uint32_t>(P.H) + static_cast<uint32_t>(h)) * static_cast<uint32_t>(bs) +
+                     static_cast<uint32_t>(i - q * bs);
     }
     if (end < 0 || end > cap) return KVBUF_DEVERR_OVERFLOW;
     const int nblk = (end + bs - 1) / bs;

@@ -2,11 +2,12 @@
 // materialisation of the effective state.
 //
 // KVBuffer: IO-aware Serving for Linear Attention (pith.science page):
-//  * Figure 1 caption -- when the buffer is full the state is updated with
-//    all buffered keys and values on the GPU and written back to the
-//    request's state slot;
-//  * abstract -- state updates are deferred and applied in batch;
-//  * Figure 2 caption -- after verification only the accepted drafts are kept.
+//  * Figure 1 caption -- a full buffer is folded into the state on the
+//    device, and the new state replaces the old one in its slot;
+//  * abstract -- the state changes once per buffer, in one batched update,
+//    not once per token;
+//  * Figure 2 caption -- of the verified drafts, the request keeps the
+//    accepted ones.
 //
 // Folding positions 0 .. T-1 (cumulative log-gates b_i since the last fold)
 // into the state S0 at the last fold:

@@ -76,5 +76,10 @@ constexpr int kMaxDrafts = 8;
 constexpr int kFoldChunk = 32;  // most tokens staged in LDS per fold round
 constexpr int kRawFoldChunk = 32;  // ... when staged as stored (bf16 rows take half the LDS)
 constexpr int kMaxTableRow = 64;
+// Most buffer positions per request (block_size * blocks_per_req): the
+// per-position LDS tables of the chunk and fold kernels (pool rows, gates,
+// scores of up to eight queries) are sized by it, and the parity tests cover
+// buffers up to this length.
+constexpr int kMaxCapacity = 512;
 
 }  // namespace kvbuf

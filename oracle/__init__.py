@@ -17,10 +17,10 @@ Two parts:
 * ``BufferModel`` -- integer bookkeeping of the key/value buffer: where each
   token's key, value and gate land in the block pool, how the per-request block
   table rotates when the buffered tokens are folded into the state, and the
-  occupancy counter (same page, Figure 1 caption: the buffer memory is split
-  into fixed-size blocks, each request owns two of them, and when the buffer is
-  full the state is updated with all buffered tokens and written back to the
-  request's state slot; Figure 2 caption: draft tokens are buffered too).
+  occupancy counter (same page, Figure 1 caption: buffer memory comes in
+  fixed-size blocks, two per request in the figure, and a full buffer is
+  folded into the state, which goes back to its slot; Figure 2 caption: drafts
+  occupy buffer positions as well).
 
 Where the pages leave a point open (they give no equation, no layout and no
 API), the plainest reading that the rest of the pages support is taken, and the
@@ -96,11 +96,11 @@ def _ptr(a):
     return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
 
 
-def recurrent(rule, S0, q, k, v, g=None, beta=None, scale=1.0, nthreads=1):
+def recurrent(rule, S0, q, k, v, g=None, beta=None, scale=1.0, nthreads=1, inplace=False):
     """Per-token recurrence over ``nsteps`` tokens for ``ntiles`` independent tiles.
 
     Arguments (any float dtype; widened exactly to fp64):
-      S0   [ntiles, dk, dv]    state before the first token (not modified)
+      S0   [ntiles, dk, dv]    state before the first token (not modified unless ``inplace``)
       q, k [nsteps, ntiles, dk]
       v    [nsteps, ntiles, dv]
       g    [nsteps, ntiles]    log-gate, gamma = exp(g) (rules 1 and 2);
@@ -108,8 +108,17 @@ def recurrent(rule, S0, q, k, v, g=None, beta=None, scale=1.0, nthreads=1):
       beta [nsteps, ntiles]    delta-rule step size (rule 2)
     Returns (out [nsteps, ntiles, dv], S [ntiles, dk, dv]): every token's output
     o_t = S_t^T (scale q_t) and the state after the last token, both fp64.
+    With ``inplace`` S0 must be a C-contiguous float64 array; it is advanced in
+    place and returned as S (no copy of a large state).  ``nthreads`` spreads
+    the independent tiles over OpenMP threads; each tile's arithmetic is the
+    same at any thread count.
     """
-    S = _f64(S0).copy()
+    if inplace:
+        if not (isinstance(S0, np.ndarray) and S0.dtype == np.float64 and S0.flags.c_contiguous):
+            raise ValueError("oracle: inplace needs a C-contiguous float64 state")
+        S = S0
+    else:
+        S = _f64(S0).copy()
     if S.ndim != 3:
         raise ValueError("oracle: S0 must be [ntiles, dk, dv]")
     ntiles, dk, dv = S.shape
@@ -154,8 +163,8 @@ class BufferModel:
 
     Logical buffer position p of request b lives in block ``table[b][p // bs]``
     at offset ``p % bs``.  Tokens are appended at p = occupancy.  Folding the
-    buffer into the state ("flush": Figure 1 caption, the state is updated with
-    all buffered tokens once the buffer is full) consumes the first m positions,
+    buffer into the state (a "flush"; Figure 1 caption: a full buffer is folded
+    into the state) consumes the first m positions,
     moves the m / bs blocks that held them to the back of the table and lowers
     the occupancy by m; tokens already buffered beyond position m keep their
     physical place and become positions 0, 1, ...

@@ -8,9 +8,9 @@
  * with the GPU library.
  *
  * What it computes (KVBuffer: IO-aware Serving for Linear Attention, pith.science
- * page, abstract: "existing serving systems ... recurrently computing and
- * updating a large linear attention state in every decoding step"; Figure 3
- * caption: the recurrent form is the buffer-size-0 case).  The pages give no
+ * page, abstract: the serving systems it improves on read and rewrite the
+ * whole state for every decoded token; Figure 3 caption: that recurrent form
+ * is the buffer-size-0 case).  The pages give no
  * equation; the three update rules below are the ones the workload definitions
  * fix, each applied once per token t with S the d_k x d_v state:
  *

@@ -5,10 +5,20 @@ Tolerances (the method must reproduce the recurrence exactly up to rounding;
 the GPU accumulates in fp32 from bf16 or fp32 inputs):
   outputs  per tile  max|o_gpu - o_ref| / max|o_ref|  <= 2e-3
   states   per tile  max|S_gpu - S_ref| / max|S_ref|  <= 1e-5 after every fold
-  block tables, occupancies and buffered key / gate bits: exact.
+  block tables, occupancies and buffered key / value / gate bits: exact.
+
+By default every (request, head) tile is compared, at every size: outputs at
+every step, effective states where a test asks for them, and the stored state
+of every tile that folds -- all of them at the first fold of a run and at
+``check_all_states``, a rotating subset of ``state_sample`` tiles at the folds
+in between (a full-size state pool is half a GiB to copy per check).  The
+oracle's state of every compared tile is kept in fp64 and advanced in place,
+its tiles spread over the host's cores.
 """
 
 from __future__ import annotations
+
+import os
 
 import numpy as np
 import torch
@@ -19,24 +29,34 @@ import linear_attention_decode_kvbuf_amd as kb
 
 TOL_OUT = 2e-3
 TOL_STATE = 1e-5
+NTHREADS = max(1, min(16, len(os.sched_getaffinity(0))))
 
 
-def rel_err_tiles(gpu, ref, axes):
-    """max over tiles of max|gpu - ref| / max|ref| (reduction over ``axes``)."""
-    gpu = np.asarray(gpu, np.float64)
-    ref = np.asarray(ref, np.float64)
-    num = np.max(np.abs(gpu - ref), axis=axes)
-    den = np.maximum(np.max(np.abs(ref), axis=axes), 1e-30)
-    return float(np.max(num / den)) if num.size else 0.0
+def rel_err_tiles(gpu, ref, axes, chunk=1024):
+    """max over tiles of max|gpu - ref| / max|ref| (reduction over ``axes``),
+    in chunks of the leading axis so that full-size states are never widened
+    whole."""
+    gpu = np.asarray(gpu)
+    ref = np.asarray(ref)
+    if gpu.shape != ref.shape:
+        raise ValueError("compared shapes differ: %s vs %s" % (gpu.shape, ref.shape))
+    if gpu.size == 0:
+        return 0.0
+    if gpu.ndim == 0:
+        gpu, ref = gpu[None], ref[None]
+    worst = 0.0
+    for i in range(0, gpu.shape[0], chunk):
+        g = np.asarray(gpu[i:i + chunk], np.float64)
+        r = np.asarray(ref[i:i + chunk], np.float64)
+        num = np.max(np.abs(g - r), axis=axes)
+        den = np.maximum(np.max(np.abs(r), axis=axes), 1e-30)
+        worst = max(worst, float(np.max(num / den)))
+    return worst
 
 
-def default_sample(w, count=24, seed=0):
-    """(b, h) tiles to compare: all of them for tiny batches, else a spread."""
-    if w.B * w.H <= 64:
-        return [(b, h) for b in range(w.B) for h in range(w.H)]
-    rs = np.random.default_rng(seed)
-    bs = np.unique(np.concatenate([[0, w.B - 1], rs.integers(0, w.B, count)]))[:count]
-    return [(int(b), int(rs.integers(0, w.H))) for b in bs]
+def all_tiles(w):
+    """Every (b, h) tile, request-major."""
+    return [(b, h) for b in range(w.B) for h in range(w.H)]
 
 
 def _np(x):
@@ -47,10 +67,17 @@ def _np(x):
     return np.asarray(x, np.float32)
 
 
+def recurrence(rule, S, q, k, v, g, beta):
+    """The oracle over [steps, tiles, ...] inputs, advancing S (fp64) in place."""
+    return oracle.recurrent(rule, S, q, k, v, g, beta, nthreads=NTHREADS, inplace=True)[0]
+
+
 class Run:
     def __init__(self, w, *, flush=kb.FLUSH_EAGER, sample=None, device_gen=None, spare_blocks=3,
-                 stateless=None, check_every_step=None):
+                 stateless=None, check_every_step=None, state_sample=64, tol_out=TOL_OUT, tol_state=TOL_STATE):
         self.w = w
+        self.tol_out = tol_out
+        self.tol_state = tol_state
         self.dev = torch.device("cuda")
         self.flush_policy = flush
         self.device_gen = device_gen if device_gen is not None else w.B * w.H > 256
@@ -85,18 +112,30 @@ class Run:
         for b in range(B):
             self.model.add_request(table[b], 0, has_state=not self.stateless[b])
 
-        self.sample = sample if sample is not None else default_sample(w)
-        self.sb = torch.tensor([b for b, _ in self.sample], device=self.dev, dtype=torch.long)
-        self.sh = torch.tensor([h for _, h in self.sample], device=self.dev, dtype=torch.long)
-        st = self.kv.state.detach()
-        S = []
-        for b, h in self.sample:
-            S.append(np.zeros((w.dk, w.dv)) if slots[b] < 0 else st[slots[b], h].double().cpu().numpy())
-        self.S = np.stack(S)  # oracle state of every sampled tile, fp64
-        self.tokens = {}  # (token id, sample index) -> (k bits, g) for the pool check
+        self.sample = list(sample) if sample is not None else all_tiles(w)
+        self.all = self.sample == all_tiles(w)
+        self.sb_np = np.array([b for b, _ in self.sample], np.int64)
+        self.sh_np = np.array([h for _, h in self.sample], np.int64)
+        self.sb = torch.from_numpy(self.sb_np).to(self.dev)
+        self.sh = torch.from_numpy(self.sh_np).to(self.dev)
+        # per request: the indices j of its sampled tiles (a slice when every tile is compared)
+        self.rows_of = {}
+        if self.all:
+            for b in range(B):
+                self.rows_of[b] = slice(b * H, (b + 1) * H)
+        else:
+            for j, b in enumerate(self.sb_np):
+                self.rows_of.setdefault(int(b), []).append(j)
+            self.rows_of = {b: np.array(js, np.int64) for b, js in self.rows_of.items()}
+        self.S = np.ascontiguousarray(self._stored_states(np.arange(len(self.sample))).astype(np.float64))
+        self.tokens = {}  # token id -> (k, v, g) rows of its request's sampled tiles, for the pool check
+        self.calls = 0
         self.max_out = 0.0
         self.max_state = 0.0
         self.folds_checked = 0
+        self.full_state_checks = 0
+        self.state_sample = state_sample
+        self._rotor = 0
 
     # ---------------------------------------------------------------- inputs
     def inputs(self, step, n=None, stream_base=0):
@@ -115,12 +154,29 @@ class Run:
         return out
 
     def _sampled(self, x, drafts=False):
-        """[ns, ...] host copy of the sampled tiles of a [B, (n,) H, ...] tensor."""
+        """[ns, (n,) ...] float32 host copy of the sampled tiles of a [B, (n,) H, ...] tensor."""
         if x is None:
             return None
+        if self.all:
+            B, H = self.w.B, self.w.H
+            if drafts:
+                x = x.transpose(1, 2)  # [B, H, n, ...]
+                return _np(x.reshape((B * H,) + tuple(x.shape[2:])))
+            return _np(x.reshape((B * H,) + tuple(x.shape[2:])))
         if drafts:
             return _np(x[self.sb, :, self.sh])
         return _np(x[self.sb, self.sh])
+
+    def _stored_states(self, js):
+        """fp32 host copy of the stored state of sampled tiles js (zeros without a slot)."""
+        js = np.asarray(js, np.int64)
+        b = self.sb_np[js]
+        slot = self.slots[b]
+        st = self.kv.state.detach()
+        got = st[torch.from_numpy(np.maximum(slot, 0)).to(self.dev), torch.from_numpy(self.sh_np[js]).to(self.dev)]
+        got = got.cpu().numpy()
+        got[slot < 0] = 0.0
+        return got
 
     # ---------------------------------------------------------------- steps
     def decode(self, t, direct=False):
@@ -137,14 +193,13 @@ class Run:
                 if self.model.decode(b, ("d", t, b), eager=eager, stateless=direct or self.stateless[b]):
                     folded.add(b)
         q, k, v, g, beta = (self._sampled(inp[x]) for x in ("q", "k", "v", "g", "beta"))
-        self._remember([("d", t, b) for b, _ in self.sample], k, v, g)
-        o_ref, self.S = oracle.recurrent(w.rule, self.S, q[None], k[None], v[None],
-                                         None if g is None else g[None],
-                                         None if beta is None else beta[None])
+        self._remember(lambda b: ("d", t, b), k, v, g)
+        o_ref = recurrence(w.rule, self.S, q[None], k[None], v[None],
+                           None if g is None else g[None], None if beta is None else beta[None])
         o_gpu = self._sampled(out)
         err = rel_err_tiles(o_gpu, o_ref[0], axes=-1)
         self.max_out = max(self.max_out, err)
-        assert err <= TOL_OUT, "step %d: output error %.3e" % (t, err)
+        assert err <= self.tol_out, "step %d: output error %.3e" % (t, err)
         self._after(folded)
         return out
 
@@ -154,7 +209,10 @@ class Run:
         self._after(folded)
 
     def verify_commit(self, call, n, accepted):
-        """One verify of n drafts per request, then commit ``accepted`` [B]."""
+        """One verify of n drafts per request, then commit ``accepted`` [B].
+        Draft d's reference output is the recurrence over drafts 0 .. d from the
+        current state; the state after commit is the recurrence over the
+        accepted prefix."""
         w = self.w
         inp = self.inputs(call, n=n, stream_base=100)
         out = self.kv.verify(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"])
@@ -162,27 +220,52 @@ class Run:
             self.model.verify(b, [("v", call, b, d) for d in range(n)])
         q, k, v, g, beta = (self._sampled(inp[x], drafts=True) for x in ("q", "k", "v", "g", "beta"))
         o_gpu = self._sampled(out, drafts=True)  # [ns, n, d]
-        for j, (b, h) in enumerate(self.sample):
-            for dd in range(n):
-                self.tokens[(("v", call, b, dd), j)] = (k[j, dd].copy(), v[j, dd].copy(),
-                                                        None if g is None else np.array(g[j, dd], np.float32))
-            tr = lambda x: None if x is None else np.swapaxes(x[j:j + 1], 0, 1)  # [n, 1, ...]
-            o_ref, _ = oracle.recurrent(w.rule, self.S[j:j + 1], tr(q), tr(k), tr(v), tr(g), tr(beta))
-            err = rel_err_tiles(o_gpu[j], o_ref[:, 0], axes=-1)
+        for dd in range(n):
+            self._remember(lambda b: ("v", call, b, dd), k[:, dd], v[:, dd], None if g is None else g[:, dd])
+        acc_tile = np.asarray(accepted, np.int64)[self.sb_np]
+        S_tmp = self.S.copy()
+        for dd in range(n):
+            col = lambda x: None if x is None else x[:, dd][None]
+            o_ref = recurrence(w.rule, S_tmp, col(q), col(k), col(v), col(g), col(beta))
+            err = rel_err_tiles(o_gpu[:, dd], o_ref[0], axes=-1)
             self.max_out = max(self.max_out, err)
-            assert err <= TOL_OUT, "verify %d tile %s: output error %.3e" % (call, (b, h), err)
-            a = int(accepted[b])
-            if a:
-                _, S1 = oracle.recurrent(w.rule, self.S[j:j + 1], tr(q)[:a], tr(k)[:a], tr(v)[:a],
-                                         None if g is None else tr(g)[:a],
-                                         None if beta is None else tr(beta)[:a])
-                self.S[j] = S1[0]
+            assert err <= self.tol_out, "verify %d draft %d: output error %.3e" % (call, dd, err)
+            keep = acc_tile == dd + 1
+            self.S[keep] = S_tmp[keep]
+        del S_tmp
         acc = torch.from_numpy(np.asarray(accepted, np.int32)).to(self.dev)
         self.kv.commit(n, acc)
         eager = self.flush_policy == kb.FLUSH_EAGER
         folded = {b for b in range(w.B) if self.model.commit(b, int(accepted[b]), eager=eager)}
         self._after(folded)
         return out
+
+    def _along_paths(self, paths, q, k, v, g, beta, S):
+        """The recurrence along each sampled tile's path of drafts (paths[b]:
+        draft indices of request b, root first), advancing S in place.  Shorter
+        paths are padded at the front with identity steps (zero key, value,
+        gate and step size leave every rule's state unchanged exactly).
+        Returns the output of each tile's last path step, or None."""
+        L = max((len(p) for p in paths.values()), default=0)
+        if L == 0:
+            return None
+        ns = len(self.sample)
+        idx = np.full((L, ns), -1, np.int64)
+        for b, p in paths.items():
+            if p and b in self.rows_of:
+                idx[L - len(p):, self.rows_of[b]] = np.asarray(p, np.int64)[:, None]
+        live = idx >= 0
+        col = np.arange(ns)[None, :]
+
+        def gather(x):
+            if x is None:
+                return None
+            y = x[col, np.maximum(idx, 0)]  # [L, ns, ...]
+            y[~live] = 0.0
+            return y
+
+        o = recurrence(self.w.rule, S, gather(q), gather(k), gather(v), gather(g), gather(beta))
+        return o[-1]
 
     def verify_tree_commit(self, call, parent, leaf):
         """One tree verify (parent [B, n]) per request, then keep the path from
@@ -197,6 +280,8 @@ class Run:
             self.model.verify(b, [("t", call, b, d) for d in range(n)])
         q, k, v, g, beta = (self._sampled(inp[x], drafts=True) for x in ("q", "k", "v", "g", "beta"))
         o_gpu = self._sampled(out, drafts=True)  # [ns, n, d]
+        for dd in range(n):
+            self._remember(lambda b: ("t", call, b, dd), k[:, dd], v[:, dd], None if g is None else g[:, dd])
 
         def path_to(b, d):
             path = []
@@ -205,23 +290,12 @@ class Run:
                 d = int(parent[b][d])
             return path[::-1]
 
-        for j, (b, h) in enumerate(self.sample):
-            for dd in range(n):
-                self.tokens[(("t", call, b, dd), j)] = (k[j, dd].copy(), v[j, dd].copy(),
-                                                        None if g is None else np.array(g[j, dd], np.float32))
-            sel = lambda x, path: None if x is None else np.swapaxes(x[j:j + 1, path], 0, 1)  # [len, 1, ...]
-            for dd in range(n):
-                path = path_to(b, dd)
-                o_ref, _ = oracle.recurrent(w.rule, self.S[j:j + 1], sel(q, path), sel(k, path), sel(v, path),
-                                            sel(g, path), sel(beta, path))
-                err = rel_err_tiles(o_gpu[j, dd][None], o_ref[-1], axes=-1)
-                self.max_out = max(self.max_out, err)
-                assert err <= TOL_OUT, "tree verify %d tile %s draft %d: output error %.3e" % (call, (b, h), dd, err)
-            path = path_to(b, int(leaf[b]))
-            if path:
-                _, S1 = oracle.recurrent(w.rule, self.S[j:j + 1], sel(q, path), sel(k, path), sel(v, path),
-                                         sel(g, path), sel(beta, path))
-                self.S[j] = S1[0]
+        for dd in range(n):
+            o_ref = self._along_paths({b: path_to(b, dd) for b in range(w.B)}, q, k, v, g, beta, self.S.copy())
+            err = rel_err_tiles(o_gpu[:, dd], o_ref, axes=-1)
+            self.max_out = max(self.max_out, err)
+            assert err <= self.tol_out, "tree verify %d draft %d: output error %.3e" % (call, dd, err)
+        self._along_paths({b: path_to(b, int(leaf[b])) for b in range(w.B)}, q, k, v, g, beta, self.S)
         lf = torch.from_numpy(np.ascontiguousarray(leaf, np.int32)).to(self.dev)
         self.kv.commit_tree(par, lf)
         eager = self.flush_policy == kb.FLUSH_EAGER
@@ -239,42 +313,76 @@ class Run:
         self.model.replace_request(b, new, 0, has_state=False)
         self.kv.block_table[b].copy_(torch.tensor(new, dtype=torch.int32))  # every head
         self.kv.occupancy[b] = 0
-        for j, (bb, _) in enumerate(self.sample):
-            if bb == b:
-                self.S[j] = 0.0
+        if b in self.rows_of:
+            self.S[self.rows_of[b]] = 0.0
 
     # ---------------------------------------------------------------- checks
-    def _remember(self, tids, k, v, g):
-        for j, tid in enumerate(tids):
-            self.tokens[(tid, j)] = (k[j].copy(), v[j].copy(), None if g is None else np.array(g[j], np.float32))
+    def _remember(self, tid_of, k, v, g):
+        """Keeps, per request, its sampled tiles' rows of one token's key,
+        value (not for the delta rule, whose pool holds pseudo-values) and gate."""
+        keep_v = self.w.rule != kb.RULE_DELTA
+        for b, rows in self.rows_of.items():
+            self.tokens[tid_of(b)] = (k[rows], v[rows] if keep_v else None, None if g is None else g[rows])
+        self.calls += 1
+        if self.calls % 16 == 0:  # forget tokens no pool position holds any more
+            live = set(self.model.physical.values())
+            for tid in [t for t in self.tokens if t not in live]:
+                del self.tokens[tid]
 
     def _after(self, folded):
         # The stored state equals the recurrence's state when the fold used up
         # every buffered token; otherwise tokens past m are still buffered and
         # only the effective state (check_effective_states) is comparable.
-        sampled_folds = [j for j, (b, _) in enumerate(self.sample)
-                         if b in folded and self.model.requests[b].occupancy == 0]
-        if sampled_folds:
-            self.check_states(sampled_folds)
+        if folded:
+            f = np.zeros(self.w.B, bool)
+            f[list(folded)] = True
+            empty = self.model.occupancies() == 0
+            js = np.nonzero((f & empty)[self.sb_np])[0]
+            if js.size:
+                if self.full_state_checks == 0:
+                    self.check_states(js)
+                    self.full_state_checks += 1
+                else:
+                    self.check_states(self._rotate(js))
         if self.check_every_step or folded:
             self.check_bookkeeping()
 
+    def _rotate(self, js):
+        if js.size <= self.state_sample:
+            return js
+        start = (self._rotor * self.state_sample) % js.size
+        self._rotor += 1
+        return np.take(js, np.arange(start, start + self.state_sample), mode="wrap")
+
     def check_states(self, js):
-        st = self.kv.state.detach()
-        for j in js:
-            b, h = self.sample[j]
-            gpu = st[self.slots[b], h].double().cpu().numpy()
-            err = rel_err_tiles(gpu[None], self.S[j][None], axes=(-2, -1))
-            self.max_state = max(self.max_state, err)
-            self.folds_checked += 1
-            assert err <= TOL_STATE, "state of tile %s: error %.3e" % ((b, h), err)
+        """Stored states of sampled tiles js against the oracle."""
+        js = np.asarray(js, np.int64)
+        gpu = self._stored_states(js)
+        err = rel_err_tiles(gpu, self.S[js], axes=(-2, -1))
+        self.max_state = max(self.max_state, err)
+        self.folds_checked += js.size
+        assert err <= self.tol_state, "stored state error %.3e" % err
+
+    def check_all_states(self):
+        """Stored state of every compared tile whose buffer is empty (its last
+        fold used every buffered token, or it has not buffered any)."""
+        empty = (self.model.occupancies() == 0)[self.sb_np]
+        js = np.nonzero(empty & (self.slots[self.sb_np] >= 0))[0]
+        if js.size:
+            self.check_states(js)
+            self.full_state_checks += 1
+        return js.size
 
     def check_effective_states(self):
         """kvbuf_materialize against the oracle state of every sampled tile."""
         eff = self.kv.materialize()
-        gpu = eff[self.sb, self.sh].double().cpu().numpy()
+        if self.all:
+            gpu = eff.reshape(-1, self.w.dk, self.w.dv).cpu().numpy()
+        else:
+            gpu = eff[self.sb, self.sh].cpu().numpy()
+        del eff
         err = rel_err_tiles(gpu, self.S, axes=(-2, -1))
-        assert err <= TOL_STATE, "materialized state error %.3e" % err
+        assert err <= self.tol_state, "materialized state error %.3e" % err
         return err
 
     def check_bookkeeping(self):
@@ -291,17 +399,39 @@ class Run:
     def check_pool(self):
         """Buffered keys, gates and (linear / gated rules) values of the sampled
         tiles are the inputs' bits."""
-        key = self.kv.key.detach()
-        value = None if self.w.rule == 2 else self.kv.value.detach()
-        gate = None if self.kv.gate is None else self.kv.gate.detach()
-        bits = lambda x: np.asarray(x, np.float32).view(np.uint32)
-        for j, (b, h) in enumerate(self.sample):
+        bf16 = self.w.io == "bf16"
+
+        def host_bits(x, io_plane):
+            if x is None:
+                return None
+            x = x.detach()
+            if io_plane and bf16:
+                return x.view(torch.int16).cpu().numpy().view(np.uint16)
+            return x.float().view(torch.int32).cpu().numpy().view(np.uint32)
+
+        def ref_bits(x, io_plane):
+            b = np.ascontiguousarray(x, np.float32).view(np.uint32)
+            return (b >> 16).astype(np.uint16) if (io_plane and bf16) else b
+
+        key = host_bits(self.kv.key, True)
+        value = None if self.w.rule == kb.RULE_DELTA else host_bits(self.kv.value, True)
+        gate = host_bits(self.kv.gate, False)
+        for b, rows in self.rows_of.items():
             toks = self.model.buffered_tokens(b)
-            for p, tid in enumerate(toks):
-                blk, off = self.model.position(b, p)
-                kref, vref, gref = self.tokens[(tid, j)]
-                np.testing.assert_array_equal(bits(key[blk, h, off].float().cpu().numpy()), bits(kref))
-                if value is not None:
-                    np.testing.assert_array_equal(bits(value[blk, h, off].float().cpu().numpy()), bits(vref))
-                if gate is not None:  # one gate, or one per key channel
-                    np.testing.assert_array_equal(bits(gate[blk, h, off].cpu().numpy()), bits(gref))
+            if not toks:
+                continue
+            heads = self.sh_np[rows]
+            pos = [self.model.position(b, p) for p in range(len(toks))]
+            blk = np.array([p[0] for p in pos], np.int64)[:, None]
+            off = np.array([p[1] for p in pos], np.int64)[:, None]
+            hh = heads[None, :]
+            kref = np.stack([self.tokens[t][0] for t in toks])  # [P, nh, d]
+            np.testing.assert_array_equal(key[blk, hh, off], ref_bits(kref, True), err_msg="key bits, request %d" % b)
+            if value is not None:
+                vref = np.stack([self.tokens[t][1] for t in toks])
+                np.testing.assert_array_equal(value[blk, hh, off], ref_bits(vref, True),
+                                              err_msg="value bits, request %d" % b)
+            if gate is not None:  # one gate, or one per key channel
+                gref = np.stack([self.tokens[t][2] for t in toks])
+                np.testing.assert_array_equal(gate[blk, hh, off], ref_bits(gref, False),
+                                              err_msg="gate bits, request %d" % b)

@@ -77,6 +77,7 @@ def _decode(layout, pools=POOLS, batch=BATCH, q=FAKE, g=FAKE, beta=None):
     (dict(m=6), kb.ECAPACITY),             # not a multiple of block_size
     (dict(m=12), kb.ECAPACITY),            # beyond capacity 8
     (dict(blocks_per_req=65), kb.ECAPACITY),
+    (dict(block_size=16, blocks_per_req=33, m=16, num_blocks=66), kb.ECAPACITY),  # 528 > 512 positions
     (dict(m=-1), kb.EINVAL),
     (dict(scale=float("nan")), kb.EINVAL),
 ])

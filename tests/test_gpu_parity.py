@@ -3,8 +3,9 @@
 Every test drives seeded synthetic inputs through kvbuf_* and through the
 fp64 per-token recurrence, and compares outputs at every step, stored states
 after every fold, effective states, and the bookkeeping (block tables,
-occupancies, buffered bits) exactly.  Small cases compare every tile; the
-full-size workloads compare a spread sample of (request, head) tiles.
+occupancies, buffered bits) exactly.  Every (request, head) tile is compared,
+at the full-size workloads too (their stored states: every tile at the first
+and the last fold, a rotating subset at the folds in between).
 """
 
 import numpy as np
@@ -452,9 +453,21 @@ def test_validation_errors_touch_nothing():
 
 
 # ---------------------------------------------------------------------------
-# Full-size workloads, sampled tiles, in the launch configuration the
-# benchmark times (eager fold inside the decode kernel).
+# Full-size workloads, every tile, in the launch configuration the benchmark
+# times (eager fold inside the decode kernel).
 # ---------------------------------------------------------------------------
+
+def _full_cycle_checks(run):
+    """End of a full-size run whose last step folded every request: every
+    tile's stored state, effective state and buffered bits."""
+    assert run.check_all_states() == run.w.B * run.w.H
+    run.check_effective_states()
+    run.check_pool()
+    run.check_bookkeeping()
+    assert run.full_state_checks == 2
+    _say("max out err %.2e, max state err %.2e, tile states checked %d"
+         % (run.max_out, run.max_state, run.folds_checked))
+
 
 def test_workload2_ungated_batched():
     w = synth.workload(2)
@@ -462,10 +475,7 @@ def test_workload2_ungated_batched():
     run = Run(w)
     for t in range(w.steps):
         run.decode(t)
-    run.check_effective_states()
-    run.check_pool()
-    _say("max out err %.2e, max state err %.2e, folds checked %d" % (run.max_out, run.max_state, run.folds_checked))
-    assert run.folds_checked == len(run.sample) * (w.steps // w.m)
+    _full_cycle_checks(run)
 
 
 def test_workload3_gated_m8_full():
@@ -474,29 +484,30 @@ def test_workload3_gated_m8_full():
     run = Run(w)
     for t in range(w.steps):
         run.decode(t)
-    run.check_effective_states()
-    run.check_pool()
-    _say("max out err %.2e, max state err %.2e, folds checked %d" % (run.max_out, run.max_state, run.folds_checked))
+    _full_cycle_checks(run)
 
 
 @pytest.mark.parametrize("m", [0, 4, 16, 32])
 def test_workload3_gated_sweep(m):
-    steps = 2 * max(m, 8)
-    w = synth.workload(3, m=m, block_size=max(m, 1), blocks_per_req=2 if m else 1, steps=steps)
+    """The other buffer sizes of the gated workload, 512 steps each (64 to 16
+    buffer cycles; m = 0 is the recurrent kernel)."""
+    w = synth.workload(3, m=m, block_size=max(m, 1), blocks_per_req=2 if m else 1)
+    assert w.steps == 512
     _say("workload 3 m=%d" % m, w)
     run = Run(w)
     for t in range(w.steps):
         run.decode(t)
     if m:
-        run.check_effective_states()
-        run.check_pool()
-    _say("max out err %.2e, max state err %.2e" % (run.max_out, run.max_state))
+        _full_cycle_checks(run)
+    else:  # recurrent: every state is current after every step
+        assert run.check_all_states() == w.B * w.H
+        _say("max out err %.2e, max state err %.2e" % (run.max_out, run.max_state))
 
 
 @pytest.mark.parametrize("n", [4, 8])
 def test_workload4_tree_verify_commit(n):
     """Tree drafts at the verification workload's full size (B=128 H=32
-    d=128 m=8), in the launch configuration the benchmark times; sampled tiles
+    d=128 m=8), in the launch configuration the benchmark times; every tile
     against the recurrence along each draft's path."""
     w = synth.workload(4)
     _say("workload 4 trees n=%d" % n, w)
@@ -526,6 +537,7 @@ def test_workload4_verify_commit(n):
         run.verify_commit(call, n, acc)
     run.check_effective_states()
     run.check_pool()
+    run.check_bookkeeping()
     _say("max out err %.2e, max state err %.2e" % (run.max_out, run.max_state))
 
 
@@ -534,8 +546,7 @@ def test_workload5_mixed_delta():
     _say("workload 5", w)
     stateless = np.zeros(w.B, bool)
     stateless[w.B - w.n_short:] = True
-    sample = [(b, h) for b, h in zip([0, 3, 100, 255, 256, 300, 401, 511], [0, 17, 31, 5, 0, 9, 22, 31])]
-    run = Run(w, stateless=stateless, sample=sample, spare_blocks=64)
+    run = Run(w, stateless=stateless, spare_blocks=64)
     short = np.arange(w.B - w.n_short, w.B)
     life = synth.short_lengths(w, 0, len(short))
     age = np.zeros(len(short), np.int64)
@@ -553,6 +564,8 @@ def test_workload5_mixed_delta():
     run.check_effective_states()
     run.check_pool()
     run.check_bookkeeping()
+    # the long requests fold at the last step: every one of their tiles
+    assert run.check_all_states() >= (w.B - w.n_short) * w.H
     _say("retired %d; max out err %.2e, max state err %.2e" % (retired, run.max_out, run.max_state))
 
 
@@ -617,13 +630,13 @@ def test_verify_recurrent_baseline(rule, n, d):
 @pytest.mark.parametrize("rule,m", [(1, 64), (1, 128), (2, 64), (2, 128), (0, 128), (3, 64)])
 def test_long_fold_full_size(rule, m):
     """kvbuf_flush of m buffered tokens at B=256 H=32 d=128, bf16, in the
-    launch configuration the benchmark times (a block of m per request):
-    sampled tiles against the recurrence over their m buffered tokens -- for
-    the delta rule over its stored pseudo-values, which a fold applies as the
-    values of the scalar-gated rule.  (The per-channel rule keeps buffers of
-    at most 64 positions.)"""
+    launch configuration the benchmark times (a block of m per request, pools
+    filled on the device): every tile against the recurrence over its m
+    buffered tokens -- for the delta rule over its stored pseudo-values,
+    which a fold applies as the values of the scalar-gated rule.  (The
+    per-channel rule keeps buffers of at most 64 positions.)"""
     import oracle
-    from tests.harness import TOL_STATE, rel_err_tiles
+    from tests.harness import NTHREADS, TOL_STATE, rel_err_tiles
 
     B, H, d = 256, 32, 128
     dev = torch.device("cuda:0")
@@ -636,38 +649,29 @@ def test_long_fold_full_size(rule, m):
     kv.value.normal_(generator=gen)
     if kv.gate is not None:
         kv.gate.uniform_(-0.1, 0.0, generator=gen)
-    # sampled tiles: seeded host data written into their state slots and blocks
-    rs = np.random.default_rng(9200 + 10 * rule + m)
-    flat = [0, B * H - 1] + [int(x) for x in rs.choice(np.arange(1, B * H - 1), 10, replace=False)]
-    tiles = [(f // H, f % H) for f in flat]
-    n = len(tiles)
-    bf16 = lambda a: torch.from_numpy(a).to(torch.bfloat16).float().numpy()
-    S0 = rs.normal(0.0, 0.02, (n, d, d)).astype(np.float32)
-    K = bf16(rs.normal(size=(m, n, d)).astype(np.float32))
-    V = rs.normal(size=(m, n, d)).astype(np.float32)
-    if rule != kb.RULE_DELTA:
-        V = bf16(V)
-    G = rs.uniform(-0.1, 0.0, (m, n, d) if rule == kb.RULE_CHANNEL else (m, n)).astype(np.float32)
-    slot = kv.state_slot.cpu().numpy()
-    block = kv.block_table.cpu().numpy()
-    for j, (b, h) in enumerate(tiles):
-        s, blk = int(slot[b]), int(block[b, h, 0])
-        kv.state[s, h] = torch.from_numpy(S0[j]).to(dev)
-        kv.key[blk, h] = torch.from_numpy(K[:, j]).to(dev, kv.key.dtype)
-        kv.value[blk, h] = torch.from_numpy(V[:, j]).to(dev, kv.value.dtype)
-        if kv.gate is not None:
-            kv.gate[blk, h] = torch.from_numpy(G[:, j]).to(dev)
+    # shuffled slots and blocks, so that tile (b, h) reads slot[b] and block[b]
+    perm = torch.randperm(B, generator=torch.Generator().manual_seed(9300 + m)).to(torch.int32)
+    kv.state_slot.copy_(perm)
+    kv.set_block_table(torch.roll(perm, 7).reshape(B, 1))
+    slot = kv.state_slot.cpu().numpy().astype(np.int64)
+    block = kv.block_table.cpu().numpy()[:, 0, 0].astype(np.int64)
+    # host copies, tile-major: S0 [B*H, d, d], K / V [m, B*H, d], G [m, B*H (, d)]
+    S0 = kv.state[torch.from_numpy(slot).to(dev)].reshape(B * H, d, d).cpu().numpy().astype(np.float64)
+    tiles = lambda x: x[torch.from_numpy(block).to(dev)].float().movedim(2, 0).reshape(m, B * H, *x.shape[3:])
+    K = tiles(kv.key).cpu().numpy()
+    V = tiles(kv.value).cpu().numpy()
+    G = None if kv.gate is None else tiles(kv.gate).cpu().numpy()
     kv.occupancy.fill_(m)
     _say("long fold full size rule %d m %d" % (rule, m))
     kv.flush()
     torch.cuda.synchronize()
     assert int(kv.error.item()) == 0
     assert int(kv.occupancy.abs().sum().item()) == 0
-    assert np.array_equal(kv.block_table.cpu().numpy(), block)  # one block per request rotates onto itself
+    assert np.array_equal(kv.block_table.cpu().numpy()[:, 0, 0], block)  # one block per request rotates onto itself
     # the fold of the delta rule is the scalar-gated rule's over pseudo-values
     ref_rule = kb.RULE_GATED if rule == kb.RULE_DELTA else rule
-    _, S_ref = oracle.recurrent(ref_rule, S0, np.zeros((m, n, d)), K, V, G if rule != kb.RULE_LINEAR else None)
-    S_gpu = np.stack([kv.state[int(slot[b]), h].cpu().numpy() for b, h in tiles])
+    _, S_ref = oracle.recurrent(ref_rule, S0, np.zeros((m, B * H, d)), K, V, G, nthreads=NTHREADS, inplace=True)
+    S_gpu = kv.state[torch.from_numpy(slot).to(dev)].reshape(B * H, d, d).cpu().numpy()
     err = rel_err_tiles(S_gpu, S_ref, axes=(-2, -1))
-    _say("max state err %.2e" % err)
+    _say("max state err over %d tiles %.2e" % (B * H, err))
     assert err <= TOL_STATE, "state error %.3e" % err
