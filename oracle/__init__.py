@@ -72,7 +72,7 @@ def _load():
         dp = ctypes.POINTER(ctypes.c_double)
         lib.oracle_recurrent.argtypes = [
             ctypes.c_int, ctypes.c_long, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-            ctypes.c_double, dp, dp, dp, dp, dp, dp, dp, ctypes.c_int,
+            ctypes.c_double, dp, dp, dp, dp, dp, dp, dp, dp, ctypes.c_int,
         ]
         lib.oracle_recurrent.restype = ctypes.c_int
         lib.oracle_threads_used.argtypes = [ctypes.c_int]
@@ -96,7 +96,8 @@ def _ptr(a):
     return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
 
 
-def recurrent(rule, S0, q, k, v, g=None, beta=None, scale=1.0, nthreads=1, inplace=False):
+def recurrent(rule, S0, q, k, v, g=None, beta=None, scale=1.0, nthreads=1, inplace=False,
+              with_magnitude=False):
     """Per-token recurrence over ``nsteps`` tokens for ``ntiles`` independent tiles.
 
     Arguments (any float dtype; widened exactly to fp64):
@@ -112,6 +113,11 @@ def recurrent(rule, S0, q, k, v, g=None, beta=None, scale=1.0, nthreads=1, inpla
     place and returned as S (no copy of a large state).  ``nthreads`` spreads
     the independent tiles over OpenMP threads; each tile's arithmetic is the
     same at any thread count.
+    With ``with_magnitude`` a third array [nsteps, ntiles, dv] is returned:
+    |S_t|^T |scale q_t|, each output computed from the absolute values of its
+    terms -- the size of the product that defines o_t, which bounds what
+    rounding in any summation order can do to it (a near-cancelling output
+    is small next to it).
     """
     if inplace:
         if not (isinstance(S0, np.ndarray) and S0.dtype == np.float64 and S0.flags.c_contiguous):
@@ -133,11 +139,14 @@ def recurrent(rule, S0, q, k, v, g=None, beta=None, scale=1.0, nthreads=1, inpla
         g = _f64(g, (nsteps, ntiles)) if rule >= 1 else None
     beta = _f64(beta, (nsteps, ntiles)) if rule == 2 else None
     out = np.zeros((nsteps, ntiles, dv), dtype=np.float64)
+    mag = np.zeros((nsteps, ntiles, dv), dtype=np.float64) if with_magnitude else None
     rc = _load().oracle_recurrent(int(rule), ntiles, nsteps, dk, dv, float(scale), _ptr(S),
                                   _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(out),
-                                  int(nthreads))
+                                  _ptr(mag), int(nthreads))
     if rc != 0:
         raise ValueError("oracle_recurrent rejected its arguments")
+    if with_magnitude:
+        return out, S, mag
     return out, S
 
 

@@ -42,6 +42,10 @@
  *   g, beta [nsteps][ntiles]     (g may be NULL for rule 0; beta only for rule 2)
  *   g       [nsteps][ntiles][dk] for rule 3
  *   out   [nsteps][ntiles][dv]
+ *   mag   [nsteps][ntiles][dv] or NULL: |S_t|^T |scale q_t|, the output
+ *         computed with every term's absolute value -- the size of the
+ *         product that defines o_t, against which the error of a result
+ *         accumulated in finite precision is measured
  */
 #include <math.h>
 #include <stddef.h>
@@ -53,7 +57,7 @@
 static void oracle_one_tile(int rule, long tile, long ntiles, int nsteps, int dk, int dv,
                             double scale, double* S, const double* q, const double* k,
                             const double* v, const double* g, const double* beta,
-                            double* out, double* work)
+                            double* out, double* mag, double* work)
 {
     for (int t = 0; t < nsteps; ++t) {
         const double* qt = q + ((size_t)t * ntiles + tile) * dk;
@@ -100,6 +104,14 @@ static void oracle_one_tile(int rule, long tile, long ntiles, int nsteps, int dk
             double qr = scale * qt[r];
             for (int c = 0; c < dv; ++c) ot[c] += S[(size_t)r * dv + c] * qr;
         }
+        if (mag) {
+            double* mt = mag + ((size_t)t * ntiles + tile) * dv;
+            for (int c = 0; c < dv; ++c) mt[c] = 0.0;
+            for (int r = 0; r < dk; ++r) {
+                double qa = fabs(scale * qt[r]);
+                for (int c = 0; c < dv; ++c) mt[c] += fabs(S[(size_t)r * dv + c]) * qa;
+            }
+        }
     }
 }
 
@@ -108,7 +120,8 @@ static void oracle_one_tile(int rule, long tile, long ntiles, int nsteps, int dk
  * each tile is unchanged).  Returns 0, or -1 on a bad argument. */
 int oracle_recurrent(int rule, long ntiles, int nsteps, int dk, int dv, double scale,
                      double* S, const double* q, const double* k, const double* v,
-                     const double* g, const double* beta, double* out, int nthreads)
+                     const double* g, const double* beta, double* out, double* mag,
+                     int nthreads)
 {
     if (rule < 0 || rule > 3 || ntiles < 0 || nsteps < 0 || dk <= 0 || dv <= 0) return -1;
     if (!S || !q || !k || !v || !out) return -1;
@@ -124,7 +137,7 @@ int oracle_recurrent(int rule, long ntiles, int nsteps, int dk, int dv, double s
         for (long tile = 0; tile < ntiles; ++tile) {
             if (!work) continue;
             oracle_one_tile(rule, tile, ntiles, nsteps, dk, dv, scale,
-                            S + (size_t)tile * dk * dv, q, k, v, g, beta, out, work);
+                            S + (size_t)tile * dk * dv, q, k, v, g, beta, out, mag, work);
         }
         free(work);
     }

@@ -53,7 +53,7 @@ def fold_guard_workload(rule, m):
 @pytest.mark.parametrize("tree", [False, True])
 def test_verify_state_products_precision(n, tree):
     w = verify_guard_workload()
-    run = Run(w, tol_out=VERIFY_BOUND)
+    run = Run(w, tol_out=VERIFY_BOUND, out_scale="output")
     assert not run.device_gen
     for call in range(3):  # occupancy 0, then wherever the commits leave it
         if tree:

@@ -257,3 +257,39 @@ def test_oracle_serial_decode_equals_exact_parallel_verify(rule):
                               g=g[:, None], beta=beta[:, None])
     for d in range(n):
         _close(out[T + d, 0], [float(x) for x in outs[d]])
+
+
+# --------------------------------------------------------------------------
+# The output magnitude |S_t|^T |scale q_t| (the scale output errors are
+# measured against): triangle inequality, equality when every term is
+# non-negative, and homogeneity in the query scale.
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("rule", [0, 1, 2, 3])
+def test_magnitude_bounds_the_output(rule):
+    T, ntiles, dk, dv = 6, 3, 4, 5
+    rs = np.random.default_rng(70 + rule)
+    S0 = rs.standard_normal((ntiles, dk, dv))
+    q, k = rs.standard_normal((T, ntiles, dk)), _unit_rows(rs.standard_normal((T, ntiles, dk)))
+    v = rs.standard_normal((T, ntiles, dv))
+    g = rs.uniform(-0.1, 0.0, (T, ntiles, dk) if rule == 3 else (T, ntiles))
+    beta = rs.uniform(0.0, 1.0, (T, ntiles))
+    out, _, mag = oracle.recurrent(rule, S0, q, k, v, g=g, beta=beta, scale=-0.75, with_magnitude=True)
+    assert np.all(mag >= np.abs(out) * (1 - 1e-12))
+    # cancellation makes the output smaller than its magnitude somewhere
+    assert np.max(mag - np.abs(out)) > 0.1
+    _, _, mag1 = oracle.recurrent(rule, S0, q, k, v, g=g, beta=beta, scale=1.5, with_magnitude=True)
+    _close(mag1, 2.0 * mag)
+
+
+@pytest.mark.parametrize("rule", [0, 1, 3])
+def test_magnitude_equals_output_without_cancellation(rule):
+    """Non-negative state, queries, keys and values: every term of every
+    output is non-negative, so the output equals its magnitude."""
+    T, ntiles, dk, dv = 5, 2, 3, 4
+    rs = np.random.default_rng(80 + rule)
+    S0 = rs.uniform(0, 1, (ntiles, dk, dv))
+    q, k, v = (rs.uniform(0, 1, (T, ntiles, n)) for n in (dk, dk, dv))
+    g = rs.uniform(-0.1, 0.0, (T, ntiles, dk) if rule == 3 else (T, ntiles))
+    out, _, mag = oracle.recurrent(rule, S0, q, k, v, g=g, with_magnitude=True)
+    _close(mag, out)
