@@ -11,8 +11,10 @@ latency is averaged over a full buffer cycle -- occupancies 0 .. m-1 and the
 state update).  Inputs are a ring of 2m pre-generated steps resident in HBM.
 
 Also measured in the same run: the m = 0 recurrent kernel at the same shape
-(the figure's normaliser), the variant with a separate flush launch, a plain
-device copy (measured bandwidth ceiling) and the oracle on the host cores.
+(the figure's normaliser), the variant with a separate flush launch,
+compute-free probe kernels streaming the same tiles (the measured ceilings of
+the access pattern), the other workloads' legs and the oracle on the host
+cores.
 
 Prints ONE JSON line.
 """
@@ -235,16 +237,98 @@ def cycle_leg(kb, synth, torch, dev, w, cycles, warmup):
             "bytes_per_token": per_tile * w.H / m}
 
 
-def sweep_leg(kb, synth, torch, dev, args):
-    """The Figure 3 analogue: buffer sizes m = 4, 16, 32 of the metric
-    workload (blocks of m, two per request), about as many decode launches
-    each as the headline run; m = 0 and m = 8 are the recurrent and headline
-    legs."""
+def separate_cycle_leg(kb, synth, torch, dev, w, cycles, warmup):
+    """Full buffer cycles under the deferred policy: m decode launches that
+    only append, then one kvbuf_flush launch folding the m tokens."""
+    m = w.m
+    kv = build_kv(kb, synth, torch, w, kb.FLUSH_DEFERRED, dev)
+    ring = make_ring(synth, w, dev, 2 * m)
+    out = torch.empty((w.B, w.H, w.dv), dtype=torch.float32, device=dev)
+
+    def cycle(i):
+        for j in range(m):
+            r = ring[(i * m + j) % len(ring)]
+            kv.decode(r["q"], r["k"], r["v"], r["g"], out=out)
+        kv.flush()
+
+    wall = time_loop(torch, cycle, cycles, warmup)
+    torch.cuda.synchronize()
+    assert int(kv.error.item()) == 0
+    del kv
+    tiles = w.B * w.H
+    per_tile = cycle_bytes_separate(m, w.dk, w.dv)
+    cyc_s = wall / cycles
+    return {"m": m, "tokens_per_s": w.B * m / cyc_s, "ms_per_cycle": cyc_s * 1e3,
+            "hbm_gbps": per_tile * tiles / cyc_s / 1e9,
+            "hbm_frac_of_peak": per_tile * tiles / cyc_s / 1e9 / PEAK_HBM_GBPS,
+            "bytes_per_token": per_tile * w.H / m}
+
+
+def ceilings_leg(torch, dev):
+    """What the memory system gives the decode path's access pattern, measured
+    with compute-free probe kernels (libkvbuf_probe.so) at the metric shape:
+    8192 fp32 tiles of 128 x 128 at shuffled slots, one 256-thread workgroup
+    per tile, 16 non-temporal 128-bit loads per thread issued at once.
+      read                  the state read alone
+      read_write_1k         + 1 KiB written per tile (a decode's output row and
+                            appended key and value)
+      read_write_back       the tile read and written back in place (a fold)
+      read_write_1k_read_24k  + 24 KiB more read per tile (a delta-rule decode's
+                            buffered rows at occupancy 32)
+    Each figure is the median of 20 launches: algorithmic bytes / duration."""
+    import ctypes
+
+    lib = ctypes.CDLL(os.path.join(ROOT, "linear_attention_decode_kvbuf_amd", "libkvbuf_probe.so"))
+    P, i32 = ctypes.c_void_p, ctypes.c_int
+    lib.kvbuf_probe_stream.argtypes = [P, P, i32, i32, i32, P, i32, P, i32, P]
+    lib.kvbuf_probe_stream.restype = i32
+    d, ntiles = 128, 256 * 32
+    tile = 4 * d * d
+    tiles = torch.empty((ntiles, d, d), dtype=torch.float32, device=dev).normal_()
+    slot = torch.randperm(ntiles, generator=torch.Generator().manual_seed(5)).to(torch.int32).to(dev)
+    extra, extra2 = 1024, 24704
+    side = torch.zeros(ntiles * extra // 4, dtype=torch.float32, device=dev)
+    side2 = torch.ones(ntiles * extra2 // 4, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
     out = {}
-    for m in (4, 16, 32):
+    for name, kind, nbytes in (("read", 0, tile), ("read_write_1k", 1, tile + extra),
+                               ("read_write_back", 2, 2 * tile),
+                               ("read_write_1k_read_24k", 3, tile + extra + extra2)):
+        def launch():
+            rc = lib.kvbuf_probe_stream(tiles.data_ptr(), slot.data_ptr(), ntiles, d, kind, side.data_ptr(),
+                                        extra if kind in (1, 3) else 0, side2.data_ptr(),
+                                        extra2 if kind == 3 else 0, stream)
+            assert rc == 0, rc
+        for _ in range(3):
+            launch()
+        ms = per_launch_ms(torch, [launch], 20, median=True)[0]
+        out[name] = {"us": ms * 1e3, "gbps": nbytes * ntiles / (ms * 1e-3) / 1e9,
+                     "frac_of_peak": nbytes * ntiles / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS}
+    torch.cuda.synchronize()
+    del tiles, side, side2
+    return out
+
+
+def sweep_leg(kb, synth, torch, dev, args):
+    """The Figure 3 protocol over buffer sizes m = 4, 8, 16, 32 of the metric
+    workload (blocks of m, two per request): per-token latency averaged over a
+    full buffer cycle -- decodes at occupancies 0 .. m-1 plus the state update
+    -- normalised by the recurrent (m = 0) kernel's per-token latency, with
+    the update fused into the decode that fills the buffer and as a separate
+    flush launch (the pages time the update as its own step)."""
+    w0 = synth.workload(3, m=0, block_size=1, blocks_per_req=1)
+    rec = cycle_leg(kb, synth, torch, dev, w0, max(5, args.steps), max(2, args.warmup))
+    rec_tok = rec["ms_per_cycle"] / w0.B  # one decode step per "cycle" at m = 0
+    out = {"m0": rec}
+    for m in (4, 8, 16, 32):
         w = synth.workload(3, m=m)
         cycles = max(5, args.steps * 8 // m)
-        out["m%d" % m] = cycle_leg(kb, synth, torch, dev, w, cycles, max(2, args.warmup * 8 // m))
+        warm = max(2, args.warmup * 8 // m)
+        fused = cycle_leg(kb, synth, torch, dev, w, cycles, warm)
+        sep = separate_cycle_leg(kb, synth, torch, dev, w, cycles, warm)
+        for leg in (fused, sep):
+            leg["normalized_latency_vs_m0"] = (leg["ms_per_cycle"] / (m * w.B)) / rec_tok
+        out["m%d" % m] = {"fused": fused, "separate_flush": sep}
     return out
 
 
@@ -380,6 +464,7 @@ def verify_leg(kb, synth, torch, dev, args):
         vbytes = tiles * (4 * w.dk * w.dv + 2 * n * (2 * w.dk + w.dv) + 4 * n * w.dv)
         res = {"verify_ms": ver, "commit_ms": com,
                "verify_hbm_gbps": vbytes / (ver * 1e-3) / 1e9,
+               "verify_frac_of_peak": vbytes / (ver * 1e-3) / 1e9 / PEAK_HBM_GBPS,
                "accepted_tokens_per_s": accepted / ((ver + com) * 1e-3)}
         res["tree"] = tree_verify(kb, synth, torch, kv, w, n, drafts, obuf, vbytes)
         del kv
@@ -432,6 +517,7 @@ def tree_verify(kb, synth, torch, kv, w, n, drafts, obuf, vbytes):
     com = sum(per[1::2]) / 8
     accepted = sum(kept) / 4
     return {"verify_ms": ver, "commit_ms": com, "verify_hbm_gbps": vbytes / (ver * 1e-3) / 1e9,
+            "verify_frac_of_peak": vbytes / (ver * 1e-3) / 1e9 / PEAK_HBM_GBPS,
             "accepted_tokens_per_s": accepted / ((ver + com) * 1e-3)}
 
 
@@ -465,6 +551,7 @@ def verify_baseline(kb, synth, torch, dev, w, n, drafts, accs):
     vbytes = tiles * (4 * w.dk * w.dv * (1 + n) + 2 * n * (2 * w.dk + w.dv) + 4 * n * (w.dv + 1))
     accepted = float(sum(int(a.sum()) for a in accs[:4]) / 4)
     return {"verify_ms": ver, "commit_ms": com, "verify_hbm_gbps": vbytes / (ver * 1e-3) / 1e9,
+            "verify_frac_of_peak": vbytes / (ver * 1e-3) / 1e9 / PEAK_HBM_GBPS,
             "accepted_tokens_per_s": accepted / ((ver + com) * 1e-3)}
 
 
@@ -499,17 +586,33 @@ def long_fold_leg(kb, synth, torch, dev, args):
             ms = sum(per[1::2]) / 4
             xb = 4 * w.dv if rule == kb.RULE_DELTA else 2 * w.dv  # pseudo-values are fp32
             tile_bytes = 8 * w.dk * w.dv + m * (2 * w.dk + xb + 4)
-            out["%s_m%d" % (name, m)] = {"flush_ms": ms,
-                                         "hbm_gbps": tile_bytes * w.B * w.H / (ms * 1e-3) / 1e9}
+            gbps = tile_bytes * w.B * w.H / (ms * 1e-3) / 1e9
+            out["%s_m%d" % (name, m)] = {"flush_ms": ms, "hbm_gbps": gbps, "frac_of_peak": gbps / PEAK_HBM_GBPS,
+                                         "algorithmic_bytes_per_launch": tile_bytes * w.B * w.H}
             del kv
     return out
+
+
+def delta_decode_bytes(j, dk, dv, stateful):
+    """Algorithmic bytes of one delta-rule decode of a tile at occupancy j:
+    state read (requests with a state), q / k / v in (bf16), log-gate and
+    step size in, j buffered rows read (bf16 key, fp32 pseudo-value, fp32
+    log-gate), the new row appended, the output written (fp32)."""
+    row = 2 * dk + 4 * dv + 4
+    return (4 * dk * dv if stateful else 0) + 2 * (2 * dk + dv) + 8 + row * (j + 1) + 4 * dv
+
+
+def delta_fold_bytes(m, dk, dv):
+    """A fold of m delta-rule rows: state read and write plus the m rows."""
+    return 8 * dk * dv + m * (2 * dk + 4 * dv + 4)
 
 
 def delta_leg(kb, synth, torch, dev, args):
     """Gated delta rule, B=512 (256 requests with a state, 256 served from the
     buffer alone), H=32 d=128 m=64: one decode launch per step (plus the fold
     launch that follows it, since 64 positions exceed one staging pass), over
-    a full 64-step cycle."""
+    a full 64-step cycle.  Every request starts the cycle empty, so at step t
+    all tiles are at occupancy t; the long requests fold at the last step."""
     w = synth.workload(5)
     kv = kb.KVBuffer(batch=w.B, heads=w.H, d=w.dk, m=w.m, block_size=w.block_size,
                      blocks_per_req=w.blocks_per_req, num_blocks=w.B * w.blocks_per_req,
@@ -537,8 +640,19 @@ def delta_leg(kb, synth, torch, dev, args):
     torch.cuda.synchronize()
     assert int(kv.error.item()) == 0
     cyc = sum(per)
+    n_long = (w.B - w.n_short) * w.H
+    n_short = w.n_short * w.H
+    step_bytes = [n_long * delta_decode_bytes(t, w.dk, w.dv, True) + n_short * delta_decode_bytes(t, w.dk, w.dv, False)
+                  for t in range(w.m)]
+    step_bytes[-1] += n_long * delta_fold_bytes(w.m, w.dk, w.dv)
+    cyc_bytes = sum(step_bytes)
+    gbps = cyc_bytes / (cyc * 1e-3) / 1e9
+    step_gbps = [b / (t * 1e-3) / 1e9 for b, t in zip(step_bytes, per)]
     return {"cycle_ms": cyc, "tokens_per_s": w.B * w.m / (cyc * 1e-3),
-            "decode_step_ms_mean": cyc / w.m, "fold_step_ms": per[-1]}
+            "decode_step_ms_mean": cyc / w.m, "fold_step_ms": per[-1],
+            "step_ms": [round(x, 4) for x in per],
+            "algorithmic_bytes_per_cycle": cyc_bytes, "hbm_gbps": gbps, "frac_of_peak": gbps / PEAK_HBM_GBPS,
+            "step_frac_of_peak": [round(x / PEAK_HBM_GBPS, 3) for x in step_gbps]}
 
 
 def main():
@@ -549,7 +663,7 @@ def main():
     ap.add_argument("--m", type=int, default=8, help="buffer size")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing on the host")
     ap.add_argument("--no-extras", action="store_true", help="skip the m=0 / separate-flush / copy legs")
-    ap.add_argument("--only", choices=["fused", "recurrent", "separate", "copy", "verify", "delta", "sweep",
+    ap.add_argument("--only", choices=["fused", "recurrent", "separate", "ceilings", "verify", "delta", "sweep",
                                        "linear", "heads4", "context", "channel", "longfold"], default=None,
                     help="run one leg only (for profiling)")
     args = ap.parse_args()
@@ -657,15 +771,18 @@ def main():
         }
         del kvd
 
-    # ---- plain device copy: measured bandwidth ceiling --------------------
-    if not args.no_extras and args.only in (None, "copy"):
-        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).normal_()
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        pc = per_launch_ms(torch, [lambda: dst.copy_(src)], 20)[0]
-        result["copy_ceiling_gbps"] = 2 * src.numel() * 4 / (pc * 1e-3) / 1e9
-        del src, dst
+    # ---- memory-system ceilings of the access pattern (probe kernels) -------
+    if not args.no_extras and args.only in (None, "ceilings"):
+        result["memory_ceilings"] = ceilings_leg(torch, dev)
+        if "roofline" in result:
+            # a compute-free stream of the cycle's traffic: m - 1 launches that
+            # read the tile and write about 1 KiB, one that writes it back
+            c = result["memory_ceilings"]
+            t_cycle = ((m - 1) * c["read_write_1k"]["us"] + c["read_write_back"]["us"] + c["read_write_1k"]["us"]
+                       - c["read"]["us"]) * 1e-6
+            ceil = cycle_bytes_fused(m, w.dk, w.dv) * tiles / t_cycle / 1e9
+            result["roofline"]["measured_ceiling_gbps"] = ceil
+            result["roofline"]["frac_of_measured_ceiling"] = result["roofline"]["achieved"] / ceil
 
     # ---- speculative verification: n drafts, then commit a ~ U{0..n} -------
     if not args.no_extras and args.only in (None, "verify"):
@@ -725,7 +842,7 @@ def main():
         "roofline": result["roofline"],
         "cpu_baseline": cpu,
     }
-    for key in ("per_occupancy_ms", "m0_recurrent", "separate_flush", "copy_ceiling_gbps", "verify",
+    for key in ("per_occupancy_ms", "m0_recurrent", "separate_flush", "memory_ceilings", "verify",
                 "delta_mixed", "m_sweep", "linear_B64", "head_share_H4", "context_sweep", "channel_gates",
                 "long_folds"):
         if key in result:

@@ -3,7 +3,9 @@
     python -m linear_attention_decode_kvbuf_amd._build
 
 Each translation unit is compiled by hipcc in parallel, then linked into one
-shared library that exports the C ABI of include/kvbuf.h.
+shared library that exports the C ABI of include/kvbuf.h.  The benchmark's
+memory-system probes (csrc/probe.hip) go into a library of their own,
+libkvbuf_probe.so, which the product library neither contains nor loads.
 """
 
 from __future__ import annotations
@@ -19,9 +21,11 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libkvbuf.so")
+PROBE_LIB = os.path.join(PKG, "libkvbuf_probe.so")
 OBJ_DIR = os.path.join(PKG, "_build")
 
 SOURCES = ["abi.cpp", "chunk.hip", "fold.hip", "recurrent.hip", "decode.hip"]
+PROBE_SOURCES = ["probe.hip"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 instructions.
@@ -52,18 +56,23 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(OBJ_DIR, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
+def _link(objs, lib):
+    tmp = lib + ".tmp%d" % os.getpid()
     cmd = [_hipcc(), "-shared", "-fPIC", "--offload-arch=" + ARCH, *objs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("link failed:\n" + res.stdout + res.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES) + len(PROBE_SOURCES))) as ex:
+        objs = list(ex.map(_compile, SOURCES + PROBE_SOURCES))
+    _link(objs[: len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], PROBE_LIB)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", PROBE_LIB)
     return LIB
 
 

@@ -1,0 +1,80 @@
+// Memory-system probes at the decode path's access pattern, for the
+// benchmark's ceilings (not part of the kvbuf C ABI; built into
+// libkvbuf_probe.so).  Each probe streams fp32 tiles of d x d (64 KiB at
+// d = 128) with one 256-thread workgroup per tile, every thread issuing its
+// 16 128-bit loads at once through a range-checked buffer resource, the way
+// the decode kernels read a state tile, and does no arithmetic beyond keeping
+// the loaded values alive:
+//   kind 0  read the tile                               (a buffered decode's state read)
+//   kind 1  read the tile, write `extra` bytes elsewhere (+ its output row and appends)
+//   kind 2  read the tile and write it back in place     (a fold's state traffic)
+//   kind 3  read the tile, write `extra` bytes elsewhere and read `extra2`
+//           more bytes from a second region               (+ buffered rows)
+// Tile w of the grid is slot[w]; reads and writes use the non-temporal hint,
+// as the decode kernels' state traffic does.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+constexpr int kFlags = 0x00020000;
+constexpr int kNT = 2;
+
+template <int D>
+__global__ __launch_bounds__(256) void probe_kernel(float* tiles, const int32_t* slot, int kind, float* side,
+                                                    int extra, const float* side2, int extra2) {
+    constexpr int TPR = D / 4, RG = 256 / TPR, RPT = D / RG;
+    const int w = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int rg = tid / TPR, c0 = (tid % TPR) * 4;
+    float* tile = tiles + static_cast<size_t>(slot[w]) * D * D;
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(tile, 0, D * D * 4, kFlags);
+    const int v = (rg * RPT * D + c0) * 4;
+    f4 s[RPT];
+#pragma unroll
+    for (int j = 0; j < RPT; ++j)
+        s[j] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(r, v, j * D * 4, kNT));
+    f4 x2 = f4{0.f, 0.f, 0.f, 0.f};
+    if (kind == 3) {  // more bytes from a second region: 16 per thread per 4 KiB
+        const float* src = side2 + static_cast<size_t>(w) * (extra2 / 4);
+        for (int o = tid * 4; o < extra2 / 4; o += 1024) x2 += *reinterpret_cast<const f4*>(src + o);
+    }
+    if (kind == 2) {
+#pragma unroll
+        for (int j = 0; j < RPT; ++j)
+            __builtin_nontemporal_store(s[j] * 1.0000001f, reinterpret_cast<f4*>(tile + (rg * RPT + j) * D + c0));
+        return;
+    }
+    f4 acc = x2;
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) acc += s[j];
+    const float a = acc.x + acc.y + acc.z + acc.w;
+    if (kind == 1 || kind == 3) {
+        float* dst = side + static_cast<size_t>(w) * (extra / 4);
+        for (int o = tid * 4; o < extra / 4; o += 1024)
+            __builtin_nontemporal_store(f4{a, a, a, a}, reinterpret_cast<f4*>(dst + o));
+    } else if (a == -1.2345e-30f) {  // never true for the probe's data; keeps the loads alive
+        side[w] = a;
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+// tiles [num_slots][d][d] fp32; slot [ntiles]; side: kind 1/3 [ntiles][extra
+// bytes], else >= ntiles floats; side2 (kind 3) [ntiles][extra2 bytes].
+// extra and extra2 are multiples of 16.  Returns a hipError_t.
+int kvbuf_probe_stream(float* tiles, const int32_t* slot, int ntiles, int d, int kind, float* side, int extra,
+                       const float* side2, int extra2, hipStream_t stream) {
+    if (ntiles <= 0 || (d != 64 && d != 128) || kind < 0 || kind > 3 || extra % 16 || extra2 % 16)
+        return static_cast<int>(hipErrorInvalidValue);
+    if (d == 128)
+        probe_kernel<128><<<ntiles, 256, 0, stream>>>(tiles, slot, kind, side, extra, side2, extra2);
+    else
+        probe_kernel<64><<<ntiles, 256, 0, stream>>>(tiles, slot, kind, side, extra, side2, extra2);
+    return static_cast<int>(hipGetLastError());
+}
+
+}  // extern "C"
