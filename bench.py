@@ -609,15 +609,18 @@ def delta_fold_bytes(m, dk, dv):
 
 def delta_leg(kb, synth, torch, dev, args):
     """Gated delta rule, B=512 (256 requests with a state, 256 served from the
-    buffer alone), H=32 d=128 m=64: one decode launch per step (plus the fold
-    launch that follows it, since 64 positions exceed one staging pass), over
-    a full 64-step cycle.  Every request starts the cycle empty, so at step t
-    all tiles are at occupancy t; the long requests fold at the last step."""
+    buffer alone), H=32 d=128 m=64, over a full 64-step cycle.  A step is
+    kvbuf_decode over the requests with a state (the chunk kernel) and
+    kvbuf_direct over the buffer-only ones (one wave per tile), each on a view
+    of its request range.  The requests with a state flush under the deferred
+    policy: every request starts the cycle empty, so at step t all tiles are
+    at occupancy t, and the last step ends with one kvbuf_flush of the 64
+    buffered tokens of every request with a state."""
     w = synth.workload(5)
     kv = kb.KVBuffer(batch=w.B, heads=w.H, d=w.dk, m=w.m, block_size=w.block_size,
                      blocks_per_req=w.blocks_per_req, num_blocks=w.B * w.blocks_per_req,
                      num_state_slots=w.B - w.n_short, rule=kb.RULE_DELTA, io_dtype=kb.BF16,
-                     flush=kb.FLUSH_EAGER, device=dev)
+                     flush=kb.FLUSH_DEFERRED, device=dev)
     perm = synth.block_permutation(w, w.B * w.blocks_per_req)
     kv.set_block_table(perm.reshape(w.B, w.blocks_per_req))
     slots = torch.full((w.B,), -1, dtype=torch.int32)
@@ -626,8 +629,19 @@ def delta_leg(kb, synth, torch, dev, args):
     kv.state.copy_(synth.device_initial_state(w, w.B - w.n_short, dev))
     ring = [synth.device_token_inputs(w, t, dev) for t in range(8)]
     out = torch.empty((w.B, w.H, w.dv), dtype=torch.float32, device=dev)
-    fns = [(lambda r: (lambda: kv.decode(r["q"], r["k"], r["v"], r["g"], r["beta"], out=out)))(ring[t % 8])
-           for t in range(w.m)]
+    # requests with a state: kvbuf_decode on a view of their range; the
+    # buffer-only ones: kvbuf_direct on a view of theirs
+    s = w.B - w.n_short
+    long_kv, short_kv = kv.view(0, s), kv.view(s, w.n_short)
+
+    def step(r, last):
+        part = lambda a, z: [None if r[x] is None else r[x][a:z] for x in ("q", "k", "v", "g", "beta")]
+        lo, hi, out_lo, out_hi = part(0, s), part(s, w.B), out[:s], out[s:]
+        if last:  # the deferred flush of the requests with a state, whose buffers are now full
+            return lambda: (long_kv.decode(*lo, out=out_lo), short_kv.direct(*hi, out=out_hi), long_kv.flush())
+        return lambda: (long_kv.decode(*lo, out=out_lo), short_kv.direct(*hi, out=out_hi))
+
+    fns = [step(ring[t % 8], t == w.m - 1) for t in range(w.m)]
     for f in fns:  # one warm cycle
         f()
     per = [0.0] * w.m

@@ -246,6 +246,25 @@ class KVBuffer:
         self.batch = Batch(self.B, _ptr(self.state_slot), _ptr(self.block_table), _ptr(self.occupancy),
                            _ptr(self.error))
 
+    def view(self, start, count):
+        """Requests start .. start+count-1 as a batch of their own: the same
+        pools, the metadata rows of those requests (views, so calls on the
+        view advance this object's metadata).  Two views over disjoint
+        request ranges may be called one after the other on a stream, e.g.
+        kvbuf_decode for requests with a state and kvbuf_direct for those
+        served from their buffer alone."""
+        import copy
+
+        if not (0 <= start and count >= 0 and start + count <= self.B):
+            raise ValueError("request range %d + %d outside the batch of %d" % (start, count, self.B))
+        v = copy.copy(self)
+        v.B = count
+        v.state_slot = self.state_slot[start:start + count]
+        v.block_table = self.block_table[start:start + count]
+        v.occupancy = self.occupancy[start:start + count]
+        v._refresh()
+        return v
+
     def set_block_table(self, table):
         """Every head's copy of the block table <- table [B, blocks_per_req]."""
         t = self.torch.as_tensor(table, dtype=self.torch.int32).to(self.block_table.device)

@@ -116,6 +116,18 @@ kvbuf_status chunk_call(const kvbuf_layout* layout, const kvbuf_pools* pools,
         if (n < 1 || n > kvbuf::kMaxDrafts) return KVBUF_EUNSUPPORTED;
         if (n > layout->block_size * layout->blocks_per_req) return KVBUF_ECAPACITY;
     }
+    if (direct) {  // every rule, any capacity: the one-wave-per-tile kernel
+        TileParams t = make_params(layout, pools, batch);
+        t.mode = mode;
+        t.n = 1;
+        t.q = q;
+        t.k = k;
+        t.v = v;
+        t.g = g;
+        t.beta = beta;
+        t.out = out;
+        return from_hip(kvbuf::launch_direct(t, layout->rule, layout->d_k, layout->io_dtype, batch->size, stream));
+    }
     // the per-channel rule is served by the one-token decode kernel only
     if (layout->rule == KVBUF_RULE_CHANNEL && layout->m > 0 &&
         (parent || !kvbuf::decode_eligible(layout->rule, n, layout->block_size * layout->blocks_per_req)))

@@ -750,14 +750,9 @@ int chunk_fold_limit(int rule, int d, int io, int n, int cap) {
 }
 
 hipError_t launch_chunk(const TileParams& p, int rule, int d, int io, int batch, hipStream_t s) {
-    // Buffer-only requests of the linear and gated rules go to this kernel at
-    // every capacity: its direct-to-LDS ring reads the rows in one round trip,
-    // where the one-token kernel passes 16 positions per round trip through its
-    // token wave and holds state waves that have no state to read (measured
-    // 1.7-1.8x faster at 32 and 64 positions).  The per-channel rule has only
-    // the one-token kernel.
-    const bool direct_here = p.mode == MODE_DIRECT && rule != KVBUF_RULE_CHANNEL;
-    if (!p.parent && !direct_here && decode_eligible(rule, p.n, p.block_size * p.blocks_per_req))
+    // (kvbuf_direct has a kernel of its own; requests without a state inside
+    // a decode or verify launch are served here or by the one-token kernel.)
+    if (!p.parent && decode_eligible(rule, p.n, p.block_size * p.blocks_per_req))
         return launch_decode(p, rule, d, io, batch, s);
     return io == KVBUF_BF16 ? launch_chunk_r<bf16_bits>(p, rule, d, batch, s)
                             : launch_chunk_r<float>(p, rule, d, batch, s);

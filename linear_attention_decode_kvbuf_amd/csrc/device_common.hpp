@@ -222,7 +222,7 @@ __device__ __forceinline__ float exp_gate(float x) { return __expf(x); }
 
 // Inclusive prefix sum of the log-gates of buffer positions 0 .. T-1 into
 // bl[0 .. T-1] (LDS), by one wave (lane = 0..63) in 64-wide segments.
-// gate_at(i) returns the log-gate of position i.
+// gate_at(i) returns the log-gate of position i (cheap: from LDS).
 template <typename GateAt>
 __device__ __forceinline__ void gate_prefix(float* bl, int T, int lane, GateAt gate_at) {
     float carry = 0.0f;
@@ -237,6 +237,37 @@ __device__ __forceinline__ void gate_prefix(float* bl, int T, int lane, GateAt g
         x += carry;
         if (i < T) bl[i] = x;
         carry = __shfl(x, 63, 64);
+    }
+}
+
+// The same when gate_at reads device memory: the gates of every segment are
+// requested before the first is summed (one round trip for a buffer of any
+// length; T <= kMaxCapacity; eight registers per lane).
+template <typename GateAt>
+__device__ __forceinline__ void gate_prefix_loads(float* bl, int T, int lane, GateAt gate_at) {
+    constexpr int KS = kMaxCapacity / 64;
+    float g[KS];
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+        const int i = 64 * k + lane;
+        g[k] = 0.0f;
+        if (64 * k < T && i < T) g[k] = gate_at(i);
+    }
+    float carry = 0.0f;
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+        if (64 * k < T) {
+            const int i = 64 * k + lane;
+            float x = g[k];
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                float y = __shfl_up(x, off, 64);
+                if (lane >= off) x += y;
+            }
+            x += carry;
+            if (i < T) bl[i] = x;
+            carry = __shfl(x, 63, 64);
+        }
     }
 }
 

@@ -446,7 +446,16 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h, int
     };
 
     if (token_wave) {
-        if constexpr (SGATE) gate_prefix(bl, T, lane, [&](int i) { return tok.gate(i); });
+        if constexpr (RAW) {
+            // The first rounds' copies need only the position table: requested
+            // before the gates, both are in flight in the same round trip.  The
+            // metadata stores above complete first (stores and loads share the
+            // counter a ring wait counts).
+            __builtin_amdgcn_s_waitcnt(0x0F70);
+            if (T > 0) issue(0);
+            if (RING && T > fc) issue(1);
+        }
+        if constexpr (SGATE) gate_prefix_loads(bl, T, lane, [&](int i) { return tok.gate(i); });
         if constexpr (CH) {
             // total log-gate of each key channel over the T positions, summed
             // in order
@@ -472,12 +481,9 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h, int
                 fwa[i] = i >= T ? 0.0f : SGATE ? exp_gate(bl[T - 1] - bl[i]) : 1.0f;
         }
         if constexpr (RING) {
-            // the metadata stores above have completed before any copy is
-            // counted (stores and loads share the counter)
-            __builtin_amdgcn_s_waitcnt(0x0F70);
-            if (T > 0) issue(0);
-            if (T > fc) issue(1);
             ring_wait(0);
+        } else if constexpr (RAW) {
+            if (T > 0) wait_lds_copies();  // round 0, requested above
         } else {
             if (T > 0) stage(0);
         }

@@ -52,15 +52,17 @@ struct TileParams {
 
 // Launchers: each picks the template instance for (rule, d, io dtype) and
 // enqueues one grid of B * H workgroups.  Return hipSuccess or the launch error.
-// launch_chunk serves decode, direct and verify; one-token calls with table
-// rows of at most 64 positions (decode and one-draft verify of the linear and
-// gated rules; decode, verify and direct of the per-channel rule) go to the
-// split-role kernel (launch_decode), the rest to the general chunk kernel.
+// launch_chunk serves decode and verify; one-token calls with table rows of
+// at most 64 positions (decode and one-draft verify of the linear, gated and
+// per-channel rules) go to the split-role kernel (launch_decode), the rest to
+// the general chunk kernel.
 hipError_t launch_chunk(const TileParams& p, int rule, int d, int io, int batch, hipStream_t s);
 hipError_t launch_decode(const TileParams& p, int rule, int d, int io, int batch, hipStream_t s);
 bool decode_eligible(int rule, int n, int cap);
 int decode_fold_limit(int rule, int d, int io);
 hipError_t launch_fold(const TileParams& p, int rule, int d, int io, int batch, hipStream_t s);
+// Buffer-only decode (kvbuf_direct), every rule: one wave per tile.
+hipError_t launch_direct(const TileParams& p, int rule, int d, int io, int batch, hipStream_t s);
 // Largest m that a decode launch of n tokens folds itself (eager policy).
 int chunk_fold_limit(int rule, int d, int io, int n, int cap);
 hipError_t launch_recurrent(const TileParams& p, int rule, int d, int io, int batch, hipStream_t s);

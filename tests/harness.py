@@ -197,10 +197,20 @@ class Run:
         return got
 
     # ---------------------------------------------------------------- steps
-    def decode(self, t, direct=False):
+    def decode(self, t, direct=False, direct_from=None):
+        """One decode step of every request: kvbuf_decode, or kvbuf_direct
+        with ``direct``; with ``direct_from`` = s, kvbuf_decode on a view of
+        requests 0 .. s-1 and kvbuf_direct on a view of s .. B-1."""
         w = self.w
         inp = self.inputs(t)
-        if direct:
+        if direct_from is not None:
+            s = direct_from
+            part = lambda x, a, z: None if x is None else x[a:z]
+            out = torch.empty((w.B, w.H, w.dv), dtype=torch.float32, device=self.dev)
+            for view, fn, a, z in ((self.kv.view(0, s), "decode", 0, s), (self.kv.view(s, w.B - s), "direct", s, w.B)):
+                if z > a:
+                    getattr(view, fn)(*(part(inp[x], a, z) for x in ("q", "k", "v", "g", "beta")), out=out[a:z])
+        elif direct:
             out = self.kv.direct(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"])
         else:
             out = self.kv.decode(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"])
@@ -208,7 +218,8 @@ class Run:
         if w.m > 0:
             eager = self.flush_policy == kb.FLUSH_EAGER
             for b in range(w.B):
-                if self.model.decode(b, ("d", t, b), eager=eager, stateless=direct or self.stateless[b]):
+                served_direct = direct or (direct_from is not None and b >= direct_from)
+                if self.model.decode(b, ("d", t, b), eager=eager, stateless=served_direct or self.stateless[b]):
                     folded.add(b)
         q, k, v, g, beta = (self._sampled(inp[x]) for x in ("q", "k", "v", "g", "beta"))
         self._remember(lambda b: ("d", t, b), k, v, g)
@@ -221,9 +232,10 @@ class Run:
         self._after(folded)
         return out
 
-    def flush(self):
-        self.kv.flush()
-        folded = {b for b in range(self.w.B) if self.model.flush(b)}
+    def flush(self, upto=None):
+        """kvbuf_flush over the batch, or over a view of requests 0 .. upto-1."""
+        (self.kv if upto is None else self.kv.view(0, upto)).flush()
+        folded = {b for b in range(self.w.B if upto is None else upto) if self.model.flush(b)}
         self._after(folded)
 
     def verify_commit(self, call, n, accepted):

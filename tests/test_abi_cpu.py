@@ -134,13 +134,13 @@ def test_recurrent_verification_validation(lib):
 
 
 def test_channel_rule_limits(lib):
-    """The per-channel rule is served by the one-token kernel: drafts beyond
-    one and table rows beyond 64 positions are refused on the host."""
+    """The per-channel rule's decode and verify are served by the one-token
+    kernel: drafts beyond one and table rows beyond 64 positions are refused
+    on the host (its buffer-only decode has no such limit)."""
     L = _layout(rule=kb.RULE_CHANNEL)
     assert kb.kvbuf_verify(L, POOLS, BATCH, 2, FAKE, FAKE, FAKE, FAKE, None, FAKE, 0, False) == kb.EUNSUPPORTED
     long_rows = _layout(rule=kb.RULE_CHANNEL, block_size=4, blocks_per_req=17, num_blocks=40)
     assert _decode(long_rows) == kb.EUNSUPPORTED
-    assert kb.kvbuf_direct(long_rows, POOLS, BATCH, FAKE, FAKE, FAKE, FAKE, None, FAKE, 0, False) == kb.EUNSUPPORTED
 
 
 def test_tree_entry_validation(lib):

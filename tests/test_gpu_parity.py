@@ -541,19 +541,31 @@ def test_workload4_verify_commit(n):
     _say("max out err %.2e, max state err %.2e" % (run.max_out, run.max_state))
 
 
-def test_workload5_mixed_delta():
+@pytest.mark.parametrize("split", [False, True])
+def test_workload5_mixed_delta(split):
+    """The mixed delta-rule workload: 256 requests with a state, 256 served
+    from their buffer alone (retired at the end of a random lifetime and
+    replaced).  Either one kvbuf_decode over the whole batch under the eager
+    policy (the fold runs in the launch that follows a decode), or -- the
+    benchmark's launch configuration -- kvbuf_decode over the requests with a
+    state and kvbuf_direct over the others, each on a view of its range,
+    under the deferred policy with a kvbuf_flush of the stateful view when
+    their buffers fill (every 64 steps: they run in lockstep)."""
     w = synth.workload(5)
-    _say("workload 5", w)
+    _say("workload 5", w, "split", split)
     stateless = np.zeros(w.B, bool)
     stateless[w.B - w.n_short:] = True
-    run = Run(w, stateless=stateless, spare_blocks=64)
+    n_long = w.B - w.n_short
+    run = Run(w, stateless=stateless, spare_blocks=64, flush=kb.FLUSH_DEFERRED if split else kb.FLUSH_EAGER)
     short = np.arange(w.B - w.n_short, w.B)
     life = synth.short_lengths(w, 0, len(short))
     age = np.zeros(len(short), np.int64)
     draws = 1
     retired = 0
     for t in range(w.steps):
-        run.decode(t)
+        run.decode(t, direct_from=n_long if split else None)
+        if split and t % w.m == w.m - 1:
+            run.flush(upto=n_long)
         age += 1
         for i in np.nonzero(age >= life)[0]:
             run.retire_and_admit(int(short[i]))
