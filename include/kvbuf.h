@@ -58,10 +58,9 @@ typedef enum kvbuf_rule {
     KVBUF_RULE_LINEAR = 0,
     KVBUF_RULE_GATED = 1,
     KVBUF_RULE_DELTA = 2,
-    /* One log-gate per key channel.  Served by decode, direct, flush, commit,
-     * materialize, one-draft verify and the recurrent (m = 0) entry points for
-     * table rows of at most 64 positions; kvbuf_verify with n > 1 and longer
-     * rows return KVBUF_EUNSUPPORTED. */
+    /* One log-gate per key channel (log-gates are decays: a buffer's gates
+     * should not sum past about 80 in any channel, where exp(sum) leaves the
+     * fp32 range).  Served by every entry point. */
     KVBUF_RULE_CHANNEL = 3
 } kvbuf_rule;
 
@@ -213,7 +212,7 @@ kvbuf_status kvbuf_commit(const kvbuf_layout* layout, const kvbuf_pools* pools,
  * path -- the output a serial decode of its root-to-node path would give.
  * Drafts are written at buffer positions occupancy + d as with kvbuf_verify;
  * the occupancy does not change.  A chain (parent[d] = d - 1) is kvbuf_verify.
- * Requires m > 0, 1 <= n <= 8, rules LINEAR, GATED, DELTA.  A parent outside
+ * Requires m > 0 and 1 <= n <= 8.  A parent outside
  * its range sets KVBUF_DEVERR_ACCEPT and skips the tile.
  */
 kvbuf_status kvbuf_verify_tree(const kvbuf_layout* layout, const kvbuf_pools* pools,

@@ -128,10 +128,6 @@ kvbuf_status chunk_call(const kvbuf_layout* layout, const kvbuf_pools* pools,
         t.out = out;
         return from_hip(kvbuf::launch_direct(t, layout->rule, layout->d_k, layout->io_dtype, batch->size, stream));
     }
-    // the per-channel rule is served by the one-token decode kernel only
-    if (layout->rule == KVBUF_RULE_CHANNEL && layout->m > 0 &&
-        (parent || !kvbuf::decode_eligible(layout->rule, n, layout->block_size * layout->blocks_per_req)))
-        return KVBUF_EUNSUPPORTED;
     TileParams t = make_params(layout, pools, batch);
     t.mode = mode;
     t.n = n;
@@ -235,7 +231,6 @@ kvbuf_status kvbuf_commit_tree(const kvbuf_layout* layout, const kvbuf_pools* po
     if (batch->size == 0) return KVBUF_OK;
     if (!parent || !leaf) return KVBUF_EINVAL;
     if (n < 1 || n > kvbuf::kMaxDrafts) return KVBUF_EUNSUPPORTED;
-    if (layout->rule == KVBUF_RULE_CHANNEL) return KVBUF_EUNSUPPORTED;
     KVBUF_TRY(check_grid(layout, batch));
     TileParams t = make_params(layout, pools, batch);
     t.mode = kvbuf::MODE_COMMIT;

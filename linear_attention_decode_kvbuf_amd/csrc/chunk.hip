@@ -742,6 +742,7 @@ hipError_t launch_chunk_r(const TileParams& p, int rule, int d, int batch, hipSt
 // first staging pass of NT / 16 positions); otherwise a fold launch follows.
 int chunk_fold_limit(int rule, int d, int io, int n, int cap) {
     if (decode_eligible(rule, n, cap)) return decode_fold_limit(rule, d, io);
+    if (rule == KVBUF_RULE_CHANNEL) return 0;  // the per-channel kernel never folds
     switch (d) {
         case 16: return Geo<16, 16>::NT / 16;
         case 64: return Geo<64, 64>::NT / 16;
@@ -754,6 +755,7 @@ hipError_t launch_chunk(const TileParams& p, int rule, int d, int io, int batch,
     // a decode or verify launch are served here or by the one-token kernel.)
     if (!p.parent && decode_eligible(rule, p.n, p.block_size * p.blocks_per_req))
         return launch_decode(p, rule, d, io, batch, s);
+    if (rule == KVBUF_RULE_CHANNEL) return launch_channel(p, d, io, batch, s);
     return io == KVBUF_BF16 ? launch_chunk_r<bf16_bits>(p, rule, d, batch, s)
                             : launch_chunk_r<float>(p, rule, d, batch, s);
 }

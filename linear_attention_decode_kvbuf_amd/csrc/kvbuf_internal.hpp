@@ -61,6 +61,9 @@ hipError_t launch_decode(const TileParams& p, int rule, int d, int io, int batch
 bool decode_eligible(int rule, int n, int cap);
 int decode_fold_limit(int rule, int d, int io);
 hipError_t launch_fold(const TileParams& p, int rule, int d, int io, int batch, hipStream_t s);
+// Per-channel rule: decode over rows of more than 64 positions, verify of
+// 1-8 drafts (chain or tree; parent != null).
+hipError_t launch_channel(const TileParams& p, int d, int io, int batch, hipStream_t s);
 // Buffer-only decode (kvbuf_direct), every rule: one wave per tile.
 hipError_t launch_direct(const TileParams& p, int rule, int d, int io, int batch, hipStream_t s);
 // Largest m that a decode launch of n tokens folds itself (eager policy).

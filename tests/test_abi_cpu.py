@@ -133,19 +133,18 @@ def test_recurrent_verification_validation(lib):
                                      False) == kb.OK
 
 
-def test_channel_rule_limits(lib):
-    """The per-channel rule's decode and verify are served by the one-token
-    kernel: drafts beyond one and table rows beyond 64 positions are refused
-    on the host (its buffer-only decode has no such limit)."""
+def test_channel_rule_validation(lib):
+    """The per-channel rule takes the same host checks as the others (it is
+    served at every draft count and row length): its gates are required."""
     L = _layout(rule=kb.RULE_CHANNEL)
-    assert kb.kvbuf_verify(L, POOLS, BATCH, 2, FAKE, FAKE, FAKE, FAKE, None, FAKE, 0, False) == kb.EUNSUPPORTED
-    long_rows = _layout(rule=kb.RULE_CHANNEL, block_size=4, blocks_per_req=17, num_blocks=40)
-    assert _decode(long_rows) == kb.EUNSUPPORTED
+    assert kb.kvbuf_verify(L, POOLS, BATCH, 9, FAKE, FAKE, FAKE, FAKE, None, FAKE, 0, False) == kb.EUNSUPPORTED
+    assert kb.kvbuf_verify(L, POOLS, BATCH, 2, FAKE, FAKE, FAKE, None, None, FAKE, 0, False) == kb.EINVAL
+    assert _decode(_layout(rule=kb.RULE_CHANNEL, block_size=4, blocks_per_req=17, num_blocks=40), g=None) == kb.EINVAL
 
 
 def test_tree_entry_validation(lib):
-    """Tree drafts need a buffer (m > 0), 1 <= n <= 8, parent (and leaf)
-    arrays, and one of the rules with a scalar or no gate."""
+    """Tree drafts need a buffer (m > 0), 1 <= n <= 8 and parent (and leaf)
+    arrays."""
     L = _layout()
     vt = lambda L, n, parent=FAKE: kb.kvbuf_verify_tree(L, POOLS, BATCH, n, parent, FAKE, FAKE, FAKE, FAKE, None,
                                                         FAKE, 0, False)
@@ -154,12 +153,10 @@ def test_tree_entry_validation(lib):
     assert vt(L, 0) == kb.EUNSUPPORTED
     assert vt(L, 9) == kb.EUNSUPPORTED
     assert vt(_layout(m=0), 2) == kb.EUNSUPPORTED
-    assert vt(_layout(rule=kb.RULE_CHANNEL), 1) == kb.EUNSUPPORTED
     assert ct(L, 2, parent=None) == kb.EINVAL
     assert ct(L, 2, leaf=None) == kb.EINVAL
     assert ct(L, 0) == kb.EUNSUPPORTED
     assert ct(L, 9) == kb.EUNSUPPORTED
     assert ct(_layout(m=0), 2) == kb.EUNSUPPORTED
-    assert ct(_layout(rule=kb.RULE_CHANNEL), 2) == kb.EUNSUPPORTED
     empty = kb.Batch(0, None, None, None, None)
     assert kb.kvbuf_commit_tree(L, POOLS, empty, 2, FAKE, FAKE, 0, False) == kb.OK

@@ -39,7 +39,7 @@ def _say(*a):
 
 @pytest.mark.parametrize("bs,bpr", [(2, 33), (8, 9)])
 @pytest.mark.parametrize("rule,d,io", [(1, 16, "f32"), (2, 16, "f32"), (0, 128, "bf16"), (1, 128, "bf16"),
-                                       (2, 128, "bf16")])
+                                       (2, 128, "bf16"), (3, 16, "f32"), (3, 128, "bf16")])
 def test_table_row_tail(bs, bpr, rule, d, io):
     """m = 64 in rows of 66 or 72 positions, deferred policy: decode to
     four positions short of the capacity, verify 4 drafts there (positions
@@ -92,7 +92,8 @@ def _promote(run):
 
 @pytest.mark.parametrize("L,rule,d,io", [(128, 1, 128, "bf16"), (256, 1, 128, "bf16"), (256, 0, 128, "bf16"),
                                          (128, 0, 16, "f32"), (256, 1, 16, "f32"), (512, 1, 16, "f32"),
-                                         (512, 0, 128, "bf16"), (512, 1, 128, "bf16")])
+                                         (512, 0, 128, "bf16"), (512, 1, 128, "bf16"), (128, 3, 128, "bf16"),
+                                         (256, 3, 16, "f32"), (128, 2, 128, "bf16")])
 def test_direct_long_buffers_and_promotion(L, rule, d, io):
     w = synth.workload(1, B=3, H=2, dk=d, dv=d, m=L, block_size=16, blocks_per_req=L // 16, steps=L,
                        rule=rule, io=io, state_std=0.02)

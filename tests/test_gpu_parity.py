@@ -58,14 +58,16 @@ def test_small_rules(rule, d, io, m, bs, bpr):
     run.check_bookkeeping()
 
 
+@pytest.mark.parametrize("rule", [1, 3])
 @pytest.mark.parametrize("m,bs,bpr,flush", [(8, 1, 64, kb.FLUSH_EAGER), (6, 2, 33, kb.FLUSH_DEFERRED),
-                                             (64, 8, 8, kb.FLUSH_EAGER)])
-def test_long_table_rows(m, bs, bpr, flush):
+                                             (6, 2, 33, kb.FLUSH_EAGER), (64, 8, 8, kb.FLUSH_EAGER)])
+def test_long_table_rows(rule, m, bs, bpr, flush):
     """Table rows up to the 64-entry limit: the fold's rotation moves m / bs
     entries of a long row (five requests, so the bookkeeping spans more than
-    one workgroup)."""
+    one workgroup); rows of 66 positions run the chunk kernel (gated rule) or
+    the per-channel kernel, eager folds in the launch that follows."""
     w = synth.workload(1, B=5, H=2, dk=16, dv=16, m=m, block_size=bs, blocks_per_req=bpr,
-                       steps=2 * m + 3, rule=1, io="f32", state_std=0.02)
+                       steps=2 * m + 3, rule=rule, io="f32", state_std=0.02)
     _say("long rows", w, "flush", flush)
     run = Run(w, flush=flush)
     for t in range(w.steps):
@@ -153,7 +155,7 @@ def test_recurrent_m0(rule):
         assert np.max(np.abs(gpu - ref)) / np.max(np.abs(ref)) <= 1e-5
 
 
-@pytest.mark.parametrize("rule,n", [(r, n) for r in (0, 1, 2) for n in (1, 3, 8)] + [(3, 1)])
+@pytest.mark.parametrize("rule,n", [(r, n) for r in (0, 1, 2, 3) for n in (1, 3, 8)])
 def test_verify_commit_small(rule, n):
     w = synth.workload(1, B=4, H=2, dk=64, dv=64, m=4, block_size=4, blocks_per_req=4, steps=6,
                        rule=rule, io="bf16", state_std=0.02)
@@ -170,7 +172,7 @@ def test_verify_commit_small(rule, n):
 
 
 @pytest.mark.parametrize("rule,d,io", [(0, 64, "bf16"), (1, 128, "bf16"), (2, 64, "bf16"), (1, 16, "f32"),
-                                       (2, 128, "f32")])
+                                       (2, 128, "f32"), (3, 128, "bf16"), (3, 16, "f32")])
 @pytest.mark.parametrize("n", [1, 5, 8])
 def test_tree_verify_commit(rule, d, io, n):
     """Random draft trees: every draft's output is the recurrence over its
@@ -236,12 +238,13 @@ def test_tree_deferred_with_flush_and_stars(rule):
         run.check_bookkeeping()
 
 
+@pytest.mark.parametrize("rule", [1, 3])
 @pytest.mark.parametrize("flush", [kb.FLUSH_EAGER, kb.FLUSH_DEFERRED])
-def test_tree_chain_matches_verify(flush):
+def test_tree_chain_matches_verify(rule, flush):
     """A chain-shaped tree gives kvbuf_verify's outputs, and committing its
     first a drafts leaves the same pools as kvbuf_commit(a)."""
     w = synth.workload(1, B=4, H=2, dk=128, dv=128, m=8, block_size=4, blocks_per_req=4, steps=4,
-                       rule=1, io="bf16", state_std=0.02)
+                       rule=rule, io="bf16", state_std=0.02)
     runs = [Run(w, flush=flush), Run(w, flush=flush)]
     n = 6
     chain = np.tile(np.arange(-1, n - 1, dtype=np.int32), (w.B, 1))
@@ -286,7 +289,7 @@ def test_tree_invalid_parent_or_leaf_skips_the_tile():
     assert torch.equal(occ[1:], occ0[1:]) and torch.all(occ[0] == occ0[0] + 3)
 
 
-@pytest.mark.parametrize("rule", [0, 1])
+@pytest.mark.parametrize("rule", [0, 1, 3])
 @pytest.mark.parametrize("n", [3, 5, 6, 7])
 @pytest.mark.parametrize("tree", [False, True])
 def test_verify_partial_query_blocks(rule, n, tree):
