@@ -390,6 +390,7 @@ def context_leg(kb, synth, torch, dev, args):
             times = []
             for _ in range(reps):
                 kv.occupancy.zero_()
+                kv.admit()
                 torch.cuda.synchronize()
                 stream = torch.cuda.current_stream()
                 e0 = torch.cuda.Event(enable_timing=True)
@@ -410,6 +411,7 @@ def context_leg(kb, synth, torch, dev, args):
                 pt = []
                 for _ in range(2):
                     kv.occupancy.fill_(L)
+                    kv.admit()
                     e0 = torch.cuda.Event(enable_timing=True)
                     e1 = torch.cuda.Event(enable_timing=True)
                     torch.cuda.synchronize()
@@ -574,6 +576,7 @@ def long_fold_leg(kb, synth, torch, dev, args):
 
             def fill():
                 kv.occupancy.fill_(m)
+                kv.admit()
 
             launches = []
             for _ in range(4):
@@ -650,6 +653,7 @@ def delta_leg(kb, synth, torch, dev, args):
         # every request starts the cycle empty: the stateful ones folded at
         # its last step, the buffer-only ones are restarted (capacity 128)
         kv.occupancy.zero_()
+        kv.admit()
         per = [a + b / reps for a, b in zip(per, per_launch_ms(torch, fns, 1))]
     torch.cuda.synchronize()
     assert int(kv.error.item()) == 0

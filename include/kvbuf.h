@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define KVBUF_ABI_VERSION 3
+#define KVBUF_ABI_VERSION 4
 
 typedef enum kvbuf_status {
     KVBUF_OK = 0,
@@ -82,6 +82,8 @@ typedef enum kvbuf_flush_policy {
 #define KVBUF_DEVERR_SLOT 2u     /* a state slot >= num_state_slots, or none where one is required */
 #define KVBUF_DEVERR_OVERFLOW 4u /* occupancy < 0, or appending would exceed the buffer capacity */
 #define KVBUF_DEVERR_ACCEPT 8u   /* accepted[b] outside [0, n] */
+#define KVBUF_DEVERR_META 16u    /* a request's head copies disagree with its row (kvbuf_check),
+                                    or kvbuf_admit was given an index outside [0, B) */
 
 /* Shapes and policy.  Host struct, read during the call only. */
 typedef struct kvbuf_layout {
@@ -117,30 +119,57 @@ typedef struct kvbuf_pools {
     float* gate;
 } kvbuf_pools;
 
-/* The batch: B requests.  All arrays are int32 in device memory, caller-owned,
- * and updated by the library in stream order.
- *   state_slot  [B]                     slot in the state pool; -1 = no state (the
- *                                       request is served from its buffer alone
- *                                       and never folds).  Never written.
- *   block_table [B][H][blocks_per_req]  pool block ids, in buffer order: buffer
- *                                       position p of head h is
- *                                       block_table[b][h][p / block_size], offset
- *                                       p % block_size.  A fold moves the
- *                                       m / block_size leading blocks to the back.
- *   occupancy   [B][H]                  tokens buffered since the last fold
- *   error       [1] or NULL             KVBUF_DEVERR_* bits are OR-ed into it
- * The table and occupancy are kept per (request, head): the H copies of a
- * request hold the same values (the caller writes all of them), and each is
- * read and advanced in place by the one workgroup that serves that head, so
- * a call needs no cross-workgroup synchronisation.  A tile whose metadata
- * fails a device check is skipped and its copy left unchanged. */
+/* The batch: B requests.  All arrays are int32 in device memory, caller-owned.
+ *   state_slot  [B]                  slot in the state pool; -1 = no state (the
+ *                                    request is served from its buffer alone and
+ *                                    never folds).  Never written.
+ *   block_table [B][blocks_per_req]  each request's pool block ids, in buffer
+ *                                    order: buffer position p is in block
+ *                                    block_table[b][p / block_size], offset
+ *                                    p % block_size.  A fold moves the
+ *                                    m / block_size leading blocks to the back.
+ *   occupancy   [B]                  tokens buffered since the last fold
+ *   error       [1] or NULL          KVBUF_DEVERR_* bits are OR-ed into it
+ *   tile_meta   [B][H][1 + blocks_per_req]  the library's working copies: for
+ *                                    every (request, head), its occupancy and
+ *                                    table row.
+ * block_table and occupancy are the caller's view: the library keeps them
+ * current in stream order (after every call they hold each request's row and
+ * occupancy), and the caller writes them only to admit a request -- then calls
+ * kvbuf_admit for it before any other call that touches it.  The kernels of a
+ * call read and advance tile_meta, whose copy of (b, h) only the workgroup
+ * serving that head touches, so a call needs no synchronisation across
+ * workgroups; head 0's workgroup writes the request's new values to
+ * block_table and occupancy.  A tile whose metadata fails a device check is
+ * skipped and its copy left unchanged (the request's heads may then disagree:
+ * kvbuf_check reports it). */
 typedef struct kvbuf_batch {
     int32_t size;
     int32_t* state_slot;
     int32_t* block_table;
     int32_t* occupancy;
     int32_t* error;
+    int32_t* tile_meta;
 } kvbuf_batch;
+
+/*
+ * kvbuf_admit -- copy requests' block_table rows and occupancies into their
+ * per-head working copies (tile_meta), for requests the caller has just given
+ * blocks (a new request, one whose blocks changed, one promoted to a state)
+ * (pith.science page, Figure 1 caption: each request owns its buffer blocks).
+ * requests: [count] int32 request indices in device memory, or NULL for all
+ * B requests (count ignored).  An index outside [0, B) sets KVBUF_DEVERR_META.
+ * Requires m > 0.
+ */
+kvbuf_status kvbuf_admit(const kvbuf_layout* layout, const kvbuf_batch* batch, const int32_t* requests,
+                         int32_t count, hipStream_t stream);
+
+/*
+ * kvbuf_check -- set KVBUF_DEVERR_META in the error word (required) if any
+ * request's per-head copies disagree with its block_table row or occupancy
+ * (after a device error skipped some of its heads).  Reads only.
+ */
+kvbuf_status kvbuf_check(const kvbuf_layout* layout, const kvbuf_batch* batch, hipStream_t stream);
 
 /*
  * kvbuf_decode -- one decode step for every request of the batch.
@@ -154,7 +183,7 @@ typedef struct kvbuf_batch {
  *         LINEAR); beta [B][H] fp32 (DELTA; else NULL).
  * Output  out [B][H][d_v] fp32, o = S_t^T (scale q) with S_t the state after
  *         this token.
- * m > 0:  appends the token at buffer position occupancy[b][h] and advances
+ * m > 0:  appends the token at buffer position occupancy[b] and advances
  *         the occupancy.  A request with a state slot computes its output from the
  *         state at its last fold plus the buffer; one without (slot -1) from
  *         the buffer alone.  With KVBUF_FLUSH_EAGER a request with a state

@@ -24,11 +24,11 @@ BF16, F32 = 0, 1
 FLUSH_EAGER, FLUSH_DEFERRED = 0, 1
 
 OK, EINVAL, EUNSUPPORTED, ECAPACITY, EHIP = 0, -1, -2, -3, -4
-DEVERR_BLOCK, DEVERR_SLOT, DEVERR_OVERFLOW, DEVERR_ACCEPT = 1, 2, 4, 8
+DEVERR_BLOCK, DEVERR_SLOT, DEVERR_OVERFLOW, DEVERR_ACCEPT, DEVERR_META = 1, 2, 4, 8, 16
 
 EXPORTED = ("kvbuf_decode", "kvbuf_flush", "kvbuf_verify", "kvbuf_commit", "kvbuf_direct",
-            "kvbuf_verify_tree", "kvbuf_commit_tree", "kvbuf_verify_recurrent", "kvbuf_commit_recurrent", "kvbuf_materialize", "kvbuf_strerror",
-            "kvbuf_abi_version")
+            "kvbuf_verify_tree", "kvbuf_commit_tree", "kvbuf_verify_recurrent", "kvbuf_commit_recurrent",
+            "kvbuf_materialize", "kvbuf_admit", "kvbuf_check", "kvbuf_strerror", "kvbuf_abi_version")
 
 
 class Layout(ctypes.Structure):
@@ -47,7 +47,7 @@ class Pools(ctypes.Structure):
 class Batch(ctypes.Structure):
     _fields_ = [("size", ctypes.c_int32), ("state_slot", ctypes.c_void_p),
                 ("block_table", ctypes.c_void_p), ("occupancy", ctypes.c_void_p),
-                ("error", ctypes.c_void_p)]
+                ("error", ctypes.c_void_p), ("tile_meta", ctypes.c_void_p)]
 
 
 class KVBufError(RuntimeError):
@@ -81,10 +81,11 @@ def load():
         lib.kvbuf_commit_tree.argtypes = [L, PO, B, i32, P, P, P]
         lib.kvbuf_verify_recurrent.argtypes = [L, PO, B, i32, P, P, P, P, P, P, P, P]
         lib.kvbuf_commit_recurrent.argtypes = [L, PO, B, i32, P, P, P]
+        lib.kvbuf_admit.argtypes = [L, B, P, i32, P]
+        lib.kvbuf_check.argtypes = [L, B, P]
         for name in ("kvbuf_decode", "kvbuf_direct", "kvbuf_verify", "kvbuf_flush",
                      "kvbuf_commit", "kvbuf_materialize", "kvbuf_verify_tree", "kvbuf_commit_tree",
-                     "kvbuf_verify_recurrent",
-                     "kvbuf_commit_recurrent"):
+                     "kvbuf_verify_recurrent", "kvbuf_commit_recurrent", "kvbuf_admit", "kvbuf_check"):
             getattr(lib, name).restype = ctypes.c_int
         lib.kvbuf_strerror.argtypes = [ctypes.c_int]
         lib.kvbuf_strerror.restype = ctypes.c_char_p
@@ -187,6 +188,16 @@ def kvbuf_commit_recurrent(layout, pools, batch, n, accepted, temp, stream=None,
     return _check(st, "kvbuf_commit_recurrent", raise_on_error)
 
 
+def kvbuf_admit(layout, batch, requests, count, stream=None, raise_on_error=True):
+    st = load().kvbuf_admit(_ref(layout), _ref(batch), _ptr(requests), int(count), _stream(stream))
+    return _check(st, "kvbuf_admit", raise_on_error)
+
+
+def kvbuf_check(layout, batch, stream=None, raise_on_error=True):
+    st = load().kvbuf_check(_ref(layout), _ref(batch), _stream(stream))
+    return _check(st, "kvbuf_check", raise_on_error)
+
+
 def kvbuf_abi_version() -> int:
     return int(load().kvbuf_abi_version())
 
@@ -201,8 +212,10 @@ class KVBuffer:
     gate       [num_blocks, H, block_size] fp32 (None for the linear rule;
                [num_blocks, H, block_size, d_k] for the per-channel rule)
     state_slot [B] int32
-    block_table [B, H, blocks_per_req] int32, occupancy [B, H] int32 (one copy
-               per head, all equal; ``set_block_table`` writes every head)
+    block_table [B, blocks_per_req] int32, occupancy [B] int32: each request's
+               row and occupancy, kept current by the library; after writing a
+               request's row / occupancy, call ``admit`` for it
+    tile_meta  [B, H, 1 + blocks_per_req] int32: the library's per-head copies
     error      [1] int32
     """
 
@@ -234,17 +247,18 @@ class KVBuffer:
             self.key = self.value = self.gate = None
         i32 = torch.int32
         self.state_slot = torch.arange(batch, dtype=i32, device=dev) % max(num_state_slots, 1)
-        self.block_table = torch.empty((batch, heads, blocks_per_req), dtype=i32, device=dev)
-        self.set_block_table(torch.arange(batch * blocks_per_req, dtype=i32).reshape(
-            batch, blocks_per_req) % max(num_blocks, 1))
-        self.occupancy = torch.zeros((batch, heads), dtype=i32, device=dev)
+        self.block_table = torch.empty((batch, blocks_per_req), dtype=i32, device=dev)
+        self.occupancy = torch.zeros(batch, dtype=i32, device=dev)
+        self.tile_meta = torch.zeros((batch, heads, 1 + blocks_per_req), dtype=i32, device=dev)
         self.error = torch.zeros(1, dtype=i32, device=dev)
         self._refresh()
+        self.set_block_table(torch.arange(batch * blocks_per_req, dtype=i32).reshape(
+            batch, blocks_per_req) % max(num_blocks, 1))
 
     def _refresh(self):
         self.pools = Pools(_ptr(self.state), _ptr(self.key), _ptr(self.value), _ptr(self.gate))
         self.batch = Batch(self.B, _ptr(self.state_slot), _ptr(self.block_table), _ptr(self.occupancy),
-                           _ptr(self.error))
+                           _ptr(self.error), _ptr(self.tile_meta))
 
     def view(self, start, count):
         """Requests start .. start+count-1 as a batch of their own: the same
@@ -262,13 +276,34 @@ class KVBuffer:
         v.state_slot = self.state_slot[start:start + count]
         v.block_table = self.block_table[start:start + count]
         v.occupancy = self.occupancy[start:start + count]
+        v.tile_meta = self.tile_meta[start:start + count]
         v._refresh()
         return v
 
-    def set_block_table(self, table):
-        """Every head's copy of the block table <- table [B, blocks_per_req]."""
+    def set_block_table(self, table, occupancy=None):
+        """Every request's table row <- table [B, blocks_per_req] (and its
+        occupancy, when given), then kvbuf_admit for all of them."""
         t = self.torch.as_tensor(table, dtype=self.torch.int32).to(self.block_table.device)
-        self.block_table.copy_(t.reshape(self.B, 1, -1).expand(self.B, self.H, t.shape[-1]))
+        self.block_table.copy_(t.reshape(self.B, -1))
+        if occupancy is not None:
+            self.occupancy.copy_(self.torch.as_tensor(occupancy, dtype=self.torch.int32).to(self.occupancy.device))
+        if self.m > 0:
+            self.admit()
+
+    def admit(self, requests=None, stream=None):
+        """kvbuf_admit: the per-head copies of the listed requests (a [k]
+        int32 device tensor of indices; None = every request) <- their
+        block_table rows and occupancies."""
+        if requests is None:
+            kvbuf_admit(self.layout, self.batch, None, 0, stream)
+        else:
+            self._need(requests, "requests", (requests.numel(),), self.torch.int32)
+            kvbuf_admit(self.layout, self.batch, requests, requests.numel(), stream)
+
+    def check_meta(self, stream=None):
+        """kvbuf_check: sets DEVERR_META in ``error`` if any request's per-head
+        copies disagree with its row or occupancy."""
+        kvbuf_check(self.layout, self.batch, stream)
 
     @property
     def capacity(self):

@@ -24,7 +24,7 @@ LIB = os.path.join(PKG, "libkvbuf.so")
 PROBE_LIB = os.path.join(PKG, "libkvbuf_probe.so")
 OBJ_DIR = os.path.join(PKG, "_build")
 
-SOURCES = ["abi.cpp", "chunk.hip", "fold.hip", "recurrent.hip", "decode.hip", "direct.hip", "channel.hip"]
+SOURCES = ["abi.cpp", "chunk.hip", "fold.hip", "recurrent.hip", "decode.hip", "direct.hip", "channel.hip", "meta.hip"]
 PROBE_SOURCES = ["probe.hip"]
 ARCH = "gfx950"
 

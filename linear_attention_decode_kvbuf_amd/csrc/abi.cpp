@@ -40,7 +40,7 @@ kvbuf_status check_batch(const kvbuf_layout* L, const kvbuf_batch* B) {
     if (B->size == 0) return KVBUF_OK;
     if (!B->state_slot) return KVBUF_EINVAL;
     if (L->m == 0) return KVBUF_OK;  // recurrent mode: no buffer metadata
-    if (!B->block_table || !B->occupancy) return KVBUF_EINVAL;
+    if (!B->block_table || !B->occupancy || !B->tile_meta) return KVBUF_EINVAL;
     return KVBUF_OK;
 }
 
@@ -86,6 +86,7 @@ TileParams make_params(const kvbuf_layout* L, const kvbuf_pools* P, const kvbuf_
     t.slot = B->state_slot;
     t.table = B->block_table;
     t.occ = B->occupancy;
+    t.tmeta = B->tile_meta;
     t.err = B->error;
     return t;
 }
@@ -300,6 +301,31 @@ kvbuf_status kvbuf_materialize(const kvbuf_layout* layout, const kvbuf_pools* po
     t.states_out = states;
     return from_hip(kvbuf::launch_fold(t, layout->rule, layout->d_k, layout->io_dtype,
                                        batch->size, stream));
+}
+
+kvbuf_status kvbuf_admit(const kvbuf_layout* layout, const kvbuf_batch* batch, const int32_t* requests,
+                         int32_t count, hipStream_t stream) {
+    KVBUF_TRY(check_layout(layout, true));
+    KVBUF_TRY(check_batch(layout, batch));
+    if (batch->size == 0) return KVBUF_OK;
+    if (requests && count < 0) return KVBUF_EINVAL;
+    const int n = requests ? count : batch->size;
+    if (n == 0) return KVBUF_OK;
+    KVBUF_TRY(check_grid(layout, batch));
+    kvbuf_pools none{};
+    TileParams t = make_params(layout, &none, batch);
+    return from_hip(kvbuf::launch_admit(t, requests, n, stream));
+}
+
+kvbuf_status kvbuf_check(const kvbuf_layout* layout, const kvbuf_batch* batch, hipStream_t stream) {
+    KVBUF_TRY(check_layout(layout, true));
+    KVBUF_TRY(check_batch(layout, batch));
+    if (batch->size == 0) return KVBUF_OK;
+    if (!batch->error) return KVBUF_EINVAL;
+    KVBUF_TRY(check_grid(layout, batch));
+    kvbuf_pools none{};
+    TileParams t = make_params(layout, &none, batch);
+    return from_hip(kvbuf::launch_check(t, stream));
 }
 
 const char* kvbuf_strerror(kvbuf_status status) {

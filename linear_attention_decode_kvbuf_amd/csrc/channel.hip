@@ -118,7 +118,7 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void channel_kernel(TileParams P
     const int slot = P.slot[b];
     int p0 = 0, blk = 0, par = -1;
     if (tid < 64) {
-        p0 = P.occ[meta_index(P, b, h)];
+        p0 = load_occupancy(P, b, h);
         blk = load_table_row(P, b, h, tid);
         if (TREE && tid < n) par = P.parent[static_cast<size_t>(b) * n + tid];
     }

@@ -229,7 +229,7 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
     int p0 = 0, blk = 0;
     int par = -1;  // tree drafts: parent of draft tid
     if (tid < 64) {  // the occupancy, the table row (and the parents) in one round trip
-        p0 = P.occ[meta_index(P, b, h)];
+        p0 = load_occupancy(P, b, h);
         blk = load_table_row(P, b, h, tid);
         if (TREE && tid < n) par = P.parent[static_cast<size_t>(b) * n + tid];
     }

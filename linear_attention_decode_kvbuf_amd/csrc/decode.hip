@@ -119,9 +119,9 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void decode_kernel(TilePar
         const int bs = P.block_size;
         const int bpr = P.blocks_per_req;  // bs * bpr <= 64 (launcher)
         const int cap = bs * bpr;
-        const int p = P.occ[meta_index(P, b, h)];
+        const int p = load_occupancy(P, b, h);
         int blk = 0;
-        if (lane < bpr) blk = P.table[meta_index(P, b, h) * bpr + lane];
+        blk = load_table_row(P, b, h, lane);
         const int T = p + 1;  // positions after the append
         unsigned bad = 0;
         if (p < 0 || p >= cap) bad |= KVBUF_DEVERR_OVERFLOW;

@@ -396,14 +396,25 @@ __device__ __forceinline__ void report(const TileParams& P, unsigned bits) {
     if (bits && P.err && threadIdx.x == 0) atomicOr(reinterpret_cast<unsigned*>(P.err), bits);
 }
 
-// Buffer metadata is kept per tile: occupancy [B][H] and block table
-// [B][H][blocks_per_req], every head of a request holding the same values.
-// The workgroup serving tile (b, h) is the only one that reads or writes its
-// copy, so it updates them in place once it is done reading them -- with no
-// atomics, fences or second launch.  Within a workgroup one wave does all the
-// reads and the update, so program order alone separates them.
-__device__ __forceinline__ size_t meta_index(const TileParams& P, int b, int h) {
-    return static_cast<size_t>(b) * P.H + h;
+// Buffer metadata: the caller sees one occupancy [B] and one table row
+// [B][blocks_per_req] per request; the kernels read and advance per-tile
+// copies, a record [B][H][1 + blocks_per_req] (occupancy, then the row) per
+// (request, head).  The workgroup serving tile (b, h) is the only one that
+// reads or writes its record, so it updates it in place once it is done
+// reading it -- with no atomics, fences or second launch; within a workgroup
+// one wave does the reads and the update, so program order alone separates
+// them.  The workgroup of head 0 also writes the request's new values to the
+// per-request arrays, which no kernel reads during a call (kvbuf_admit copies
+// them into the records; kvbuf_check compares them).
+__device__ __forceinline__ int32_t* tile_meta(const TileParams& P, int b, int h) {
+    return P.tmeta + (static_cast<size_t>(b) * P.H + h) * (1 + P.blocks_per_req);
+}
+__device__ __forceinline__ int load_occupancy(const TileParams& P, int b, int h) { return tile_meta(P, b, h)[0]; }
+
+// The tile's occupancy <- v (one lane), and the request's if h = 0.
+__device__ __forceinline__ void store_occupancy(const TileParams& P, int b, int h, int v) {
+    tile_meta(P, b, h)[0] = v;
+    if (h == 0) P.occ[b] = v;
 }
 
 // By the wave that read the metadata (lane = 0..63, all active; blk = table
@@ -413,14 +424,17 @@ __device__ __forceinline__ size_t meta_index(const TileParams& P, int b, int h) 
 // trip at the end of the wave's chain.
 __device__ __forceinline__ void update_meta(const TileParams& P, int b, int h, int p_new, int k, int lane,
                                             int blk) {
-    const size_t t = meta_index(P, b, h);
+    int32_t* rec = tile_meta(P, b, h);
+    const int bpr = P.blocks_per_req;
     if (k > 0) {
-        const int bpr = P.blocks_per_req;
         const int src = lane + k < bpr ? lane + k : lane + k - bpr;
         const int v = __shfl(blk, src & 63, 64);
-        if (lane < bpr) P.table[t * bpr + lane] = v;
+        if (lane < bpr) {
+            rec[1 + lane] = v;
+            if (h == 0) P.table[static_cast<size_t>(b) * bpr + lane] = v;
+        }
     }
-    if (lane == 0) P.occ[t] = p_new;
+    if (lane == 0) store_occupancy(P, b, h, p_new);
 }
 
 // One wave (lane = 0..63) reads the tile's whole table row with a single
@@ -457,7 +471,7 @@ __device__ __forceinline__ unsigned stage_row_from(const TileParams& P, int h, i
 }
 __device__ __forceinline__ int load_table_row(const TileParams& P, int b, int h, int lane) {
     const int bpr = P.blocks_per_req;  // <= 64 (host-checked)
-    return lane < bpr ? P.table[meta_index(P, b, h) * bpr + lane] : 0;
+    return lane < bpr ? tile_meta(P, b, h)[1 + lane] : 0;
 }
 
 }  // namespace kvbuf

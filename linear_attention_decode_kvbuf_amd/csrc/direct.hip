@@ -141,9 +141,8 @@ __global__ __launch_bounds__(64 * kDirectWaves) void direct_kernel(TileParams P)
     const int c0 = lane * C;
 
     // ---- metadata and this call's token: one round trip ----------------------
-    const size_t mi = meta_index(P, b, h);
-    const int p_raw = P.occ[mi];
-    const int blk = lane < bpr ? P.table[mi * bpr + lane] : 0;
+    const int p_raw = load_occupancy(P, b, h);
+    const int blk = load_table_row(P, b, h, lane);
     const size_t in_row = static_cast<size_t>(b) * P.H + h;
     RawChunk<IO, C> qv, kt, vt;
     qv.zero();
@@ -329,7 +328,7 @@ __global__ __launch_bounds__(64 * kDirectWaves) void direct_kernel(TileParams P)
     if constexpr (SGATE) {
         if (lane == 0) P.gate[arow] = gnew;
     }
-    if (lane == 0) P.occ[mi] = p + 1;
+    if (lane == 0) store_occupancy(P, b, h, p + 1);
 }
 
 // The linear, gated and delta rules: 16 lanes per buffered row.  Lane l
@@ -363,9 +362,8 @@ __global__ __launch_bounds__(64 * kDirectWaves) void direct_rows_kernel(TilePara
     const int cl = lane & 15;  // 1/16 of a row
 
     // ---- metadata and this call's token (every slot holds the same chunks) ------
-    const size_t mi = meta_index(P, b, h);
-    const int p_raw = P.occ[mi];
-    const int blk = lane < bpr ? P.table[mi * bpr + lane] : 0;
+    const int p_raw = load_occupancy(P, b, h);
+    const int blk = load_table_row(P, b, h, lane);
     const size_t in_row = static_cast<size_t>(b) * P.H + h;
     RawChunk<IO, E> qc, kt, vt;
     qc.load(static_cast<const IO*>(P.q) + in_row * D + cl * E);
@@ -481,7 +479,7 @@ __global__ __launch_bounds__(64 * kDirectWaves) void direct_rows_kernel(TilePara
     if constexpr (SGATE) {
         if (lane == 0) P.gate[arow] = gnew;
     }
-    if (lane == 0) P.occ[mi] = p + 1;
+    if (lane == 0) store_occupancy(P, b, h, p + 1);
 }
 
 template <int RULE, int D, typename IO>

@@ -236,7 +236,7 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h, int
     if (token_wave) {
         // occupancy, table row, accepted count / parents and leaf: all
         // requested before any is used (one round trip)
-        const int p = P.occ[meta_index(P, b, h)];
+        const int p = load_occupancy(P, b, h);
         const int blk = load_table_row(P, b, h, lane);
         unsigned bad = 0;
         uint32_t path = 0;  // tree commit: bit d set = draft d is kept
@@ -771,7 +771,7 @@ __attribute__((amdgpu_waves_per_eu(MULTI ? 4 : 1))) void fold_sparse_kernel(Tile
             const int h = t / P.batch;
             const int b = t - h * P.batch;
             const int slot = P.slot[b];
-            const int p = P.occ[meta_index(P, b, h)];
+            const int p = load_occupancy(P, b, h);
             const int cap = P.block_size * P.blocks_per_req;
             need = p < 0 || p > cap || slot >= P.num_slots || (slot >= 0 && p >= P.m);
         }

@@ -34,8 +34,9 @@ struct TileParams {
     void* value;
     float* gate;
     const int32_t* slot;  // [B]
-    int32_t* table;       // [B][H][blocks_per_req]
-    int32_t* occ;         // [B][H]
+    int32_t* table;       // [B][blocks_per_req]: the requests' rows, written by head 0's workgroup
+    int32_t* occ;         // [B]: the requests' occupancies, likewise
+    int32_t* tmeta;       // [B][H][1 + blocks_per_req]: per-tile occupancy and row, read and advanced
     int32_t* err;
     const void* q;
     const void* k;
@@ -64,6 +65,10 @@ hipError_t launch_fold(const TileParams& p, int rule, int d, int io, int batch, 
 // Per-channel rule: decode over rows of more than 64 positions, verify of
 // 1-8 drafts (chain or tree; parent != null).
 hipError_t launch_channel(const TileParams& p, int d, int io, int batch, hipStream_t s);
+// Per-request metadata into the per-tile copies (requests [count], or all
+// B when null), and the comparison of the two.
+hipError_t launch_admit(const TileParams& p, const int32_t* requests, int count, hipStream_t s);
+hipError_t launch_check(const TileParams& p, hipStream_t s);
 // Buffer-only decode (kvbuf_direct), every rule: one wave per tile.
 hipError_t launch_direct(const TileParams& p, int rule, int d, int io, int batch, hipStream_t s);
 // Largest m that a decode launch of n tokens folds itself (eager policy).

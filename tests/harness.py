@@ -343,8 +343,9 @@ class Run:
         new = [self.free.pop(0) for _ in range(bpr)]
         self.free.extend(old)
         self.model.replace_request(b, new, 0, has_state=False)
-        self.kv.block_table[b].copy_(torch.tensor(new, dtype=torch.int32))  # every head
+        self.kv.block_table[b].copy_(torch.tensor(new, dtype=torch.int32))
         self.kv.occupancy[b] = 0
+        self.kv.admit(torch.tensor([b], dtype=torch.int32, device=self.dev))
         if b in self.rows_of:
             self.S[self.rows_of[b]] = 0.0
 
@@ -422,11 +423,12 @@ class Run:
             return
         torch.cuda.synchronize()
         assert int(self.kv.error.item()) == 0, "device error flags %d" % int(self.kv.error.item())
-        # every head's copy of the table and occupancy equals the model's
-        bt = self.kv.block_table.cpu().numpy()
-        occ = self.kv.occupancy.cpu().numpy()
-        np.testing.assert_array_equal(bt, np.broadcast_to(self.model.tables()[:, None, :], bt.shape))
-        np.testing.assert_array_equal(occ, np.broadcast_to(self.model.occupancies()[:, None], occ.shape))
+        # each request's table row and occupancy, and every head's copy of them
+        np.testing.assert_array_equal(self.kv.block_table.cpu().numpy(), self.model.tables())
+        np.testing.assert_array_equal(self.kv.occupancy.cpu().numpy(), self.model.occupancies())
+        tm = self.kv.tile_meta.cpu().numpy()
+        np.testing.assert_array_equal(tm[:, :, 0], np.broadcast_to(self.model.occupancies()[:, None], tm.shape[:2]))
+        np.testing.assert_array_equal(tm[:, :, 1:], np.broadcast_to(self.model.tables()[:, None, :], tm[:, :, 1:].shape))
 
     def check_pool(self):
         """Buffered keys, gates and (linear / gated rules) values of the sampled

@@ -37,14 +37,14 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_struct_sizes_match_header(lib):
-    # kvbuf_layout: 11 int32 + 1 float; pools: 4 pointers; batch: int32 (+pad) + 5 pointers
+    # kvbuf_layout: 11 int32 + 1 float; pools: 4 pointers; batch: int32 (+pad) + 6 pointers
     assert ctypes.sizeof(kb.Layout) == 48
     assert ctypes.sizeof(kb.Pools) == 32
-    assert ctypes.sizeof(kb.Batch) == 40
+    assert ctypes.sizeof(kb.Batch) == 48
 
 
 def test_abi_version_and_strerror(lib):
-    assert kb.kvbuf_abi_version() == 3
+    assert kb.kvbuf_abi_version() == 4
     for st in (kb.OK, kb.EINVAL, kb.EUNSUPPORTED, kb.ECAPACITY, kb.EHIP):
         assert len(kb.strerror(st)) > 5
     assert "unknown" in kb.strerror(-99)
@@ -59,7 +59,7 @@ def _layout(**kw):
 
 FAKE = 0x1000  # never dereferenced: every case below fails validation first
 POOLS = kb.Pools(FAKE, FAKE, FAKE, FAKE)
-BATCH = kb.Batch(2, FAKE, FAKE, FAKE, None)
+BATCH = kb.Batch(2, FAKE, FAKE, FAKE, None, FAKE)
 
 
 def _decode(layout, pools=POOLS, batch=BATCH, q=FAKE, g=FAKE, beta=None):
@@ -90,9 +90,10 @@ def test_null_arguments(lib):
     assert kb.kvbuf_decode(None, POOLS, BATCH, FAKE, FAKE, FAKE, FAKE, None, FAKE, 0, False) == kb.EINVAL
     assert _decode(L, pools=kb.Pools(FAKE, None, FAKE, FAKE)) == kb.EINVAL
     assert _decode(L, pools=kb.Pools(FAKE, FAKE, FAKE, None)) == kb.EINVAL  # gated rule needs gates
-    assert _decode(L, batch=kb.Batch(2, FAKE, None, FAKE, None)) == kb.EINVAL
-    assert _decode(L, batch=kb.Batch(2, FAKE, FAKE, None, None)) == kb.EINVAL  # occupancy
-    assert _decode(L, batch=kb.Batch(-1, FAKE, FAKE, FAKE, None)) == kb.EINVAL
+    assert _decode(L, batch=kb.Batch(2, FAKE, None, FAKE, None, FAKE)) == kb.EINVAL
+    assert _decode(L, batch=kb.Batch(2, FAKE, FAKE, FAKE, None, None)) == kb.EINVAL  # per-tile copies
+    assert _decode(L, batch=kb.Batch(2, FAKE, FAKE, None, None, FAKE)) == kb.EINVAL  # occupancy
+    assert _decode(L, batch=kb.Batch(-1, FAKE, FAKE, FAKE, None, FAKE)) == kb.EINVAL
     assert _decode(L, q=None) == kb.EINVAL
     assert _decode(L, g=None) == kb.EINVAL
     assert _decode(_layout(rule=kb.RULE_DELTA), beta=None) == kb.EINVAL
@@ -160,3 +161,17 @@ def test_tree_entry_validation(lib):
     assert ct(_layout(m=0), 2) == kb.EUNSUPPORTED
     empty = kb.Batch(0, None, None, None, None)
     assert kb.kvbuf_commit_tree(L, POOLS, empty, 2, FAKE, FAKE, 0, False) == kb.OK
+
+
+def test_metadata_entry_validation(lib):
+    """kvbuf_admit needs a buffer (m > 0) and a non-negative count with a
+    request list; kvbuf_check needs the error word it reports through."""
+    L = _layout()
+    assert kb.kvbuf_admit(_layout(m=0), BATCH, None, 0, 0, False) == kb.EUNSUPPORTED
+    assert kb.kvbuf_admit(L, BATCH, FAKE, -1, 0, False) == kb.EINVAL
+    assert kb.kvbuf_admit(L, kb.Batch(2, FAKE, FAKE, FAKE, None, None), None, 0, 0, False) == kb.EINVAL
+    assert kb.kvbuf_admit(L, BATCH, FAKE, 0, 0, False) == kb.OK  # nothing listed: nothing enqueued
+    assert kb.kvbuf_check(L, BATCH, 0, False) == kb.EINVAL  # no error word
+    empty = kb.Batch(0, None, None, None, None, None)
+    assert kb.kvbuf_admit(L, empty, None, 0, 0, False) == kb.OK
+    assert kb.kvbuf_check(L, empty, 0, False) == kb.OK

@@ -82,7 +82,7 @@ def test_buffer_cycle_replayed_from_a_graph(rule):
         assert int(eager.error.item()) == 0 and int(graphed.error.item()) == 0
         assert torch.equal(outs_g, outs_e), "replay %d: decode outputs" % call
         assert torch.equal(v_g, v_e), "replay %d: verify outputs" % call
-        for name in ("state", "key", "value", "gate", "block_table", "occupancy"):
+        for name in ("state", "key", "value", "gate", "block_table", "occupancy", "tile_meta"):
             a, b = getattr(graphed, name), getattr(eager, name)
             if a is not None:
                 assert torch.equal(a, b), "replay %d: %s" % (call, name)

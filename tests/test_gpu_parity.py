@@ -259,7 +259,7 @@ def test_tree_chain_matches_verify(rule, flush):
         # the tree path sums the drafts' gates one by one, the chain path by a
         # parallel scan: equal up to rounding
         torch.testing.assert_close(o_tree, o_chain, rtol=0, atol=1e-5 * float(o_chain.abs().max()))
-        for name in ("state", "key", "value", "gate", "block_table", "occupancy"):
+        for name in ("state", "key", "value", "gate", "block_table", "occupancy", "tile_meta"):
             assert torch.equal(getattr(runs[0].kv, name), getattr(runs[1].kv, name)), name
         if flush == kb.FLUSH_DEFERRED:
             runs[0].flush()
@@ -400,34 +400,54 @@ def _errors(kv):
 
 
 def test_device_errors_skip_the_request():
+    """Metadata the kernels find out of range skips the request (all its
+    heads, when the caller's row is bad), leaves its row and occupancy as
+    they were and sets the error bit; a bad per-head copy skips that head
+    only, which kvbuf_check then reports."""
     w = synth.workload(1, B=3, H=2, dk=16, dv=16, m=4, block_size=4, blocks_per_req=2, steps=1,
                        rule=1, io="f32", state_std=0.02)
     run = Run(w)
     kv = run.kv
     before_state = kv.state.clone()
-    # request 1: a block id outside the pool (every head's copy)
-    kv.block_table[1, :, 0] = 10_000
+    one = lambda b: torch.tensor([b], dtype=torch.int32, device="cuda")
+    # request 1: a block id outside the pool, admitted to every head
+    kv.block_table[1, 0] = 10_000
+    kv.admit(one(1))
     inp = run.inputs(0)
     out = kv.decode(inp["q"], inp["k"], inp["v"], inp["g"])
     assert _errors(kv) & kb.DEVERR_BLOCK
-    assert kv.occupancy.cpu().tolist() == [[1, 1], [0, 0], [1, 1]]  # request 1 was skipped
+    assert kv.occupancy.cpu().tolist() == [1, 0, 1]  # request 1 was skipped
+    assert kv.tile_meta[:, :, 0].cpu().tolist() == [[1, 1], [0, 0], [1, 1]]
     kv.error.zero_()
+    kv.check_meta()
+    assert _errors(kv) == 0  # every request's heads agree with it
     # request 0: occupancy at capacity -> overflow, nothing written
     cap = run.kv.capacity
     kv.occupancy[0] = cap
-    kv.block_table[1, :, 0] = run.model.requests[1].table[0]
+    kv.block_table[1, 0] = run.model.requests[1].table[0]
+    kv.admit(torch.tensor([0, 1], dtype=torch.int32, device="cuda"))
     kv.decode(inp["q"], inp["k"], inp["v"], inp["g"], out=out)
     assert _errors(kv) & kb.DEVERR_OVERFLOW
-    assert kv.occupancy.cpu().tolist() == [[cap, cap], [1, 1], [2, 2]]
+    assert kv.occupancy.cpu().tolist() == [cap, 1, 2]
     kv.error.zero_()
-    # a bad copy in one head skips that tile only; the other head advances
-    kv.block_table[2, 1, 0] = -3
+    # a bad copy in one head (head 1 of request 2) skips that tile only: head
+    # 0 advances (and with it the request's occupancy), head 1 does not
+    kv.tile_meta[2, 1, 1] = -3
     kv.decode(inp["q"], inp["k"], inp["v"], inp["g"], out=out)
     assert _errors(kv) & kb.DEVERR_BLOCK
-    assert kv.occupancy[2].cpu().tolist() == [3, 2]
+    assert kv.tile_meta[2, :, 0].cpu().tolist() == [3, 2]
+    assert kv.occupancy[2].item() == 3
+    kv.error.zero_()
+    kv.check_meta()
+    assert _errors(kv) == kb.DEVERR_META
+    kv.error.zero_()
+    # an admit index outside the batch is reported
+    kv.admit(one(7))
+    assert _errors(kv) == kb.DEVERR_META
     kv.error.zero_()
     # accepted count beyond n
     kv.occupancy[0] = 0
+    kv.admit(one(0))
     acc = torch.tensor([0, 5, 0], dtype=torch.int32, device="cuda")
     kv.commit(2, acc)
     assert _errors(kv) & kb.DEVERR_ACCEPT
@@ -449,10 +469,11 @@ def test_validation_errors_touch_nothing():
     assert kb.kvbuf_verify(kv.layout, kv.pools, kv.batch, 9, z, z, z, g, None, z,
                            raise_on_error=False) == kb.EUNSUPPORTED
     torch.cuda.synchronize()
-    assert kv.occupancy.cpu().tolist() == [[0, 0], [0, 0]]
+    assert kv.occupancy.cpu().tolist() == [0, 0]
     kb.kvbuf_decode(kv.layout, kv.pools, kv.batch, z, z, z, g, None, z)
     torch.cuda.synchronize()
-    assert kv.occupancy.cpu().tolist() == [[1, 1], [1, 1]]
+    assert kv.occupancy.cpu().tolist() == [1, 1]
+    assert kv.tile_meta[:, :, 0].cpu().tolist() == [[1, 1], [1, 1]]
 
 
 # ---------------------------------------------------------------------------
@@ -669,7 +690,7 @@ def test_long_fold_full_size(rule, m):
     kv.state_slot.copy_(perm)
     kv.set_block_table(torch.roll(perm, 7).reshape(B, 1))
     slot = kv.state_slot.cpu().numpy().astype(np.int64)
-    block = kv.block_table.cpu().numpy()[:, 0, 0].astype(np.int64)
+    block = kv.block_table.cpu().numpy()[:, 0].astype(np.int64)
     # host copies, tile-major: S0 [B*H, d, d], K / V [m, B*H, d], G [m, B*H (, d)]
     S0 = kv.state[torch.from_numpy(slot).to(dev)].reshape(B * H, d, d).cpu().numpy().astype(np.float64)
     tiles = lambda x: x[torch.from_numpy(block).to(dev)].float().movedim(2, 0).reshape(m, B * H, *x.shape[3:])
@@ -677,12 +698,14 @@ def test_long_fold_full_size(rule, m):
     V = tiles(kv.value).cpu().numpy()
     G = None if kv.gate is None else tiles(kv.gate).cpu().numpy()
     kv.occupancy.fill_(m)
+    kv.admit()
     _say("long fold full size rule %d m %d" % (rule, m))
     kv.flush()
     torch.cuda.synchronize()
     assert int(kv.error.item()) == 0
     assert int(kv.occupancy.abs().sum().item()) == 0
-    assert np.array_equal(kv.block_table.cpu().numpy()[:, 0, 0], block)  # one block per request rotates onto itself
+    assert int(kv.tile_meta[:, :, 0].abs().sum().item()) == 0
+    assert np.array_equal(kv.block_table.cpu().numpy()[:, 0], block)  # one block per request rotates onto itself
     # the fold of the delta rule is the scalar-gated rule's over pseudo-values
     ref_rule = kb.RULE_GATED if rule == kb.RULE_DELTA else rule
     _, S_ref = oracle.recurrent(ref_rule, S0, np.zeros((m, B * H, d)), K, V, G, nthreads=NTHREADS, inplace=True)
