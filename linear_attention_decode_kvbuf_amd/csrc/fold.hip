@@ -35,12 +35,20 @@ namespace {
 // values and -- fp32 staging -- weights), the state weight e^{b_{T-1}} (per
 // key channel for the per-channel rule: DK of them).  Keys and values are
 // staged as fp32 (kb = xb = 4) or, for the matrix-core folds, raw: as stored
-// in the pool (kb, xb = element bytes), by direct-to-LDS copies.
+// in the pool (kb, xb = element bytes), by direct-to-LDS copies.  The
+// matrix-core folds reuse the staging area, once the last round is applied,
+// to turn the update into whole rows (64 rows of 128 floats at a time), so
+// it spans at least kFoldConvFloats.
+constexpr int kFoldConvFloats = 64 * 128;
 __host__ __device__ inline int fold_stage_floats(int DK, int DV, int fc, int kb, int xb, bool raw) {
     return (fc * (DK * kb + DV * xb)) / 4 + (raw ? 0 : ((fc + 3) & ~3));
 }
-__host__ __device__ inline int fold_lds_floats(int DK, int DV, int cap, int stage_floats, int nb, bool ch) {
-    return 2 * ((cap + 3) & ~3) + ((cap + 31) & ~31) + nb * stage_floats + (ch ? DK : 4);
+__host__ __device__ inline int fold_stage_area(int stage_floats, int nb, bool mf) {
+    const int a = nb * stage_floats;
+    return (mf && a < kFoldConvFloats) ? kFoldConvFloats : a;
+}
+__host__ __device__ inline int fold_lds_floats(int DK, int DV, int cap, int stage_area, bool ch) {
+    return 2 * ((cap + 3) & ~3) + ((cap + 31) & ~31) + stage_area + (ch ? DK : 4);
 }
 // raw multi-round folds of bf16 rows keep this many staging buffers: the
 // copies of round r + 2 are in flight while round r is applied
@@ -337,7 +345,7 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h, int
     constexpr int KB = RAW ? static_cast<int>(sizeof(IO)) : 4, XB = RAW ? static_cast<int>(sizeof(XIO)) : 4;
     const int srows = TR ? 32 : fc;  // rows of a staging buffer (TR: a whole product chunk)
     const int stage_floats = fold_stage_floats(DK, DV, srows, KB, XB, RAW);
-    float* e0p = stage0 + NBUF * stage_floats;
+    float* e0p = stage0 + fold_stage_area(stage_floats, NBUF, MF);
 
     TileTokens<DK, DV, IO, XIO> tok;
     tok.kpool = static_cast<const IO*>(P.key);
@@ -491,24 +499,14 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h, int
     }
     f4 s[RPT];
     const int mw = tid >> 6, ml = tid & 63;  // MF: wave and lane
-    auto mf_offset = [&](int j) {            // MF: float offset of s[j] in the tile
-        if constexpr (COLS) {                // rows 16 (j / 2) + l % 16, columns 32 mw + 16 (j % 2) + 4 (l / 16)
-            const int row = 16 * (j >> 1) + (ml & 15);
-            return row * DV + 32 * mw + 16 * (j & 1) + 4 * (ml >> 4);
-        }
-        const int row = 32 * mw + 16 * (j >> 3) + (ml & 15);
-        return row * DV + 16 * (j & 7) + 4 * (ml >> 4);
-    };
+    const float* tile = has_state ? P.state + (static_cast<size_t>(slot) * P.H + h) * DK * DV : P.state;
     if (!token_wave) {
-        const float* tile = has_state ? P.state + (static_cast<size_t>(slot) * P.H + h) * DK * DV : P.state;
         if constexpr (MF) {
+            // the matrix cores accumulate the update alone, from zero; the
+            // state is read after the last round, in whole rows
             static_assert(RPT == 16, "16 blocks of 16 x 16 per wave");
-            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-                const_cast<float*>(tile), 0, has_state ? DK * DV * static_cast<int>(sizeof(float)) : 0, kBufferFlags);
 #pragma unroll
-            for (int j = 0; j < RPT; ++j)
-                s[j] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(rs, mf_offset(j) * 4, 0,
-                                                                                   kCachePolicyNT));
+            for (int j = 0; j < RPT; ++j) s[j] = f4{0.0f, 0.0f, 0.0f, 0.0f};
         } else {
             load_tile<RPT, DK, DV>(s, tile, has_state, rg, c0);
         }
@@ -516,9 +514,7 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h, int
     if constexpr (RING) ring_barrier();  // round 0 has landed
     else __syncthreads();
     if (!token_wave) {
-        if constexpr (CH && MF) {
-#pragma unroll
-            for (int j = 0; j < RPT; ++j) s[j] *= exp_gate(e0p[32 * mw + 16 * (j >> 3) + (ml & 15)]);
+        if constexpr (MF) {
         } else if constexpr (CH) {
 #pragma unroll
             for (int j = 0; j < RPT; ++j) s[j] *= exp_gate(e0p[rg * RPT + j]);
@@ -723,20 +719,95 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h, int
         }
         if (tree && token_wave) move_kept();  // every round is staged
     }
-    if (!token_wave) {
-        float* dst = materialize ? P.states_out + (static_cast<size_t>(b) * P.H + h) * DK * DV
-                                 : P.state + (static_cast<size_t>(slot) * P.H + h) * DK * DV;
-        // The matrix-core layout writes 64-byte runs of a row per store;
-        // streaming (non-temporal) stores of such runs reach HBM as partial
-        // lines (22-45% more bytes written, measured), ordinary stores merge
-        // in L2 first.  Whole rows (the vector layout) stream.
+    float* dst = materialize ? P.states_out + (static_cast<size_t>(b) * P.H + h) * DK * DV
+                             : P.state + (static_cast<size_t>(slot) * P.H + h) * DK * DV;
+    if constexpr (!MF) {
+        if (!token_wave) {
 #pragma unroll
-        for (int j = 0; j < RPT; ++j) {
-            if constexpr (MF)
-                *reinterpret_cast<f4*>(dst + mf_offset(j)) = s[j];
-            else
+            for (int j = 0; j < RPT; ++j)
                 __builtin_nontemporal_store(s[j], reinterpret_cast<f4*>(dst + (rg * RPT + j) * DV + c0));
         }
+    } else {
+        // Matrix-core folds: the update is held in the accumulator layout, in
+        // which one instruction covers 64-byte pieces of 16 rows; read and
+        // written that way the state streams at about four fifths of the rate of
+        // whole rows (measured).  So the state is read here in whole rows -- one
+        // instruction covers two rows of 512 bytes -- and the update is turned
+        // into the same layout through LDS (the staging area, free once every
+        // wave has applied the last round), in two passes of 64 rows.  Wave mw
+        // ends with the rows strip(p) .. strip(p) + 15 of pass p, lane l holding
+        // columns 4 (l % 32) .. + 3 of row strip(p) + 2 i + l / 32 in vector i.
+        // The 16-byte piece c of LDS row R sits at slot c ^ (R % 16), so that
+        // the 16 rows of an accumulator block fall in distinct banks.
+        if constexpr (!MULTI) ring_barrier();  // (a multi-round fold ended its last round with one)
+        // lane indices from an opaque copy of the thread index: the
+        // addresses below are formed here, not hoisted above the rounds and
+        // held (or spilled) across them
+        int et = tid;
+        asm volatile("" : "+v"(et));
+        const int mw = et >> 6, ml = et & 63;
+        const int half = ml >> 5, cc = ml & 31;
+        auto strip = [&](int p) { return COLS ? 64 * p + 16 * mw : 32 * mw + 16 * p; };
+        char* conv = reinterpret_cast<char*>(stage0);
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float*>(tile), 0, has_state ? DK * DV * static_cast<int>(sizeof(float)) : 0, kBufferFlags);
+        // the state rows of pass p; every wave issues them, the token wave's
+        // past the end of the resource (the range check drops them: they
+        // read zeros and touch no memory), so that the registers that receive
+        // them are not held across a branch
+        const int past = token_wave ? DK * DV * static_cast<int>(sizeof(float)) : 0;
+        auto load_rows = [&](int p, f4 (&st)[8]) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int row = strip(p) + 2 * i + half;
+                st[i] = __builtin_bit_cast(
+                    f4, __builtin_amdgcn_raw_buffer_load_b128(rs, past + (row * DV + 4 * cc) * 4, 0, kCachePolicyNT));
+            }
+        };
+        // accumulator vectors 8p .. 8p + 7 into LDS: rows 16 (jj / 2) + l % 16
+        // of the pass, columns 32 mw + 16 (jj % 2) + 4 (l / 16) (COLS), or
+        // rows strip(p) + l % 16, columns 16 jj + 4 (l / 16)
+        auto put = [&](int p) {
+            const int r = ml & 15, G = ml >> 4;
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) {
+                const int R = COLS ? 16 * (jj >> 1) + r : 16 * mw + r;
+                const int c = COLS ? 8 * mw + 4 * (jj & 1) + G : 4 * jj + G;
+                *reinterpret_cast<f4*>(conv + R * 512 + ((c ^ r) << 4)) = s[8 * p + jj];
+            }
+        };
+        const float e0 = CH ? 1.0f : *e0p;
+        auto finish = [&](int p, const f4 (&st)[8]) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int rr = 2 * i + half;
+                const f4 d = *reinterpret_cast<const f4*>(conv + (16 * mw + rr) * 512 + ((cc ^ rr) << 4));
+                const int row = strip(p) + rr;
+                const float e = CH ? exp_gate(e0p[row]) : e0;
+                __builtin_nontemporal_store(st[i] * e + d, reinterpret_cast<f4*>(dst + row * DV + 4 * cc));
+                if ((i & 3) == 3) __builtin_amdgcn_sched_barrier(0);  // four rows at a time (registers)
+            }
+        };
+        // COLS: a pass reads rows that other waves' columns make up;
+        // otherwise each wave reads back only its own rows
+        auto sync = [&]() {
+            if constexpr (COLS) ring_barrier();
+            else __builtin_amdgcn_s_waitcnt(0xC07F);
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        };
+        // the state loads are issued once the first pass's accumulators are
+        // in LDS (their registers are free then)
+        f4 st0[8], st1[8];
+        if (!token_wave) put(0);
+        __builtin_amdgcn_sched_barrier(0);
+        load_rows(0, st0);
+        load_rows(1, st1);
+        sync();
+        if (!token_wave) finish(0, st0);
+        sync();  // the second pass overwrites what the first read
+        if (!token_wave) put(1);
+        sync();
+        if (!token_wave) finish(1, st1);
     }
 }
 
@@ -817,8 +888,11 @@ hipError_t launch_fold_t(const TileParams& p, int batch, hipStream_t s) {
     const bool multi = most > q.fold_chunk;
     const bool tr = raw && multi && kb == 2;  // staged in whole chunks of 32 rows
     const size_t lds = sizeof(float) * fold_lds_floats(D, D, cap,
-                                                       fold_stage_floats(D, D, tr ? 32 : q.fold_chunk, kb, xb, raw),
-                                                       raw && multi && xb == 2 ? kFoldRing : 2, CH);
+                                                       fold_stage_area(fold_stage_floats(D, D, tr ? 32 : q.fold_chunk,
+                                                                                         kb, xb, raw),
+                                                                       raw && multi && xb == 2 ? kFoldRing : 2,
+                                                                       mf && D == 128),
+                                                       CH);
     if (q.sparse) {  // a flush after a decode launch (never a tree commit)
         const dim3 sgrid((static_cast<unsigned>(batch) * q.H + kSparseTiles - 1) / kSparseTiles);
         if (multi) fold_sparse_kernel<RULE, D, D, IO, true, true><<<sgrid, block, lds, s>>>(q);
