@@ -335,13 +335,17 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
     float graw = 0.f;  // log-gate of position tid
     if (GATED && tid < T) graw = tok.gate(tid);
     // delta rule, one new token: its value and step size for this thread's
-    // column (step 6), loaded with the rest rather than after the reductions
+    // column (step 6), loaded with the rest rather than after the reductions;
+    // the value is kept as loaded and converted where it is used (converting
+    // here would wait for it, and with it for every copy and load above,
+    // before the state tile is requested)
     constexpr bool PRE = DELTA && NQ == 1;
-    float vpre = 0.f, bpre = 0.f;
+    IO vpre{};
+    float bpre = 0.f;
     if constexpr (PRE) {
         static_assert(NT >= DV, "one column per thread");
         if (n > 0 && tid < DV) {
-            vpre = load1(tok.new_value(0) + tid);
+            vpre = tok.new_value(0)[tid];
             bpre = P.beta[in_row];
         }
     }
@@ -650,7 +654,7 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
                 u[d] = 0.f;
                 if (d < n) {
                     const int t = p + d;
-                    float x = (PRE ? vpre : load1(tok.new_value(d) + c)) - lds[L.sk + d * DV + c];
+                    float x = (PRE ? as_float(vpre) : load1(tok.new_value(d) + c)) - lds[L.sk + d * DV + c];
                     float o = lds[L.sq + d * DV + c];
 #pragma unroll
                     for (int e = 0; e < d; ++e) x -= ck[d * ldc + p + e] * u[e];

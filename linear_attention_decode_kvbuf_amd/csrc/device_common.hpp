@@ -56,6 +56,18 @@ __device__ __forceinline__ float bf2f(uint32_t bits16) { return __uint_as_float(
 
 __device__ __forceinline__ float load1(const float* p) { return *p; }
 __device__ __forceinline__ float load1(const bf16_bits* p) { return bf2f(*p); }
+// An element kept as loaded, converted where it is used.  The bf16 widening
+// is written as one instruction of inline assembly so that the optimizer
+// cannot move it next to the load (a conditional load joined with a
+// constant otherwise has the shift folded into its branch, which then waits
+// for the load, and with it for everything the wave issued before it).
+__device__ __forceinline__ float as_float(float x) { return x; }
+__device__ __forceinline__ float as_float(bf16_bits x) {
+    const uint32_t v = x;
+    float f;
+    asm("v_lshlrev_b32 %0, 16, %1" : "=v"(f) : "v"(v));
+    return f;
+}
 
 // Four consecutive elements as fp32.
 __device__ __forceinline__ f4 load4(const float* p) { return *reinterpret_cast<const f4*>(p); }
@@ -351,6 +363,24 @@ __device__ __forceinline__ void stage_rows(const TileTokens<DK, DV, IO, XIO>& to
     }
 }
 
+// One direct-to-LDS copy instruction: lane L's 16 bytes at src land at LDS
+// byte window + 16 L (window uniform across the wave, 16-byte aligned).  It
+// is written as inline assembly so that the compiler does not track it.  A
+// tracked copy makes the compiler wait for every outstanding load of the
+// wave -- a whole state tile, say -- before the next LDS read that might
+// alias the copied bytes, and at a loop head or a branch join it assumes the
+// worst; here the LDS rows a copy fills are read only after an explicit wait
+// on the wave's copies (s_waitcnt vmcnt) and, by other waves, after a
+// barrier.  Instructions the compiler does not count only lengthen its own
+// vmcnt waits, never shorten them.  The copy writes no register.
+__device__ __forceinline__ uint32_t lds_byte_address(const void* p) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)(p)));
+}
+__device__ __forceinline__ void lds_dma16(const void* src, void* window) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_byte_address(window));
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(m0) : "memory", "m0");
+}
+
 // Direct-to-LDS copy of `rows` rows of RB bytes (RB a multiple of 16, at
 // most 1 KiB) by one wave: row i is read from src(i) and lands at dst + i RB.
 // One instruction carries 1 KiB, 16 bytes per lane: lane L writes dst + 16 L
@@ -366,8 +396,7 @@ __device__ __forceinline__ void lds_copy_rows(char* dst, int rows, SrcOf src, in
     for (int r0 = 0; r0 < rows; r0 += RPI) {
         const int row = r0 + rr;
         const char* a = src(row < rows ? row : r0) + off;
-        if (row < rows)
-            __builtin_amdgcn_global_load_lds(a, (__attribute__((address_space(3))) void*)(dst + r0 * RB), 16, 0, 0);
+        if (row < rows) lds_dma16(a, dst + r0 * RB);
     }
 }
 

@@ -140,8 +140,7 @@ __device__ __forceinline__ void lds_copy_swz(char* dst, int rows, SrcOf src, int
     for (int r0 = 0; r0 < rows; r0 += 4) {
         const int r = r0 + (lane >> 4);
         const char* a = src(r < rows ? r : r0) + 16 * ((lane & 15) ^ tr_swz(r));
-        if (r < rows)
-            __builtin_amdgcn_global_load_lds(a, (__attribute__((address_space(3))) void*)(dst + r0 * 256), 16, 0, 0);
+        if (r < rows) lds_dma16(a, dst + r0 * 256);
     }
 }
 // fp32 rows of 128 (512 bytes, the delta rule's pseudo-values), read one
@@ -152,8 +151,7 @@ __device__ __forceinline__ void lds_copy_swz32(char* dst, int rows, SrcOf src, i
     for (int r0 = 0; r0 < rows; r0 += 2) {
         const int r = r0 + (lane >> 5);
         const char* a = src(r < rows ? r : r0) + 16 * ((lane & 31) ^ (4 * ((r >> 3) & 3)));
-        if (r < rows)
-            __builtin_amdgcn_global_load_lds(a, (__attribute__((address_space(3))) void*)(dst + r0 * 512), 16, 0, 0);
+        if (r < rows) lds_dma16(a, dst + r0 * 512);
     }
 }
 // LDS byte address of a pointer into the workgroup's LDS, and reads at one
