@@ -275,6 +275,9 @@ def ceilings_leg(torch, dev):
       read_write_back       the tile read and written back in place (a fold)
       read_write_1k_read_24k  + 24 KiB more read per tile (a delta-rule decode's
                             buffered rows at occupancy 32)
+      fold_m64, fold_m128   the tile read and written back plus 32 / 64 KiB
+                            more read per tile (a flush of 64 / 128 bf16 key
+                            and value rows)
     Each figure is the median of 20 launches: algorithmic bytes / duration."""
     import ctypes
 
@@ -286,18 +289,19 @@ def ceilings_leg(torch, dev):
     tile = 4 * d * d
     tiles = torch.empty((ntiles, d, d), dtype=torch.float32, device=dev).normal_()
     slot = torch.randperm(ntiles, generator=torch.Generator().manual_seed(5)).to(torch.int32).to(dev)
-    extra, extra2 = 1024, 24704
+    extra = 1024
     side = torch.zeros(ntiles * extra // 4, dtype=torch.float32, device=dev)
-    side2 = torch.ones(ntiles * extra2 // 4, dtype=torch.float32, device=dev)
+    side2 = torch.ones(ntiles * 65536 // 4, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream().cuda_stream
     out = {}
-    for name, kind, nbytes in (("read", 0, tile), ("read_write_1k", 1, tile + extra),
-                               ("read_write_back", 2, 2 * tile),
-                               ("read_write_1k_read_24k", 3, tile + extra + extra2)):
+    for name, kind, extra2 in (("read", 0, 0), ("read_write_1k", 1, 0), ("read_write_back", 2, 0),
+                               ("read_write_1k_read_24k", 3, 24704), ("fold_m64", 4, 32768),
+                               ("fold_m128", 4, 65536)):
+        nbytes = tile * (2 if kind in (2, 4) else 1) + (extra if kind in (1, 3) else 0) + extra2
+
         def launch():
             rc = lib.kvbuf_probe_stream(tiles.data_ptr(), slot.data_ptr(), ntiles, d, kind, side.data_ptr(),
-                                        extra if kind in (1, 3) else 0, side2.data_ptr(),
-                                        extra2 if kind == 3 else 0, stream)
+                                        extra if kind in (1, 3) else 0, side2.data_ptr(), extra2, stream)
             assert rc == 0, rc
         for _ in range(3):
             launch()
@@ -389,8 +393,9 @@ def context_leg(kb, synth, torch, dev, args):
                 kv.state_slot.fill_(-1)
             times = []
             for _ in range(reps):
-                kv.occupancy.zero_()
-                kv.admit()
+                if wl.m > 0:  # (the recurrent form keeps no buffer)
+                    kv.occupancy.zero_()
+                    kv.admit()
                 torch.cuda.synchronize()
                 stream = torch.cuda.current_stream()
                 e0 = torch.cuda.Event(enable_timing=True)
@@ -596,6 +601,27 @@ def long_fold_leg(kb, synth, torch, dev, args):
     return out
 
 
+def copy_leg(torch, dev):
+    """A 1 GiB device-to-device copy, repeated: it reads 1 GiB and writes
+    1 GiB per dispatch, so the HBM counters' readings for it (rocprofv3
+    FETCH_SIZE, WRITE_SIZE) give the factors that turn their readings for the
+    library's kernels into bytes."""
+    n = 1 << 28
+    src = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 5
+    return {"bytes_read": 4 * n, "bytes_written": 4 * n, "ms": ms, "gbps": 8 * n / (ms * 1e-3) / 1e9}
+
+
 def delta_decode_bytes(j, dk, dv, stateful):
     """Algorithmic bytes of one delta-rule decode of a tile at occupancy j:
     state read (requests with a state), q / k / v in (bf16), log-gate and
@@ -681,7 +707,7 @@ def main():
     ap.add_argument("--m", type=int, default=8, help="buffer size")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing on the host")
     ap.add_argument("--no-extras", action="store_true", help="skip the m=0 / separate-flush / copy legs")
-    ap.add_argument("--only", choices=["fused", "recurrent", "separate", "ceilings", "verify", "delta", "sweep",
+    ap.add_argument("--only", choices=["fused", "recurrent", "separate", "ceilings", "copy", "verify", "delta", "sweep",
                                        "linear", "heads4", "context", "channel", "longfold"], default=None,
                     help="run one leg only (for profiling)")
     args = ap.parse_args()
@@ -802,6 +828,10 @@ def main():
             result["roofline"]["measured_ceiling_gbps"] = ceil
             result["roofline"]["frac_of_measured_ceiling"] = result["roofline"]["achieved"] / ceil
 
+    # ---- counter calibration: a device copy of known size (only on request) -
+    if args.only == "copy":
+        result["copy_calibration"] = copy_leg(torch, dev)
+
     # ---- speculative verification: n drafts, then commit a ~ U{0..n} -------
     if not args.no_extras and args.only in (None, "verify"):
         result["verify"] = verify_leg(kb, synth, torch, dev, args)
@@ -823,6 +853,13 @@ def main():
         result["channel_gates"] = channel_leg(kb, synth, torch, dev, args)
     if not args.no_extras and args.only in (None, "longfold"):
         result["long_folds"] = long_fold_leg(kb, synth, torch, dev, args)
+        if "memory_ceilings" in result:
+            # the compute-free stream of a flush's traffic (tile read and
+            # written back, the buffered rows read): its time over the flush's
+            for key, probe in (("gated_m64", "fold_m64"), ("gated_m128", "fold_m128")):
+                lf, c = result["long_folds"][key], result["memory_ceilings"][probe]
+                lf["measured_ceiling_us"] = c["us"]
+                lf["frac_of_measured_ceiling"] = c["us"] / (lf["flush_ms"] * 1e3)
 
     if args.only not in (None, "fused"):
         print(json.dumps(result))

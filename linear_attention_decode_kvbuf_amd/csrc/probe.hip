@@ -10,6 +10,8 @@
 //   kind 2  read the tile and write it back in place     (a fold's state traffic)
 //   kind 3  read the tile, write `extra` bytes elsewhere and read `extra2`
 //           more bytes from a second region               (+ buffered rows)
+//   kind 4  read the tile and `extra2` bytes from a second region, write the
+//           tile back in place                            (a fold of buffered rows)
 // Tile w of the grid is slot[w]; reads and writes use the non-temporal hint,
 // as the decode kernels' state traffic does.
 #include <hip/hip_runtime.h>
@@ -36,14 +38,26 @@ __global__ __launch_bounds__(256) void probe_kernel(float* tiles, const int32_t*
     for (int j = 0; j < RPT; ++j)
         s[j] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(r, v, j * D * 4, kNT));
     f4 x2 = f4{0.f, 0.f, 0.f, 0.f};
-    if (kind == 3) {  // more bytes from a second region: 16 per thread per 4 KiB
+    if (kind == 3 || kind == 4) {
+        // more bytes from a second region, 16 per thread per 4 KiB (at most
+        // 64 KiB): every load issued before any is summed
         const float* src = side2 + static_cast<size_t>(w) * (extra2 / 4);
-        for (int o = tid * 4; o < extra2 / 4; o += 1024) x2 += *reinterpret_cast<const f4*>(src + o);
+        f4 e[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int o = tid * 4 + 1024 * i;
+            e[i] = o < extra2 / 4 ? *reinterpret_cast<const f4*>(src + o) : f4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) x2 += e[i];
     }
-    if (kind == 2) {
+    if (kind == 2 || kind == 4) {
+        // (kind 4: the second region's sum enters at 1e-30 of its size, so
+        // the reads stay live)
+        const float e = 1.0000001f + 1e-30f * (x2.x + x2.y + x2.z + x2.w);
 #pragma unroll
         for (int j = 0; j < RPT; ++j)
-            __builtin_nontemporal_store(s[j] * 1.0000001f, reinterpret_cast<f4*>(tile + (rg * RPT + j) * D + c0));
+            __builtin_nontemporal_store(s[j] * e, reinterpret_cast<f4*>(tile + (rg * RPT + j) * D + c0));
         return;
     }
     f4 acc = x2;
@@ -64,11 +78,13 @@ __global__ __launch_bounds__(256) void probe_kernel(float* tiles, const int32_t*
 extern "C" {
 
 // tiles [num_slots][d][d] fp32; slot [ntiles]; side: kind 1/3 [ntiles][extra
-// bytes], else >= ntiles floats; side2 (kind 3) [ntiles][extra2 bytes].
+// bytes], else >= ntiles floats; side2 (kind 3/4) [ntiles][extra2 bytes],
+// extra2 <= 64 KiB.
 // extra and extra2 are multiples of 16.  Returns a hipError_t.
 int kvbuf_probe_stream(float* tiles, const int32_t* slot, int ntiles, int d, int kind, float* side, int extra,
                        const float* side2, int extra2, hipStream_t stream) {
-    if (ntiles <= 0 || (d != 64 && d != 128) || kind < 0 || kind > 3 || extra % 16 || extra2 % 16)
+    if (ntiles <= 0 || (d != 64 && d != 128) || kind < 0 || kind > 4 || extra % 16 || extra2 % 16 ||
+        extra2 > 65536)
         return static_cast<int>(hipErrorInvalidValue);
     if (d == 128)
         probe_kernel<128><<<ntiles, 256, 0, stream>>>(tiles, slot, kind, side, extra, side2, extra2);
