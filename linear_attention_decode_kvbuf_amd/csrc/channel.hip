@@ -173,14 +173,18 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void channel_kernel(TileParams P
             vdr[r].load(static_cast<const IO*>(P.v) + (in_row + d * in_stride) * DV + cl * (DV / 16));
         }
     }
-    float gdr[NQ], qv[NQ];  // channel owners: the drafts' gates and queries of channel tid
+    // channel owners: the drafts' gates and queries of channel tid (the
+    // queries kept as loaded and widened where used: widening them here would
+    // wait for them, and with them for the state tile requested above)
+    float gdr[NQ];
+    IO qv[NQ];
 #pragma unroll
     for (int d = 0; d < NQ; ++d) {
         gdr[d] = 0.f;
-        qv[d] = 0.f;
+        qv[d] = IO{};
         if (tid < DK && d < n) {
             gdr[d] = P.g[(in_row + d * in_stride) * DK + tid];
-            qv[d] = load1(static_cast<const IO*>(P.q) + (in_row + d * in_stride) * DK + tid);
+            qv[d] = static_cast<const IO*>(P.q)[(in_row + d * in_stride) * DK + tid];
         }
     }
 
@@ -223,7 +227,7 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void channel_kernel(TileParams P
             for (int e = 0; e < NQ; ++e)
                 if (e < n && d < n && seen(d, e)) D += gdr[e];
             if (d < n) {
-                qh[d * DK + tid] = P.scale * qv[d] * exp_gate(D);
+                qh[d * DK + tid] = P.scale * as_float(qv[d]) * exp_gate(D);
                 fd[d * DK + tid] = exp_gate(-D);
                 gd[d * DK + tid] = gdr[d];
             }

@@ -157,13 +157,16 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void decode_kernel(TilePar
         qc.load(qin + cl * E);
         // per-channel rule: this lane's channels of the query and of the new
         // token's gate row, loaded with the rest (each later use would
-        // otherwise cost the chain a round trip)
-        float qch[CH ? CPL : 1], gnew[CH ? CPL : 1];
+        // otherwise cost the chain a round trip); the query is kept as loaded
+        // and widened where it is used (widening it here would wait for it,
+        // and with it for every load above, before the rows are requested)
+        IO qch[CH ? CPL : 1];
+        float gnew[CH ? CPL : 1];
         if constexpr (CH) {
 #pragma unroll
             for (int c = 0; c < CPL; ++c) {
                 const int ch = lane + 64 * c;
-                qch[c] = ch < DK ? load1(qin + ch) : 0.0f;
+                qch[c] = ch < DK ? qin[ch] : IO{};
                 gnew[c] = ch < DK ? P.g[in_row * DK + ch] : 0.0f;
             }
         }
@@ -208,7 +211,7 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void decode_kernel(TilePar
                     }
                     const float ebt = exp_gate(run);
                     btv[ch] = ebt;                              // e^{B_t}
-                    qdv[ch] = qch[c] * ebt;                     // e^{B_t} q
+                    qdv[ch] = as_float(qch[c]) * ebt;           // e^{B_t} q
                     if (fold) frow[ch] = exp_gate(-dg[(P.m - 1) * DK + ch]);  // e^{B_{m-1} - B_t}
                 }
             }
