@@ -254,23 +254,23 @@ __device__ __forceinline__ void gate_prefix(float* bl, int T, int lane, GateAt g
 
 // The same when gate_at reads device memory: the gates of every segment are
 // requested before the first is summed (one round trip for a buffer of any
-// length; T <= kMaxCapacity; eight registers per lane).
+// length; T <= kMaxCapacity; eight registers per lane).  All eight loads are
+// issued whatever T, with no branch between them -- segments past the end
+// read position T - 1 again and count as zeros -- since loads under a branch
+// each end with a wait for the counter to drain.
 template <typename GateAt>
 __device__ __forceinline__ void gate_prefix_loads(float* bl, int T, int lane, GateAt gate_at) {
     constexpr int KS = kMaxCapacity / 64;
+    if (T <= 0) return;
     float g[KS];
 #pragma unroll
-    for (int k = 0; k < KS; ++k) {
-        const int i = 64 * k + lane;
-        g[k] = 0.0f;
-        if (64 * k < T && i < T) g[k] = gate_at(i);
-    }
+    for (int k = 0; k < KS; ++k) g[k] = gate_at(min(64 * k + lane, T - 1));
     float carry = 0.0f;
 #pragma unroll
     for (int k = 0; k < KS; ++k) {
         if (64 * k < T) {
             const int i = 64 * k + lane;
-            float x = g[k];
+            float x = i < T ? g[k] : 0.0f;
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
                 float y = __shfl_up(x, off, 64);

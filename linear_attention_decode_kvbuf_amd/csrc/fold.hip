@@ -54,11 +54,12 @@ __host__ __device__ inline int fold_lds_floats(int DK, int DV, int cap, int stag
 // copies of round r + 2 are in flight while round r is applied
 constexpr int kFoldRing = 3;
 
-// The barrier between ring rounds.  __syncthreads() makes every wave wait for
-// all of its outstanding memory operations, the direct-to-LDS copies of later
-// rounds included; here the token wave has already waited for the round that
-// is read next, and each wave only completes its LDS accesses (lgkmcnt(0))
-// before the barrier.  The signal fences keep the compiler from moving memory
+// A barrier for LDS only: after the metadata, and between ring rounds.
+// __syncthreads() makes every wave wait for all of its outstanding memory
+// operations (the metadata stores, the direct-to-LDS copies of later rounds);
+// here each wave only completes its LDS accesses (lgkmcnt(0)) before the
+// barrier, and between rounds the token wave has already waited for the round
+// that is read next.  The signal fences keep the compiler from moving memory
 // accesses across it.
 __device__ __forceinline__ void ring_barrier() {
     __builtin_amdgcn_s_waitcnt(0xC07F);
@@ -221,6 +222,11 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h, int
     extern __shared__ __attribute__((aligned(16))) float lds[];  // 16-byte rows for the LDS copies
     __shared__ unsigned s_bad;
     __shared__ int s_T, s_fold;
+    // the metadata update, made by the token wave once its copies are issued:
+    // whether there is one, the new occupancy, the table entries rotated, and
+    // the table row as read
+    __shared__ int s_upd, s_pnew, s_rot;
+    __shared__ int s_blk[kMaxTableRow];
     // tree commit: pool rows of the k-th kept draft before (src) and after
     // (dst) its move to buffer position p + k
     __shared__ uint32_t s_src[TREE ? kMaxDrafts : 1], s_dst[TREE ? kMaxDrafts : 1];
@@ -300,17 +306,28 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h, int
             s_bad = bad;
             s_T = T0;
             s_fold = fold0 ? 1 : 0;
+            s_upd = !bad && !materialize && (fold0 || a != 0);
+            s_pnew = fold0 ? pn - P.m : pn;
+            s_rot = fold0 ? P.m / P.block_size : 0;
         }
-        if (!bad && !materialize && (fold0 || a != 0))
-            update_meta(P, b, h, fold0 ? pn - P.m : pn, fold0 ? P.m / P.block_size : 0, lane, blk);
+        s_blk[lane] = blk;
     }
-    __syncthreads();  // the position table, s_T, s_fold and s_bad are complete
+    // The position table, s_T, s_fold and s_bad are complete.  The token
+    // wave's metadata stores need not be: nothing in this workgroup reads
+    // them back, so the barrier waits for LDS accesses only.
+    ring_barrier();
     if (s_bad) {
         report(P, s_bad);
         return;
     }
     const bool fold = s_fold != 0;
     const int T = s_T;
+    // Token wave: the metadata stores are issued last, so that no wait on
+    // them stands between the metadata and the first copies, or before a
+    // barrier the state waves take.
+    auto meta = [&]() __attribute__((always_inline)) {
+        if (s_upd) update_meta(P, b, h, s_pnew, s_rot, lane, s_blk[lane]);
+    };
 
     // Token wave, tree commit: copy the kept drafts' key, value and gate rows
     // to their new positions.  Every load is issued before the first store and
@@ -330,7 +347,10 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h, int
         }
     };
     if (!materialize && !fold) {  // no state change for this tile
-        if (tree && token_wave) move_kept();
+        if (token_wave) {
+            if (tree) move_kept();
+            meta();
+        }
         return;
     }
 
@@ -455,9 +475,10 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h, int
         if constexpr (RAW) {
             // The first rounds' copies need only the position table: requested
             // before the gates, both are in flight in the same round trip.  The
-            // metadata stores above complete first (stores and loads share the
-            // counter a ring wait counts).
-            __builtin_amdgcn_s_waitcnt(0x0F70);
+            // metadata stores may still be outstanding: the ring waits count
+            // them as well, which only makes a wait longer, never shorter
+            // (loads complete in order, so no copy of a round is outstanding
+            // once fewer operations than the later rounds' copies are).
             if (T > 0) issue(0);
             if (RING && T > fc) issue(1);
         }
@@ -800,6 +821,11 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h, int
         __builtin_amdgcn_sched_barrier(0);
         load_rows(0, st0);
         load_rows(1, st1);
+        // Both passes' rows are waited for before the first store, by every
+        // wave (the token wave's are the dropped ones): stores and loads share
+        // the counter, and a count taken behind the first pass's stores would
+        // make the second pass wait for them too.
+        __builtin_amdgcn_s_waitcnt(0x0F70);
         sync();
         if (!token_wave) finish(0, st0);
         sync();  // the second pass overwrites what the first read
@@ -807,6 +833,7 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h, int
         sync();
         if (!token_wave) finish(1, st1);
     }
+    if (token_wave) meta();
 }
 
 // One workgroup per tile.
