@@ -317,23 +317,25 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
         __builtin_amdgcn_sched_barrier(0);  // the copies go first
     }
     // this call's queries, and its keys (and values, linear / gated rules) for
-    // the appends
+    // the appends.  The token loads below are issued with no branch between
+    // them, from clamped indices (draft n - 1 and position T - 1 exist: n >= 1);
+    // every use of a slot past the end is guarded (d < n, i < T).  Loads under
+    // per-lane branches each ended with a wait for the counter to drain, which
+    // put them a round trip apart.
     RawChunk<IO, E> qraw[NQR], kdraw[NQR];
     RawChunk<IO, EV> vdraw[DELTA ? 1 : NQR];
 #pragma unroll
     for (int r = 0; r < NQR; ++r) {
-        const int d = gp + NG * r;
-        qraw[r].zero();
-        kdraw[r].zero();
-        if constexpr (!DELTA) vdraw[r].zero();
-        if (d < n) {
-            qraw[r].load(static_cast<const IO*>(P.q) + (in_row + d * P.H) * DK + cl * E);
-            kdraw[r].load(tok.kin + d * tok.in_stride_k + cl * E);
-            if constexpr (!DELTA) vdraw[r].load(tok.new_value(d) + cl * EV);
-        }
+        const int d = min(gp + NG * r, n - 1);
+        qraw[r].load(static_cast<const IO*>(P.q) + (in_row + d * P.H) * DK + cl * E);
+        kdraw[r].load(tok.kin + d * tok.in_stride_k + cl * E);
+        if constexpr (!DELTA) vdraw[r].load(tok.new_value(d) + cl * EV);
     }
     float graw = 0.f;  // log-gate of position tid
-    if (GATED && tid < T) graw = tok.gate(tid);
+    if constexpr (GATED) {
+        const int i = min(tid, T - 1);
+        graw = *(i < p ? tok.gpool + tok.slot_index(i) : tok.gin + static_cast<size_t>(i - p) * P.H);
+    }
     // delta rule, one new token: its value and step size for this thread's
     // column (step 6), loaded with the rest rather than after the reductions;
     // the value is kept as loaded and converted where it is used (converting
@@ -344,24 +346,20 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
     float bpre = 0.f;
     if constexpr (PRE) {
         static_assert(NT >= DV, "one column per thread");
-        if (n > 0 && tid < DV) {
-            vpre = tok.new_value(0)[tid];
-            bpre = P.beta[in_row];
-        }
+        vpre = tok.new_value(0)[min(tid, DV - 1)];  // (columns c = tid < DV use it)
+        bpre = P.beta[in_row];
     }
     RawChunk<IO, E> kr;
     RawChunk<XIO, EV> xr;
+    // (the position clamped to T - 1 as above: stage_pass uses i < T only)
     auto load_pass = [&](int i0) {
-        const int i = i0 + gp;
-        kr.zero();
-        xr.zero();
-        if (i < T) {
-            kr.load(tok.key(i) + cl * E);
-            if (i < p) {
-                xr.load(tok.pooled_value(i) + cl * EV);
-            } else if constexpr (!DELTA) {
-                xr.load(tok.new_value(i - p) + cl * EV);
-            }
+        const int i = min(i0 + gp, T - 1);
+        kr.load(tok.key(i) + cl * E);
+        if constexpr (DELTA) {
+            xr.zero();
+            if (i < p) xr.load(tok.pooled_value(i) + cl * EV);
+        } else {
+            xr.load((i < p ? tok.pooled_value(i) : tok.new_value(i - p)) + cl * EV);
         }
     };
     if constexpr (!DMA) load_pass(0);
