@@ -247,13 +247,23 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
         if constexpr (TREE) {
             const bool bad_par = tid < n && (par < -1 || par >= tid);  // parents precede children
             if (__ballot(bad_par)) bad |= KVBUF_DEVERR_ACCEPT;
-            // ancestor mask of draft `tid`: follow the parents (at most n steps)
-            uint32_t anc = 0;
-            int cur = (tid < n && !bad_par) ? tid : -1;
-            for (int step = 0; step < n; ++step) {
-                if (cur >= 0) anc |= 1u << cur;
-                const int up = __shfl(par, cur >= 0 ? cur : 0, 64);
-                cur = (cur > 0 && up >= 0 && up < cur) ? up : -1;
+            // ancestor mask of draft `tid` by pointer doubling: after a round
+            // with span s, anc holds the draft and its ancestors less than 2s
+            // levels up and `up` the one 2s levels up (-1: past the root), so
+            // three rounds cover the deepest path of kMaxDrafts drafts (a tile
+            // with invalid parents is skipped, whatever its masks)
+            const bool mine = tid < n && !bad_par;
+            uint32_t anc = mine ? 1u << tid : 0u;
+            int up = mine ? par : -1;
+#pragma unroll
+            for (int span = 1; span < kMaxDrafts; span <<= 1) {
+                const int src = up >= 0 ? up : 0;
+                const uint32_t a = static_cast<uint32_t>(__shfl(static_cast<int>(anc), src, 64));
+                const int u = __shfl(up, src, 64);
+                if (up >= 0) {
+                    anc |= a;
+                    up = u;
+                }
             }
             if (tid < n) s_anc[tid] = anc;
         }
@@ -430,18 +440,22 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
     // ---- 3. cumulative log-gates (wave 0), decay weights of S0 -----------------
     if (tid < 64) {
         if constexpr (GATED) {
-            float graw_d = 0.0f;  // tree drafts: log-gate of draft tid
-            if constexpr (TREE) graw_d = tid < n ? bl[p + tid] : 0.0f;
+            // tree drafts: every draft's log-gate, read by every lane (the
+            // same LDS word for all lanes) before the prefix overwrites it
+            float gd[TREE ? kMaxDrafts : 1];
+            if constexpr (TREE) {
+#pragma unroll
+                for (int e = 0; e < kMaxDrafts; ++e) gd[e] = e < n ? bl[p + e] : 0.0f;
+            }
             gate_prefix(bl, T, tid, [&](int i) { return bl[i]; });
             if constexpr (TREE) {
                 // tree drafts: the decay of draft d runs along its own path,
                 // b_{p+d} = b_{p-1} + the log-gates of d and its ancestors
                 const uint32_t anc = tid < n ? s_anc[tid] : 0u;
                 float acc = p > 0 ? bl[p - 1] : 0.0f;
-                for (int e = 0; e < n; ++e) {
-                    const float ge = __shfl(graw_d, e, 64);
-                    if ((anc >> e) & 1u) acc += ge;
-                }
+#pragma unroll
+                for (int e = 0; e < kMaxDrafts; ++e)
+                    if (e < n && ((anc >> e) & 1u)) acc += gd[e];
                 if (tid < n) bl[p + tid] = acc;
             }
         } else {
