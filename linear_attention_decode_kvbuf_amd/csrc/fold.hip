@@ -54,13 +54,13 @@ __host__ __device__ inline int fold_lds_floats(int DK, int DV, int cap, int stag
 // copies of round r + 2 are in flight while round r is applied
 constexpr int kFoldRing = 3;
 
-// A barrier for LDS only: after the metadata, and between ring rounds.
-// __syncthreads() makes every wave wait for all of its outstanding memory
-// operations (the metadata stores, the direct-to-LDS copies of later rounds);
-// here each wave only completes its LDS accesses (lgkmcnt(0)) before the
-// barrier, and between rounds the token wave has already waited for the round
-// that is read next.  The signal fences keep the compiler from moving memory
-// accesses across it.
+// A barrier for LDS only: after the metadata, and between ring rounds.  At a
+// __syncthreads() the compiler may make a wave drain its vector-memory
+// counter first (it did after the metadata), which would wait for stores and
+// for the direct-to-LDS copies of later rounds; here each wave only completes
+// its LDS accesses (lgkmcnt(0)) before the barrier, and between rounds the
+// token wave has already waited for the round that is read next.  The signal
+// fences keep the compiler from moving memory accesses across it.
 __device__ __forceinline__ void ring_barrier() {
     __builtin_amdgcn_s_waitcnt(0xC07F);
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -222,7 +222,7 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h, int
     extern __shared__ __attribute__((aligned(16))) float lds[];  // 16-byte rows for the LDS copies
     __shared__ unsigned s_bad;
     __shared__ int s_T, s_fold;
-    // the metadata update, made by the token wave once its copies are issued:
+    // the metadata update, stored by the token wave at the end of the tile:
     // whether there is one, the new occupancy, the table entries rotated, and
     // the table row as read
     __shared__ int s_upd, s_pnew, s_rot;
@@ -474,11 +474,9 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h, int
     if (token_wave) {
         if constexpr (RAW) {
             // The first rounds' copies need only the position table: requested
-            // before the gates, both are in flight in the same round trip.  The
-            // metadata stores may still be outstanding: the ring waits count
-            // them as well, which only makes a wait longer, never shorter
-            // (loads complete in order, so no copy of a round is outstanding
-            // once fewer operations than the later rounds' copies are).
+            // before the gates, both are in flight in the same round trip.
+            // Nothing else is outstanding on the wave's counter here (the
+            // metadata stores come last), so the ring waits' counts hold.
             if (T > 0) issue(0);
             if (RING && T > fc) issue(1);
         }
