@@ -62,7 +62,11 @@ __host__ __device__ inline ChunkLds chunk_lds(int rule, int DK, int DV, int NQ, 
     L.kr = o; o += round4(slots * NG * DK * io / 4);    // keys of one pass of positions (raw)
     L.vr = o; o += round4(slots * NG * DV * xo / 4);    // their values (raw)
     L.fw = o; o += fold ? round4(m) : 0;                // fold weights
-    L.red = o; o += RG * DV * (delta ? 2 : NQ);         // row-group partial sums
+    // row-group partial sums; the matrix-core instance of eight queries keeps
+    // one slot per wave (its two row groups summed first), which lets four of
+    // its workgroups share a CU's LDS
+    const bool ws = !delta && NQ == 8 && DK == 128 && DV == 128 && io == 2;
+    L.red = o; o += (ws ? RG / 2 : RG) * DV * (delta ? 2 : NQ);
     L.sq = o; o += delta ? NQ * DV : 0;                 // reduced outputs before the new tokens
     L.sk = o; o += delta ? NQ * DV : 0;                 // reduced e^{b_t} S0^T k_t + buffer part
     L.total = o;
@@ -79,9 +83,10 @@ __host__ __device__ inline ChunkLds chunk_lds(int rule, int DK, int DV, int NQ, 
 // The fp32 state goes in as two bf16 terms, hi = bf16(S) and lo = bf16(S -
 // hi), so each product is exact and S is represented to about 2^-17 of its
 // size; the bf16 queries are exact.  The wave's partial sums over its 32 rows
-// are added (times scale e^{b_t}) into the row-group-2w slots of `red`, which
-// already hold this wave's value sums.
-template <int DK, int DV, int RG>
+// are added (times scale e^{b_t}) into the wave's slot of `red` (RGS slots per
+// query: the wave's own, or that of its first row group, 2w), which already
+// holds the wave's value sums.
+template <int DK, int DV, int RG, int RGS>
 __device__ __forceinline__ void state_products_mfma(const f4 (&s)[16], const bf16_bits* qr, float* red,
                                                     const float* es, float scale, int n, int tid) {
     typedef short s4 __attribute__((ext_vector_type(4)));
@@ -122,7 +127,7 @@ __device__ __forceinline__ void state_products_mfma(const f4 (&s)[16], const bf1
     for (int i = 0; i < 4; ++i) {
         const int dq = 4 * (g & 1) + i;
         if (dq < n) {
-            f4* dst = reinterpret_cast<f4*>(red + (dq * RG + 2 * w) * DV + 64 * (g >> 1) + 4 * nn);
+            f4* dst = reinterpret_cast<f4*>(red + (dq * RGS + (RGS == RG ? 2 * w : w)) * DV + 64 * (g >> 1) + 4 * nn);
             *dst += f4{d[0][i], d[1][i], d[2][i], d[3][i]} * (scale * es[dq]);
         }
     }
@@ -176,6 +181,10 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
     // four or eight bf16 queries of d = 128: the scores and the state products
     // run on the matrix cores, and the value sums go straight to LDS
     constexpr bool MF = !DELTA && NQ >= 4 && DK == 128 && DV == 128 && std::is_same<IO, bf16_bits>::value;
+    // eight queries: one slot of `red` per wave and query (its two row groups
+    // summed first), so that four workgroups share a CU's LDS
+    constexpr bool WS = MF && NQ == 8;
+    constexpr int RGS = WS ? RG / 2 : RG;  // row-group slots of `red` per query
     // One new token (decode / direct with long rows) and the delta rule: the
     // keys and values (pseudo-values) of each pass are copied straight into a
     // two-slot LDS ring by direct-to-LDS loads.  The first two passes are
@@ -526,17 +535,25 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
         // weighted sums: row group rg takes the pass positions ii = rg, rg+RG, ...
         const int cnt = min(NG, tacc - i0);
         if constexpr (MF) {
-            // one query at a time, straight into this thread's slot of `red`
+            // one query at a time, straight into this wave's slot of `red`
             // (no accumulator stays live next to the tile)
             float* red = lds + L.red;
+            // (WS: lanes l and l + 32 of a wave hold the same columns of its
+            // two row groups; their sums are added and the wave's slot updated)
 #pragma unroll
             for (int d = 0; d < NQ; ++d) {
                 if (d < n) {
-                    f4* own = reinterpret_cast<f4*>(red + (d * RG + rg) * DV + c0);
-                    f4 a = i0 > 0 ? *own : f4{0.f, 0.f, 0.f, 0.f};
+                    f4 a = f4{0.f, 0.f, 0.f, 0.f};
                     for (int ii = rg; ii < cnt; ii += RG)
                         a += cq[d * ldc + i0 + ii] * load4(vrs + (rbase + ii) * DV + c0);
-                    *own = a;
+                    if constexpr (WS) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) a[e] += __shfl_xor(a[e], 32, 64);
+                    }
+                    if (!WS || (tid & 32) == 0) {
+                        f4* own = reinterpret_cast<f4*>(red + (d * RGS + (WS ? tid >> 6 : rg)) * DV + c0);
+                        *own = i0 > 0 ? *own + a : a;
+                    }
                 }
             }
         } else {
@@ -585,7 +602,7 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
     float* outp = P.out + in_row * DV;
     const size_t out_stride = static_cast<size_t>(P.H) * DV;
     if constexpr (MF) {  // the value sums are in `red` already
-        if (has_state) state_products_mfma<DK, DV, RG>(s, qr, red, es, P.scale, n, tid);
+        if (has_state) state_products_mfma<DK, DV, RG, RGS>(s, qr, red, es, P.scale, n, tid);
     }
     if constexpr (!DELTA) {
         // every query's row-group partials at once, then one reduction
@@ -603,7 +620,7 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
                     for (int j = 0; j < RPT; ++j) sa += s[j] * qf[j];
                     a += sa * (P.scale * es[d]);
                 }
-                *reinterpret_cast<f4*>(red + (d * RG + rg) * DV + c0) = a;
+                *reinterpret_cast<f4*>(red + (d * RGS + rg) * DV + c0) = a;
             }
         }
         __syncthreads();
@@ -613,7 +630,7 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
             const int c = idx - d * DV;
             float sum = 0.f;
 #pragma unroll
-            for (int g2 = 0; g2 < RG; ++g2) sum += red[(d * RG + g2) * DV + c];
+            for (int g2 = 0; g2 < RGS; ++g2) sum += red[(d * RGS + g2) * DV + c];
             outp[d * out_stride + c] = sum;
         }
     } else {
