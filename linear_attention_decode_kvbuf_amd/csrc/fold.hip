@@ -181,7 +181,12 @@ __device__ __forceinline__ f4 mf_mac32(mf_b8 a, mf_b8 b, f4 c) {
 // position is staged before the state loads are issued, which keeps the
 // token wave's registers out of the tile's live range.
 // TREE: a commit of a root-to-leaf path of tree drafts.
-template <int RULE, int DK, int DV, typename IO, bool MULTI, bool TREE, bool MFT>
+// W4: four waves, wave 0 taking the token wave's part as well (rows staged as
+// stored, not a tree commit).  A workgroup of five waves is placed on a CU
+// only while every SIMD has room for two of its waves, which left the fold at
+// two workgroups per CU where its registers allow three (measured); with four
+// waves the registers and LDS decide.
+template <int RULE, int DK, int DV, typename IO, bool MULTI, bool TREE, bool MFT, bool W4 = false>
 __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h, int tid) {
     using G = Geo<DK, DV>;
     constexpr int NT = G::NT, TPR = G::TPR, RPT = G::RPT;
@@ -218,6 +223,7 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h, int
     // so that it splits only its own columns of the pseudo-values
     constexpr bool COLS = TR && !XEXACT;
     constexpr int NBUF = RING ? kFoldRing : 2;
+    static_assert(!W4 || (RAW && !TREE), "four waves: rows staged as stored, no tree commit");
 
     extern __shared__ __attribute__((aligned(16))) float lds[];  // 16-byte rows for the LDS copies
     __shared__ unsigned s_bad;
@@ -231,8 +237,11 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h, int
     // (dst) its move to buffer position p + k
     __shared__ uint32_t s_src[TREE ? kMaxDrafts : 1], s_dst[TREE ? kMaxDrafts : 1];
 
-    const bool token_wave = tid >= NT;
-    const int lane = tid - NT;
+    // the wave with the token part (metadata, copies, gates, weights) and the
+    // waves holding the tile
+    const bool token_wave = W4 ? tid < 64 : tid >= NT;
+    const bool state_wave = W4 || tid < NT;
+    const int lane = W4 ? tid : tid - NT;
     const int rg = tid / TPR;
     const int c0 = (tid % TPR) * 4;
     const int cap = P.block_size * P.blocks_per_req;
@@ -363,7 +372,11 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h, int
     constexpr int KB = RAW ? static_cast<int>(sizeof(IO)) : 4, XB = RAW ? static_cast<int>(sizeof(XIO)) : 4;
     const int srows = TR ? 32 : fc;  // rows of a staging buffer (TR: a whole product chunk)
     const int stage_floats = fold_stage_floats(DK, DV, srows, KB, XB, RAW);
-    float* e0p = stage0 + fold_stage_area(stage_floats, NBUF, MF);
+    // W4: a ring fold of at most two rounds allocates two staging buffers (the
+    // launcher sizes LDS the same way); round r stays in buffer r % NBUF
+    const int most = materialize ? cap : P.m;  // most positions a tile applies
+    const int nbuf = (W4 && RING && most <= 2 * kRawFoldChunk) ? 2 : NBUF;
+    float* e0p = stage0 + fold_stage_area(stage_floats, nbuf, MF);
 
     TileTokens<DK, DV, IO, XIO> tok;
     tok.kpool = static_cast<const IO*>(P.key);
@@ -517,7 +530,7 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h, int
     f4 s[RPT];
     const int mw = tid >> 6, ml = tid & 63;  // MF: wave and lane
     const float* tile = has_state ? P.state + (static_cast<size_t>(slot) * P.H + h) * DK * DV : P.state;
-    if (!token_wave) {
+    if (state_wave) {
         if constexpr (MF) {
             // the matrix cores accumulate the update alone, from zero; the
             // state is read after the last round, in whole rows
@@ -530,7 +543,7 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h, int
     }
     if constexpr (RING) ring_barrier();  // round 0 has landed
     else __syncthreads();
-    if (!token_wave) {
+    if (state_wave) {
         if constexpr (MF) {
         } else if constexpr (CH) {
 #pragma unroll
@@ -716,11 +729,26 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h, int
         }
     };
     if constexpr (!MULTI) {
-        if (!token_wave && T > 0) apply(0);
+        if (state_wave && T > 0) apply(0);
     } else {
         const int rounds = (T + fc - 1) / fc;
         for (int r = 0; r < rounds; ++r) {
-            if (token_wave) {
+            if constexpr (W4) {
+                // wave 0 requests a later round, applies its share of this one,
+                // then waits for the next round's copies
+                if (token_wave) {
+                    if constexpr (RING) {
+                        if (r + 2 < rounds) issue(r + 2);  // buffer (r + 2) % 3, last read by round r - 1
+                    } else {
+                        if (r + 1 < rounds) issue(r + 1);  // buffer (r + 1) % 2, last read by round r - 1
+                    }
+                }
+                apply(r);
+                if (token_wave && r + 1 < rounds) {
+                    if constexpr (RING) ring_wait(r + 1);
+                    else wait_lds_copies();
+                }
+            } else if (token_wave) {
                 if constexpr (RING) {
                     // buffer (r + 2) % 3 was last read by round r - 1
                     if (r + 2 < rounds) issue(r + 2);
@@ -739,7 +767,7 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h, int
     float* dst = materialize ? P.states_out + (static_cast<size_t>(b) * P.H + h) * DK * DV
                              : P.state + (static_cast<size_t>(slot) * P.H + h) * DK * DV;
     if constexpr (!MF) {
-        if (!token_wave) {
+        if (state_wave) {
 #pragma unroll
             for (int j = 0; j < RPT; ++j)
                 __builtin_nontemporal_store(s[j], reinterpret_cast<f4*>(dst + (rg * RPT + j) * DV + c0));
@@ -772,7 +800,7 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h, int
         // past the end of the resource (the range check drops them: they
         // read zeros and touch no memory), so that the registers that receive
         // them are not held across a branch
-        const int past = token_wave ? DK * DV * static_cast<int>(sizeof(float)) : 0;
+        const int past = state_wave ? 0 : DK * DV * static_cast<int>(sizeof(float));
         auto load_rows = [&](int p, f4 (&st)[8]) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
@@ -815,7 +843,7 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h, int
         // the state loads are issued once the first pass's accumulators are
         // in LDS (their registers are free then)
         f4 st0[8], st1[8];
-        if (!token_wave) put(0);
+        if (state_wave) put(0);
         __builtin_amdgcn_sched_barrier(0);
         load_rows(0, st0);
         load_rows(1, st1);
@@ -825,21 +853,21 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h, int
         // make the second pass wait for them too.
         __builtin_amdgcn_s_waitcnt(0x0F70);
         sync();
-        if (!token_wave) finish(0, st0);
+        if (state_wave) finish(0, st0);
         sync();  // the second pass overwrites what the first read
-        if (!token_wave) put(1);
+        if (state_wave) put(1);
         sync();
-        if (!token_wave) finish(1, st1);
+        if (state_wave) finish(1, st1);
     }
     if (token_wave) meta();
 }
 
-// One workgroup per tile.
-template <int RULE, int DK, int DV, typename IO, bool MULTI, bool TREE, bool MFT>
-__global__ __launch_bounds__((Geo<DK, DV>::NTHREADS))
-__attribute__((amdgpu_waves_per_eu(RULE == KVBUF_RULE_DELTA && MULTI ? 4 : 1))) void fold_kernel(TileParams P) {
+// One workgroup per tile (W4: of four waves).
+template <int RULE, int DK, int DV, typename IO, bool MULTI, bool TREE, bool MFT, bool W4 = false>
+__global__ __launch_bounds__((W4 ? Geo<DK, DV>::NT : Geo<DK, DV>::NTHREADS))
+__attribute__((amdgpu_waves_per_eu((RULE == KVBUF_RULE_DELTA && MULTI) || W4 ? 4 : 1))) void fold_kernel(TileParams P) {
     const TileIndex ti = tile_index(P);
-    fold_tile<RULE, DK, DV, IO, MULTI, TREE, MFT>(P, ti.b, ti.h, threadIdx.x);
+    fold_tile<RULE, DK, DV, IO, MULTI, TREE, MFT, W4>(P, ti.b, ti.h, threadIdx.x);
 }
 
 // The flush that follows a decode launch whose eager fold does not fit the
@@ -910,12 +938,18 @@ hipError_t launch_fold_t(const TileParams& p, int batch, hipStream_t s) {
     // multi-round folds always exceed 16 positions (the chunk is at least 16 then)
     const bool multi = most > q.fold_chunk;
     const bool tr = raw && multi && kb == 2;  // staged in whole chunks of 32 rows
+    // rows staged as stored (d = 128, not per-channel), not a tree commit:
+    // four-wave workgroups, whose ring folds of at most two rounds keep two
+    // staging buffers (the kernel lays out LDS the same way)
+    const bool w4 = raw && D == 128 && !tree && !q.sparse;
+    const bool ring = raw && multi && xb == 2;
+    const int nbuf = ring && !(w4 && most <= 2 * kRawFoldChunk) ? kFoldRing : 2;
     const size_t lds = sizeof(float) * fold_lds_floats(D, D, cap,
                                                        fold_stage_area(fold_stage_floats(D, D, tr ? 32 : q.fold_chunk,
                                                                                          kb, xb, raw),
-                                                                       raw && multi && xb == 2 ? kFoldRing : 2,
-                                                                       mf && D == 128),
+                                                                       nbuf, mf && D == 128),
                                                        CH);
+    const dim3 block4(G::NT);
     if (q.sparse) {  // a flush after a decode launch (never a tree commit)
         const dim3 sgrid((static_cast<unsigned>(batch) * q.H + kSparseTiles - 1) / kSparseTiles);
         if (multi) fold_sparse_kernel<RULE, D, D, IO, true, true><<<sgrid, block, lds, s>>>(q);
@@ -923,12 +957,17 @@ hipError_t launch_fold_t(const TileParams& p, int batch, hipStream_t s) {
         else fold_sparse_kernel<RULE, D, D, IO, false, false><<<sgrid, block, lds, s>>>(q);
         return hipGetLastError();
     }
+    constexpr bool W4_OK = D == 128 && !CH;  // instances that can stage rows as stored
     if (multi) {
         if (tree) fold_kernel<RULE, D, D, IO, true, true, true><<<grid, block, lds, s>>>(q);
-        else fold_kernel<RULE, D, D, IO, true, false, true><<<grid, block, lds, s>>>(q);
+        else if (w4) {
+            if constexpr (W4_OK) fold_kernel<RULE, D, D, IO, true, false, true, true><<<grid, block4, lds, s>>>(q);
+        } else fold_kernel<RULE, D, D, IO, true, false, true><<<grid, block, lds, s>>>(q);
     } else if (mf) {
         if (tree) fold_kernel<RULE, D, D, IO, false, true, true><<<grid, block, lds, s>>>(q);
-        else fold_kernel<RULE, D, D, IO, false, false, true><<<grid, block, lds, s>>>(q);
+        else if (w4) {
+            if constexpr (W4_OK) fold_kernel<RULE, D, D, IO, false, false, true, true><<<grid, block4, lds, s>>>(q);
+        } else fold_kernel<RULE, D, D, IO, false, false, true><<<grid, block, lds, s>>>(q);
     } else {
         if (tree) fold_kernel<RULE, D, D, IO, false, true, false><<<grid, block, lds, s>>>(q);
         else fold_kernel<RULE, D, D, IO, false, false, false><<<grid, block, lds, s>>>(q);
