@@ -211,7 +211,9 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h, int
     constexpr bool RAW = MF && !CH;
     // Multi-round folds of bf16 rows keep three staging buffers, the copies of
     // round r + 2 in flight while round r is applied (three buffers of fp32
-    // rows would cost a workgroup per CU).
+    // rows would cost a workgroup per CU); four-wave workgroups keep two, the
+    // copies of round r + 1 in flight (measured: a fourth workgroup per CU
+    // outweighs the deeper ring, 289 against 300 us at m = 128).
     constexpr bool RING = RAW && MULTI && sizeof(XIO) == 2;
     // multi-round folds of bf16 keys: 16 x 16 x 32 products on transposing
     // LDS reads (their wider operands cost a wave per SIMD, which a single
@@ -222,7 +224,7 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h, int
     // ... and then each state wave holds 32 columns of the tile (all rows),
     // so that it splits only its own columns of the pseudo-values
     constexpr bool COLS = TR && !XEXACT;
-    constexpr int NBUF = RING ? kFoldRing : 2;
+    constexpr int NBUF = (RING && !W4) ? kFoldRing : 2;
     static_assert(!W4 || (RAW && !TREE), "four waves: rows staged as stored, no tree commit");
 
     extern __shared__ __attribute__((aligned(16))) float lds[];  // 16-byte rows for the LDS copies
@@ -372,11 +374,7 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h, int
     constexpr int KB = RAW ? static_cast<int>(sizeof(IO)) : 4, XB = RAW ? static_cast<int>(sizeof(XIO)) : 4;
     const int srows = TR ? 32 : fc;  // rows of a staging buffer (TR: a whole product chunk)
     const int stage_floats = fold_stage_floats(DK, DV, srows, KB, XB, RAW);
-    // W4: a ring fold of at most two rounds allocates two staging buffers (the
-    // launcher sizes LDS the same way); round r stays in buffer r % NBUF
-    const int most = materialize ? cap : P.m;  // most positions a tile applies
-    const int nbuf = (W4 && RING && most <= 2 * kRawFoldChunk) ? 2 : NBUF;
-    float* e0p = stage0 + fold_stage_area(stage_floats, nbuf, MF);
+    float* e0p = stage0 + fold_stage_area(stage_floats, NBUF, MF);
 
     TileTokens<DK, DV, IO, XIO> tok;
     tok.kpool = static_cast<const IO*>(P.key);
@@ -737,17 +735,13 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h, int
                 // wave 0 requests a later round, applies its share of this one,
                 // then waits for the next round's copies
                 if (token_wave) {
-                    if constexpr (RING) {
-                        if (r + 2 < rounds) issue(r + 2);  // buffer (r + 2) % 3, last read by round r - 1
-                    } else {
-                        if (r + 1 < rounds) issue(r + 1);  // buffer (r + 1) % 2, last read by round r - 1
-                    }
+                    // buffer (r + 1) % 2 was last read by round r - 1 (the
+                    // ring's round 1 was requested with round 0)
+                    if (r >= (RING ? 1 : 0) && r + 1 < rounds) issue(r + 1);
                 }
                 apply(r);
-                if (token_wave && r + 1 < rounds) {
-                    if constexpr (RING) ring_wait(r + 1);
-                    else wait_lds_copies();
-                }
+                // no later round is in flight: the wait is for everything
+                if (token_wave && r + 1 < rounds) wait_lds_copies();
             } else if (token_wave) {
                 if constexpr (RING) {
                     // buffer (r + 2) % 3 was last read by round r - 1
@@ -939,11 +933,10 @@ hipError_t launch_fold_t(const TileParams& p, int batch, hipStream_t s) {
     const bool multi = most > q.fold_chunk;
     const bool tr = raw && multi && kb == 2;  // staged in whole chunks of 32 rows
     // rows staged as stored (d = 128, not per-channel), not a tree commit:
-    // four-wave workgroups, whose ring folds of at most two rounds keep two
-    // staging buffers (the kernel lays out LDS the same way)
+    // four-wave workgroups, whose rings keep two staging buffers
     const bool w4 = raw && D == 128 && !tree && !q.sparse;
     const bool ring = raw && multi && xb == 2;
-    const int nbuf = ring && !(w4 && most <= 2 * kRawFoldChunk) ? kFoldRing : 2;
+    const int nbuf = ring && !w4 ? kFoldRing : 2;
     const size_t lds = sizeof(float) * fold_lds_floats(D, D, cap,
                                                        fold_stage_area(fold_stage_floats(D, D, tr ? 32 : q.fold_chunk,
                                                                                          kb, xb, raw),
