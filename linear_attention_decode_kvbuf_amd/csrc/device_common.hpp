@@ -372,7 +372,11 @@ __device__ __forceinline__ void stage_rows(const TileTokens<DK, DV, IO, XIO>& to
 // worst; here the LDS rows a copy fills are read only after an explicit wait
 // on the wave's copies (s_waitcnt vmcnt) and, by other waves, after a
 // barrier.  Instructions the compiler does not count only lengthen its own
-// vmcnt waits, never shorten them.  The copy writes no register.
+// vmcnt waits, never shorten them.  The copy writes no register.  It sets
+// m0, which the compiler may not treat as clobbered (it warns so); the
+// compiler's own code for these kernels never uses m0 (none in their
+// generated assembly outside these copies), so nothing it holds there is
+// lost.
 __device__ __forceinline__ uint32_t lds_byte_address(const void* p) {
     return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)(p)));
 }
