@@ -225,7 +225,7 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h, int
     // so that it splits only its own columns of the pseudo-values
     constexpr bool COLS = TR && !XEXACT;
     constexpr int NBUF = (RING && !W4) ? kFoldRing : 2;
-    static_assert(!W4 || (RAW && !TREE), "four waves: rows staged as stored, no tree commit");
+    static_assert(!W4 || (!CH && !TREE && (MF || !MULTI)), "four waves: no per-channel rule, no tree commit");
 
     extern __shared__ __attribute__((aligned(16))) float lds[];  // 16-byte rows for the LDS copies
     __shared__ unsigned s_bad;
@@ -482,7 +482,13 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h, int
         __builtin_amdgcn_sched_barrier(0);
     };
 
+    f4 s[RPT];
+    const int mw = tid >> 6, ml = tid & 63;  // MF: wave and lane
+    const float* tile = has_state ? P.state + (static_cast<size_t>(slot) * P.H + h) * DK * DV : P.state;
     if (token_wave) {
+        // four waves, vector-ALU fold: wave 0 requests its share of the tile
+        // before it stages the rows, both in flight together
+        if constexpr (W4 && !MF) load_tile<RPT, DK, DV>(s, tile, has_state, rg, c0);
         if constexpr (RAW) {
             // The first rounds' copies need only the position table: requested
             // before the gates, both are in flight in the same round trip.
@@ -525,9 +531,6 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h, int
         }
         if (tree && !MULTI) move_kept();  // the fold's rows are staged
     }
-    f4 s[RPT];
-    const int mw = tid >> 6, ml = tid & 63;  // MF: wave and lane
-    const float* tile = has_state ? P.state + (static_cast<size_t>(slot) * P.H + h) * DK * DV : P.state;
     if (state_wave) {
         if constexpr (MF) {
             // the matrix cores accumulate the update alone, from zero; the
@@ -535,7 +538,7 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h, int
             static_assert(RPT == 16, "16 blocks of 16 x 16 per wave");
 #pragma unroll
             for (int j = 0; j < RPT; ++j) s[j] = f4{0.0f, 0.0f, 0.0f, 0.0f};
-        } else {
+        } else if (!(W4 && token_wave)) {
             load_tile<RPT, DK, DV>(s, tile, has_state, rg, c0);
         }
     }
@@ -950,7 +953,7 @@ hipError_t launch_fold_t(const TileParams& p, int batch, hipStream_t s) {
         else fold_sparse_kernel<RULE, D, D, IO, false, false><<<sgrid, block, lds, s>>>(q);
         return hipGetLastError();
     }
-    constexpr bool W4_OK = D == 128 && !CH;  // instances that can stage rows as stored
+    constexpr bool W4_OK = D == 128 && !CH;  // instances with a four-wave form
     if (multi) {
         if (tree) fold_kernel<RULE, D, D, IO, true, true, true><<<grid, block, lds, s>>>(q);
         else if (w4) {
@@ -962,8 +965,15 @@ hipError_t launch_fold_t(const TileParams& p, int batch, hipStream_t s) {
             if constexpr (W4_OK) fold_kernel<RULE, D, D, IO, false, false, true, true><<<grid, block4, lds, s>>>(q);
         } else fold_kernel<RULE, D, D, IO, false, false, true><<<grid, block, lds, s>>>(q);
     } else {
+        // vector-ALU folds (at most 16 positions, one round) of d = 128: a
+        // commit runs four waves (most of its tiles only advance their
+        // metadata, and more workgroups per CU hide that chain: 66 -> 62 us at
+        // eight drafts); a flush, whose every tile streams its state, stays on
+        // five (four measured 3% slower)
         if (tree) fold_kernel<RULE, D, D, IO, false, true, false><<<grid, block, lds, s>>>(q);
-        else fold_kernel<RULE, D, D, IO, false, false, false><<<grid, block, lds, s>>>(q);
+        else if (D == 128 && !CH && q.mode == MODE_COMMIT) {
+            if constexpr (W4_OK) fold_kernel<RULE, D, D, IO, false, false, false, true><<<grid, block4, lds, s>>>(q);
+        } else fold_kernel<RULE, D, D, IO, false, false, false><<<grid, block, lds, s>>>(q);
     }
     return hipGetLastError();
 }
