@@ -225,7 +225,7 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h, int
     // so that it splits only its own columns of the pseudo-values
     constexpr bool COLS = TR && !XEXACT;
     constexpr int NBUF = (RING && !W4) ? kFoldRing : 2;
-    static_assert(!W4 || (!CH && !TREE && (MF || !MULTI)), "four waves: no per-channel rule, no tree commit");
+    static_assert(!W4 || (!CH && (MF || !MULTI)), "four waves: not the per-channel rule");
 
     extern __shared__ __attribute__((aligned(16))) float lds[];  // 16-byte rows for the LDS copies
     __shared__ unsigned s_bad;
@@ -935,9 +935,9 @@ hipError_t launch_fold_t(const TileParams& p, int batch, hipStream_t s) {
     // multi-round folds always exceed 16 positions (the chunk is at least 16 then)
     const bool multi = most > q.fold_chunk;
     const bool tr = raw && multi && kb == 2;  // staged in whole chunks of 32 rows
-    // rows staged as stored (d = 128, not per-channel), not a tree commit:
-    // four-wave workgroups, whose rings keep two staging buffers
-    const bool w4 = raw && D == 128 && !tree && !q.sparse;
+    // rows staged as stored (d = 128, not per-channel): four-wave workgroups,
+    // whose rings keep two staging buffers
+    const bool w4 = raw && D == 128 && !q.sparse;
     const bool ring = raw && multi && xb == 2;
     const int nbuf = ring && !w4 ? kFoldRing : 2;
     const size_t lds = sizeof(float) * fold_lds_floats(D, D, cap,
@@ -955,25 +955,34 @@ hipError_t launch_fold_t(const TileParams& p, int batch, hipStream_t s) {
     }
     constexpr bool W4_OK = D == 128 && !CH;  // instances with a four-wave form
     if (multi) {
-        if (tree) fold_kernel<RULE, D, D, IO, true, true, true><<<grid, block, lds, s>>>(q);
-        else if (w4) {
-            if constexpr (W4_OK) fold_kernel<RULE, D, D, IO, true, false, true, true><<<grid, block4, lds, s>>>(q);
-        } else fold_kernel<RULE, D, D, IO, true, false, true><<<grid, block, lds, s>>>(q);
+        if (w4) {
+            if constexpr (W4_OK) {
+                if (tree) fold_kernel<RULE, D, D, IO, true, true, true, true><<<grid, block4, lds, s>>>(q);
+                else fold_kernel<RULE, D, D, IO, true, false, true, true><<<grid, block4, lds, s>>>(q);
+            }
+        } else if (tree) fold_kernel<RULE, D, D, IO, true, true, true><<<grid, block, lds, s>>>(q);
+        else fold_kernel<RULE, D, D, IO, true, false, true><<<grid, block, lds, s>>>(q);
     } else if (mf) {
-        if (tree) fold_kernel<RULE, D, D, IO, false, true, true><<<grid, block, lds, s>>>(q);
-        else if (w4) {
-            if constexpr (W4_OK) fold_kernel<RULE, D, D, IO, false, false, true, true><<<grid, block4, lds, s>>>(q);
-        } else fold_kernel<RULE, D, D, IO, false, false, true><<<grid, block, lds, s>>>(q);
+        if (w4) {
+            if constexpr (W4_OK) {
+                if (tree) fold_kernel<RULE, D, D, IO, false, true, true, true><<<grid, block4, lds, s>>>(q);
+                else fold_kernel<RULE, D, D, IO, false, false, true, true><<<grid, block4, lds, s>>>(q);
+            }
+        } else if (tree) fold_kernel<RULE, D, D, IO, false, true, true><<<grid, block, lds, s>>>(q);
+        else fold_kernel<RULE, D, D, IO, false, false, true><<<grid, block, lds, s>>>(q);
     } else {
         // vector-ALU folds (at most 16 positions, one round) of d = 128: a
         // commit runs four waves (most of its tiles only advance their
         // metadata, and more workgroups per CU hide that chain: 66 -> 62 us at
         // eight drafts); a flush, whose every tile streams its state, stays on
         // five (four measured 3% slower)
-        if (tree) fold_kernel<RULE, D, D, IO, false, true, false><<<grid, block, lds, s>>>(q);
-        else if (D == 128 && !CH && q.mode == MODE_COMMIT) {
-            if constexpr (W4_OK) fold_kernel<RULE, D, D, IO, false, false, false, true><<<grid, block4, lds, s>>>(q);
-        } else fold_kernel<RULE, D, D, IO, false, false, false><<<grid, block, lds, s>>>(q);
+        if (D == 128 && !CH && q.mode == MODE_COMMIT) {
+            if constexpr (W4_OK) {
+                if (tree) fold_kernel<RULE, D, D, IO, false, true, false, true><<<grid, block4, lds, s>>>(q);
+                else fold_kernel<RULE, D, D, IO, false, false, false, true><<<grid, block4, lds, s>>>(q);
+            }
+        } else if (tree) fold_kernel<RULE, D, D, IO, false, true, false><<<grid, block, lds, s>>>(q);
+        else fold_kernel<RULE, D, D, IO, false, false, false><<<grid, block, lds, s>>>(q);
     }
     return hipGetLastError();
 }
