@@ -138,7 +138,8 @@ kvbuf_status chunk_call(const kvbuf_layout* layout, const kvbuf_pools* pools,
     const bool eager_decode = mode == kvbuf::MODE_DECODE && t.fuse && layout->m > 0;
     const bool fused = eager_decode &&
                        layout->m <= kvbuf::chunk_fold_limit(layout->rule, layout->d_k, layout->io_dtype, n,
-                                                            layout->block_size * layout->blocks_per_req);
+                                                            layout->block_size * layout->blocks_per_req, layout->m,
+                                                            static_cast<int64_t>(batch->size) * layout->num_heads);
     t.fold_chunk = fused ? layout->m : 0;
     t.q = q;
     t.k = k;

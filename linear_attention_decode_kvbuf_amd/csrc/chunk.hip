@@ -773,8 +773,8 @@ hipError_t launch_chunk_r(const TileParams& p, int rule, int d, int batch, hipSt
 // The eager fold happens inside the decode launch when its m tokens fit what
 // that kernel stages (the one-token kernel: an LDS budget; this kernel: the
 // first staging pass of NT / 16 positions); otherwise a fold launch follows.
-int chunk_fold_limit(int rule, int d, int io, int n, int cap) {
-    if (decode_eligible(rule, n, cap)) return decode_fold_limit(rule, d, io);
+int chunk_fold_limit(int rule, int d, int io, int n, int cap, int m, int64_t tiles) {
+    if (decode_eligible(rule, d, io, n, cap, m, tiles)) return decode_fold_limit(rule, d, io);
     if (rule == KVBUF_RULE_CHANNEL) return 0;  // the per-channel kernel never folds
     switch (d) {
         case 16: return Geo<16, 16>::NT / 16;
@@ -786,7 +786,8 @@ int chunk_fold_limit(int rule, int d, int io, int n, int cap) {
 hipError_t launch_chunk(const TileParams& p, int rule, int d, int io, int batch, hipStream_t s) {
     // (kvbuf_direct has a kernel of its own; requests without a state inside
     // a decode or verify launch are served here or by the one-token kernel.)
-    if (!p.parent && decode_eligible(rule, p.n, p.block_size * p.blocks_per_req))
+    if (!p.parent && decode_eligible(rule, d, io, p.n, p.block_size * p.blocks_per_req, p.m,
+                                     static_cast<int64_t>(batch) * p.H))
         return launch_decode(p, rule, d, io, batch, s);
     if (rule == KVBUF_RULE_CHANNEL) return launch_channel(p, d, io, batch, s);
     return io == KVBUF_BF16 ? launch_chunk_r<bf16_bits>(p, rule, d, batch, s)

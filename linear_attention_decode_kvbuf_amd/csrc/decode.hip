@@ -450,8 +450,18 @@ int decode_fold_limit(int rule, int d, int io) {
     return 32768 / bytes_per_pos;
 }
 
-bool decode_eligible(int rule, int n, int cap) {
-    return rule != KVBUF_RULE_DELTA && n == 1 && cap <= 64;
+bool decode_eligible(int rule, int d, int io, int n, int cap, int m, int64_t tiles) {
+    if (rule == KVBUF_RULE_DELTA || n != 1 || cap > 64) return false;
+    if (rule == KVBUF_RULE_CHANNEL) return true;
+    // A launch of a few workgroup generations (d = 128, bf16) goes to the
+    // chunk kernel when it folds there too (m within its first staging pass).
+    // This kernel's five-wave workgroups are placed three to a CU, the chunk
+    // kernel's four-wave ones four (registers), which decides the last,
+    // partial generation.  Measured, B * H = 1024 / 2048 tiles: 0.71 / 0.70
+    // of the HBM peak against 0.63 / 0.67 here; 4096 and 8192 tiles: the same
+    // within 0.1%.
+    const bool few = d == 128 && io == KVBUF_BF16 && tiles <= kFewTiles && m <= Geo<128, 128>::NT / 16;
+    return !few;
 }
 
 hipError_t launch_decode(const TileParams& p, int rule, int d, int io, int batch, hipStream_t s) {

@@ -56,10 +56,12 @@ struct TileParams {
 // launch_chunk serves decode and verify; one-token calls with table rows of
 // at most 64 positions (decode and one-draft verify of the linear, gated and
 // per-channel rules) go to the split-role kernel (launch_decode), the rest to
-// the general chunk kernel.
+// the general chunk kernel.  Exception: launches of at most kFewTiles tiles
+// at d = 128, bf16, whose m the chunk kernel folds itself (decode_eligible).
 hipError_t launch_chunk(const TileParams& p, int rule, int d, int io, int batch, hipStream_t s);
 hipError_t launch_decode(const TileParams& p, int rule, int d, int io, int batch, hipStream_t s);
-bool decode_eligible(int rule, int n, int cap);
+constexpr int64_t kFewTiles = 4096;
+bool decode_eligible(int rule, int d, int io, int n, int cap, int m, int64_t tiles);
 int decode_fold_limit(int rule, int d, int io);
 hipError_t launch_fold(const TileParams& p, int rule, int d, int io, int batch, hipStream_t s);
 // Per-channel rule: decode over rows of more than 64 positions, verify of
@@ -71,8 +73,9 @@ hipError_t launch_admit(const TileParams& p, const int32_t* requests, int count,
 hipError_t launch_check(const TileParams& p, hipStream_t s);
 // Buffer-only decode (kvbuf_direct), every rule: one wave per tile.
 hipError_t launch_direct(const TileParams& p, int rule, int d, int io, int batch, hipStream_t s);
-// Largest m that a decode launch of n tokens folds itself (eager policy).
-int chunk_fold_limit(int rule, int d, int io, int n, int cap);
+// Largest m that a decode launch of n tokens over `tiles` tiles folds itself
+// (eager policy).
+int chunk_fold_limit(int rule, int d, int io, int n, int cap, int m, int64_t tiles);
 hipError_t launch_recurrent(const TileParams& p, int rule, int d, int io, int batch, hipStream_t s);
 // Verification with temporary states (m = 0) and its commit, temp
 // [n][B][H][d][d] fp32.

@@ -493,8 +493,12 @@ def _full_cycle_checks(run):
          % (run.max_out, run.max_state, run.folds_checked))
 
 
-def test_workload2_ungated_batched():
-    w = synth.workload(2)
+@pytest.mark.parametrize("B", [64, 160])
+def test_workload2_ungated_batched(B):
+    """The ungated workload (B = 64: 2048 tiles, served by the chunk kernel)
+    and the same at B = 160 (5120 tiles, above the launch size the chunk
+    kernel takes: the one-token kernel)."""
+    w = synth.workload(2, B=B)
     _say("workload 2", w)
     run = Run(w)
     for t in range(w.steps):
