@@ -493,6 +493,25 @@ def _full_cycle_checks(run):
          % (run.max_out, run.max_state, run.folds_checked))
 
 
+@pytest.mark.parametrize("B,m", [(4096, 8), (4097, 8), (4096, 32), (4096, 16)])
+def test_decode_kernel_choice_boundary(B, m):
+    """One-token decode at d = 128, bf16, one head per request, around the
+    launch size at which the chunk kernel stops taking it (4096 tiles, when m
+    fits that kernel's first staging pass of 16 positions): each side folds
+    in the decode launch, and m = 32 stays on the one-token kernel, whose
+    fused fold covers it."""
+    w = synth.workload(3, B=B, H=1, m=m, block_size=m, blocks_per_req=2, steps=m + 3)
+    _say("kernel choice boundary", w)
+    run = Run(w)
+    for t in range(w.steps):
+        run.decode(t)
+    run.check_effective_states()
+    run.check_pool()
+    run.check_bookkeeping()
+    assert run.folds_checked == B
+    _say("max out err %.2e, max state err %.2e" % (run.max_out, run.max_state))
+
+
 @pytest.mark.parametrize("B", [64, 160])
 def test_workload2_ungated_batched(B):
     """The ungated workload (B = 64: 2048 tiles, served by the chunk kernel)
