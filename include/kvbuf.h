@@ -71,7 +71,9 @@ typedef enum kvbuf_dtype {
 
 typedef enum kvbuf_flush_policy {
     /* kvbuf_decode and kvbuf_commit fold a request's buffer into its state in
-     * the same kernel as soon as it holds m tokens. */
+     * the same call as soon as it holds m tokens (kvbuf_commit and, for the
+     * usual m, kvbuf_decode in the same kernel; a decode whose m exceeds what
+     * its kernel stages enqueues a fold launch right after it). */
     KVBUF_FLUSH_EAGER = 0,
     /* they only append; the caller folds with kvbuf_flush. */
     KVBUF_FLUSH_DEFERRED = 1
@@ -187,7 +189,8 @@ kvbuf_status kvbuf_check(const kvbuf_layout* layout, const kvbuf_batch* batch, h
  *         the occupancy.  A request with a state slot computes its output from the
  *         state at its last fold plus the buffer; one without (slot -1) from
  *         the buffer alone.  With KVBUF_FLUSH_EAGER a request with a state
- *         whose buffer reaches m folds in the same kernel.
+ *         whose buffer reaches m folds in the same call (see
+ *         KVBUF_FLUSH_EAGER).
  * m = 0:  recurrent: reads, updates and writes back every request's state.
  */
 kvbuf_status kvbuf_decode(const kvbuf_layout* layout, const kvbuf_pools* pools,
