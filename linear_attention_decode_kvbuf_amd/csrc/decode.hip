@@ -63,8 +63,13 @@ __host__ __device__ inline DecodeLds decode_lds(int DK, int DV, int RG, int mf, 
     return L;
 }
 
+// bf16, d = 128, scalar or no gates: at most 80 registers, six waves per SIMD,
+// so that a CU places four of these five-wave workgroups (each needs room for
+// two of its waves on every SIMD) instead of three.
 template <int RULE, int DK, int DV, typename IO>
-__global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void decode_kernel(TileParams P) {
+__global__ __launch_bounds__((Geo<DK, DV>::NTHREADS))
+__attribute__((amdgpu_waves_per_eu(DK == 128 && RULE != KVBUF_RULE_CHANNEL && sizeof(IO) == 2 ? 6 : 1)))
+void decode_kernel(TileParams P) {
     using G = Geo<DK, DV>;
     constexpr int NT = G::NT, TPR = G::TPR, RG = G::RG, RPT = G::RPT;
     constexpr int E = DK / 16, EV = DV / 16;
@@ -136,6 +141,7 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void decode_kernel(TilePar
         const uint32_t bi = static_cast<uint32_t>(__shfl(blk, qb, 64));
         const uint32_t prow = (bi * static_cast<uint32_t>(P.H) + static_cast<uint32_t>(h)) *
                                   static_cast<uint32_t>(bs) + static_cast<uint32_t>(lane - qb * bs);
+        s_blk[lane] = blk;  // the table row as read, for the metadata update at the end
 
         const int gl = lane >> 4;  // position slot of the lane in a round
         const int cl = lane & 15;  // its 1/16 of a row
@@ -218,9 +224,9 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void decode_kernel(TilePar
         }
 
         // cumulative log-gates b_i of positions 0 .. T-1, lane i holds b_i
-        const float graw = g;  // the new token's log-gate in lane pc, appended below
         float bcum = 0.0f;
         if constexpr (GATED) {
+            if (lane == pc) s_ag = g;  // the new token's log-gate, appended after the barrier
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
                 const float y = __shfl_up(g, off, 64);
@@ -284,11 +290,12 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void decode_kernel(TilePar
             ob[e] += __shfl_xor(ob[e], 32, 64);
         }
         if (gl == 0) {
+            // the columns from an opaque copy of the lane: formed here, not
+            // kept in a register through the rounds
+            int el = lane;
+            asm volatile("" : "+v"(el));
 #pragma unroll
-            for (int e = 0; e < EV; ++e) obuf[cl * EV + e] = ob[e];
-        }
-        if constexpr (GATED) {
-            if (lane == pc) s_ag = graw;
+            for (int e = 0; e < EV; ++e) obuf[(el & 15) * EV + e] = ob[e];
         }
         if constexpr (CH) {  // the new token's gate row
 #pragma unroll
@@ -308,8 +315,7 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void decode_kernel(TilePar
             s_es = GATED ? exp_gate(bt) : 1.0f;
         }
         // this wave read the tile's metadata above; it advances it in place
-        // after the barrier
-        s_blk[lane] = blk;
+        // after the barrier (the table row is in s_blk)
         if (lane == 0) {
             s_pnew = fold ? Tl - P.m : Tl;
             s_rot = fold ? P.m / bs : 0;
@@ -325,11 +331,9 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void decode_kernel(TilePar
         load_tile<RPT, DK, DV>(s, present ? P.state + (static_cast<size_t>(slot) * P.H + h) * DK * DV : P.state,
                                present, rg, c0);
         if constexpr (!CH) {
-            float qf[RPT];
-            qrow.to_float(qf);
             f4 sa = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int j = 0; j < RPT; ++j) sa += s[j] * qf[j];
+            for (int j = 0; j < RPT; ++j) sa += s[j] * qrow.at(j);
             *reinterpret_cast<f4*>(red + rg * DV + c0) = sa;
         }
     }
@@ -404,20 +408,24 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void decode_kernel(TilePar
 #pragma unroll
             for (int j = 0; j < RPT; ++j) s[j] *= e0;
             for (int ii = 0; ii < P.m; ++ii) {
-                const f4 x = load4(vrs + ii * DV + c0);
+                // the weight goes with the value (4 products, not 16); the
+                // keys are widened one at a time as they are used
+                const f4 wx = fw[ii] * load4(vrs + ii * DV + c0);
                 RawChunk<IO, RPT> krow;
-                float kf[RPT];
                 krow.load(krs + ii * DK + rg * RPT);
-                krow.to_float(kf);
-                const float w = fw[ii];
 #pragma unroll
-                for (int j = 0; j < RPT; ++j) s[j] += (w * kf[j]) * x;
+                for (int j = 0; j < RPT; ++j) s[j] += krow.at(j) * wx;
             }
         }
         float* wt = P.state + (static_cast<size_t>(slot) * P.H + h) * DK * DV;
+        // the thread's rows and columns from an opaque copy of its index:
+        // formed here, not kept in registers through the kernel
+        int et = tid;
+        asm volatile("" : "+v"(et));
+        const int rgs = et / TPR, cs = (et % TPR) * 4;
 #pragma unroll
         for (int j = 0; j < RPT; ++j)
-            __builtin_nontemporal_store(s[j], reinterpret_cast<f4*>(wt + (rg * RPT + j) * DV + c0));
+            __builtin_nontemporal_store(s[j], reinterpret_cast<f4*>(wt + (rgs * RPT + j) * DV + cs));
     }
 }
 

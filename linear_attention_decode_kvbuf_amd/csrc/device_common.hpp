@@ -155,6 +155,12 @@ struct RawChunk {
             *reinterpret_cast<uint16_t*>(p) = static_cast<uint16_t>(w[0]);
         }
     }
+    // element i as fp32 (i a compile-time index after unrolling)
+    __device__ __forceinline__ float at(int i) const {
+        if constexpr (sizeof(T) == 4) return __uint_as_float(w[i]);
+        else if constexpr (E == 1) return __uint_as_float(w[0] << 16);
+        else return (i & 1) ? __uint_as_float(w[i / 2] & 0xffff0000u) : __uint_as_float(w[i / 2] << 16);
+    }
     __device__ __forceinline__ void to_float(float (&o)[E]) const {
         if constexpr (sizeof(T) == 4) {
 #pragma unroll
