@@ -463,11 +463,10 @@ bool decode_eligible(int rule, int d, int io, int n, int cap, int m, int64_t til
     if (rule == KVBUF_RULE_CHANNEL) return true;
     // A launch of a few workgroup generations (d = 128, bf16) goes to the
     // chunk kernel when it folds there too (m within its first staging pass).
-    // This kernel's five-wave workgroups are placed three to a CU, the chunk
-    // kernel's four-wave ones four (registers), which decides the last,
-    // partial generation.  Measured, B * H = 1024 / 2048 tiles: 0.71 / 0.70
-    // of the HBM peak against 0.63 / 0.67 here; 4096 and 8192 tiles: the same
-    // within 0.1%.
+    // Both kernels hold four tiles per CU; at these sizes the last, partial
+    // generation decides, and the chunk kernel's is as short or shorter.
+    // Measured, B * H = 1024 / 2048 tiles: 0.698 / 0.695 of the HBM peak
+    // against 0.700 / 0.689 here.
     const bool few = d == 128 && io == KVBUF_BF16 && tiles <= kFewTiles && m <= Geo<128, 128>::NT / 16;
     return !few;
 }
