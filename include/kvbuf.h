@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define KVBUF_ABI_VERSION 4
+#define KVBUF_ABI_VERSION 5
 
 typedef enum kvbuf_status {
     KVBUF_OK = 0,
@@ -68,6 +68,16 @@ typedef enum kvbuf_dtype {
     KVBUF_BF16 = 0,
     KVBUF_F32 = 1
 } kvbuf_dtype;
+
+/* Element type of the outputs (`out` of kvbuf_decode, kvbuf_direct,
+ * kvbuf_verify, kvbuf_verify_tree and kvbuf_verify_recurrent).  The sums are
+ * formed in fp32 either way; KVBUF_OUT_BF16 rounds each output to the
+ * nearest bf16 (ties to even) when it is stored.  Zero, the value of a
+ * zero-initialised layout, is fp32. */
+typedef enum kvbuf_out_dtype {
+    KVBUF_OUT_F32 = 0,
+    KVBUF_OUT_BF16 = 1
+} kvbuf_out_dtype;
 
 typedef enum kvbuf_flush_policy {
     /* kvbuf_decode and kvbuf_commit fold a request's buffer into its state in
@@ -103,6 +113,7 @@ typedef struct kvbuf_layout {
                                 (and of its value plane for the linear and gated rules) */
     int32_t flush;           /* kvbuf_flush_policy */
     float scale;             /* queries are multiplied by it (1.0 = none) */
+    int32_t out_dtype;       /* kvbuf_out_dtype of every `out` argument */
 } kvbuf_layout;
 
 /* Device memory pools (caller-owned, row-major):
@@ -183,7 +194,7 @@ kvbuf_status kvbuf_check(const kvbuf_layout* layout, const kvbuf_batch* batch, h
  * Inputs  q, k [B][H][d_k] and v [B][H][d_v] in io_dtype; g [B][H] fp32
  *         log-gates (rules GATED, DELTA; [B][H][d_k] for CHANNEL; NULL for
  *         LINEAR); beta [B][H] fp32 (DELTA; else NULL).
- * Output  out [B][H][d_v] fp32, o = S_t^T (scale q) with S_t the state after
+ * Output  out [B][H][d_v] (layout->out_dtype), o = S_t^T (scale q) with S_t the state after
  *         this token.
  * m > 0:  appends the token at buffer position occupancy[b] and advances
  *         the occupancy.  A request with a state slot computes its output from the
@@ -195,7 +206,7 @@ kvbuf_status kvbuf_check(const kvbuf_layout* layout, const kvbuf_batch* batch, h
  */
 kvbuf_status kvbuf_decode(const kvbuf_layout* layout, const kvbuf_pools* pools,
                           const kvbuf_batch* batch, const void* q, const void* k,
-                          const void* v, const float* g, const float* beta, float* out,
+                          const void* v, const float* g, const float* beta, void* out,
                           hipStream_t stream);
 
 /*
@@ -214,7 +225,7 @@ kvbuf_status kvbuf_flush(const kvbuf_layout* layout, const kvbuf_pools* pools,
  * together, without a temporary state per draft).
  * Inputs  q, k [B][n][H][d_k], v [B][n][H][d_v] (io_dtype); g, beta [B][n][H]
  *         (g [B][n][H][d_k] for the per-channel rule).
- * Output  out [B][n][H][d_v] fp32: draft d attends to the state, the buffer and
+ * Output  out [B][n][H][d_v] (layout->out_dtype): draft d attends to the state, the buffer and
  *         drafts 0..d (causal within the drafts).
  * The drafts are written at buffer positions occupancy .. occupancy+n-1; the
  * occupancy does not change.  Requires m > 0 and 1 <= n <= 8.
@@ -222,7 +233,7 @@ kvbuf_status kvbuf_flush(const kvbuf_layout* layout, const kvbuf_pools* pools,
 kvbuf_status kvbuf_verify(const kvbuf_layout* layout, const kvbuf_pools* pools,
                           const kvbuf_batch* batch, int32_t n, const void* q,
                           const void* k, const void* v, const float* g,
-                          const float* beta, float* out, hipStream_t stream);
+                          const float* beta, void* out, hipStream_t stream);
 
 /*
  * kvbuf_commit -- keep the first accepted[b] (0..n) drafts of the preceding
@@ -250,7 +261,7 @@ kvbuf_status kvbuf_commit(const kvbuf_layout* layout, const kvbuf_pools* pools,
 kvbuf_status kvbuf_verify_tree(const kvbuf_layout* layout, const kvbuf_pools* pools,
                                const kvbuf_batch* batch, int32_t n, const int32_t* parent,
                                const void* q, const void* k, const void* v, const float* g,
-                               const float* beta, float* out, hipStream_t stream);
+                               const float* beta, void* out, hipStream_t stream);
 
 /*
  * kvbuf_commit_tree -- keep the drafts on the path from the root to leaf[b]
@@ -270,7 +281,7 @@ kvbuf_status kvbuf_commit_tree(const kvbuf_layout* layout, const kvbuf_pools* po
  * recurrent form and keeps a temporary state for every draft).  Recurrent
  * mode only (m = 0).  For every request, drafts 0..n-1 are applied one at a
  * time to a copy of its state: draft d's output goes to out [B][n][H][d_v]
- * fp32 and the state after draft d to temp [n][B][H][d_k][d_v] fp32
+ * (layout->out_dtype) and the state after draft d to temp [n][B][H][d_k][d_v] fp32
  * (caller-owned device memory, n states per request).  The state pool is not
  * modified.  Inputs as kvbuf_verify.  Requires 1 <= n <= 8; a request
  * without a valid state slot sets KVBUF_DEVERR_SLOT and is skipped.
@@ -278,7 +289,7 @@ kvbuf_status kvbuf_commit_tree(const kvbuf_layout* layout, const kvbuf_pools* po
 kvbuf_status kvbuf_verify_recurrent(const kvbuf_layout* layout, const kvbuf_pools* pools,
                                     const kvbuf_batch* batch, int32_t n, const void* q,
                                     const void* k, const void* v, const float* g,
-                                    const float* beta, float* out, float* temp,
+                                    const float* beta, void* out, float* temp,
                                     hipStream_t stream);
 
 /*
@@ -302,7 +313,7 @@ kvbuf_status kvbuf_commit_recurrent(const kvbuf_layout* layout, const kvbuf_pool
  */
 kvbuf_status kvbuf_direct(const kvbuf_layout* layout, const kvbuf_pools* pools,
                           const kvbuf_batch* batch, const void* q, const void* k,
-                          const void* v, const float* g, const float* beta, float* out,
+                          const void* v, const float* g, const float* beta, void* out,
                           hipStream_t stream);
 
 /*

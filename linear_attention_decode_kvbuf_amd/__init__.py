@@ -22,6 +22,7 @@ LIB_PATH = os.path.join(_HERE, "libkvbuf.so")
 RULE_LINEAR, RULE_GATED, RULE_DELTA, RULE_CHANNEL = 0, 1, 2, 3
 BF16, F32 = 0, 1
 FLUSH_EAGER, FLUSH_DEFERRED = 0, 1
+OUT_F32, OUT_BF16 = 0, 1
 
 OK, EINVAL, EUNSUPPORTED, ECAPACITY, EHIP = 0, -1, -2, -3, -4
 DEVERR_BLOCK, DEVERR_SLOT, DEVERR_OVERFLOW, DEVERR_ACCEPT, DEVERR_META = 1, 2, 4, 8, 16
@@ -36,7 +37,8 @@ class Layout(ctypes.Structure):
                 ("m", ctypes.c_int32), ("block_size", ctypes.c_int32),
                 ("blocks_per_req", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
                 ("num_state_slots", ctypes.c_int32), ("rule", ctypes.c_int32),
-                ("io_dtype", ctypes.c_int32), ("flush", ctypes.c_int32), ("scale", ctypes.c_float)]
+                ("io_dtype", ctypes.c_int32), ("flush", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("out_dtype", ctypes.c_int32)]
 
 
 class Pools(ctypes.Structure):
@@ -221,7 +223,7 @@ class KVBuffer:
 
     def __init__(self, *, batch, heads, d, m, block_size=None, blocks_per_req=2, num_blocks=None,
                  num_state_slots=None, rule=RULE_GATED, io_dtype=BF16, flush=FLUSH_EAGER,
-                 scale=1.0, device="cuda"):
+                 scale=1.0, out_dtype=OUT_F32, device="cuda"):
         import torch
 
         load()
@@ -230,11 +232,12 @@ class KVBuffer:
         num_blocks = num_blocks if num_blocks is not None else batch * blocks_per_req
         num_state_slots = num_state_slots if num_state_slots is not None else batch
         self.layout = Layout(heads, d, d, m, block_size, blocks_per_req, num_blocks,
-                             num_state_slots, rule, io_dtype, flush, float(scale))
+                             num_state_slots, rule, io_dtype, flush, float(scale), out_dtype)
         self.B, self.H, self.d, self.m = batch, heads, d, m
         self.rule, self.io_dtype = rule, io_dtype
         io = torch.bfloat16 if io_dtype == BF16 else torch.float32
         self.io_torch = io
+        self.out_torch = torch.bfloat16 if out_dtype == OUT_BF16 else torch.float32
         dev = torch.device(device)
         self.state = torch.zeros((max(num_state_slots, 1), heads, d, d), dtype=torch.float32, device=dev)
         if m > 0:
@@ -326,8 +329,8 @@ class KVBuffer:
 
     def _tokens(self, lead, q, k, v, g, beta, out):
         """Checks q, k, v [*lead, H, d] (io dtype), g / beta [*lead, H] fp32
-        (g [*lead, H, d] for the per-channel rule) and out [*lead, H, d] fp32;
-        allocates out when it is None."""
+        (g [*lead, H, d] for the per-channel rule) and out [*lead, H, d] (the
+        layout's output dtype); allocates out when it is None."""
         H, d, f32 = self.H, self.d, self.torch.float32
         for name, x in (("q", q), ("k", k), ("v", v)):
             self._need(x, name, lead + (H, d), self.io_torch)
@@ -341,8 +344,8 @@ class KVBuffer:
         else:
             beta = None
         if out is None:
-            out = self.torch.empty(lead + (H, d), dtype=f32, device=self.state.device)
-        self._need(out, "out", lead + (H, d), f32)
+            out = self.torch.empty(lead + (H, d), dtype=self.out_torch, device=self.state.device)
+        self._need(out, "out", lead + (H, d), self.out_torch)
         return g, beta, out
 
     def _drafts(self, q):

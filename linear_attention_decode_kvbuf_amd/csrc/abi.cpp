@@ -20,6 +20,7 @@ kvbuf_status check_layout(const kvbuf_layout* L, bool need_buffer) {
     if (L->flush != KVBUF_FLUSH_EAGER && L->flush != KVBUF_FLUSH_DEFERRED) return KVBUF_EINVAL;
     if (L->d_k != L->d_v || !kvbuf::supported_dim(L->d_k)) return KVBUF_EUNSUPPORTED;
     if (!(L->scale == L->scale)) return KVBUF_EINVAL;  // NaN scale
+    if (L->out_dtype != KVBUF_OUT_F32 && L->out_dtype != KVBUF_OUT_BF16) return KVBUF_EINVAL;
     if (need_buffer && L->m == 0) return KVBUF_EUNSUPPORTED;
     if (L->m > 0) {
         if (L->block_size <= 0 || L->blocks_per_req <= 0 || L->num_blocks <= 0) return KVBUF_EINVAL;
@@ -61,7 +62,7 @@ kvbuf_status check_pools(const kvbuf_layout* L, const kvbuf_pools* P, bool need_
 }
 
 kvbuf_status check_tokens(const kvbuf_layout* L, const void* q, const void* k, const void* v,
-                          const float* g, const float* beta, const float* out) {
+                          const float* g, const float* beta, const void* out) {
     if (!q || !k || !v || !out) return KVBUF_EINVAL;
     if (L->rule != KVBUF_RULE_LINEAR && !g) return KVBUF_EINVAL;
     if (L->rule == KVBUF_RULE_DELTA && !beta) return KVBUF_EINVAL;
@@ -79,6 +80,7 @@ TileParams make_params(const kvbuf_layout* L, const kvbuf_pools* P, const kvbuf_
     t.num_slots = L->num_state_slots;
     t.fuse = L->flush == KVBUF_FLUSH_EAGER;
     t.scale = L->scale;
+    t.out_bf16 = L->out_dtype == KVBUF_OUT_BF16;
     t.state = P->state;
     t.key = P->key;
     t.value = P->value;
@@ -105,7 +107,7 @@ kvbuf_status from_hip(hipError_t e) { return e == hipSuccess ? KVBUF_OK : KVBUF_
 kvbuf_status chunk_call(const kvbuf_layout* layout, const kvbuf_pools* pools,
                         const kvbuf_batch* batch, int mode, int n, const void* q,
                         const void* k, const void* v, const float* g, const float* beta,
-                        float* out, hipStream_t stream, const int32_t* parent = nullptr) {
+                        void* out, hipStream_t stream, const int32_t* parent = nullptr) {
     const bool direct = mode == kvbuf::MODE_DIRECT;
     KVBUF_TRY(check_layout(layout, mode != kvbuf::MODE_DECODE));
     KVBUF_TRY(check_batch(layout, batch));
@@ -166,14 +168,14 @@ extern "C" {
 
 kvbuf_status kvbuf_decode(const kvbuf_layout* layout, const kvbuf_pools* pools,
                           const kvbuf_batch* batch, const void* q, const void* k,
-                          const void* v, const float* g, const float* beta, float* out,
+                          const void* v, const float* g, const float* beta, void* out,
                           hipStream_t stream) {
     return chunk_call(layout, pools, batch, kvbuf::MODE_DECODE, 1, q, k, v, g, beta, out, stream);
 }
 
 kvbuf_status kvbuf_direct(const kvbuf_layout* layout, const kvbuf_pools* pools,
                           const kvbuf_batch* batch, const void* q, const void* k,
-                          const void* v, const float* g, const float* beta, float* out,
+                          const void* v, const float* g, const float* beta, void* out,
                           hipStream_t stream) {
     return chunk_call(layout, pools, batch, kvbuf::MODE_DIRECT, 1, q, k, v, g, beta, out, stream);
 }
@@ -181,7 +183,7 @@ kvbuf_status kvbuf_direct(const kvbuf_layout* layout, const kvbuf_pools* pools,
 kvbuf_status kvbuf_verify(const kvbuf_layout* layout, const kvbuf_pools* pools,
                           const kvbuf_batch* batch, int32_t n, const void* q,
                           const void* k, const void* v, const float* g,
-                          const float* beta, float* out, hipStream_t stream) {
+                          const float* beta, void* out, hipStream_t stream) {
     return chunk_call(layout, pools, batch, kvbuf::MODE_VERIFY, n, q, k, v, g, beta, out, stream);
 }
 
@@ -219,7 +221,7 @@ kvbuf_status kvbuf_commit(const kvbuf_layout* layout, const kvbuf_pools* pools,
 kvbuf_status kvbuf_verify_tree(const kvbuf_layout* layout, const kvbuf_pools* pools,
                                const kvbuf_batch* batch, int32_t n, const int32_t* parent,
                                const void* q, const void* k, const void* v, const float* g,
-                               const float* beta, float* out, hipStream_t stream) {
+                               const float* beta, void* out, hipStream_t stream) {
     if (!parent) return KVBUF_EINVAL;
     return chunk_call(layout, pools, batch, kvbuf::MODE_VERIFY, n, q, k, v, g, beta, out, stream, parent);
 }
@@ -246,7 +248,7 @@ kvbuf_status kvbuf_commit_tree(const kvbuf_layout* layout, const kvbuf_pools* po
 kvbuf_status kvbuf_verify_recurrent(const kvbuf_layout* layout, const kvbuf_pools* pools,
                                     const kvbuf_batch* batch, int32_t n, const void* q,
                                     const void* k, const void* v, const float* g,
-                                    const float* beta, float* out, float* temp,
+                                    const float* beta, void* out, float* temp,
                                     hipStream_t stream) {
     KVBUF_TRY(check_layout(layout, false));
     if (layout->m != 0) return KVBUF_EUNSUPPORTED;  // the baseline has no buffer

@@ -348,14 +348,14 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void channel_kernel(TileParams P
         }
     }
     __syncthreads();
-    float* outp = P.out + in_row * DV;
+    const size_t outp = in_row * DV;  // output element of (request, draft 0, head)
     for (int idx = tid; idx < n * DV; idx += NT) {
         const int d = idx / DV;
         const int c = idx - d * DV;
         float sum = 0.f;
 #pragma unroll
         for (int g2 = 0; g2 < RG; ++g2) sum += red[(d * RG + g2) * DV + c];
-        outp[d * in_stride * DV + c] = sum;
+        store_out(P, outp + d * in_stride * DV + c, sum);
     }
 
     // ---- appends: the drafts' key, value and gate rows; metadata (decode) ------------

@@ -599,7 +599,7 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
 
     // ---- 5. the state tile: S^T q (and S^T k), reduced over row groups --------
     float* red = lds + L.red;
-    float* outp = P.out + in_row * DV;
+    const size_t outp = in_row * DV;  // output element of (request, draft 0, head)
     const size_t out_stride = static_cast<size_t>(P.H) * DV;
     if constexpr (MF) {  // the value sums are in `red` already
         if (has_state) state_products_mfma<DK, DV, RG, RGS>(s, qr, red, es, P.scale, n, tid);
@@ -631,7 +631,7 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
             float sum = 0.f;
 #pragma unroll
             for (int g2 = 0; g2 < RGS; ++g2) sum += red[(d * RGS + g2) * DV + c];
-            outp[d * out_stride + c] = sum;
+            store_out(P, outp + d * out_stride + c, sum);
         }
     } else {
 #pragma unroll
@@ -691,7 +691,7 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void chunk_kernel(TileParams P) 
                     u[d] = x;
 #pragma unroll
                     for (int e = 0; e <= d; ++e) o += cq[d * ldc + p + e] * u[e];
-                    outp[d * out_stride + c] = o;
+                    store_out(P, outp + d * out_stride + c, o);
                     xpool[tok.slot_index(t) * DV + c] = x;
                     if (fold && t < P.m) vrs[t * DV + c] = x;  // the new token is folded too
                 }

@@ -384,7 +384,7 @@ void decode_kernel(TileParams P) {
         float sum = 0.f;
 #pragma unroll
         for (int g2 = 0; g2 < RG; ++g2) sum += red[g2 * DV + tid];
-        P.out[in_row * DV + tid] = sum * (CH ? P.scale : P.scale * s_es) + obuf[tid];
+        store_out(P, in_row * DV + tid, sum * (CH ? P.scale : P.scale * s_es) + obuf[tid]);
     }
 
     // ---- eager fold: the buffer reached m tokens ---------------------------------

@@ -238,6 +238,13 @@ __device__ __forceinline__ float group16_sum(float x) {
 // 1e-6.
 __device__ __forceinline__ float exp_gate(float x) { return __expf(x); }
 
+// Output element i of a call: fp32, or rounded to the nearest bf16 (ties to
+// even) when the layout asks for bf16 outputs.
+__device__ __forceinline__ void store_out(const TileParams& P, size_t i, float v) {
+    if (P.out_bf16) static_cast<__bf16*>(P.out)[i] = static_cast<__bf16>(v);
+    else static_cast<float*>(P.out)[i] = v;
+}
+
 // Inclusive prefix sum of the log-gates of buffer positions 0 .. T-1 into
 // bl[0 .. T-1] (LDS), by one wave (lane = 0..63) in 64-wide segments.
 // gate_at(i) returns the log-gate of position i (cheap: from LDS).

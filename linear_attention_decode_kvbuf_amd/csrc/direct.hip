@@ -311,7 +311,7 @@ __global__ __launch_bounds__(64 * kDirectWaves) void direct_kernel(TileParams P)
     const size_t arow = row_of(p);
     if (live) {
 #pragma unroll
-        for (int c = 0; c < C; ++c) P.out[out_row + c] = acc[c] + qk * x[c];
+        for (int c = 0; c < C; ++c) store_out(P, out_row + c, acc[c] + qk * x[c]);
         // appends: key, value (delta rule: its pseudo-value), gate
         kt.store(static_cast<IO*>(P.key) + arow * D + c0);
         if constexpr (DELTA) {
@@ -464,9 +464,9 @@ __global__ __launch_bounds__(64 * kDirectWaves) void direct_rows_kernel(TilePara
     const uint32_t ba = static_cast<uint32_t>(__builtin_amdgcn_readlane(blk, qa));
     const size_t arow = (static_cast<size_t>(ba) * H + h) * bs + (p - qa * bs);
     if (rs == 0) {
-        float* o = P.out + in_row * D + cl * E;
+        const size_t o = in_row * D + cl * E;
 #pragma unroll
-        for (int e = 0; e < E; ++e) o[e] = acc[e] + qk * x[e];
+        for (int e = 0; e < E; ++e) store_out(P, o + e, acc[e] + qk * x[e]);
         // appends: key, value (delta rule: its pseudo-value), gate
         kt.store(static_cast<IO*>(P.key) + arow * D + cl * E);
         if constexpr (DELTA) {

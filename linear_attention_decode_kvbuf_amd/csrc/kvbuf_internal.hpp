@@ -43,7 +43,8 @@ struct TileParams {
     const void* v;
     const float* g;
     const float* beta;
-    float* out;
+    void* out;            // fp32, or bf16 when out_bf16 (store_out)
+    int out_bf16;
     const int32_t* accepted;
     float* states_out;
     const int32_t* parent;  // tree drafts: [B][n] parent of each draft (-1 = the buffer), else null

@@ -117,7 +117,7 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void recurrent_kernel(Tile
         float sum = 0.f;
 #pragma unroll
         for (int g2 = 0; g2 < RG; ++g2) sum += red[g2 * DV + c];
-        P.out[in_row * DV + c] = sum;
+        store_out(P, in_row * DV + c, sum);
     }
 }
 
@@ -229,7 +229,7 @@ __global__ __launch_bounds__((Geo<DK, DV>::NTHREADS)) void verify_recurrent_kern
             float sum = 0.f;
 #pragma unroll
             for (int g2 = 0; g2 < RG; ++g2) sum += rd[g2 * DV + c];
-            P.out[orow * DV + c] = sum;
+            store_out(P, orow * DV + c, sum);
         }
         if constexpr (DELTA) __syncthreads();  // sk and both partial buffers are reused
     }

@@ -39,10 +39,11 @@ TOL_STATE = 1e-5
 NTHREADS = max(1, min(16, len(os.sched_getaffinity(0))))
 
 
-def rel_err_tiles(gpu, ref, axes, chunk=1024, den=None):
+def rel_err_tiles(gpu, ref, axes, chunk=1024, den=None, slack=0.0):
     """max over tiles of max|gpu - ref| / max|den| (den = ref unless given;
     reduction over ``axes``), in chunks of the leading axis so that full-size
-    states are never widened whole."""
+    states are never widened whole.  With ``slack`` each element's error is
+    counted beyond slack |ref| (the rounding of a narrower output type)."""
     gpu = np.asarray(gpu)
     ref = np.asarray(ref)
     if gpu.shape != ref.shape:
@@ -56,7 +57,7 @@ def rel_err_tiles(gpu, ref, axes, chunk=1024, den=None):
         g = np.asarray(gpu[i:i + chunk], np.float64)
         r = np.asarray(ref[i:i + chunk], np.float64)
         d = r if den is None else np.asarray(den[i:i + chunk], np.float64)
-        num = np.max(np.abs(g - r), axis=axes)
+        num = np.max(np.maximum(np.abs(g - r) - slack * np.abs(r), 0.0), axis=axes)
         worst = max(worst, float(np.max(num / np.maximum(np.max(np.abs(d), axis=axes), 1e-30))))
     return worst
 
@@ -82,16 +83,21 @@ def recurrence(rule, S, q, k, v, g, beta):
     return out, mag
 
 
-def out_err_tiles(gpu, ref, mag, out_scale="magnitude"):
+# bf16 outputs: rounding to nearest moves an element by at most half an ulp,
+# 2^-8 of its size (8 significant bits)
+BF16_HALF_ULP = 2.0 ** -8
+
+
+def out_err_tiles(gpu, ref, mag, out_scale="magnitude", slack=0.0):
     """max over tiles of max|gpu - ref| / max(scale): the output magnitude, or
-    max|ref| with out_scale="output"."""
-    return rel_err_tiles(gpu, ref, axes=-1, den=(mag if out_scale == "magnitude" else None))
+    max|ref| with out_scale="output"; errors counted beyond slack |ref|."""
+    return rel_err_tiles(gpu, ref, axes=-1, den=(mag if out_scale == "magnitude" else None), slack=slack)
 
 
 class Run:
     def __init__(self, w, *, flush=kb.FLUSH_EAGER, sample=None, device_gen=None, spare_blocks=3,
                  stateless=None, check_every_step=None, state_sample=64, tol_out=TOL_OUT, tol_state=TOL_STATE,
-                 out_scale="magnitude"):
+                 out_scale="magnitude", out_dtype=kb.OUT_F32):
         self.w = w
         self.out_scale = out_scale
         self.tol_out = tol_out
@@ -106,7 +112,10 @@ class Run:
         nslots = B + 1
         self.kv = kb.KVBuffer(batch=B, heads=H, d=d, m=w.m, block_size=w.block_size if w.m > 0 else 1,
                               blocks_per_req=bpr, num_blocks=nb, num_state_slots=nslots, rule=w.rule,
-                              io_dtype=kb.BF16 if w.io == "bf16" else kb.F32, flush=flush)
+                              io_dtype=kb.BF16 if w.io == "bf16" else kb.F32, flush=flush,
+                              out_dtype=out_dtype)
+        # bf16 outputs are compared beyond their own rounding
+        self.out_slack = BF16_HALF_ULP if out_dtype == kb.OUT_BF16 else 0.0
         if w.m > 0:
             perm = synth.block_permutation(w, nb)
             self.free = list(perm[B * bpr:])
@@ -206,7 +215,7 @@ class Run:
         if direct_from is not None:
             s = direct_from
             part = lambda x, a, z: None if x is None else x[a:z]
-            out = torch.empty((w.B, w.H, w.dv), dtype=torch.float32, device=self.dev)
+            out = torch.empty((w.B, w.H, w.dv), dtype=self.kv.out_torch, device=self.dev)
             for view, fn, a, z in ((self.kv.view(0, s), "decode", 0, s), (self.kv.view(s, w.B - s), "direct", s, w.B)):
                 if z > a:
                     getattr(view, fn)(*(part(inp[x], a, z) for x in ("q", "k", "v", "g", "beta")), out=out[a:z])
@@ -226,7 +235,7 @@ class Run:
         o_ref, mag = recurrence(w.rule, self.S, q[None], k[None], v[None],
                                 None if g is None else g[None], None if beta is None else beta[None])
         o_gpu = self._sampled(out)
-        err = out_err_tiles(o_gpu, o_ref[0], mag[0], self.out_scale)
+        err = out_err_tiles(o_gpu, o_ref[0], mag[0], self.out_scale, self.out_slack)
         self.max_out = max(self.max_out, err)
         assert err <= self.tol_out, "step %d: output error %.3e" % (t, err)
         self._after(folded)
@@ -257,7 +266,7 @@ class Run:
         for dd in range(n):
             col = lambda x: None if x is None else x[:, dd][None]
             o_ref, mag = recurrence(w.rule, S_tmp, col(q), col(k), col(v), col(g), col(beta))
-            err = out_err_tiles(o_gpu[:, dd], o_ref[0], mag[0], self.out_scale)
+            err = out_err_tiles(o_gpu[:, dd], o_ref[0], mag[0], self.out_scale, self.out_slack)
             self.max_out = max(self.max_out, err)
             assert err <= self.tol_out, "verify %d draft %d: output error %.3e" % (call, dd, err)
             keep = acc_tile == dd + 1
@@ -324,7 +333,7 @@ class Run:
         for dd in range(n):
             o_ref, mag = self._along_paths({b: path_to(b, dd) for b in range(w.B)}, q, k, v, g, beta,
                                            self.S.copy())
-            err = out_err_tiles(o_gpu[:, dd], o_ref, mag, self.out_scale)
+            err = out_err_tiles(o_gpu[:, dd], o_ref, mag, self.out_scale, self.out_slack)
             self.max_out = max(self.max_out, err)
             assert err <= self.tol_out, "tree verify %d draft %d: output error %.3e" % (call, dd, err)
         self._along_paths({b: path_to(b, int(leaf[b])) for b in range(w.B)}, q, k, v, g, beta, self.S)

@@ -5,6 +5,8 @@ bad arguments on the host before any HIP call (no kernel is launched here)."""
 import ctypes
 import os
 import re
+import subprocess
+import tempfile
 
 import pytest
 
@@ -37,14 +39,37 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_struct_sizes_match_header(lib):
-    # kvbuf_layout: 11 int32 + 1 float; pools: 4 pointers; batch: int32 (+pad) + 6 pointers
-    assert ctypes.sizeof(kb.Layout) == 48
+    # kvbuf_layout: 11 int32 + 1 float + 1 int32; pools: 4 pointers; batch: int32 (+pad) + 6 pointers
+    assert ctypes.sizeof(kb.Layout) == 52
     assert ctypes.sizeof(kb.Pools) == 32
     assert ctypes.sizeof(kb.Batch) == 48
 
 
+def test_structs_match_a_c_compiler():
+    """Sizes and field offsets of the binding's structs against the header
+    as a C compiler lays it out."""
+    fields = {"kvbuf_layout": kb.Layout, "kvbuf_pools": kb.Pools, "kvbuf_batch": kb.Batch}
+    lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "kvbuf.h"', "int main(void) {"]
+    for cname, py in fields.items():
+        lines.append('printf("%%zu\\n", sizeof(%s));' % cname)
+        for f, _ in py._fields_:
+            lines.append('printf("%%zu\\n", offsetof(%s, %s));' % (cname, f))
+    lines.append("return 0; }")
+    with tempfile.TemporaryDirectory() as tmp:
+        src, exe = os.path.join(tmp, "t.c"), os.path.join(tmp, "t")
+        open(src, "w").write("\n".join(lines))
+        subprocess.run(["gcc", "-x", "c", "-std=c11", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
+                        "-I", "/opt/rocm/include", src, "-o", exe], check=True)
+        got = [int(x) for x in subprocess.run([exe], check=True, capture_output=True, text=True).stdout.split()]
+    want = []
+    for py in fields.values():
+        want.append(ctypes.sizeof(py))
+        want += [getattr(py, f).offset for f, _ in py._fields_]
+    assert got == want
+
+
 def test_abi_version_and_strerror(lib):
-    assert kb.kvbuf_abi_version() == 4
+    assert kb.kvbuf_abi_version() == 5
     for st in (kb.OK, kb.EINVAL, kb.EUNSUPPORTED, kb.ECAPACITY, kb.EHIP):
         assert len(kb.strerror(st)) > 5
     assert "unknown" in kb.strerror(-99)
@@ -52,7 +77,8 @@ def test_abi_version_and_strerror(lib):
 
 def _layout(**kw):
     base = dict(num_heads=2, d_k=16, d_v=16, m=4, block_size=4, blocks_per_req=2, num_blocks=4,
-                num_state_slots=2, rule=kb.RULE_GATED, io_dtype=kb.F32, flush=kb.FLUSH_EAGER, scale=1.0)
+                num_state_slots=2, rule=kb.RULE_GATED, io_dtype=kb.F32, flush=kb.FLUSH_EAGER, scale=1.0,
+                out_dtype=kb.OUT_F32)
     base.update(kw)
     return kb.Layout(*[base[f] for f, _ in kb.Layout._fields_])
 
@@ -80,6 +106,8 @@ def _decode(layout, pools=POOLS, batch=BATCH, q=FAKE, g=FAKE, beta=None):
     (dict(block_size=16, blocks_per_req=33, m=16, num_blocks=66), kb.ECAPACITY),  # 528 > 512 positions
     (dict(m=-1), kb.EINVAL),
     (dict(scale=float("nan")), kb.EINVAL),
+    (dict(out_dtype=2), kb.EINVAL),
+    (dict(out_dtype=-1), kb.EINVAL),
 ])
 def test_layout_validation(lib, kw, status):
     assert _decode(_layout(**kw)) == status

@@ -493,6 +493,85 @@ def _full_cycle_checks(run):
          % (run.max_out, run.max_state, run.folds_checked))
 
 
+# bf16 outputs: errors beyond the rounding itself (half an ulp, 2^-8 of the
+# value), relative to the output magnitude: fp32 sums of exact products stay
+# near 1e-6 of it.
+TOL_BF16_OUT = 2e-5
+
+
+@pytest.mark.parametrize("rule,d", [(0, 64), (1, 128), (2, 128), (3, 128), (1, 16), (3, 64)])
+def test_bf16_outputs(rule, d):
+    """Outputs stored as bf16 (layout out_dtype): every output of decode, of
+    verify with chains of 1, 4 and 8 drafts (the matrix-core instances among
+    them) and of a tree verify is the oracle's output rounded to nearest bf16,
+    to within the fp32 error of the sums."""
+    w = synth.workload(1, B=5, H=3, dk=d, dv=d, m=8, block_size=4, blocks_per_req=5, steps=8,
+                       rule=rule, io="bf16", state_std=0.5)
+    _say("bf16 outputs", w)
+    run = Run(w, out_dtype=kb.OUT_BF16, tol_out=TOL_BF16_OUT)
+    t = 0
+    for call, n in enumerate((1, 4, 8)):
+        run.decode(t)
+        t += 1
+        run.verify_commit(call, n, synth.accepted_lengths(w, call, w.B, n))
+    parent, leaf = synth.draft_tree(w, 7, w.B, 5)
+    run.verify_tree_commit(7, parent, leaf)
+    for _ in range(3):
+        run.decode(t)
+        t += 1
+    run.check_effective_states()
+    run.check_pool()
+    run.check_bookkeeping()
+    _say("max out err beyond rounding %.2e" % run.max_out)
+
+
+@pytest.mark.parametrize("rule", [0, 1])
+def test_bf16_outputs_one_token_kernel(rule):
+    """bf16 outputs of the one-token kernel (d = 128, bf16, above 4096 tiles),
+    through a fused fold."""
+    w = synth.workload(3, B=130, rule=rule, steps=10)
+    _say("bf16 outputs, one-token kernel", w)
+    run = Run(w, out_dtype=kb.OUT_BF16, tol_out=TOL_BF16_OUT)
+    for t in range(w.steps):
+        run.decode(t)
+    assert run.folds_checked == w.B * w.H
+    _say("max out err beyond rounding %.2e" % run.max_out)
+
+
+@pytest.mark.parametrize("rule", [0, 1, 2, 3])
+def test_bf16_outputs_buffer_only_and_recurrent(rule):
+    """bf16 outputs of buffer-only decode (one wave per tile) and of the m = 0
+    recurrent kernel and its temporary-state verification."""
+    w = synth.workload(1, B=3, H=2, dk=128, dv=128, m=8, block_size=8, blocks_per_req=2, steps=10,
+                       rule=rule, io="bf16", state_std=0.5)
+    run = Run(w, stateless=np.ones(3, bool), flush=kb.FLUSH_DEFERRED, out_dtype=kb.OUT_BF16,
+              tol_out=TOL_BF16_OUT)
+    for t in range(w.steps):
+        run.decode(t, direct=True)
+    run.check_effective_states()
+    import oracle
+
+    w0 = synth.workload(1, B=3, H=2, dk=128, dv=128, m=0, block_size=1, blocks_per_req=1, steps=4,
+                        rule=rule, io="bf16", state_std=0.5)
+    run0 = Run(w0, out_dtype=kb.OUT_BF16, tol_out=TOL_BF16_OUT)
+    for t in range(w0.steps):
+        run0.decode(t)
+    n = 3
+    inp = run0.inputs(0, n=n, stream_base=100)
+    out, _ = run0.kv.verify_recurrent(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"])
+    assert out.dtype == torch.bfloat16
+    torch.cuda.synchronize()
+    q, k, v, g, beta = (run0._sampled(inp[x], drafts=True) for x in ("q", "k", "v", "g", "beta"))
+    o_gpu = run0._sampled(out, drafts=True)
+    o_ref, _, mag = oracle.recurrent(rule, run0.S, q.transpose(1, 0, 2), k.transpose(1, 0, 2),
+                                     v.transpose(1, 0, 2), None if g is None else np.swapaxes(g, 0, 1),
+                                     None if beta is None else beta.T, with_magnitude=True)
+    from tests.harness import BF16_HALF_ULP, out_err_tiles
+    for dd in range(n):
+        err = out_err_tiles(o_gpu[:, dd], o_ref[dd], mag[dd], slack=BF16_HALF_ULP)
+        assert err <= TOL_BF16_OUT, (dd, err)
+
+
 @pytest.mark.parametrize("B,m", [(4096, 8), (4097, 8), (4096, 32), (4096, 16)])
 def test_decode_kernel_choice_boundary(B, m):
     """One-token decode at d = 128, bf16, one head per request, around the
