@@ -485,10 +485,17 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h, int
     f4 s[RPT];
     const int mw = tid >> 6, ml = tid & 63;  // MF: wave and lane
     const float* tile = has_state ? P.state + (static_cast<size_t>(slot) * P.H + h) * DK * DV : P.state;
+    // Four waves, vector-ALU fold (commits): a chain commit's wave 0 requests
+    // its share of the tile before it stages the rows, both in flight
+    // together.  A tree commit's wave 0 requests it with the other waves,
+    // after the path walk and the staging, which keeps its registers at five
+    // waves per SIMD (five workgroups per CU instead of four; measured, tree
+    // commits 30.4 / 35.4 / 42.8 / 50.5 -> 28.1 / 32.8 / 39.4 / 46.9 us at
+    // n = 1 / 2 / 4 / 8; chain commits gained at n <= 4 and lost 2.6% at n = 8,
+    // where half the tiles fold and wait for wave 0's later share).
+    constexpr bool W4_EARLY_TILE = W4 && !MF && !TREE;
     if (token_wave) {
-        // four waves, vector-ALU fold: wave 0 requests its share of the tile
-        // before it stages the rows, both in flight together
-        if constexpr (W4 && !MF) load_tile<RPT, DK, DV>(s, tile, has_state, rg, c0);
+        if constexpr (W4_EARLY_TILE) load_tile<RPT, DK, DV>(s, tile, has_state, rg, c0);
         if constexpr (RAW) {
             // The first rounds' copies need only the position table: requested
             // before the gates, both are in flight in the same round trip.
@@ -538,7 +545,7 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h, int
             static_assert(RPT == 16, "16 blocks of 16 x 16 per wave");
 #pragma unroll
             for (int j = 0; j < RPT; ++j) s[j] = f4{0.0f, 0.0f, 0.0f, 0.0f};
-        } else if (!(W4 && token_wave)) {
+        } else if (!(W4_EARLY_TILE && token_wave)) {
             load_tile<RPT, DK, DV>(s, tile, has_state, rg, c0);
         }
     }
@@ -862,7 +869,8 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h, int
 // One workgroup per tile (W4: of four waves).
 template <int RULE, int DK, int DV, typename IO, bool MULTI, bool TREE, bool MFT, bool W4 = false>
 __global__ __launch_bounds__((W4 ? Geo<DK, DV>::NT : Geo<DK, DV>::NTHREADS))
-__attribute__((amdgpu_waves_per_eu((RULE == KVBUF_RULE_DELTA && MULTI) || W4 ? 4 : 1))) void fold_kernel(TileParams P) {
+__attribute__((amdgpu_waves_per_eu((W4 && TREE && !MFT) ? 5 : ((RULE == KVBUF_RULE_DELTA && MULTI) || W4 ? 4 : 1))))
+void fold_kernel(TileParams P) {
     const TileIndex ti = tile_index(P);
     fold_tile<RULE, DK, DV, IO, MULTI, TREE, MFT, W4>(P, ti.b, ti.h, threadIdx.x);
 }
