@@ -499,14 +499,15 @@ def _full_cycle_checks(run):
 TOL_BF16_OUT = 2e-5
 
 
-@pytest.mark.parametrize("rule,d", [(0, 64), (1, 128), (2, 128), (3, 128), (1, 16), (3, 64)])
-def test_bf16_outputs(rule, d):
+@pytest.mark.parametrize("rule,d,io", [(0, 64, "bf16"), (1, 128, "bf16"), (2, 128, "bf16"), (3, 128, "bf16"),
+                                       (1, 16, "bf16"), (3, 64, "bf16"), (1, 128, "f32"), (2, 16, "f32")])
+def test_bf16_outputs(rule, d, io):
     """Outputs stored as bf16 (layout out_dtype): every output of decode, of
     verify with chains of 1, 4 and 8 drafts (the matrix-core instances among
     them) and of a tree verify is the oracle's output rounded to nearest bf16,
     to within the fp32 error of the sums."""
     w = synth.workload(1, B=5, H=3, dk=d, dv=d, m=8, block_size=4, blocks_per_req=5, steps=8,
-                       rule=rule, io="bf16", state_std=0.5)
+                       rule=rule, io=io, state_std=0.5)
     _say("bf16 outputs", w)
     run = Run(w, out_dtype=kb.OUT_BF16, tol_out=TOL_BF16_OUT)
     t = 0
