@@ -494,6 +494,17 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h, int
     // n = 1 / 2 / 4 / 8; chain commits gained at n <= 4 and lost 2.6% at n = 8,
     // where half the tiles fold and wait for wave 0's later share).
     constexpr bool W4_EARLY_TILE = W4 && !MF && !TREE;
+    // Four-wave matrix-core folds (not tree commits): wave 1 forms the decay
+    // weights while wave 0 copies the rows.  A wave's loads retire in order,
+    // so gate loads issued behind the copies waited for every round in
+    // flight; on a wave of their own they are formed during the copies'
+    // round trip (measured: m = 32 folds 204 -> 199 us gated, 209 -> 206 us
+    // delta rule; m = 64 gated 210 -> 207 us).  The delta rule's fp32 rows
+    // keep one round ahead: requesting its first two rounds together took
+    // m = 64 from 265 to 270 us.
+    constexpr bool GW = W4 && RAW && !TREE;
+    const bool gate_wave = GW ? (tid >> 6) == 1 : token_wave;
+    const int glane = GW ? tid - 64 : lane;
     if (token_wave) {
         if constexpr (W4_EARLY_TILE) load_tile<RPT, DK, DV>(s, tile, has_state, rg, c0);
         if constexpr (RAW) {
@@ -504,7 +515,9 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h, int
             if (T > 0) issue(0);
             if (RING && T > fc) issue(1);
         }
-        if constexpr (SGATE) gate_prefix_loads(bl, T, lane, [&](int i) { return tok.gate(i); });
+    }
+    if (gate_wave) {
+        if constexpr (SGATE) gate_prefix_loads(bl, T, glane, [&](int i) { return tok.gate(i); });
         if constexpr (CH) {
             // total log-gate of each key channel over the T positions, summed
             // in order
@@ -523,12 +536,14 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h, int
             for (int c = 0; c < CPL; ++c)
                 if (lane + 64 * c < DK) e0p[lane + 64 * c] = tot[c];
         } else {
-            if (lane == 0) *e0p = (SGATE && T > 0) ? exp_gate(bl[T - 1]) : 1.0f;
+            if (glane == 0) *e0p = (SGATE && T > 0) ? exp_gate(bl[T - 1]) : 1.0f;
         }
         if constexpr (RAW) {
-            for (int i = lane; i < ((T + 31) & ~31); i += 64)
+            for (int i = glane; i < ((T + 31) & ~31); i += 64)
                 fwa[i] = i >= T ? 0.0f : SGATE ? exp_gate(bl[T - 1] - bl[i]) : 1.0f;
         }
+    }
+    if (token_wave) {
         if constexpr (RING) {
             ring_wait(0);
         } else if constexpr (RAW) {
@@ -549,7 +564,7 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h, int
             load_tile<RPT, DK, DV>(s, tile, has_state, rg, c0);
         }
     }
-    if constexpr (RING) ring_barrier();  // round 0 has landed
+    if constexpr (RING || GW) ring_barrier();  // round 0 has landed
     else __syncthreads();
     if (state_wave) {
         if constexpr (MF) {
@@ -763,7 +778,7 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h, int
             } else {
                 apply(r);
             }
-            if constexpr (RING) ring_barrier();
+            if constexpr (RING || GW) ring_barrier();
             else __syncthreads();
         }
         if (tree && token_wave) move_kept();  // every round is staged
