@@ -394,6 +394,17 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h, int
     // Token wave: stage round r (tokens r*fc ..) into buffer r % NBUF.  Raw
     // rows are only issued here: stage() waits for them, a ring fold
     // (ring_wait) counts them.
+    // Four-wave folds other than tree commits: wave 1 forms the decay weights
+    // while wave 0 requests the rows (and, vector-ALU folds, its share of the
+    // tile).  A wave's loads retire in order, so gate loads issued behind the
+    // copies or the tile waited for them; on a wave of their own they are
+    // formed during that round trip (measured: m = 32 folds 204 -> 199 us
+    // gated, 209 -> 206 us delta rule; m = 64 gated 210 -> 207 us).  The
+    // delta rule's fp32 rows keep one round ahead: requesting its first two
+    // rounds together took m = 64 from 265 to 270 us.
+    constexpr bool GW = W4 && !TREE;
+    const bool gate_wave = GW ? (tid >> 6) == 1 : token_wave;
+    const int glane = GW ? tid - 64 : lane;
     auto issue = [&](int r) {
         char* fk = reinterpret_cast<char*>(stage0 + (r % NBUF) * stage_floats);
         char* fx = fk + srows * DK * KB;
@@ -462,7 +473,7 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h, int
                 }
             }
             for (int ii = lane; ii < cnt; ii += 64) fw[ii] = 1.0f;
-        } else {
+        } else if constexpr (!GW) {  // (GW: wave 1 writes them)
             for (int ii = lane; ii < cnt; ii += 64)
                 fw[ii] = SGATE ? exp_gate(bl[T - 1] - bl[i0 + ii]) : 1.0f;
         }
@@ -494,17 +505,6 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h, int
     // n = 1 / 2 / 4 / 8; chain commits gained at n <= 4 and lost 2.6% at n = 8,
     // where half the tiles fold and wait for wave 0's later share).
     constexpr bool W4_EARLY_TILE = W4 && !MF && !TREE;
-    // Four-wave matrix-core folds (not tree commits): wave 1 forms the decay
-    // weights while wave 0 copies the rows.  A wave's loads retire in order,
-    // so gate loads issued behind the copies waited for every round in
-    // flight; on a wave of their own they are formed during the copies'
-    // round trip (measured: m = 32 folds 204 -> 199 us gated, 209 -> 206 us
-    // delta rule; m = 64 gated 210 -> 207 us).  The delta rule's fp32 rows
-    // keep one round ahead: requesting its first two rounds together took
-    // m = 64 from 265 to 270 us.
-    constexpr bool GW = W4 && RAW && !TREE;
-    const bool gate_wave = GW ? (tid >> 6) == 1 : token_wave;
-    const int glane = GW ? tid - 64 : lane;
     if (token_wave) {
         if constexpr (W4_EARLY_TILE) load_tile<RPT, DK, DV>(s, tile, has_state, rg, c0);
         if constexpr (RAW) {
@@ -541,6 +541,12 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h, int
         if constexpr (RAW) {
             for (int i = glane; i < ((T + 31) & ~31); i += 64)
                 fwa[i] = i >= T ? 0.0f : SGATE ? exp_gate(bl[T - 1] - bl[i]) : 1.0f;
+        } else if constexpr (GW) {
+            // the one staging round's weights (four-wave vector-ALU folds
+            // take at most 16 positions)
+            static_assert(!GW || MF || !MULTI, "one round");
+            float* fw0 = stage0 + srows * DK * KB / 4 + srows * DV * XB / 4;
+            for (int i = glane; i < T; i += 64) fw0[i] = SGATE ? exp_gate(bl[T - 1] - bl[i]) : 1.0f;
         }
     }
     if (token_wave) {
