@@ -401,7 +401,9 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h, int
     // formed during that round trip (measured: m = 32 folds 204 -> 199 us
     // gated, 209 -> 206 us delta rule; m = 64 gated 210 -> 207 us).  The
     // delta rule's fp32 rows keep one round ahead: requesting its first two
-    // rounds together took m = 64 from 265 to 270 us.
+    // rounds together took m = 64 from 265 to 270 us.  Tree commits keep the
+    // weights on wave 0: its moves of the kept rows rewrite gate entries that
+    // another wave would be reading.
     constexpr bool GW = W4 && !TREE;
     const bool gate_wave = GW ? (tid >> 6) == 1 : token_wave;
     const int glane = GW ? tid - 64 : lane;
