@@ -401,10 +401,10 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h, int
     // formed during that round trip (measured: m = 32 folds 204 -> 199 us
     // gated, 209 -> 206 us delta rule; m = 64 gated 210 -> 207 us).  The
     // delta rule's fp32 rows keep one round ahead: requesting its first two
-    // rounds together took m = 64 from 265 to 270 us.  Tree commits keep the
-    // weights on wave 0: its moves of the kept rows rewrite gate entries that
-    // another wave would be reading.
-    constexpr bool GW = W4 && !TREE;
+    // rounds together took m = 64 from 265 to 270 us.  A one-round tree
+    // commit moves its kept rows after the barrier that ends the weights'
+    // reads of their gates; a multi-round one keeps the weights on wave 0.
+    constexpr bool GW = W4 && !(TREE && MULTI);
     const bool gate_wave = GW ? (tid >> 6) == 1 : token_wave;
     const int glane = GW ? tid - 64 : lane;
     auto issue = [&](int r) {
@@ -559,7 +559,7 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h, int
         } else {
             if (T > 0) stage(0);
         }
-        if (tree && !MULTI) move_kept();  // the fold's rows are staged
+        if (tree && !MULTI && !GW) move_kept();  // the fold's rows are staged
     }
     if (state_wave) {
         if constexpr (MF) {
@@ -574,6 +574,8 @@ __device__ __forceinline__ void fold_tile(const TileParams& P, int b, int h, int
     }
     if constexpr (RING || GW) ring_barrier();  // round 0 has landed
     else __syncthreads();
+    // (GW: every gate the weights read has been read)
+    if (GW && tree && !MULTI && token_wave) move_kept();
     if (state_wave) {
         if constexpr (MF) {
         } else if constexpr (CH) {
