@@ -103,6 +103,39 @@ def test_long_folds(rule, io, flush):
     run.check_bookkeeping()
 
 
+@pytest.mark.parametrize("rule", [0, 1, 2])
+@pytest.mark.parametrize("m", [24, 32])
+def test_single_round_matrix_core_folds(rule, m):
+    """Folds of 17-32 positions at d = 128 through the fold kernel: one
+    staging round on the matrix cores, in four-wave workgroups whose decay
+    weights come from their second wave.  Deferred flushes of m = 24 / 32
+    (a partial and a full round), then eager commits that fill the buffer."""
+    w = synth.workload(1, B=3, H=2, dk=128, dv=128, m=m, block_size=8, blocks_per_req=8, steps=2 * m + 4,
+                       rule=rule, io="bf16", state_std=0.02)
+    _say("single-round folds", w)
+    run = Run(w, flush=kb.FLUSH_DEFERRED)
+    for t in range(w.steps):
+        run.decode(t)
+        if t % m == m - 1:
+            run.flush()
+            run.check_effective_states()
+    run.check_pool()
+    run.check_bookkeeping()
+    # eager commits: the buffer fills inside kvbuf_commit
+    we = synth.workload(1, B=4, H=2, dk=128, dv=128, m=m, block_size=8, blocks_per_req=8, steps=12,
+                        rule=rule, io="bf16", state_std=0.02)
+    rune = Run(we)
+    t = 0
+    for call in range(12):
+        rune.decode(t)
+        t += 1
+        rune.verify_commit(call, 8, synth.accepted_lengths(we, call, we.B, 8))
+        rune.check_effective_states()
+    rune.check_pool()
+    rune.check_bookkeeping()
+    assert rune.folds_checked > 0
+
+
 @pytest.mark.parametrize("rule,d", [(1, 64), (2, 64), (3, 64), (1, 16), (2, 16)])
 def test_long_folds_small_dims(rule, d):
     """Folds of 48 positions at d = 64 and 16: several staging rounds of fp32
