@@ -109,7 +109,8 @@ def test_single_round_matrix_core_folds(rule, m):
     """Folds of 17-32 positions at d = 128 through the fold kernel: one
     staging round on the matrix cores, in four-wave workgroups whose decay
     weights come from their second wave.  Deferred flushes of m = 24 / 32
-    (a partial and a full round), then eager commits that fill the buffer."""
+    (a partial and a full round), then eager commits and tree commits that
+    fill the buffer."""
     w = synth.workload(1, B=3, H=2, dk=128, dv=128, m=m, block_size=8, blocks_per_req=8, steps=2 * m + 4,
                        rule=rule, io="bf16", state_std=0.02)
     _say("single-round folds", w)
@@ -134,6 +135,18 @@ def test_single_round_matrix_core_folds(rule, m):
     rune.check_pool()
     rune.check_bookkeeping()
     assert rune.folds_checked > 0
+    # eager tree commits: kept rows move after the fold has read them
+    runt = Run(we)
+    t = 0
+    for call in range(12):
+        runt.decode(t)
+        t += 1
+        parent, leaf = synth.draft_tree(we, call, we.B, 8)
+        runt.verify_tree_commit(call, parent, leaf)
+        runt.check_effective_states()
+    runt.check_pool()
+    runt.check_bookkeeping()
+    assert runt.folds_checked > 0
 
 
 @pytest.mark.parametrize("rule,d", [(1, 64), (2, 64), (3, 64), (1, 16), (2, 16)])
